@@ -1,0 +1,139 @@
+"""Seeded synthetic inputs, shared by the GPU tests, the benchmark and the oracle
+checks.
+
+This module draws random numbers and encodes them as bf16 bit patterns. It
+holds none of the product's arithmetic, and neither the GPU library nor the
+oracle imports the other through it.
+
+Recipe (one GPU's share of the LLM projections the pages discuss; no trained
+weights exist here, so every operand is synthetic):
+
+* generator: numpy PCG64 ``default_rng(seed)`` with seed = 1000 * case + op,
+  op = 1 for A, 2 for B, 3 and 4 for the integer-valued A and B;
+* real-valued entries are drawn in float64, scaled in float64 and rounded
+  once to bf16 (round to nearest, ties to even);
+* N(0, s2) names the variance: N(0, 1/8192) has standard deviation 8192^-1/2,
+  which keeps every C entry near unit variance at K = 8192;
+* integer-valued entries are uniform on {-3, ..., 3}; they are exact in bf16
+  and every product sum is an exact integer, so the result is unique;
+* a column-major B is generated as its N x K row-major storage and used
+  through the transposed view.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """Round float64 to bf16 bits, once (nearest, ties to even).
+
+    Method: narrow to fp32 with round-to-odd (truncate, then set the last bit
+    if anything was dropped), then round that fp32 pattern to bf16 with
+    integer nearest-even rounding. fp32 keeps 16 more bits than bf16, so the
+    odd-rounded intermediate never creates a false tie: the two steps equal a
+    single rounding of the fp64 value. Inputs here are finite and far from the
+    fp32 subnormal and overflow ranges.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    t = x.astype(np.float32)
+    back = t.astype(np.float64)
+    away = np.abs(back) > np.abs(x)
+    u = t.view(np.uint32).copy()
+    u[away] -= np.uint32(1)          # step one fp32 ulp toward zero: truncation
+    inexact = back != x
+    u[inexact] |= np.uint32(1)       # sticky bit: round to odd
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    u = u + np.uint32(0x7FFF) + lsb
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def draw(rows: int, cols: int, dist: str, seed: int, scale: float = 1.0) -> np.ndarray:
+    """A rows x cols C-contiguous uint16 array of bf16 bit patterns."""
+    rng = np.random.default_rng(seed)
+    shape = (int(rows), int(cols))
+    if dist == "normal":
+        x = rng.standard_normal(shape) * float(scale)
+    elif dist == "uniform":
+        x = rng.uniform(-1.0, 1.0, shape) * float(scale)
+    elif dist == "int3":
+        x = rng.integers(-3, 4, shape).astype(np.float64)
+    else:
+        raise ValueError(f"unknown distribution {dist!r}")
+    return f64_to_bf16_bits(x)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    case: int              # seed family: seeds are 1000 * case + op
+    M: int
+    N: int
+    K: int
+    b_col_major: bool
+    outs: tuple            # output dtypes checked: "f32" and/or "bf16"
+    a_dist: str
+    b_dist: str
+    a_scale: float = 1.0
+    b_scale: float = 1.0
+    note: str = ""
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    def algorithmic_bytes(self, out: str) -> int:
+        """Each operand read once plus C written once."""
+        esz = 4 if out == "f32" else 2
+        return 2 * (self.M * self.K + self.K * self.N) + esz * self.M * self.N
+
+
+_S = 1.0 / np.sqrt(8192.0)
+
+WORKLOADS = {
+    "gemm256": Workload(
+        "gemm256", 1, 256, 256, 256, False, ("f32",), "uniform", "uniform",
+        note="256^3, U[-1,1] entries; integer {-3..3} variant gives an exact result"),
+    "square4096": Workload(
+        "square4096", 2, 4096, 4096, 4096, False, ("bf16", "f32"), "normal", "normal",
+        note="4096^3 square, N(0,1) entries, bf16 and fp32 outputs"),
+    "qkv_shard": Workload(
+        "qkv_shard", 3, 8192, 1280, 8192, False, ("f32",), "normal", "normal",
+        b_scale=_S,
+        note="attention QKV projection, one of 8 column shards: 8192 tokens x 8192 hidden -> 1280"),
+    "mlp_gate_up_shard": Workload(
+        "mlp_gate_up_shard", 4, 8192, 7168, 8192, True, ("bf16",), "normal", "normal",
+        b_scale=_S,
+        note="MLP gate+up projection shard, B stored column-major, bf16 output"),
+    "decode": Workload(
+        "decode", 5, 16, 28672, 8192, False, ("bf16",), "normal", "normal",
+        b_scale=_S,
+        note="decode-shaped skinny GEMM, 16 tokens, HBM-bound"),
+}
+
+
+@dataclass
+class Operands:
+    A: np.ndarray          # (M, K) uint16 view
+    B: np.ndarray          # (K, N) uint16 view (transposed view when column-major)
+    B_storage: np.ndarray  # the C-contiguous array that holds B
+
+
+def operands(w: Workload, integer: bool = False, M: int | None = None,
+             N: int | None = None, K: int | None = None) -> Operands:
+    """Seeded operands for workload ``w`` (optionally at another shape)."""
+    M = w.M if M is None else M
+    N = w.N if N is None else N
+    K = w.K if K is None else K
+    if integer:
+        A = draw(M, K, "int3", 1000 * w.case + 3)
+        Bs = draw(N, K, "int3", 1000 * w.case + 4) if w.b_col_major else \
+            draw(K, N, "int3", 1000 * w.case + 4)
+    else:
+        A = draw(M, K, w.a_dist, 1000 * w.case + 1, w.a_scale)
+        Bs = draw(N, K, w.b_dist, 1000 * w.case + 2, w.b_scale) if w.b_col_major else \
+            draw(K, N, w.b_dist, 1000 * w.case + 2, w.b_scale)
+    B = Bs.T if w.b_col_major else Bs
+    return Operands(A, B, Bs)
