@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the tile-partitioned GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one C = A.B over the headline workload's synthetic operands (the
+planner, the owned-tile map, the LDS-staged K loop, MFMA and the owned-tile
+store all run in it); the decode-shaped workload exercises the skinny
+HBM-streaming kernel and is reported on the same line. Inputs are resident in
+HBM before timing starts; each step uses the next of several copies of the
+operands so that the 256 MB last-level cache cannot hold them between steps.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s & % MFMA peak (large); HBM GB/s & % peak (decode shape)"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+MIN_ROTATION_BYTES = 600 << 20  # > 2x the 256 MB last-level cache
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mlp_gate_up_shard")
+    ap.add_argument("--secondary", default="qkv_shard,square4096,decode,gemm256",
+                    help="comma-separated extra workloads reported on the same line ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time for the oracle baseline sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (for counter calibration)")
+    return ap.parse_args()
+
+
+class Bench:
+    def __init__(self, torch, tg, synth):
+        self.torch, self.tg, self.synth = torch, tg, synth
+        self.g = tg.TileGemm(0)
+
+    def make(self, w, out):
+        torch, synth = self.torch, self.synth
+        t0 = time.time()
+        ops = synth.operands(w)
+        A = torch.from_numpy(ops.A.view(np.int16)).cuda().view(torch.bfloat16)
+        Bs = torch.from_numpy(ops.B_storage.view(np.int16)).cuda().view(torch.bfloat16)
+        odt = torch.float32 if out == "f32" else torch.bfloat16
+        set_bytes = w.algorithmic_bytes(out)
+        copies = max(1, min(8, -(-MIN_ROTATION_BYTES // set_bytes)))
+        sets = []
+        for i in range(copies):
+            Ai = A if i == 0 else A.clone()
+            Bi = Bs if i == 0 else Bs.clone()
+            Bv = Bi.t() if w.b_col_major else Bi
+            Ci = torch.empty((w.M, w.N), dtype=odt, device="cuda")
+            sets.append((Ai, Bv, Ci))
+        torch.cuda.synchronize()
+        log(f"[bench] {w.name}: {w.M}x{w.N}x{w.K} out={out} copies={copies} "
+            f"(operands ready in {time.time() - t0:.1f}s)")
+        return ops, sets
+
+    def time_workload(self, w, out, steps, warmup):
+        torch = self.torch
+        ops, sets = self.make(w, out)
+        g = self.g
+        for i in range(warmup):
+            A, B, C = sets[i % len(sets)]
+            g(A, B, C)
+        torch.cuda.synchronize()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            A, B, C = sets[i % len(sets)]
+            starts[i].record()
+            g(A, B, C)
+            ends[i].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms per launch
+        plan = self.tg.tile_gemm_plan(w.M, w.N, w.K, w.b_col_major, 256)
+        res = {
+            "workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+            "b_layout": "column-major" if w.b_col_major else "row-major", "out": out,
+            "wall_ms_per_step": 1e3 * wall / steps,
+            "kernel_ms_mean": float(per.mean()), "kernel_ms_median": float(np.median(per)),
+            "kernel_ms_min": float(per.min()), "kernel_ms_max": float(per.max()),
+            "flop": w.flops, "bytes": w.algorithmic_bytes(out),
+            "plan": {"variant": "tile" if plan.variant == 1 else "skinny", "bm": plan.bm,
+                     "bn": plan.bn, "grid": int(plan.grid), "k_split": plan.k_split},
+        }
+        mean_s = res["kernel_ms_mean"] * 1e-3
+        res["tflops"] = w.flops / mean_s / 1e12
+        res["gbs"] = w.algorithmic_bytes(out) / mean_s / 1e9
+        res["frac_mfma"] = res["tflops"] / PEAK_BF16_TFLOPS
+        res["frac_hbm"] = res["gbs"] / PEAK_HBM_GBS
+        log(f"[bench] {w.name}: mean {res['kernel_ms_mean'] * 1e3:.1f} us "
+            f"(median {res['kernel_ms_median'] * 1e3:.1f}, min {res['kernel_ms_min'] * 1e3:.1f}) "
+            f"-> {res['tflops']:.1f} TFLOP/s ({100 * res['frac_mfma']:.1f}% MFMA), "
+            f"{res['gbs']:.0f} GB/s ({100 * res['frac_hbm']:.1f}% HBM)")
+        del sets
+        torch.cuda.empty_cache()
+        return ops, res
+
+
+def roofline(res, hbm_bound):
+    if hbm_bound:
+        return {"bound": "hbm", "achieved": round(res["gbs"], 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(res["frac_hbm"], 4), "traffic": None}
+    return {"bound": "mfma", "achieved": round(res["tflops"], 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(res["frac_mfma"], 4), "traffic": None}
+
+
+def cpu_baseline(w, ops, seconds):
+    """The fp64 triple-loop oracle, as it stands, on the first rows of the same
+    operands; rows chosen for roughly `seconds` of CPU time."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    oracle.build(force=False)
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.gemm(ops.A[:rows], ops.B, want_d=False, threads=threads)
+        return time.perf_counter() - t0
+
+    # rows run in parallel, one per thread: two probes of one and three rows
+    # per thread give the cost of a round of rows and the fixed cost (the
+    # decode of B); then time whole rounds for about `seconds`
+    t1, t3 = run(threads), run(3 * threads)
+    per_round = max((t3 - t1) / 2, 1e-6)
+    fixed = max(t1 - per_round, 0.0)
+    rounds = int(max(1, (seconds - fixed) / per_round))
+    rows = int(min(w.M, rounds * threads))
+    t = run(rows)
+    flop = 2.0 * rows * w.N * w.K
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(flop / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {rows} of {w.M} rows of {w.name} ({w.M}x{w.N}x{w.K}), fp64 triple "
+                      f"loop incl. its B decode, C only, {t:.2f}s wall on {cpu} "
+                      f"({platform.machine()})",
+            "seconds": round(t, 3)}
+
+
+def copy_calibration(torch, mib):
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {mib} MiB read + {mib} MiB written")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this library has no "
+              "multi-GPU path", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    import tile_partitioned_dense_amd as tg
+    from tile_partitioned_dense_amd import synth
+    tg.load_library()
+
+    b = Bench(torch, tg, synth)
+    head = synth.WORKLOADS[args.workload]
+    head_out = head.outs[0]
+    ops, res = b.time_workload(head, head_out, args.steps, args.warmup)
+    secondary = []
+    for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
+        w = synth.WORKLOADS[name]
+        _, r = b.time_workload(w, w.outs[0], args.steps, args.warmup)
+        r["roofline"] = roofline(r, hbm_bound=(name == "decode"))
+        secondary.append(r)
+    if args.copy_calibration_mib:
+        copy_calibration(torch, args.copy_calibration_mib)
+
+    hbm_head = head.name == "decode"
+    line = {
+        "metric": METRIC,
+        "value": round(res["gbs"] if hbm_head else res["tflops"], 2),
+        "unit": "GB/s" if hbm_head else "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["wall_ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": head.name, "M": head.M, "N": head.N, "K": head.K,
+                   "b_layout": res["b_layout"], "out": head_out, "parallelism": "none (1 GPU)",
+                   "plan": res["plan"]},
+        "roofline": roofline(res, hbm_head),
+        "kernel_ms": {k: round(res[k], 5) for k in
+                      ("kernel_ms_mean", "kernel_ms_median", "kernel_ms_min", "kernel_ms_max")},
+        "secondary": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+                      for r in secondary],
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample of the headline workload")
+        line["cpu_baseline"] = cpu_baseline(head, ops, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

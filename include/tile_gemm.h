@@ -1,0 +1,211 @@
+/*
+ * tile_gemm.h -- C ABI of the tile-partitioned dense GEMM for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Operation: C = A . B with bf16 inputs, fp32 accumulation and an fp32 or
+ * bf16 output. This is the dense product the pages measure at
+ * M = N = K = 8192 ("GPU speed, without leaving Rust's safety model",
+ * section "Safety without a visible tax"), built on the partition discipline
+ * of the same page (sections "Ownership crosses the launch boundary" and
+ * "The useful boundary"): the output is split into disjoint tiles before
+ * launch, each workgroup exclusively owns one tile and is the only writer of
+ * it, and A and B are shared read-only views.
+ *
+ * Numerics: every output element is the sum of its K products accumulated in
+ * fp32 in one fixed ascending-k order that depends only on the shape and the
+ * B layout, never on the output type, timing or run. There is no split-K and
+ * no atomic accumulation, so results are bit-identical from run to run, and
+ * a bf16 output is the round-to-nearest-even of the fp32 result of the same
+ * shape.
+ *
+ * Threading: a handle is read-only after tile_gemm_create, so concurrent
+ * tile_gemm_run calls on different streams may share it.
+ */
+#ifndef TILE_GEMM_H
+#define TILE_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TILE_GEMM_ABI_VERSION 1
+
+/* Opaque, host-side handle. */
+typedef struct tile_gemm_handle* tile_gemm_t;
+
+typedef enum {
+  TILE_GEMM_OK = 0,
+  TILE_GEMM_ERR_NULL_ARG = 1,   /* a required pointer is NULL */
+  TILE_GEMM_ERR_BAD_SHAPE = 2,  /* M, N or K negative, or too large for 32-bit tile indices */
+  TILE_GEMM_ERR_BAD_STRIDE = 3, /* a layout other than the accepted ones below */
+  TILE_GEMM_ERR_MISALIGNED = 4, /* base pointer or leading dimension not 16-byte aligned */
+  TILE_GEMM_ERR_ALIAS = 5,      /* C's bytes overlap A's or B's */
+  TILE_GEMM_ERR_DTYPE = 6,      /* unknown tile_gemm_dtype_t */
+  TILE_GEMM_ERR_DEVICE = 7,     /* no such device, not gfx950, or not the current device */
+  TILE_GEMM_ERR_HIP = 8         /* the HIP runtime refused a call or a launch */
+} tile_gemm_status_t;
+
+/* Input is always bf16 with fp32 accumulation; the enum picks the output. */
+typedef enum {
+  TILE_GEMM_BF16_TO_F32 = 0,
+  TILE_GEMM_BF16_TO_BF16 = 1
+} tile_gemm_dtype_t;
+
+/*
+ * Strides in elements (not bytes). Element (i, k) of A is A[i*a_m + k*a_k],
+ * element (k, j) of B is B[k*b_k + j*b_n], element (i, j) of C is
+ * C[i*c_m + j*c_n]. Accepted layouts (anything else is
+ * TILE_GEMM_ERR_BAD_STRIDE):
+ *   A: a_k == 1 and a_m >= K                       (row-major)
+ *   B: b_n == 1 and b_k >= N                       (row-major), or
+ *      b_k == 1 and b_n >= K                       (column-major)
+ *   C: c_n == 1 and c_m >= N                       (row-major)
+ */
+typedef struct {
+  int64_t a_m, a_k;
+  int64_t b_k, b_n;
+  int64_t c_m, c_n;
+} tile_gemm_strides_t;
+
+/*
+ * One-time set-up for `device` (a HIP device ordinal): checks that it is a
+ * gfx950 and records its compute-unit count, which the planner uses. Allocates
+ * no device memory. On success *out holds a new handle; on failure *out is
+ * set to NULL (when out is not NULL).
+ * Errors: TILE_GEMM_ERR_NULL_ARG (out == NULL), TILE_GEMM_ERR_DEVICE.
+ */
+tile_gemm_status_t tile_gemm_create(tile_gemm_t* out, int device);
+
+/*
+ * Enqueue C := A . B on `stream` (a hipStream_t; NULL means the default
+ * stream) and return without waiting. A and B are device pointers to bf16
+ * data, C a device pointer to fp32 or bf16 data per `dtype`; all three must be
+ * 16-byte aligned, and each leading dimension (a_m, the non-unit B stride,
+ * c_m) times the element size must be a multiple of 16 bytes.
+ *
+ * Ownership: A and B are borrowed read-only and C exclusively until the
+ * stream reaches this work; the caller must not free, write (or, for C, read)
+ * them before then. The library neither frees nor retains caller memory.
+ * tile_gemm_run allocates nothing and never synchronises, so it may be
+ * captured into a HIP graph.
+ *
+ * Shapes: M = 0 or N = 0 is a successful no-op (pointers are not checked);
+ * K = 0 writes zeros to C (A and B are not read: they may be NULL and their
+ * strides are not checked). M, N and K must be below 2^31.
+ *
+ * Errors are returned before anything is enqueued and leave C untouched:
+ * NULL_ARG, BAD_SHAPE, BAD_STRIDE, MISALIGNED, ALIAS, DTYPE, DEVICE (the
+ * calling thread's current device is not the handle's). A launch the
+ * runtime rejects returns TILE_GEMM_ERR_HIP. Faults during execution surface
+ * at the caller's next synchronisation of the stream.
+ */
+tile_gemm_status_t tile_gemm_run(tile_gemm_t h, const void* A, const void* B, void* C,
+                                 int64_t M, int64_t N, int64_t K,
+                                 const tile_gemm_strides_t* strides,
+                                 tile_gemm_dtype_t dtype, void* stream);
+
+/* Release a handle (host memory only). NULL is accepted and returns OK. */
+tile_gemm_status_t tile_gemm_destroy(tile_gemm_t h);
+
+/* Static text for a status code; never NULL. */
+const char* tile_gemm_status_str(tile_gemm_status_t s);
+
+/*
+ * Text naming the argument (and axis) behind the last non-OK status returned
+ * on the calling thread, in the spirit of the pages' record-time shape
+ * contracts, which name the parameter, axis, expected and actual extent
+ * ("Rust Compute Kernels", section "Shape contracts"). Empty when none.
+ */
+const char* tile_gemm_last_error_detail(void);
+
+/* ---------------------------------------------------------------------- */
+/* Host-only introspection. No device is touched; these work without a GPU. */
+
+/*
+ * The argument checks tile_gemm_run performs before any launch, in the same
+ * order and with the same results (except the device check, which needs a
+ * handle).
+ */
+tile_gemm_status_t tile_gemm_check_args(const void* A, const void* B, const void* C,
+                                        int64_t M, int64_t N, int64_t K,
+                                        const tile_gemm_strides_t* strides,
+                                        tile_gemm_dtype_t dtype);
+
+/* Kernel variants the planner chooses between. */
+typedef enum {
+  TILE_GEMM_VARIANT_NONE = 0,   /* M == 0 or N == 0: nothing to launch */
+  TILE_GEMM_VARIANT_TILE = 1,   /* LDS-staged MFMA tile kernel */
+  TILE_GEMM_VARIANT_SKINNY = 2  /* HBM-streaming kernel for M <= 64 */
+} tile_gemm_variant_t;
+
+/*
+ * The launch plan for a shape: a pure function of (M, N, K, B layout,
+ * compute-unit count). The output type never changes it.
+ *   tile kernel:   each workgroup owns a bm x bn tile; grid = tiles_m*tiles_n.
+ *   skinny kernel: each workgroup owns rows [0, M) x bn columns; the waves of
+ *                  one workgroup split K and combine their partial sums in a
+ *                  fixed order; grid = tiles_n, tiles_m = 1.
+ */
+typedef struct {
+  int32_t variant;      /* tile_gemm_variant_t */
+  int32_t config;       /* index into the compiled configuration table */
+  int32_t bm, bn, bk;   /* owned tile rows, columns; K slab per step */
+  int32_t threads;      /* threads per workgroup */
+  int32_t lds_bytes;    /* static LDS per workgroup */
+  int32_t tiles_m, tiles_n;
+  int32_t group_m;      /* tile rows per raster group */
+  int32_t xcds;         /* dispatch remap width (XCD count), 1 = identity */
+  int32_t k_split;      /* skinny kernel: waves sharing K inside one workgroup */
+  int64_t grid;         /* workgroups launched */
+} tile_gemm_plan_t;
+
+/* b_col_major: 0 for row-major B, 1 for column-major B. cu_count > 0. */
+tile_gemm_status_t tile_gemm_plan(int64_t M, int64_t N, int64_t K, int b_col_major,
+                                  int cu_count, tile_gemm_plan_t* out);
+
+/*
+ * The owned tile of workgroup `wg` under `plan`: rows [m0, m0 + rows) and
+ * columns [n0, n0 + cols) of C, clipped to M x N. This is the very function
+ * the kernels run, compiled for the host, so tests can check that the map is
+ * a bijection onto the tiles and that the tiles exactly cover C.
+ */
+tile_gemm_status_t tile_gemm_tile_of(const tile_gemm_plan_t* plan, int64_t M, int64_t N,
+                                     int64_t wg, int64_t* m0, int64_t* n0,
+                                     int64_t* rows, int64_t* cols);
+
+/* ---------------------------------------------------------------------- */
+/* Test instrumentation. Same kernels, extra bookkeeping; not for production. */
+
+enum {
+  TILE_GEMM_DEBUG_COUNT_WRITES = 1, /* each element store also adds 1 to counts[i*N + j] */
+  TILE_GEMM_DEBUG_COLLIDE = 2       /* negative control: workgroup 1 takes workgroup 0's tile */
+};
+/* Run a given compiled configuration instead of the planner's choice, so tests
+ * can cover every configuration at small sizes. A forced skinny configuration
+ * needs M <= its row capacity (16 * row groups). */
+#define TILE_GEMM_DEBUG_FORCE_TILE(c) ((((c) + 1) & 0xff) << 8)
+#define TILE_GEMM_DEBUG_FORCE_SKINNY(c) ((((c) + 1) & 0xff) << 16)
+
+/*
+ * As tile_gemm_run, with instrumentation. `counts` is a device array of M*N
+ * uint32 (row-major, N columns) that the caller zeroes; it is required when
+ * TILE_GEMM_DEBUG_COUNT_WRITES is set and ignored otherwise. Every element of
+ * a correct run has count 1; TILE_GEMM_DEBUG_COLLIDE deliberately breaks the
+ * tile map (two workgroups own one tile, another tile has no owner) so tests
+ * can show that their checks catch a partition error. The collision needs at
+ * least two tiles and applies to the tile kernel only. Unknown flag bits or an
+ * unknown forced configuration return TILE_GEMM_ERR_BAD_SHAPE.
+ */
+tile_gemm_status_t tile_gemm_run_debug(tile_gemm_t h, const void* A, const void* B, void* C,
+                                       int64_t M, int64_t N, int64_t K,
+                                       const tile_gemm_strides_t* strides,
+                                       tile_gemm_dtype_t dtype, void* stream,
+                                       uint32_t* counts, int flags);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILE_GEMM_H */

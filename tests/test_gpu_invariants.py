@@ -1,0 +1,152 @@
+"""GPU invariants of the partition discipline:
+
+* bit-identical results over 10 runs (the pages report 17-35% of elements
+  differing run to run when two tile programs share a destination; here the
+  fraction must be 0) -- "GPU speed, without leaving Rust's safety model",
+  section "Disjointness outside. Ordering inside.";
+* every element written exactly once (a test-only write counter) and no NaN
+  sentinel left behind;
+* a deliberately colliding tile map (negative control) is caught by the same
+  checks;
+* argument errors return before launch and leave C untouched;
+* work goes to the caller's stream.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import tile_partitioned_dense_amd as tg
+from tile_partitioned_dense_amd import synth
+
+from gpu_helpers import Case, host_out, workload_case
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    with tg.TileGemm(0) as gg:
+        yield gg
+
+
+def _as_int(C):
+    return C.view(torch.int32) if C.dtype == torch.float32 else C.view(torch.int16)
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+def test_ten_runs_bit_identical(g, name):
+    w, ops, A, B = workload_case(name)
+    dt = torch.bfloat16 if "bf16" in w.outs and "f32" not in w.outs else torch.float32
+    print(f"[determinism {name} {dt}]", flush=True)
+    ref = torch.empty((w.M, w.N), dtype=dt, device="cuda")
+    g(A, B, ref)
+    scratch = torch.empty_like(ref)
+    differing = 0
+    for _ in range(10):
+        scratch.fill_(float("nan"))
+        g(A, B, scratch)
+        differing += int((_as_int(scratch) != _as_int(ref)).sum().item())
+    torch.cuda.synchronize()
+    frac = differing / (10 * ref.numel())
+    print(f"  fraction of elements differing across 10 runs: {frac}", flush=True)
+    assert differing == 0
+
+
+def _counts_run(g, case, dt, flags):
+    store, C = case.out(dt)
+    counts = torch.zeros((case.M, case.N), dtype=torch.int32, device="cuda")
+    g.run_debug(case.A_dev, case.B_dev, C, counts=counts, flags=flags)
+    torch.cuda.synchronize()
+    return store, C, counts
+
+
+@pytest.mark.parametrize("M,N,K,bcol", [
+    (1000, 1000, 200, False), (1000, 1000, 200, True), (40, 3000, 500, False),
+    (40, 3000, 500, True), (16, 28672, 256, False), (8192, 1280, 64, False),
+    (8192, 7168, 64, True), (4096, 4096, 64, False), (256, 256, 256, False)])
+def test_every_element_written_once(g, M, N, K, bcol):
+    print(f"[write-once {M}x{N}x{K} bcol={bcol}]", flush=True)
+    case = Case(M, N, K, bcol, seed=7, pad=8)
+    for dt in (torch.float32, torch.bfloat16):
+        store, C, counts = _counts_run(g, case, dt, tg.DEBUG_COUNT_WRITES)
+        assert int(counts.min()) == 1 and int(counts.max()) == 1
+        assert not torch.isnan(C.float()).any()
+        assert torch.isnan(store[:, N:].float()).all()
+
+
+@pytest.mark.parametrize("cfg", range(tg.N_TILE_CONFIGS))
+def test_every_config_writes_once(g, cfg):
+    case = Case(300, 500, 70, False, seed=cfg)
+    store, C, counts = _counts_run(g, case, torch.float32,
+                                   tg.DEBUG_COUNT_WRITES | tg.DEBUG_FORCE_TILE(cfg))
+    assert int(counts.min()) == 1 and int(counts.max()) == 1
+
+
+@pytest.mark.parametrize("cfg", range(tg.N_SKINNY_CONFIGS))
+def test_every_skinny_config_writes_once(g, cfg):
+    case = Case(13, 1500, 333, False, seed=cfg)
+    store, C, counts = _counts_run(g, case, torch.float32,
+                                   tg.DEBUG_COUNT_WRITES | tg.DEBUG_FORCE_SKINNY(cfg))
+    assert int(counts.min()) == 1 and int(counts.max()) == 1
+
+
+def test_negative_control_collision_is_caught(g):
+    """Workgroup 1 is made to take workgroup 0's tile: one tile is written
+    twice and another never. The write counter and the sentinel both see it."""
+    case = Case(1024, 1024, 128, False, seed=3)
+    store, C, counts = _counts_run(g, case, torch.float32,
+                                   tg.DEBUG_COUNT_WRITES | tg.DEBUG_COLLIDE)
+    cnt = counts.cpu().numpy()
+    assert cnt.max() == 2 and cnt.min() == 0
+    plan = tg.tile_gemm_plan(1024, 1024, 128, False, 256)
+    assert (cnt == 2).sum() == plan.bm * plan.bn == (cnt == 0).sum()
+    assert torch.isnan(C).sum().item() == plan.bm * plan.bn
+
+
+def test_errors_leave_output_untouched(g):
+    case = Case(128, 128, 64, False, seed=5)
+    store, C = case.out(torch.float32, fill=7.0)
+    s = tg.Strides(case.A_dev.stride(0), 1, case.B_dev.stride(0), 1, C.stride(0), 1)
+    h = g.handle
+    # misaligned A pointer
+    st = tg.tile_gemm_run(h, case.A_dev.data_ptr() + 2, case.B_dev.data_ptr(), C.data_ptr(),
+                          128, 128, 64, s, tg.Dtype.BF16_TO_F32, None, check=False)
+    assert st == tg.Status.ERR_MISALIGNED
+    # C aliasing A
+    st = tg.tile_gemm_run(h, case.A_dev.data_ptr(), case.B_dev.data_ptr(),
+                          case.A_dev.data_ptr(), 128, 128, 64, s, tg.Dtype.BF16_TO_F32, None,
+                          check=False)
+    assert st == tg.Status.ERR_ALIAS
+    # unknown dtype
+    st = tg.tile_gemm_run(h, case.A_dev.data_ptr(), case.B_dev.data_ptr(), C.data_ptr(),
+                          128, 128, 64, s, 5, None, check=False)
+    assert st == tg.Status.ERR_DTYPE
+    torch.cuda.synchronize()
+    assert bool((store == 7.0).all())
+
+
+def test_runs_on_the_callers_stream(g):
+    case = Case(512, 512, 256, False, seed=6)
+    Cr, _ = case.ref()
+    side = torch.cuda.Stream()
+    store, C = case.out(torch.float32)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        g(case.A_dev, case.B_dev, C)           # binding picks up the current stream
+    side.synchronize()
+    out = host_out(C)
+    assert np.all(np.abs(out - Cr) <= 1e-5 * case.ref()[1])
+
+
+def test_handle_checks_current_device(g):
+    lib = tg.load_library()
+    h = ctypes.c_void_p()
+    assert lib.tile_gemm_create(ctypes.byref(h), 10_000) == tg.Status.ERR_DEVICE
+    assert lib.tile_gemm_create(ctypes.byref(h), 0) == tg.Status.OK
+    assert lib.tile_gemm_destroy(h) == tg.Status.OK

@@ -1,0 +1,174 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Acceptance, per element: fp32 output within 1e-5 * (|A|.|B|)_ij of the
+oracle; bf16 output inside the RNE bracket of that interval; integer-valued
+inputs exactly equal. Every output starts as a NaN sentinel (padding columns
+included), so a missed element or a write outside the owned region shows.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import tile_partitioned_dense_amd as tg
+from tile_partitioned_dense_amd import synth
+
+from gpu_helpers import Case, check, host_out, workload_case
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    with tg.TileGemm(0) as gg:
+        yield gg
+
+
+def _run(g, case, dtype, flags=0, counts=None):
+    store, C = case.out(dtype)
+    if flags:
+        g.run_debug(case.A_dev, case.B_dev, C, counts=counts, flags=flags)
+    else:
+        g(case.A_dev, case.B_dev, C)
+    torch.cuda.synchronize()
+    return store, C
+
+
+def _assert_padding_untouched(store, N):
+    pad = store[:, N:]
+    if pad.numel():
+        assert torch.isnan(pad.float()).all(), "a store landed outside the owned columns"
+
+
+def _parity(g, case, dtype, flags=0, integer=False):
+    store, C = _run(g, case, dtype, flags)
+    out = host_out(C)
+    Cr, Dr = case.ref()
+    rep = check(out, Cr, Dr, dtype == torch.bfloat16, integer)
+    assert rep.ok, f"{case.M}x{case.N}x{case.K} bcol={case.bcol} {dtype}: {rep}"
+    _assert_padding_untouched(store, case.N)
+    return out
+
+
+# ------------------------------------------------ every compiled configuration
+
+def tile_shape(cfg):
+    bm, bn = {0: (256, 256), 1: (256, 224), 2: (256, 160), 3: (128, 256), 4: (256, 128),
+              5: (128, 128), 6: (64, 64)}[cfg]
+    return 2 * bm + 37, 2 * bn + 19     # several tiles plus a ragged edge in M and N
+
+
+@pytest.mark.parametrize("cfg", range(tg.N_TILE_CONFIGS))
+@pytest.mark.parametrize("bcol", [False, True], ids=["Brow", "Bcol"])
+def test_tile_configs(g, cfg, bcol):
+    M, N = tile_shape(cfg)
+    print(f"[tile cfg {cfg} bcol={bcol} {M}x{N}x200]", flush=True)
+    case = Case(M, N, 200, bcol, seed=cfg, pad=8)     # K = 3 slabs + a partial one
+    for dt in (torch.float32, torch.bfloat16):
+        _parity(g, case, dt, flags=tg.DEBUG_FORCE_TILE(cfg))
+
+
+@pytest.mark.parametrize("cfg", range(tg.N_TILE_CONFIGS))
+def test_tile_configs_integer_k_tail(g, cfg):
+    """Integer data, K not a multiple of 8: exact, and the K tail is masked."""
+    M, N = tile_shape(cfg)
+    print(f"[tile int cfg {cfg} {M}x{N}x131]", flush=True)
+    for bcol in (False, True):
+        case = Case(M, N, 131, bcol, dist="int3", seed=10 + cfg)
+        for dt in (torch.float32, torch.bfloat16):
+            _parity(g, case, dt, flags=tg.DEBUG_FORCE_TILE(cfg), integer=True)
+
+
+SKINNY_MG = {0: 1, 1: 1, 2: 2, 3: 2, 4: 4, 5: 4}
+
+
+@pytest.mark.parametrize("cfg", range(tg.N_SKINNY_CONFIGS))
+@pytest.mark.parametrize("bcol", [False, True], ids=["Brow", "Bcol"])
+def test_skinny_configs(g, cfg, bcol):
+    mg = SKINNY_MG[cfg]
+    for M in sorted({1, 5, 16 * mg - 3, 16 * mg}):
+        N, K = 16 * 8 * 5 + 13, 8 * 32 * 3 + 24 + 5      # ragged N; K tail inside a 32-block
+        print(f"[skinny cfg {cfg} bcol={bcol} {M}x{N}x{K}]", flush=True)
+        case = Case(M, N, K, bcol, seed=20 + cfg, pad=8)
+        for dt in (torch.float32, torch.bfloat16):
+            _parity(g, case, dt, flags=tg.DEBUG_FORCE_SKINNY(cfg))
+        icase = Case(M, N, K, bcol, dist="int3", seed=30 + cfg)
+        _parity(g, icase, torch.float32, flags=tg.DEBUG_FORCE_SKINNY(cfg), integer=True)
+
+
+# ------------------------------------------------------------- planner path
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (17, 33, 65), (257, 257, 257), (1000, 1000, 1000),
+                                   (65, 300, 64), (64, 1, 9), (3, 5000, 300), (300, 7, 48),
+                                   (4096, 256, 512), (130, 130, 0)])
+@pytest.mark.parametrize("bcol", [False, True], ids=["Brow", "Bcol"])
+def test_edge_shapes(g, M, N, K, bcol):
+    print(f"[edge {M}x{N}x{K} bcol={bcol}]", flush=True)
+    case = Case(M, N, K, bcol, seed=M + N + K)
+    for dt in (torch.float32, torch.bfloat16):
+        _parity(g, case, dt)     # K == 0: D == 0, so the check demands exact zeros
+    icase = Case(M, N, K, bcol, dist="int3", seed=M + N + K + 1)
+    _parity(g, icase, torch.float32, integer=True)
+
+
+def test_empty_is_noop(g):
+    A = torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros(64, 64, dtype=torch.bfloat16, device="cuda")
+    C = torch.zeros(0, 64, dtype=torch.float32, device="cuda")
+    assert g(A, B, C) == tg.Status.OK
+
+
+# ----------------------------------------------------------- full workloads
+
+WORKLOADS = sorted(synth.WORKLOADS)
+
+
+def _run_workload(g, A, B, w, dtype):
+    C = torch.full((w.M, w.N), float("nan"), dtype=dtype, device="cuda")
+    g(A, B, C)
+    torch.cuda.synchronize()
+    return C
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_workload_parity(g, name):
+    w, ops, A, B = workload_case(name)
+    print(f"[workload {name} {w.M}x{w.N}x{w.K}]", flush=True)
+    outs = {dt: host_out(_run_workload(g, A, B, w, dt))
+            for dt in (torch.float32, torch.bfloat16)}
+    Cr, Dr = oracle.gemm_blas(ops.A, ops.B)
+    for dt, out in outs.items():
+        rep = check(out, Cr, Dr, dt == torch.bfloat16)
+        assert rep.ok, f"{name} {dt}: {rep}"
+        print(f"  {dt}: max |g-C|/D = {rep.max_ratio:.3e}", flush=True)
+    # sampled elements against the plain triple loop (one element at a time)
+    rng = np.random.default_rng(9)
+    ii = np.concatenate([rng.integers(0, w.M, 400), [0, w.M - 1, 0, w.M - 1]])
+    jj = np.concatenate([rng.integers(0, w.N, 400), [0, 0, w.N - 1, w.N - 1]])
+    c, d = oracle.gemm_at(ops.A, ops.B, ii, jj)
+    rep = oracle.check_f32(outs[torch.float32][ii, jj], c, d)
+    assert rep.ok, rep
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_workload_integer_exact(g, name):
+    w, ops, A, B = workload_case(name, integer=True)
+    print(f"[workload int {name}]", flush=True)
+    Cr, _ = oracle.gemm_blas(ops.A, ops.B, want_d=False)
+    for dt in (torch.float32, torch.bfloat16):
+        out = host_out(_run_workload(g, A, B, w, dt))
+        rep = oracle.check_exact(out, Cr, dt == torch.bfloat16)
+        assert rep.ok, f"{name} {dt}: {rep}"
+
+
+def test_bf16_output_is_rne_of_fp32_output(g):
+    """One shape in both output modes: same plan, same K order, so the bf16
+    result is the round-to-nearest-even of the fp32 result, bitwise."""
+    w, ops, A, B = workload_case("square4096")
+    f32 = host_out(_run_workload(g, A, B, w, torch.float32))
+    b16 = host_out(_run_workload(g, A, B, w, torch.bfloat16))
+    assert np.array_equal(b16, oracle.rne_bf16(f32.astype(np.float64)))

@@ -1,0 +1,125 @@
+"""Host-only checks of the C ABI: the library loads and exports every entry
+point the header declares, argument checks return the documented codes, and
+create refuses a machine without a gfx950. No compute is launched here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import tile_partitioned_dense_amd as tg
+from tile_partitioned_dense_amd.binding import Dtype, Status, Strides
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tile_gemm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b(tile_gemm_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tg.load_library()
+    names = declared_functions()
+    assert len(names) >= 9, names
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    for s in Status:
+        txt = tg.tile_gemm_status_str(s)
+        assert isinstance(txt, str) and txt
+    assert tg.tile_gemm_status_str(99) == "unknown status"
+
+
+def test_create_without_gfx950_fails_cleanly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible; covered by the GPU tests")
+    lib = tg.load_library()
+    h = ctypes.c_void_p(1234)
+    st = lib.tile_gemm_create(ctypes.byref(h), 0)
+    assert st == Status.ERR_DEVICE
+    assert h.value is None
+    assert "device" in tg.last_error_detail()
+    assert lib.tile_gemm_create(None, 0) == Status.ERR_NULL_ARG
+
+
+def test_destroy_null_is_ok_and_run_null_handle():
+    lib = tg.load_library()
+    assert lib.tile_gemm_destroy(None) == Status.OK
+    s = Strides(8, 1, 8, 1, 8, 1)
+    st = lib.tile_gemm_run(None, 16, 16, 4096, 4, 4, 4, ctypes.byref(s), 0, None)
+    assert st == Status.ERR_NULL_ARG
+
+
+# --- argument checks (pointers are plain aligned integers; nothing is touched)
+A0, B0, C0 = 0x100000, 0x200000, 0x300000
+
+
+def chk(A=A0, B=B0, C=C0, M=64, N=64, K=64, s=(64, 1, 64, 1, 64, 1), dtype=Dtype.BF16_TO_F32):
+    return tg.tile_gemm_check_args(A, B, C, M, N, K, s, dtype)
+
+
+def test_check_args_ok_layouts():
+    assert chk() == Status.OK
+    assert chk(s=(64, 1, 1, 64, 64, 1)) == Status.OK           # column-major B
+    assert chk(s=(72, 1, 80, 1, 96, 1)) == Status.OK           # padded leading dims
+    assert chk(dtype=Dtype.BF16_TO_BF16) == Status.OK
+    assert chk(M=0, A=0, B=0, C=0) == Status.OK                # empty: pointers unchecked
+    assert chk(N=0, A=0, B=0, C=0) == Status.OK
+    assert chk(K=0, s=(0, 1, 64, 1, 64, 1)) == Status.OK       # K = 0 writes zeros
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=7), Status.ERR_DTYPE),
+    (dict(M=-1), Status.ERR_BAD_SHAPE),
+    (dict(K=-3), Status.ERR_BAD_SHAPE),
+    (dict(N=1 << 31), Status.ERR_BAD_SHAPE),
+    (dict(A=0), Status.ERR_NULL_ARG),
+    (dict(B=0), Status.ERR_NULL_ARG),
+    (dict(C=0), Status.ERR_NULL_ARG),
+    (dict(s=(64, 2, 64, 1, 64, 1)), Status.ERR_BAD_STRIDE),    # A not K-contiguous
+    (dict(s=(32, 1, 64, 1, 64, 1)), Status.ERR_BAD_STRIDE),    # a_m < K
+    (dict(s=(64, 1, 32, 1, 64, 1)), Status.ERR_BAD_STRIDE),    # b_k < N
+    (dict(s=(64, 1, 1, 32, 64, 1)), Status.ERR_BAD_STRIDE),    # b_n < K
+    (dict(s=(64, 1, 64, 2, 64, 1)), Status.ERR_BAD_STRIDE),    # B neither layout
+    (dict(s=(64, 1, 64, 1, 64, 2)), Status.ERR_BAD_STRIDE),    # C not row-major
+    (dict(s=(64, 1, 64, 1, 32, 1)), Status.ERR_BAD_STRIDE),    # c_m < N
+    (dict(A=A0 + 2), Status.ERR_MISALIGNED),
+    (dict(B=B0 + 8), Status.ERR_MISALIGNED),
+    (dict(C=C0 + 4), Status.ERR_MISALIGNED),
+    (dict(K=60, s=(60, 1, 64, 1, 64, 1)), Status.ERR_MISALIGNED),   # a_m*2 not /16
+    (dict(N=60, s=(64, 1, 60, 1, 64, 1)), Status.ERR_MISALIGNED),   # b_k*2 not /16
+    (dict(N=62, s=(64, 1, 64, 1, 62, 1)), Status.ERR_MISALIGNED),   # fp32 c_m*4 not /16
+    (dict(C=A0 + 1024), Status.ERR_ALIAS),                           # C inside A
+    (dict(C=B0 - 1024), Status.ERR_ALIAS),                           # C runs into B
+    (dict(s=None), Status.ERR_NULL_ARG),
+])
+def test_check_args_errors(kw, want):
+    if "s" in kw and kw["s"] is None:
+        lib = tg.load_library()
+        st = lib.tile_gemm_check_args(A0, B0, C0, 64, 64, 64, None, 0)
+        assert st == want
+        return
+    assert chk(**kw) == want
+    assert tg.last_error_detail(), "a failed check names its argument"
+
+
+def test_bf16_output_alignment_rule():
+    # c_m = 60 bf16 elements = 120 bytes, not a multiple of 16
+    assert chk(N=60, s=(64, 1, 64, 1, 60, 1), dtype=Dtype.BF16_TO_BF16) == Status.ERR_MISALIGNED
+    # c_m = 56 bf16 elements = 112 bytes: fine; fp32 the same c_m = 224 bytes: fine
+    assert chk(N=56, s=(64, 1, 64, 1, 56, 1), dtype=Dtype.BF16_TO_BF16) == Status.OK
+
+
+def test_alias_adjacent_is_not_overlap():
+    # A occupies [A0, A0 + 2*(63*64 + 64)); C starting exactly at its end is fine
+    a_end = A0 + 2 * (63 * 64 + 64)
+    assert chk(C=a_end) == Status.OK
+    assert chk(C=a_end - 16) == Status.ERR_ALIAS

@@ -1,0 +1,132 @@
+"""Host-side checks of the planner and the owned-tile map.
+
+The output is partitioned into disjoint tiles before launch and each
+workgroup owns exactly one ("GPU speed, without leaving Rust's safety model",
+section "Ownership crosses the launch boundary"). tile_gemm_tile_of runs the
+same tile_of function the kernels run, compiled for the host, so these tests
+check the device map itself: a bijection from workgroup ids onto the tile
+grid whose tiles cover C exactly once.
+"""
+
+import itertools
+import random
+
+import pytest
+
+import tile_partitioned_dense_amd as tg
+from tile_partitioned_dense_amd import synth
+
+CU = 256
+
+
+def cover_check(M, N, K, bcol=False, cu=CU):
+    plan = tg.tile_gemm_plan(M, N, K, bcol, cu)
+    if M == 0 or N == 0:
+        assert plan.variant == tg.VARIANT_NONE and plan.grid == 0
+        return plan
+    seen = set()
+    area = 0
+    for wg in range(plan.grid):
+        m0, n0, rows, cols = tg.tile_gemm_tile_of(plan, M, N, wg)
+        assert (m0, n0) not in seen, f"tile ({m0},{n0}) owned twice"
+        seen.add((m0, n0))
+        assert 0 <= m0 < M and 0 <= n0 < N
+        assert 0 < rows <= plan.bm and 0 < cols <= plan.bn
+        assert m0 % plan.bm == 0 and n0 % plan.bn == 0
+        assert rows == min(plan.bm, M - m0) and cols == min(plan.bn, N - n0)
+        area += rows * cols
+    # distinct grid-aligned tiles whose clipped areas sum to M*N cover C exactly
+    assert area == M * N
+    assert len(seen) == plan.grid
+    return plan
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+def test_workload_partitions(name):
+    w = synth.WORKLOADS[name]
+    plan = cover_check(w.M, w.N, w.K, w.b_col_major)
+    assert plan.grid >= 1
+
+
+def test_expected_plans_for_workloads():
+    W = synth.WORKLOADS
+    p = tg.tile_gemm_plan(W["qkv_shard"].M, W["qkv_shard"].N, W["qkv_shard"].K, False, CU)
+    assert (p.variant, p.bm, p.bn, p.grid) == (tg.VARIANT_TILE, 256, 160, 256)
+    p = tg.tile_gemm_plan(8192, 7168, 8192, True, CU)
+    assert (p.variant, p.bm, p.bn, p.grid) == (tg.VARIANT_TILE, 256, 224, 1024)
+    p = tg.tile_gemm_plan(4096, 4096, 4096, False, CU)
+    assert (p.variant, p.bm, p.bn, p.grid) == (tg.VARIANT_TILE, 256, 256, 256)
+    p = tg.tile_gemm_plan(16, 28672, 8192, False, CU)
+    assert p.variant == tg.VARIANT_SKINNY and p.k_split == 8 and p.bm == 16
+    assert p.grid * p.bn >= 28672 and (p.grid - 1) * p.bn < 28672
+
+
+def test_plan_is_a_pure_function_of_shape():
+    a = tg.tile_gemm_plan(1000, 777, 333, False, CU).as_dict()
+    for _ in range(3):
+        assert tg.tile_gemm_plan(1000, 777, 333, False, CU).as_dict() == a
+
+
+@pytest.mark.parametrize("M,N", [(1, 1), (65, 65), (257, 255), (1000, 1000), (17, 33),
+                                 (64, 100000), (300, 7), (4096, 256), (8192, 1280),
+                                 (2049, 4095), (63, 65), (65, 1), (512, 64 * 257)])
+def test_edge_shape_partitions(M, N):
+    for bcol in (False, True):
+        cover_check(M, N, 64, bcol)
+
+
+def test_random_shapes_partition():
+    rng = random.Random(1234)
+    for _ in range(60):
+        M = rng.choice([rng.randint(1, 70), rng.randint(1, 3000)])
+        N = rng.randint(1, 3000)
+        cover_check(M, N, rng.randint(0, 500), rng.random() < 0.5)
+
+
+@pytest.mark.parametrize("cu", [1, 7, 80, 256, 304])
+def test_other_cu_counts(cu):
+    cover_check(3000, 2000, 100, False, cu)
+    cover_check(40, 5000, 100, False, cu)
+
+
+def test_xcd_remap_keeps_neighbours_on_one_xcd():
+    """Workgroups dispatched to one XCD (ids equal mod 8) get consecutive tile
+    indices, so co-running tiles share panels."""
+    plan = tg.tile_gemm_plan(8192, 7168, 8192, True, CU)
+    assert plan.xcds == 8
+    by_xcd = {}
+    for wg in range(plan.grid):
+        m0, n0, _, _ = tg.tile_gemm_tile_of(plan, 8192, 7168, wg)
+        by_xcd.setdefault(wg % 8, []).append((m0 // plan.bm, n0 // plan.bn))
+    for x, tiles in by_xcd.items():
+        first = tiles[:32]                       # one dispatch round of 32 CUs
+        rows = {t[0] for t in first}
+        cols = {t[1] for t in first}
+        assert len(rows) * len(cols) <= 64, (x, rows, cols)
+
+
+def test_plan_rejects_bad_input():
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(-1, 4, 4)
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(4, 4, 4, cu_count=0)
+    plan = tg.tile_gemm_plan(512, 512, 64)
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_tile_of(plan, 512, 512, plan.grid)
+
+
+def _colliding_tile_of(plan, M, N, wg):
+    """The negative-control map the debug entry point can force: workgroup 1
+    takes workgroup 0's tile."""
+    return tg.tile_gemm_tile_of(plan, M, N, 0 if wg == 1 else wg)
+
+
+def test_negative_control_map_is_caught_by_cover_check():
+    plan = tg.tile_gemm_plan(1024, 1024, 64)
+    seen = set()
+    dup = False
+    for wg in range(plan.grid):
+        t = _colliding_tile_of(plan, 1024, 1024, wg)[:2]
+        dup |= t in seen
+        seen.add(t)
+    assert dup and len(seen) == plan.grid - 1

@@ -14,10 +14,13 @@ points raises if ``libtile_gemm.so`` has not been built: there is no
 fallback path.
 """
 
-__all__ = ["tile_gemm_create", "tile_gemm_run", "tile_gemm_destroy",
+__all__ = ["tile_gemm_create", "tile_gemm_run", "tile_gemm_run_debug", "tile_gemm_destroy",
            "tile_gemm_status_str", "tile_gemm_check_args", "tile_gemm_plan",
            "tile_gemm_tile_of", "TileGemm", "TileGemmError", "Status", "Dtype",
-           "Strides", "Plan", "library_path", "load_library"]
+           "Strides", "Plan", "library_path", "load_library", "last_error_detail",
+           "DEBUG_COUNT_WRITES", "DEBUG_COLLIDE", "DEBUG_FORCE_TILE",
+           "DEBUG_FORCE_SKINNY", "N_TILE_CONFIGS", "N_SKINNY_CONFIGS", "VARIANT_NONE", "VARIANT_TILE",
+           "VARIANT_SKINNY"]
 
 
 def __getattr__(name):

@@ -1,0 +1,268 @@
+"""Thin ctypes binding of libtile_gemm.so (include/tile_gemm.h).
+
+Argument marshalling only: torch supplies device memory and the current
+stream; every step of the product runs in the library's HIP kernels. There is
+no fallback: if the library is missing, loading it raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import enum
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libtile_gemm.so")
+_lib = None
+
+
+class Status(enum.IntEnum):
+    OK = 0
+    ERR_NULL_ARG = 1
+    ERR_BAD_SHAPE = 2
+    ERR_BAD_STRIDE = 3
+    ERR_MISALIGNED = 4
+    ERR_ALIAS = 5
+    ERR_DTYPE = 6
+    ERR_DEVICE = 7
+    ERR_HIP = 8
+
+
+class Dtype(enum.IntEnum):
+    BF16_TO_F32 = 0
+    BF16_TO_BF16 = 1
+
+
+DEBUG_COUNT_WRITES = 1
+DEBUG_COLLIDE = 2
+
+
+def DEBUG_FORCE_TILE(c: int) -> int:
+    return ((c + 1) & 0xFF) << 8
+
+
+def DEBUG_FORCE_SKINNY(c: int) -> int:
+    return ((c + 1) & 0xFF) << 16
+
+
+N_TILE_CONFIGS = 7
+N_SKINNY_CONFIGS = 6
+
+VARIANT_NONE, VARIANT_TILE, VARIANT_SKINNY = 0, 1, 2
+
+
+class Strides(ctypes.Structure):
+    _fields_ = [("a_m", ctypes.c_int64), ("a_k", ctypes.c_int64),
+                ("b_k", ctypes.c_int64), ("b_n", ctypes.c_int64),
+                ("c_m", ctypes.c_int64), ("c_n", ctypes.c_int64)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("config", ctypes.c_int32),
+                ("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32),
+                ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+                ("tiles_m", ctypes.c_int32), ("tiles_n", ctypes.c_int32),
+                ("group_m", ctypes.c_int32), ("xcds", ctypes.c_int32),
+                ("k_split", ctypes.c_int32), ("grid", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class TileGemmError(RuntimeError):
+    def __init__(self, status, detail=""):
+        self.status = Status(status)
+        self.detail = detail
+        super().__init__(f"{self.status.name}: {status_text(status)}"
+                         + (f" ({detail})" if detail else ""))
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libtile_gemm.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise FileNotFoundError(
+            f"{_LIB_PATH} is missing: build it with `python -m tile_partitioned_dense_amd.build`"
+            " (there is no fallback implementation)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    P = ctypes.POINTER
+    lib.tile_gemm_create.argtypes = [P(vp), i32]
+    lib.tile_gemm_create.restype = i32
+    lib.tile_gemm_destroy.argtypes = [vp]
+    lib.tile_gemm_destroy.restype = i32
+    lib.tile_gemm_run.argtypes = [vp, vp, vp, vp, i64, i64, i64, P(Strides), i32, vp]
+    lib.tile_gemm_run.restype = i32
+    lib.tile_gemm_run_debug.argtypes = [vp, vp, vp, vp, i64, i64, i64, P(Strides), i32, vp,
+                                        vp, i32]
+    lib.tile_gemm_run_debug.restype = i32
+    lib.tile_gemm_status_str.argtypes = [i32]
+    lib.tile_gemm_status_str.restype = ctypes.c_char_p
+    lib.tile_gemm_last_error_detail.argtypes = []
+    lib.tile_gemm_last_error_detail.restype = ctypes.c_char_p
+    lib.tile_gemm_check_args.argtypes = [vp, vp, vp, i64, i64, i64, P(Strides), i32]
+    lib.tile_gemm_check_args.restype = i32
+    lib.tile_gemm_plan.argtypes = [i64, i64, i64, i32, i32, P(Plan)]
+    lib.tile_gemm_plan.restype = i32
+    lib.tile_gemm_tile_of.argtypes = [P(Plan), i64, i64, i64, P(i64), P(i64), P(i64), P(i64)]
+    lib.tile_gemm_tile_of.restype = i32
+    _lib = lib
+    return lib
+
+
+def status_text(s) -> str:
+    return load_library().tile_gemm_status_str(int(s)).decode()
+
+
+tile_gemm_status_str = status_text
+
+
+def last_error_detail() -> str:
+    return load_library().tile_gemm_last_error_detail().decode()
+
+
+def _raise_if(st):
+    if st != Status.OK:
+        raise TileGemmError(st, last_error_detail())
+
+
+# ----------------------------------------------------------------- handles
+
+def tile_gemm_create(device: int = 0):
+    """Create a handle for HIP device `device` (must be gfx950)."""
+    lib = load_library()
+    h = ctypes.c_void_p()
+    _raise_if(lib.tile_gemm_create(ctypes.byref(h), int(device)))
+    return h
+
+
+def tile_gemm_destroy(h) -> None:
+    _raise_if(load_library().tile_gemm_destroy(h))
+
+
+# ----------------------------------------------------------------- marshalling
+
+def _is_tensor(x):
+    return hasattr(x, "data_ptr") and hasattr(x, "stride")
+
+
+def _operands(A, B, C, M, N, K, strides, dtype):
+    """Pointers, shape, strides and dtype from torch tensors or raw values."""
+    if _is_tensor(A) and _is_tensor(B) and _is_tensor(C):
+        import torch
+        if A.dim() != 2 or B.dim() != 2 or C.dim() != 2:
+            raise ValueError("A, B and C must be 2-D")
+        if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+            raise TypeError("A and B must be bfloat16")
+        M_, K_ = A.shape
+        K2, N_ = B.shape
+        if K2 != K_ or tuple(C.shape) != (M_, N_):
+            raise ValueError(f"shapes do not chain: A{tuple(A.shape)} B{tuple(B.shape)} "
+                             f"C{tuple(C.shape)}")
+        if dtype is None:
+            if C.dtype == torch.float32:
+                dtype = Dtype.BF16_TO_F32
+            elif C.dtype == torch.bfloat16:
+                dtype = Dtype.BF16_TO_BF16
+            else:
+                raise TypeError("C must be float32 or bfloat16")
+        s = Strides(A.stride(0), A.stride(1), B.stride(0), B.stride(1), C.stride(0), C.stride(1))
+        return (A.data_ptr(), B.data_ptr(), C.data_ptr(), M_, N_, K_, s, int(dtype))
+    if None in (M, N, K, strides, dtype):
+        raise ValueError("raw pointers need M, N, K, strides and dtype")
+    s = strides if isinstance(strides, Strides) else Strides(*strides)
+    return (A, B, C, int(M), int(N), int(K), s, int(dtype))
+
+
+def _stream_ptr(stream, C):
+    if stream is None:
+        if _is_tensor(C) and C.is_cuda:
+            import torch
+            return torch.cuda.current_stream(C.device).cuda_stream
+        return None
+    if hasattr(stream, "cuda_stream"):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def tile_gemm_run(h, A, B, C, M=None, N=None, K=None, strides=None, dtype=None, stream=None,
+                  check: bool = True):
+    """Enqueue C := A.B. With torch tensors the shape, strides, output dtype and
+    (unless given) the current stream are taken from them. Returns the status;
+    raises TileGemmError on a non-OK status when `check` is true."""
+    a, b, c, M_, N_, K_, s, dt = _operands(A, B, C, M, N, K, strides, dtype)
+    st = load_library().tile_gemm_run(h, a, b, c, M_, N_, K_, ctypes.byref(s), dt,
+                                      _stream_ptr(stream, C))
+    if check:
+        _raise_if(st)
+    return Status(st)
+
+
+def tile_gemm_run_debug(h, A, B, C, counts=None, flags=0, M=None, N=None, K=None, strides=None,
+                        dtype=None, stream=None, check: bool = True):
+    """tile_gemm_run with test instrumentation (write counts, collision)."""
+    a, b, c, M_, N_, K_, s, dt = _operands(A, B, C, M, N, K, strides, dtype)
+    cnt = counts.data_ptr() if _is_tensor(counts) else counts
+    st = load_library().tile_gemm_run_debug(h, a, b, c, M_, N_, K_, ctypes.byref(s), dt,
+                                            _stream_ptr(stream, C), cnt, int(flags))
+    if check:
+        _raise_if(st)
+    return Status(st)
+
+
+def tile_gemm_check_args(A, B, C, M, N, K, strides, dtype) -> Status:
+    """Host-only argument checks (pointers are plain integers here)."""
+    s = strides if isinstance(strides, Strides) else Strides(*strides)
+    return Status(load_library().tile_gemm_check_args(A, B, C, int(M), int(N), int(K),
+                                                      ctypes.byref(s), int(dtype)))
+
+
+def tile_gemm_plan(M, N, K, b_col_major=False, cu_count=256) -> Plan:
+    p = Plan()
+    _raise_if(load_library().tile_gemm_plan(int(M), int(N), int(K), int(bool(b_col_major)),
+                                            int(cu_count), ctypes.byref(p)))
+    return p
+
+
+def tile_gemm_tile_of(plan: Plan, M, N, wg):
+    vals = [ctypes.c_int64() for _ in range(4)]
+    _raise_if(load_library().tile_gemm_tile_of(ctypes.byref(plan), int(M), int(N), int(wg),
+                                               *[ctypes.byref(v) for v in vals]))
+    return tuple(v.value for v in vals)
+
+
+class TileGemm:
+    """Owns one handle; ``g(A, B, C)`` enqueues C := A.B on the current stream."""
+
+    def __init__(self, device: int = 0):
+        self.handle = tile_gemm_create(device)
+
+    def __call__(self, A, B, C, stream=None):
+        return tile_gemm_run(self.handle, A, B, C, stream=stream)
+
+    def run_debug(self, A, B, C, counts=None, flags=0, stream=None):
+        return tile_gemm_run_debug(self.handle, A, B, C, counts=counts, flags=flags,
+                                   stream=stream)
+
+    def close(self):
+        if self.handle is not None:
+            tile_gemm_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):  # pragma: no cover - best effort
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,186 @@
+// plan.hpp -- output-tile partitioner and launch planner.
+//
+// The output C is split into disjoint tiles before launch and each workgroup
+// exclusively owns one of them: the host-side partition that "GPU speed,
+// without leaving Rust's safety model" describes in "Ownership crosses the
+// launch boundary" (a mutable output partitioned into exclusive
+// sub-tensors, inputs broadcast as shared views) and "Disjointness outside.
+// Ordering inside." (the owned sub-tensor is the destination; no program
+// picks a store index of its own).
+//
+// tile_of() is compiled for both host and device: the kernels call it to find
+// their owned tile, and the host-side tests call the very same function to
+// check that it is a bijection onto the tile grid.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define TG_HD __host__ __device__ __forceinline__
+#else
+#define TG_HD inline
+#endif
+
+namespace tg {
+
+constexpr int kBK = 64;            // K slab staged per step in the tile kernel
+constexpr int kSkinnyMaxM = 64;    // M at or below this takes the skinny kernel
+constexpr int kSkinnyWaves = 8;    // waves per skinny workgroup, splitting K
+constexpr int kXcds = 8;           // MI355X: 8 accelerator dies share one dispatcher
+
+// Tile-kernel configurations compiled into the library. `eff` is the fraction
+// of the MFMA peak a compute unit sustains when running this configuration;
+// the planner uses it only to rank configurations for a shape.
+struct TileConfig {
+  int bm, bn;   // owned tile
+  int wm, wn;   // wave grid inside the workgroup (each wave owns (bm/wm) x (bn/wn))
+  float eff;
+};
+
+constexpr int kNumTileConfigs = 7;
+constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
+    {256, 256, 2, 2, 1.00f},  // 0: 4 waves of 128x128
+    {256, 224, 4, 1, 0.93f},  // 1: 4 waves of 64x224
+    {256, 160, 4, 1, 0.85f},  // 2: 4 waves of 64x160
+    {128, 256, 2, 2, 0.85f},  // 3: 4 waves of 64x128
+    {256, 128, 2, 2, 0.85f},  // 4: 4 waves of 128x64
+    {128, 128, 2, 2, 0.70f},  // 5: 4 waves of 64x64
+    {64, 64, 2, 2, 0.35f},    // 6: 4 waves of 32x32
+};
+
+// Skinny-kernel configurations: T output columns per lane (16*T per
+// workgroup) and MG groups of 16 rows.
+struct SkinnyConfig {
+  int t, mg;
+};
+constexpr int kNumSkinnyConfigs = 6;
+constexpr SkinnyConfig kSkinnyConfigs[kNumSkinnyConfigs] = {
+    {4, 1}, {8, 1}, {4, 2}, {8, 2}, {4, 4}, {8, 4},
+};
+
+// Owned-tile map parameters (kernel argument; plain data).
+struct TileMap {
+  int32_t tiles_m, tiles_n;
+  int32_t group_m;  // tile rows per raster group
+  int32_t xcds;     // dispatch remap width; 1 = identity
+};
+
+TG_HD int32_t tg_min(int32_t a, int32_t b) { return a < b ? a : b; }
+
+// Workgroup id -> owned tile (tm, tn). A bijection from [0, tiles_m*tiles_n)
+// onto the tile grid, composed of two bijections:
+//  1. dispatch remap: consecutive workgroup ids land on different XCDs
+//     (round-robin), so give XCD x one contiguous range of tile indices and
+//     let its workgroups walk that range in dispatch order; tiles that run
+//     at the same time on one XCD then share its L2;
+//  2. grouped raster: group_m tile rows at a time, walking down the rows of a
+//     group before moving to the next column, so co-running tiles reuse the
+//     same A row panels and B column panels.
+TG_HD void tile_of(const TileMap& mp, int32_t wg, int32_t& tm, int32_t& tn) {
+  const int32_t T = mp.tiles_m * mp.tiles_n;
+  int32_t t = wg;
+  if (mp.xcds > 1) {
+    const int32_t q = T / mp.xcds, r = T - (T / mp.xcds) * mp.xcds;
+    const int32_t x = wg % mp.xcds, i = wg / mp.xcds;
+    t = x * q + tg_min(x, r) + i;
+  }
+  const int32_t per_group = mp.group_m * mp.tiles_n;
+  const int32_t g = t / per_group;
+  const int32_t first_m = g * mp.group_m;
+  const int32_t gsz = tg_min(mp.tiles_m - first_m, mp.group_m);
+  const int32_t local = t - g * per_group;
+  tm = first_m + local % gsz;
+  tn = local / gsz;
+}
+
+struct Plan {
+  int variant;  // 0 none, 1 tile, 2 skinny
+  int config;
+  int bm, bn, bk, threads, lds_bytes;
+  TileMap map;
+  int k_split;
+  int64_t grid;
+};
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline int tile_lds_bytes(const TileConfig& c) { return 2 * (c.bm + c.bn) * kBK * 2; }
+inline int skinny_lds_bytes(const SkinnyConfig& c) {
+  return (kSkinnyWaves / 2) * c.mg * c.t * 64 * 16;
+}
+
+// Raster group height: enough tile rows that the tiles co-running on one XCD
+// (32 compute units) form a roughly square block of the tile grid.
+inline int32_t pick_group_m(int32_t tiles_m, int32_t tiles_n) {
+  int32_t g = 4;
+  if (tiles_n < 8) g = 8;
+  if (g > tiles_m) g = tiles_m;
+  return g < 1 ? 1 : g;
+}
+
+// The launch geometry of one configuration for an M x N output.
+inline Plan plan_for(int variant, int config, int64_t M, int64_t N) {
+  Plan p{};
+  p.bk = kBK;
+  p.map.xcds = 1;
+  p.variant = variant;
+  p.config = config;
+  if (variant == 2) {
+    const SkinnyConfig& c = kSkinnyConfigs[config];
+    p.bm = 16 * c.mg;
+    p.bn = 16 * c.t;
+    p.threads = kSkinnyWaves * 64;
+    p.lds_bytes = skinny_lds_bytes(c);
+    p.k_split = kSkinnyWaves;
+    p.map.tiles_m = 1;
+    p.map.tiles_n = (int32_t)ceil_div(N, p.bn);
+    p.map.group_m = 1;
+    p.grid = p.map.tiles_n;
+  } else if (variant == 1) {
+    const TileConfig& c = kTileConfigs[config];
+    p.bm = c.bm;
+    p.bn = c.bn;
+    p.threads = c.wm * c.wn * 64;
+    p.lds_bytes = tile_lds_bytes(c);
+    p.k_split = 1;
+    p.map.tiles_m = (int32_t)ceil_div(M, c.bm);
+    p.map.tiles_n = (int32_t)ceil_div(N, c.bn);
+    p.map.group_m = pick_group_m(p.map.tiles_m, p.map.tiles_n);
+    p.map.xcds = kXcds;
+    p.grid = (int64_t)ceil_div(M, c.bm) * ceil_div(N, c.bn);
+  }
+  return p;
+}
+
+// Pure function of (M, N, K, B layout, CU count). The output type is not an
+// input, so fp32 and bf16 outputs of one shape share kernel, tile and K order.
+inline Plan make_plan(int64_t M, int64_t N, int64_t K, bool b_col_major, int cu_count) {
+  (void)K;
+  (void)b_col_major;
+  if (M <= 0 || N <= 0) return plan_for(0, 0, M, N);
+  if (M <= kSkinnyMaxM) {
+    const int mg = (int)ceil_div(M, 16);
+    const int mgp = mg <= 1 ? 1 : (mg <= 2 ? 2 : 4);
+    // wide column stripes only when there are still enough workgroups
+    const int t = (ceil_div(N, 128) >= cu_count) ? 8 : 4;
+    int idx = 0;
+    for (int i = 0; i < kNumSkinnyConfigs; ++i)
+      if (kSkinnyConfigs[i].t == t && kSkinnyConfigs[i].mg == mgp) idx = i;
+    return plan_for(2, idx, M, N);
+  }
+  // Tile kernel: minimise (tiles on the busiest CU) x (tile area) / efficiency.
+  int best = 0;
+  double best_cost = 0.0;
+  for (int i = 0; i < kNumTileConfigs; ++i) {
+    const TileConfig& c = kTileConfigs[i];
+    const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
+    const double cost = (double)ceil_div(tiles, cu_count) * c.bm * c.bn / c.eff;
+    if (i == 0 || cost < best_cost * 0.999) {
+      best = i;
+      best_cost = cost;
+    }
+  }
+  return plan_for(1, best, M, N);
+}
+
+}  // namespace tg

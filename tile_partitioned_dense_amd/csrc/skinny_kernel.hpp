@@ -1,0 +1,197 @@
+// skinny_kernel.hpp -- bandwidth-oriented kernel for decode-shaped GEMMs
+// (M <= 64), where streaming B from HBM is the whole cost: with M rows the
+// arithmetic intensity is about M flops per byte of B, far below the MFMA
+// ridge point, the memory-bound regime the tensor-parallel page describes
+// for small GEMMs ("Implementing Tensor Parallelism Communication Overlays
+// for Distributed LLM Inference in Rust", section "Performance Tradeoffs:
+// Choosing the Right Chunk Size").
+//
+// Ownership: workgroup w owns C[0:M, 16*T*w : 16*T*(w+1)] and is its only
+// writer; B's column stripe for those columns is read exactly once, by this
+// workgroup. Its eight waves split K into contiguous ranges, and their
+// partial sums meet in LDS along a fixed pairwise tree (wave w adds wave
+// w + h for h = 4, 2, 1), the pattern of the fixed-order workgroup
+// reductions in "Rust Compute Kernels" (section "Signature mapping"), so
+// the per-element summation order is fixed and results are bit-identical.
+//
+// MFMA 16x16x32: lane l (column group nl = l % 16, k group kg = l / 16) holds
+// for a 32-k block: A rows 16g + nl, k = 8kg..8kg+7 (one 16-byte load of
+// the K-contiguous A), and B columns n0 + T*nl + c (c < T) for the same 8 k.
+// A row-major B is read as eight k rows of T contiguous columns (coalesced:
+// 16 lanes cover 32*T contiguous bytes of a row) and transposed in registers.
+#pragma once
+
+#include "common.hpp"
+#include "plan.hpp"
+
+namespace tg {
+
+struct SkinnyArgs {
+  const uint16_t* A;
+  const uint16_t* B;
+  void* C;
+  int32_t M, N, K;
+  int64_t lda, ldb, ldc;
+  uint32_t* counts;  // debug instrumentation only
+  int32_t flags;
+};
+
+template <int T>
+struct RowChunk;  // T contiguous bf16 of one row
+template <>
+struct RowChunk<4> {
+  uint32_t w[2];
+};
+template <>
+struct RowChunk<8> {
+  uint32_t w[4];
+};
+
+template <int T>
+__device__ __forceinline__ RowChunk<T> load_row_chunk(const uint16_t* src, int c, int len, bool fast) {
+  RowChunk<T> r;
+  if (fast || c + T <= len) {
+    if constexpr (T == 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src + c);
+      r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(src + c);
+      r.w[0] = v.x; r.w[1] = v.y;
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < T / 2; ++d) r.w[d] = 0u;
+#pragma unroll
+    for (int e = 0; e < T; ++e)
+      if (c + e < len) r.w[e >> 1] |= ((uint32_t)src[c + e]) << (16 * (e & 1));
+  }
+  return r;
+}
+
+template <int T, int NW, int MG, int U, bool BCOL, bool OUT_BF16, bool DEBUG>
+__global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(SkinnyArgs p) {
+  static_assert(NW == 8 || NW == 4 || NW == 2, "pairwise tree needs a power of two");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int kg = lane >> 4, nl = lane & 15;
+  const int M = p.M, N = p.N, K = p.K;
+  const int n0 = blockIdx.x * (16 * T);
+  const int ncol = n0 + T * nl;  // first of this lane's T columns
+  const bool cols_full = (n0 + 16 * T) <= N;
+
+  const int nkb = (K + 31) >> 5;
+  const int kb0 = (wave * nkb) / NW;
+  const int kb1 = ((wave + 1) * nkb) / NW;
+
+  floatx4 acc[MG][T];
+#pragma unroll
+  for (int g = 0; g < MG; ++g)
+#pragma unroll
+    for (int c = 0; c < T; ++c) acc[g][c] = floatx4{};
+
+  for (int kb = kb0; kb < kb1; kb += U) {
+    bf16x8 af[U][MG];
+    bf16x8 bt[U][T];
+    // issue every load of U blocks before the first MFMA
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool valid = (kb + u) < kb1;
+      const int kbase = (kb + u) * 32 + 8 * kg;  // this lane's 8 k values
+      const bool kfull = valid && (kb + u) * 32 + 32 <= K;
+#pragma unroll
+      for (int g = 0; g < MG; ++g) {
+        const int row = 16 * g + nl;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (valid && row < M) v = load8_masked(p.A + (int64_t)row * p.lda, kbase, K);
+        af[u][g] = as_bf16x8(v);
+      }
+      if constexpr (BCOL) {
+#pragma unroll
+        for (int c = 0; c < T; ++c) {
+          const int col = ncol + c;
+          uint4 v = make_uint4(0, 0, 0, 0);
+          if (valid && col < N) v = load8_masked(p.B + (int64_t)col * p.ldb, kbase, K);
+          bt[u][c] = as_bf16x8(v);
+        }
+      } else {
+        RowChunk<T> rows[8];
+        const bool fast = kfull && cols_full;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int gk = kbase + r;
+          if (valid && gk < K && ncol < N) {
+            rows[r] = load_row_chunk<T>(p.B + (int64_t)gk * p.ldb, ncol, N, fast);
+          } else {
+#pragma unroll
+            for (int d = 0; d < T / 2; ++d) rows[r].w[d] = 0u;
+          }
+        }
+        // regroup: column c of this lane = 8 k values (rows 0..7)
+#pragma unroll
+        for (int c = 0; c < T; ++c) {
+          uint32_t w[4];
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            w[d] = pack_halves(rows[2 * d].w[c >> 1], rows[2 * d + 1].w[c >> 1], (c & 1) != 0);
+          bt[u][c] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int g = 0; g < MG; ++g)
+#pragma unroll
+        for (int c = 0; c < T; ++c) acc[g][c] = mfma16(af[u][g], bt[u][c], acc[g][c]);
+  }
+
+  // Fixed pairwise tree over the waves: for h = NW/2, ..., 1 wave w < h adds
+  // wave w + h's partial sums.
+  __shared__ floatx4 red[NW / 2][MG * T][64];
+#pragma unroll
+  for (int h = NW / 2; h >= 1; h >>= 1) {
+    if (wave >= h && wave < 2 * h) {
+#pragma unroll
+      for (int g = 0; g < MG; ++g)
+#pragma unroll
+        for (int c = 0; c < T; ++c) red[wave - h][g * T + c][lane] = acc[g][c];
+    }
+    __syncthreads();
+    if (wave < h) {
+#pragma unroll
+      for (int g = 0; g < MG; ++g)
+#pragma unroll
+        for (int c = 0; c < T; ++c) acc[g][c] += red[wave][g * T + c][lane];
+    }
+    __syncthreads();
+  }
+
+  if (wave == 0) {
+#pragma unroll
+    for (int g = 0; g < MG; ++g) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = 16 * g + 4 * kg + v;
+        if (row < M) {
+#pragma unroll
+          for (int c = 0; c < T; ++c) {
+            const int col = ncol + c;
+            if (col < N) {
+              const int64_t off = (int64_t)row * p.ldc + col;
+              if constexpr (OUT_BF16) {
+                static_cast<uint16_t*>(p.C)[off] = f32_to_bf16_rne(acc[g][c][v]);
+              } else {
+                static_cast<float*>(p.C)[off] = acc[g][c][v];
+              }
+              if constexpr (DEBUG) {
+                if (p.flags & kDbgCount) atomicAdd(p.counts + (int64_t)row * N + col, 1u);
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace tg

@@ -1,0 +1,345 @@
+// tile_gemm.hip -- the C ABI (include/tile_gemm.h): argument checks, planning
+// and launch.
+//
+// Conventions follow the pages:
+//  * create is one-time preparation and run only records work on a stream
+//    ("Rust Compute Kernels": prepare compiles or hits the cache once, record
+//    only appends; "GPU speed, without leaving Rust's safety model", section
+//    "Build once, choose how to execute");
+//  * run allocates nothing, so it can be captured into a graph ("Why scoped
+//    graph capture helps borrowing": capture is limited to non-allocating
+//    operations);
+//  * argument errors are reported before anything is recorded and name the
+//    argument and axis ("Rust Compute Kernels", section "Shape contracts");
+//  * a written argument may not overlap another argument ("Rust Compute
+//    Kernels", section "Fusing invocations", which rejects exactly that).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "launch.hpp"
+#include "plan.hpp"
+#include "tile_gemm.h"
+
+struct tile_gemm_handle {
+  int device;
+  int cu_count;
+};
+
+namespace {
+
+thread_local char g_detail[320];
+
+tile_gemm_status_t fail(tile_gemm_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof g_detail, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+// B is row-major when its n stride is 1 and the k stride covers a row;
+// otherwise column-major when its k stride is 1 and the n stride covers a
+// column. (A vector B with both strides 1 is taken as row-major.)
+bool b_is_row_major(const tile_gemm_strides_t* s, int64_t N) {
+  return s->b_n == 1 && s->b_k >= N;
+}
+bool b_is_col_major(const tile_gemm_strides_t* s, int64_t K) {
+  return s->b_k == 1 && s->b_n >= K;
+}
+
+bool overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
+  return a0 < a1 && b0 < b1 && a0 < b1 && b0 < a1;
+}
+
+tile_gemm_status_t check_args(const void* A, const void* B, const void* C, int64_t M, int64_t N,
+                              int64_t K, const tile_gemm_strides_t* s, int dtype) {
+  g_detail[0] = '\0';
+  if (dtype != TILE_GEMM_BF16_TO_F32 && dtype != TILE_GEMM_BF16_TO_BF16)
+    return fail(TILE_GEMM_ERR_DTYPE, "dtype: unknown value %d", dtype);
+  if (M < 0 || N < 0 || K < 0)
+    return fail(TILE_GEMM_ERR_BAD_SHAPE, "shape: M=%lld N=%lld K=%lld, each must be >= 0",
+                (long long)M, (long long)N, (long long)K);
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+    return fail(TILE_GEMM_ERR_BAD_SHAPE, "shape: M=%lld N=%lld K=%lld, each must be < 2^31",
+                (long long)M, (long long)N, (long long)K);
+  if (!s) return fail(TILE_GEMM_ERR_NULL_ARG, "strides: NULL");
+  if (M == 0 || N == 0) return TILE_GEMM_OK;
+  if (K > 0 && !A) return fail(TILE_GEMM_ERR_NULL_ARG, "A: NULL");
+  if (K > 0 && !B) return fail(TILE_GEMM_ERR_NULL_ARG, "B: NULL");
+  if (!C) return fail(TILE_GEMM_ERR_NULL_ARG, "C: NULL");
+
+  // With K == 0 neither A nor B is read, so only C's layout matters.
+  const bool brow = K == 0 || b_is_row_major(s, N);
+  if (K > 0) {
+    if (s->a_k != 1 || s->a_m < K)
+      return fail(TILE_GEMM_ERR_BAD_STRIDE,
+                  "A strides (a_m=%lld, a_k=%lld): need a_k == 1 and a_m >= K=%lld",
+                  (long long)s->a_m, (long long)s->a_k, (long long)K);
+    const bool bcol = !brow && b_is_col_major(s, K);
+    if (!brow && !bcol)
+      return fail(TILE_GEMM_ERR_BAD_STRIDE,
+                  "B strides (b_k=%lld, b_n=%lld): need b_n == 1 and b_k >= N=%lld (row-major) "
+                  "or b_k == 1 and b_n >= K=%lld (column-major)",
+                  (long long)s->b_k, (long long)s->b_n, (long long)N, (long long)K);
+  }
+  if (s->c_n != 1 || s->c_m < N)
+    return fail(TILE_GEMM_ERR_BAD_STRIDE,
+                "C strides (c_m=%lld, c_n=%lld): need c_n == 1 and c_m >= N=%lld",
+                (long long)s->c_m, (long long)s->c_n, (long long)N);
+
+  const int64_t esz = (dtype == TILE_GEMM_BF16_TO_F32) ? 4 : 2;
+  if ((uintptr_t)C % 16) return fail(TILE_GEMM_ERR_MISALIGNED, "C: base pointer not 16-byte aligned");
+  if ((s->c_m * esz) % 16)
+    return fail(TILE_GEMM_ERR_MISALIGNED, "C: c_m=%lld elements is not a multiple of 16 bytes",
+                (long long)s->c_m);
+  if (K == 0) return TILE_GEMM_OK;
+  if ((uintptr_t)A % 16) return fail(TILE_GEMM_ERR_MISALIGNED, "A: base pointer not 16-byte aligned");
+  if ((uintptr_t)B % 16) return fail(TILE_GEMM_ERR_MISALIGNED, "B: base pointer not 16-byte aligned");
+  if ((s->a_m * 2) % 16)
+    return fail(TILE_GEMM_ERR_MISALIGNED, "A: a_m=%lld elements is not a multiple of 16 bytes",
+                (long long)s->a_m);
+  const int64_t ldb = brow ? s->b_k : s->b_n;
+  if ((ldb * 2) % 16)
+    return fail(TILE_GEMM_ERR_MISALIGNED, "B: %s=%lld elements is not a multiple of 16 bytes",
+                brow ? "b_k" : "b_n", (long long)ldb);
+
+  // Byte extents actually touched.
+  const uintptr_t a0 = (uintptr_t)A, b0 = (uintptr_t)B, c0 = (uintptr_t)C;
+  const uintptr_t a1 = a0 + (uintptr_t)(2 * ((M - 1) * s->a_m + K));
+  const uintptr_t b1 = b0 + (uintptr_t)(2 * (brow ? (K - 1) * s->b_k + N : (N - 1) * s->b_n + K));
+  const uintptr_t c1 = c0 + (uintptr_t)(esz * ((M - 1) * s->c_m + N));
+  if (overlap(c0, c1, a0, a1)) return fail(TILE_GEMM_ERR_ALIAS, "C overlaps A (C is written)");
+  if (overlap(c0, c1, b0, b1)) return fail(TILE_GEMM_ERR_ALIAS, "C overlaps B (C is written)");
+  return TILE_GEMM_OK;
+}
+
+void fill_plan(const tg::Plan& p, tile_gemm_plan_t* out) {
+  out->variant = p.variant;
+  out->config = p.config;
+  out->bm = p.bm;
+  out->bn = p.bn;
+  out->bk = p.bk;
+  out->threads = p.threads;
+  out->lds_bytes = p.lds_bytes;
+  out->tiles_m = p.map.tiles_m;
+  out->tiles_n = p.map.tiles_n;
+  out->group_m = p.map.group_m;
+  out->xcds = p.map.xcds;
+  out->k_split = p.k_split;
+  out->grid = p.grid;
+}
+
+hipError_t dispatch_tile(int cfg, const tg::TileArgs& a, const tg::Variant& v, hipStream_t st) {
+  switch (cfg) {
+    case 0: return tg::launch_tile<0>(a, v, st);
+    case 1: return tg::launch_tile<1>(a, v, st);
+    case 2: return tg::launch_tile<2>(a, v, st);
+    case 3: return tg::launch_tile<3>(a, v, st);
+    case 4: return tg::launch_tile<4>(a, v, st);
+    case 5: return tg::launch_tile<5>(a, v, st);
+    case 6: return tg::launch_tile<6>(a, v, st);
+  }
+  return hipErrorInvalidValue;
+}
+static_assert(tg::kNumTileConfigs == 7, "dispatch_tile covers every tile configuration");
+
+hipError_t dispatch_skinny(int cfg, const tg::SkinnyArgs& a, int64_t grid, const tg::Variant& v,
+                           hipStream_t st) {
+  switch (cfg) {
+    case 0: return tg::launch_skinny<0>(a, grid, v, st);
+    case 1: return tg::launch_skinny<1>(a, grid, v, st);
+    case 2: return tg::launch_skinny<2>(a, grid, v, st);
+    case 3: return tg::launch_skinny<3>(a, grid, v, st);
+    case 4: return tg::launch_skinny<4>(a, grid, v, st);
+    case 5: return tg::launch_skinny<5>(a, grid, v, st);
+  }
+  return hipErrorInvalidValue;
+}
+static_assert(tg::kNumSkinnyConfigs == 6, "dispatch_skinny covers every skinny configuration");
+
+tile_gemm_status_t run_impl(tile_gemm_t h, const void* A, const void* B, void* C, int64_t M,
+                            int64_t N, int64_t K, const tile_gemm_strides_t* s,
+                            tile_gemm_dtype_t dtype, void* stream, uint32_t* counts, int flags) {
+  if (!h) return fail(TILE_GEMM_ERR_NULL_ARG, "handle: NULL");
+  const tile_gemm_status_t st = check_args(A, B, C, M, N, K, s, (int)dtype);
+  if (st != TILE_GEMM_OK) return st;
+  if (M == 0 || N == 0) return TILE_GEMM_OK;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != h->device)
+    return fail(TILE_GEMM_ERR_DEVICE, "current device %d is not the handle's device %d", cur,
+                h->device);
+  if ((flags & TILE_GEMM_DEBUG_COUNT_WRITES) && !counts)
+    return fail(TILE_GEMM_ERR_NULL_ARG, "counts: NULL with TILE_GEMM_DEBUG_COUNT_WRITES");
+
+  const bool brow = K == 0 || b_is_row_major(s, N);
+  tg::Plan p = tg::make_plan(M, N, K, !brow, h->cu_count);
+  const int force_tile = (flags >> 8) & 0xff, force_skinny = (flags >> 16) & 0xff;
+  if (force_tile && force_skinny)
+    return fail(TILE_GEMM_ERR_BAD_SHAPE, "debug: force one configuration only");
+  if (force_tile) {
+    if (force_tile > tg::kNumTileConfigs)
+      return fail(TILE_GEMM_ERR_BAD_SHAPE, "debug: no tile configuration %d", force_tile - 1);
+    p = tg::plan_for(1, force_tile - 1, M, N);
+  } else if (force_skinny) {
+    if (force_skinny > tg::kNumSkinnyConfigs)
+      return fail(TILE_GEMM_ERR_BAD_SHAPE, "debug: no skinny configuration %d", force_skinny - 1);
+    if (M > 16 * tg::kSkinnyConfigs[force_skinny - 1].mg)
+      return fail(TILE_GEMM_ERR_BAD_SHAPE, "debug: M=%lld exceeds skinny configuration %d",
+                  (long long)M, force_skinny - 1);
+    p = tg::plan_for(2, force_skinny - 1, M, N);
+  }
+  if (p.grid > 0x7fffffff)
+    return fail(TILE_GEMM_ERR_BAD_SHAPE, "shape: %lld workgroups exceed the launch limit",
+                (long long)p.grid);
+  if ((flags & TILE_GEMM_DEBUG_COLLIDE) && (p.variant != 1 || p.grid < 2))
+    return fail(TILE_GEMM_ERR_BAD_SHAPE, "debug collide: needs the tile kernel and >= 2 tiles");
+
+  const tg::Variant v{!brow, dtype == TILE_GEMM_BF16_TO_BF16, flags != 0};
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (p.variant == 1) {
+    tg::TileArgs a{};
+    a.A = static_cast<const uint16_t*>(A);
+    a.B = static_cast<const uint16_t*>(B);
+    a.C = C;
+    a.M = (int32_t)M;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    a.lda = s->a_m;
+    a.ldb = brow ? s->b_k : s->b_n;
+    a.ldc = s->c_m;
+    a.map = p.map;
+    a.counts = counts;
+    a.flags = flags;
+    e = dispatch_tile(p.config, a, v, hs);
+  } else {
+    tg::SkinnyArgs a{};
+    a.A = static_cast<const uint16_t*>(A);
+    a.B = static_cast<const uint16_t*>(B);
+    a.C = C;
+    a.M = (int32_t)M;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    a.lda = s->a_m;
+    a.ldb = brow ? s->b_k : s->b_n;
+    a.ldc = s->c_m;
+    a.counts = counts;
+    a.flags = flags;
+    e = dispatch_skinny(p.config, a, p.grid, v, hs);
+  }
+  if (e != hipSuccess) return fail(TILE_GEMM_ERR_HIP, "launch: %s", hipGetErrorString(e));
+  return TILE_GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tile_gemm_status_str(tile_gemm_status_t s) {
+  switch (s) {
+    case TILE_GEMM_OK: return "ok";
+    case TILE_GEMM_ERR_NULL_ARG: return "a required pointer is NULL";
+    case TILE_GEMM_ERR_BAD_SHAPE: return "bad shape";
+    case TILE_GEMM_ERR_BAD_STRIDE: return "unsupported strides";
+    case TILE_GEMM_ERR_MISALIGNED: return "pointer or leading dimension not 16-byte aligned";
+    case TILE_GEMM_ERR_ALIAS: return "output overlaps an input";
+    case TILE_GEMM_ERR_DTYPE: return "unknown dtype";
+    case TILE_GEMM_ERR_DEVICE: return "device unavailable, not gfx950, or not current";
+    case TILE_GEMM_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* tile_gemm_last_error_detail(void) { return g_detail; }
+
+tile_gemm_status_t tile_gemm_create(tile_gemm_t* out, int device) {
+  g_detail[0] = '\0';
+  if (!out) return fail(TILE_GEMM_ERR_NULL_ARG, "out: NULL");
+  *out = nullptr;
+  int n = 0;
+  const hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n <= 0)
+    return fail(TILE_GEMM_ERR_DEVICE, "no HIP device visible (%s)", hipGetErrorString(e));
+  if (device < 0 || device >= n)
+    return fail(TILE_GEMM_ERR_DEVICE, "device %d out of range [0, %d)", device, n);
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess)
+    return fail(TILE_GEMM_ERR_DEVICE, "cannot query device %d", device);
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(TILE_GEMM_ERR_DEVICE, "device %d is %s, not gfx950", device, prop.gcnArchName);
+  tile_gemm_handle* hnd = new (std::nothrow) tile_gemm_handle{device, prop.multiProcessorCount};
+  if (!hnd) return fail(TILE_GEMM_ERR_HIP, "out of host memory");
+  *out = hnd;
+  return TILE_GEMM_OK;
+}
+
+tile_gemm_status_t tile_gemm_destroy(tile_gemm_t h) {
+  delete h;
+  return TILE_GEMM_OK;
+}
+
+tile_gemm_status_t tile_gemm_run(tile_gemm_t h, const void* A, const void* B, void* C, int64_t M,
+                                 int64_t N, int64_t K, const tile_gemm_strides_t* strides,
+                                 tile_gemm_dtype_t dtype, void* stream) {
+  return run_impl(h, A, B, C, M, N, K, strides, dtype, stream, nullptr, 0);
+}
+
+tile_gemm_status_t tile_gemm_run_debug(tile_gemm_t h, const void* A, const void* B, void* C,
+                                       int64_t M, int64_t N, int64_t K,
+                                       const tile_gemm_strides_t* strides, tile_gemm_dtype_t dtype,
+                                       void* stream, uint32_t* counts, int flags) {
+  if (flags & ~(TILE_GEMM_DEBUG_COUNT_WRITES | TILE_GEMM_DEBUG_COLLIDE | 0x00ffff00))
+    return fail(TILE_GEMM_ERR_BAD_SHAPE, "flags: unknown bits 0x%x", flags);
+  return run_impl(h, A, B, C, M, N, K, strides, dtype, stream, counts, flags);
+}
+
+tile_gemm_status_t tile_gemm_check_args(const void* A, const void* B, const void* C, int64_t M,
+                                        int64_t N, int64_t K, const tile_gemm_strides_t* strides,
+                                        tile_gemm_dtype_t dtype) {
+  return check_args(A, B, C, M, N, K, strides, (int)dtype);
+}
+
+tile_gemm_status_t tile_gemm_plan(int64_t M, int64_t N, int64_t K, int b_col_major, int cu_count,
+                                  tile_gemm_plan_t* out) {
+  g_detail[0] = '\0';
+  if (!out) return fail(TILE_GEMM_ERR_NULL_ARG, "out: NULL");
+  if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+    return fail(TILE_GEMM_ERR_BAD_SHAPE, "shape out of range");
+  if (cu_count <= 0) return fail(TILE_GEMM_ERR_DEVICE, "cu_count: %d", cu_count);
+  fill_plan(tg::make_plan(M, N, K, b_col_major != 0, cu_count), out);
+  return TILE_GEMM_OK;
+}
+
+tile_gemm_status_t tile_gemm_tile_of(const tile_gemm_plan_t* plan, int64_t M, int64_t N,
+                                     int64_t wg, int64_t* m0, int64_t* n0, int64_t* rows,
+                                     int64_t* cols) {
+  g_detail[0] = '\0';
+  if (!plan || !m0 || !n0 || !rows || !cols) return fail(TILE_GEMM_ERR_NULL_ARG, "NULL argument");
+  if (wg < 0 || wg >= plan->grid) return fail(TILE_GEMM_ERR_BAD_SHAPE, "wg out of range");
+  int64_t r0, c0;
+  if (plan->variant == TILE_GEMM_VARIANT_TILE) {
+    tg::TileMap mp{plan->tiles_m, plan->tiles_n, plan->group_m, plan->xcds};
+    int32_t tm, tn;
+    tg::tile_of(mp, (int32_t)wg, tm, tn);
+    r0 = (int64_t)tm * plan->bm;
+    c0 = (int64_t)tn * plan->bn;
+    *rows = (r0 + plan->bm <= M) ? plan->bm : (M > r0 ? M - r0 : 0);
+  } else if (plan->variant == TILE_GEMM_VARIANT_SKINNY) {
+    r0 = 0;
+    c0 = wg * plan->bn;
+    *rows = M;
+  } else {
+    return fail(TILE_GEMM_ERR_BAD_SHAPE, "plan launches nothing");
+  }
+  *m0 = r0;
+  *n0 = c0;
+  *cols = (c0 + plan->bn <= N) ? plan->bn : (N > c0 ? N - c0 : 0);
+  return TILE_GEMM_OK;
+}
+
+}  // extern "C"

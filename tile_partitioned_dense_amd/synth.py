@@ -40,29 +40,39 @@ def f64_to_bf16_bits(x) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     t = x.astype(np.float32)
     back = t.astype(np.float64)
-    away = np.abs(back) > np.abs(x)
-    u = t.view(np.uint32).copy()
-    u[away] -= np.uint32(1)          # step one fp32 ulp toward zero: truncation
-    inexact = back != x
-    u[inexact] |= np.uint32(1)       # sticky bit: round to odd
+    away = (np.abs(back) > np.abs(x)).astype(np.uint32)
+    inexact = (back != x).astype(np.uint32)
+    u = (t.view(np.uint32) - away) | inexact     # truncate toward zero, then sticky bit
     lsb = (u >> np.uint32(16)) & np.uint32(1)
     u = u + np.uint32(0x7FFF) + lsb
     return (u >> np.uint32(16)).astype(np.uint16)
 
 
+_CHUNK = 1 << 20
+
+
 def draw(rows: int, cols: int, dist: str, seed: int, scale: float = 1.0) -> np.ndarray:
-    """A rows x cols C-contiguous uint16 array of bf16 bit patterns."""
-    rng = np.random.default_rng(seed)
-    shape = (int(rows), int(cols))
-    if dist == "normal":
-        x = rng.standard_normal(shape) * float(scale)
-    elif dist == "uniform":
-        x = rng.uniform(-1.0, 1.0, shape) * float(scale)
-    elif dist == "int3":
-        x = rng.integers(-3, 4, shape).astype(np.float64)
-    else:
+    """A rows x cols C-contiguous uint16 array of bf16 bit patterns.
+
+    Values are drawn in row-major order, a million at a time (the generator's
+    stream is the same as one single draw; chunking only bounds the size of
+    the float64 temporaries).
+    """
+    if dist not in ("normal", "uniform", "int3"):
         raise ValueError(f"unknown distribution {dist!r}")
-    return f64_to_bf16_bits(x)
+    rng = np.random.default_rng(seed)
+    out = np.empty((int(rows), int(cols)), np.uint16)
+    flat = out.reshape(-1)
+    for s in range(0, flat.size, _CHUNK):
+        n = min(_CHUNK, flat.size - s)
+        if dist == "normal":
+            x = rng.standard_normal(n) * float(scale)
+        elif dist == "uniform":
+            x = rng.uniform(-1.0, 1.0, n) * float(scale)
+        else:
+            x = rng.integers(-3, 4, n).astype(np.float64)
+        flat[s:s + n] = f64_to_bf16_bits(x)
+    return out
 
 
 @dataclass(frozen=True)
