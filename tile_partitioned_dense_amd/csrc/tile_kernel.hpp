@@ -19,6 +19,8 @@
 // into eight 8-k columns before storing them.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "plan.hpp"
 
@@ -81,15 +83,22 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
   uint4 ra[A_PER];
   uint4 rb[BCOL ? BC_PER : 8 * BR_BLK];
 
-  auto load_slab = [&](int k0, bool fast) {
+  // Fetch one K slab into registers. FAST (a compile-time constant) means the
+  // whole slab is in range: plain vector loads with no per-load branches, so
+  // every load of the slab is in flight at once. Otherwise rows are clamped
+  // into range (the value is then replaced by zero) and the K / N tail of a
+  // chunk is read element by element.
+  auto load_slab = [&](int k0, auto fast_c) {
+    constexpr bool FAST = decltype(fast_c)::value;
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
-      const int gm = m0 + a_r0 + i * A_ROW_STEP;
       const uint16_t* src = a_base + (int64_t)i * A_ROW_STEP * p.lda;
-      if (fast) {
+      if constexpr (FAST) {
         ra[i] = *reinterpret_cast<const uint4*>(src + k0);
       } else {
-        ra[i] = (gm < M) ? load8_masked(src - 8 * a_c, k0 + 8 * a_c, K) : make_uint4(0, 0, 0, 0);
+        const int gm = m0 + a_r0 + i * A_ROW_STEP;
+        const uint4 v = (gm < M) ? load8_masked(src - 8 * a_c, k0 + 8 * a_c, K) : make_uint4(0, 0, 0, 0);
+        ra[i] = v;
       }
     }
     if constexpr (BCOL) {
@@ -97,26 +106,25 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
       for (int i = 0; i < BC_PER; ++i) {
         const int q = i * NT + tid;
         const int r = q >> 3, c = q & 7;
-        const int gn = n0 + r;
-        const uint16_t* src = p.B + (int64_t)gn * p.ldb;
-        if (fast) {
-          rb[i] = *reinterpret_cast<const uint4*>(src + k0 + 8 * c);
+        const uint16_t* src = p.B + (int64_t)(n0 + r) * p.ldb + 8 * c;
+        if constexpr (FAST) {
+          rb[i] = *reinterpret_cast<const uint4*>(src + k0);
         } else {
-          rb[i] = (gn < N) ? load8_masked(src, k0 + 8 * c, K) : make_uint4(0, 0, 0, 0);
+          rb[i] = (n0 + r < N) ? load8_masked(src - 8 * c, k0 + 8 * c, K) : make_uint4(0, 0, 0, 0);
         }
       }
     } else {
 #pragma unroll
       for (int i = 0; i < BR_BLK; ++i) {
         const int q = i * NT + tid;
-        if (q < BN) {
+        if (BN % NT == 0 || q < BN) {
           const int kb = q / BR_NB, nb = q - (q / BR_NB) * BR_NB;
           const int gc = n0 + 8 * nb;
 #pragma unroll
           for (int rr = 0; rr < 8; ++rr) {
             const int gk = k0 + 8 * kb + rr;
             const uint16_t* src = p.B + (int64_t)gk * p.ldb;
-            if (fast) {
+            if constexpr (FAST) {
               rb[8 * i + rr] = *reinterpret_cast<const uint4*>(src + gc);
             } else {
               rb[8 * i + rr] = (gk < K) ? load8_masked(src, gc, N) : make_uint4(0, 0, 0, 0);
@@ -146,7 +154,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
 #pragma unroll
       for (int i = 0; i < BR_BLK; ++i) {
         const int q = i * NT + tid;
-        if (q < BN) {
+        if (BN % NT == 0 || q < BN) {
           const int kb = q / BR_NB, nb = q - (q / BR_NB) * BR_NB;
           // rb[8i + rr] holds columns 8nb..8nb+7 of k row 8kb+rr; column c
           // is dword c/2, half c%2. Regroup into column-major 8-k chunks.
@@ -176,45 +184,71 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx16{};
 
-  const int nk = (K + kBK - 1) / kBK;
   const int lrow = lane & 31;
   const int lgrp = lane >> 5;
 
-  if (nk > 0) {
-    load_slab(0, full_mn && kBK <= K);
-    store_slab(0);
-  }
-  __syncthreads();
-
-  for (int s = 0; s < nk; ++s) {
-    const int cur = s & 1;
-    const bool more = (s + 1) < nk;
-    if (more) {
-      const int k1 = (s + 1) * kBK;
-      load_slab(k1, full_mn && (k1 + kBK <= K));
-    }
-    const uint4* const cA = sA + cur * A_CH;
-    const uint4* const cB = sB + cur * B_CH;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
+  // Multiply one staged slab: four 16-k steps; the operands of step kk+1 are
+  // read from LDS while the MFMAs of step kk run.
+  auto compute_slab = [&](int buf) {
+    const uint4* const cA = sA + buf * A_CH;
+    const uint4* const cB = sB + buf * B_CH;
+    bf16x8 af[2][FM], bfr[2][FN];
+    auto read_frags = [&](int kk, int slot) {
       const int ch = 2 * kk + lgrp;
-      bf16x8 af[FM], bfr[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int r = wm * WTM + 32 * i + lrow;
-        af[i] = as_bf16x8(cA[r * 8 + (ch ^ swz(r))]);
+        af[slot][i] = as_bf16x8(cA[r * 8 + (ch ^ swz(r))]);
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int n = wn * WTN + 32 * j + lrow;
-        bfr[j] = as_bf16x8(cB[n * 8 + (ch ^ swz(n))]);
+        bfr[slot][j] = as_bf16x8(cB[n * 8 + (ch ^ swz(n))]);
       }
+    };
+    read_frags(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      if (kk + 1 < kBK / 16) read_frags(kk + 1, (kk + 1) & 1);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(af[kk & 1][i], bfr[kk & 1][j], acc[i][j]);
     }
-    if (more) store_slab(cur ^ 1);
+  };
+
+  const std::integral_constant<bool, true> kFast{};
+  const std::integral_constant<bool, false> kMasked{};
+  const int nk = (K + kBK - 1) / kBK;
+  // slabs [0, nk_fast) need no masking: interior tile and K fully covered
+  const int nk_fast = full_mn ? K / kBK : 0;
+
+  if (nk > 0) {
+    if (nk_fast > 0) load_slab(0, kFast);
+    else load_slab(0, kMasked);
+    store_slab(0);
+  }
+  __syncthreads();
+
+  int s = 0;
+  // steady state: the next slab is complete, so its loads are branch-free
+  // (the scheduling barriers keep the compiler from sinking the loads of
+  // slab s+1 below the MFMAs of slab s, which would expose their latency)
+  for (; s + 1 < nk_fast; ++s) {
+    load_slab((s + 1) * kBK, kFast);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_slab(s & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    store_slab((s & 1) ^ 1);
+    __syncthreads();
+  }
+  for (; s < nk; ++s) {
+    const bool more = (s + 1) < nk;
+    if (more) load_slab((s + 1) * kBK, kMasked);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_slab(s & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) store_slab((s & 1) ^ 1);
     __syncthreads();
   }
 
