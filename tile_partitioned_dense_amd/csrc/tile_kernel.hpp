@@ -1,22 +1,43 @@
 // tile_kernel.hpp -- the LDS-staged bf16 MFMA tile kernel for gfx950.
 //
 // One workgroup owns one BM x BN tile of C (found with tile_of) and is its
-// only writer. It walks K in 64-wide slabs in ascending order:
-//   global -> registers -> LDS (double-buffered: slab s+1 is fetched while slab
-//   s is multiplied) -> MFMA operands -> fp32 accumulators,
-// then stores its tile once. A and B are only read, so fetching ahead is
-// always legal; C is never read.
+// only writer. It walks K in 32-wide slabs in ascending order through a ring
+// of kStages LDS buffers:
 //
-// LDS layout: each slab row (64 bf16 = 128 bytes) is eight 16-byte chunks,
-// and chunk c of row r is stored at position c ^ swz(r), swz(r) = (r ^ (r >> 3))
-// & 7. MFMA operand reads (32 consecutive rows, one chunk) and the stores of
-// both the row-major copy and the transposed copy (8 rows apart) then touch
-// eight different chunk positions per group of eight lanes.
+//   global --(buffer load straight into LDS, no registers)--> LDS stage
+//   LDS stage --(ds_read)--> MFMA operands --> fp32 accumulators
 //
-// Both MFMA operands want 8 consecutive k values per lane. A is K-contiguous;
-// so is a column-major B. A row-major B is transposed in registers: a thread
-// loads an 8 (k) x 8 (n) block as eight 16-byte rows and regroups the halves
-// into eight 8-k columns before storing them.
+// and stores its tile once at the end. A and B are only read, so slabs are
+// fetched up to kStages - 1 ahead; C is never read.
+//
+// Pipeline (per wave, slab s, two 16-k steps kk = 0, 1):
+//   MFMAs(s, 0)  while reading the operands of (s, 1)
+//   wait for this wave's loads of slab s+1, barrier (every wave's loads of
+//   slab s+1 have landed, and every wave is done with slab s-1), then issue
+//   the loads of slab s+3 into slab s-1's stage
+//   MFMAs(s, 1)  while reading the operands of (s+1, 0)
+// The barrier is a bare s_barrier with explicit vmcnt waits: a full fence
+// would also wait for the loads that are meant to stay in flight.
+//
+// LDS layouts (all reads conflict-free on 64 banks):
+//  * A, and B when column-major (both K-contiguous): a slab row is 32 bf16 =
+//    64 bytes = four 16-byte chunks; chunk c of row r sits at position
+//    c ^ ((r >> 2) & 3), so the 16 rows one MFMA read touches land in 16
+//    distinct 16-byte bank groups.
+//  * B row-major (N-contiguous): a slab is 32 k rows of BN bf16. MFMA wants 8
+//    consecutive k per lane; ds_read_b64_tr_b16 delivers them: within each
+//    group of 16 lanes, lane 4j + q names row j, columns 4q..4q+3 of a 4 x 16
+//    block and receives column (lane % 16), rows 0..3. When the row pitch is a
+//    multiple of 256 bytes, 64-byte block b of row k sits at b ^ (k & 3) so
+//    the four rows one group reads hit different banks; other pitches already
+//    stagger them.
+//
+// Bounds: each slab's buffer resources start at the slab and end at the last
+// valid element of the operand, so rows (or, for a row-major B, columns) past
+// the edge read as zero and no load can leave the operand. Values read for
+// rows >= M or columns >= N only reach accumulators that are never stored. A K tail (K % 32 != 0) must be
+// exact zeros in both operands; that one slab is fetched through registers
+// with element masks and written to LDS with ds_write.
 #pragma once
 
 #include <type_traits>
@@ -39,30 +60,92 @@ struct TileArgs {
   int32_t flags;     // debug instrumentation only
 };
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTileBK = 32;  // K per slab
+constexpr int kStages = 4;   // LDS ring depth
+
+// Raw buffer resource over [base, base + bytes): loads beyond it return zero
+// and touch no memory.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t n = bytes <= 0 ? 0u : (bytes > 0xffffffffll ? 0xffffffffu : (uint32_t)bytes);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int32_t)((a >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane((int32_t)n);
+  r.w = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from rsrc + voff + soff straight into LDS at lds + 16 *
+// lane (one contiguous KiB per wave). Tracked by vmcnt only. gfx9 LDS
+// instructions do not read M0, and nothing else in these kernels sets it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(uint32_t lds, const i32x4& rsrc, uint32_t voff,
+                                      uint32_t soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt with only the vector-memory counter constrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ int swzA(int r) { return (r >> 2) & 3; }
+
+// 16-byte LDS read at a byte address.
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)addr;
+}
 
 template <int BM, int BN, int WM, int WN, bool BCOL, bool OUT_BF16, bool DEBUG>
 __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) {
-  constexpr int NT = WM * WN * 64;
+  constexpr int NW = WM * WN;
+  constexpr int NT = NW * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
-  constexpr int A_CH = BM * 8;  // 16-byte chunks per A slab
-  constexpr int B_CH = BN * 8;
-  static_assert(A_CH % NT == 0, "A slab must split evenly over the threads");
-  constexpr int A_PER = A_CH / NT;
-  static_assert(!BCOL || B_CH % NT == 0, "B slab must split evenly over the threads");
-  constexpr int BC_PER = BCOL ? B_CH / NT : 1;        // column-major B: chunks per thread
-  constexpr int BR_BLK = (BN + NT - 1) / NT;          // row-major B: 8x8 blocks per thread
-  constexpr int BR_NB = BN / 8;                       // 8-column groups per slab row
+  static_assert(NW == 4, "four waves per workgroup");
+  constexpr int BK = kTileBK;
+  constexpr int A_BYTES = BM * BK * 2;  // per stage
+  constexpr int B_BYTES = BN * BK * 2;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_DMA = A_BYTES / 1024;  // one KiB per wave instruction
+  constexpr int B_DMA = B_BYTES / 1024;
+  static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "slabs are whole KiB");
+  static_assert(A_DMA % NW == 0, "A slab splits evenly over the waves");
+  constexpr int A_PER = A_DMA / NW;
+  constexpr int B_MAX = (B_DMA + NW - 1) / NW;  // B instructions of waves < B_DMA % NW
+  constexpr int B_MIN = B_DMA / NW;
+  constexpr int PITCH = BN * 2;  // row-major B: bytes per k row
+  constexpr bool SWB = !BCOL && (PITCH % 256 == 0);
+  constexpr int CPR = BN / 8;  // row-major B: 16-byte chunks per k row
 
-  __shared__ uint4 smem[2 * (A_CH + B_CH)];
-  uint4* const sA = smem;
-  uint4* const sB = smem + 2 * A_CH;
+  __shared__ __attribute__((aligned(1024))) uint4 smem[kStages * STAGE / 16];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave - (wave / WN) * WN;
 
   int wg = blockIdx.x;
@@ -73,110 +156,108 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
   tile_of(p.map, wg, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int M = p.M, N = p.N, K = p.K;
-  const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
+  const int64_t lda = p.lda, ldb = p.ldb;
 
-  // Per-thread global source rows (64-bit offsets, formed once).
-  const int a_r0 = tid >> 3, a_c = tid & 7;  // chunk (row, col) for pass 0
-  constexpr int A_ROW_STEP = NT / 8;          // rows between passes
-  const uint16_t* const a_base = p.A + (int64_t)(m0 + a_r0) * p.lda + 8 * a_c;
+  // ---- this tile's panels and their valid extents in bytes (to the last
+  // valid element of the operand)
+  const char* a_panel = reinterpret_cast<const char*>(p.A + (int64_t)m0 * lda);
+  const int64_t a_bytes = K > 0 ? (((int64_t)(M - 1) * lda + K) - (int64_t)m0 * lda) * 2 : 0;
+  const char* b_panel = reinterpret_cast<const char*>(BCOL ? p.B + (int64_t)n0 * ldb : p.B + n0);
+  const int64_t b_bytes = K <= 0 ? 0
+                          : BCOL ? (((int64_t)(N - 1) * ldb + K) - (int64_t)n0 * ldb) * 2
+                                 : (((int64_t)(K - 1) * ldb + N) - n0) * 2;
+  // bytes between consecutive slabs in each panel
+  const int64_t a_step = BK * 2;
+  const int64_t b_step = BCOL ? BK * 2 : BK * ldb * 2;
 
-  uint4 ra[A_PER];
-  uint4 rb[BCOL ? BC_PER : 8 * BR_BLK];
-
-  // Fetch one K slab into registers. FAST (a compile-time constant) means the
-  // whole slab is in range: plain vector loads with no per-load branches, so
-  // every load of the slab is in flight at once. Otherwise rows are clamped
-  // into range (the value is then replaced by zero) and the K / N tail of a
-  // chunk is read element by element.
-  auto load_slab = [&](int k0, auto fast_c) {
-    constexpr bool FAST = decltype(fast_c)::value;
+  // ---- per-lane DMA source offsets (bytes), fixed for the whole K loop
+  uint32_t voA[A_PER];
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      const uint16_t* src = a_base + (int64_t)i * A_ROW_STEP * p.lda;
-      if constexpr (FAST) {
-        ra[i] = *reinterpret_cast<const uint4*>(src + k0);
+  for (int t = 0; t < A_PER; ++t) {
+    const int ins = wave + NW * t;
+    const int r = 16 * ins + (lane >> 2);
+    const int c = (lane & 3) ^ swzA(r);
+    voA[t] = (uint32_t)(r * lda * 2) + c * 16;
+  }
+  const int b_cnt = (wave < B_DMA % NW) ? B_MAX : B_MIN;
+  uint32_t voB[B_MAX];
+#pragma unroll
+  for (int t = 0; t < B_MAX; ++t) {
+    const int ins = wave + NW * t;
+    if constexpr (BCOL) {
+      const int r = 16 * ins + (lane >> 2);
+      const int c = (lane & 3) ^ swzA(r);
+      voB[t] = (uint32_t)(r * ldb * 2) + c * 16;
+    } else {
+      const int q = 64 * ins + lane;
+      const int row = q / CPR, pc = q - (q / CPR) * CPR;
+      const int lc = SWB ? ((((pc >> 2) ^ (row & 3)) << 2) | (pc & 3)) : pc;
+      voB[t] = (uint32_t)(row * ldb * 2) + lc * 16;
+    }
+  }
+
+  const int nk = (K + BK - 1) / BK;
+  const int nk_full = K / BK;  // slabs with no K tail
+
+  // Issue the loads of slab s into its stage.
+  auto issue_slab = [&](int s) {
+    const int st = s % kStages;
+    const uint32_t la = lds0 + st * STAGE;
+    const uint32_t lb = la + A_BYTES;
+    if (s < nk_full) {
+      // the resources start at slab s (the range check then covers every
+      // byte a lane reads; the scalar offset stays zero)
+      const i32x4 rsA = make_rsrc(a_panel + s * a_step, a_bytes - s * a_step);
+      const i32x4 rsB = make_rsrc(b_panel + s * b_step, b_bytes - s * b_step);
+#pragma unroll
+      for (int t = 0; t < A_PER; ++t) dma16(la + 1024 * (wave + NW * t), rsA, voA[t], 0u);
+#pragma unroll
+      for (int t = 0; t < B_MAX; ++t)
+        if (t < B_MIN || t < b_cnt) dma16(lb + 1024 * (wave + NW * t), rsB, voB[t], 0u);
+    } else {
+      // K tail: exact zeros past K in both operands, through registers.
+      const int k0 = s * BK;
+      uint4* dA = reinterpret_cast<uint4*>(reinterpret_cast<char*>(smem) + st * STAGE);
+      uint4* dB = reinterpret_cast<uint4*>(reinterpret_cast<char*>(smem) + st * STAGE + A_BYTES);
+      for (int q = tid; q < BM * 4; q += NT) {
+        const int r = q >> 2, c = q & 3;
+        const uint4 v = (m0 + r < M) ? load8_masked(p.A + (int64_t)(m0 + r) * lda, k0 + 8 * c, K)
+                                     : make_uint4(0, 0, 0, 0);
+        dA[r * 4 + (c ^ swzA(r))] = v;
+      }
+      if constexpr (BCOL) {
+        for (int q = tid; q < BN * 4; q += NT) {
+          const int r = q >> 2, c = q & 3;
+          const uint4 v = (n0 + r < N) ? load8_masked(p.B + (int64_t)(n0 + r) * ldb, k0 + 8 * c, K)
+                                       : make_uint4(0, 0, 0, 0);
+          dB[r * 4 + (c ^ swzA(r))] = v;
+        }
       } else {
-        const int gm = m0 + a_r0 + i * A_ROW_STEP;
-        const uint4 v = (gm < M) ? load8_masked(src - 8 * a_c, k0 + 8 * a_c, K) : make_uint4(0, 0, 0, 0);
-        ra[i] = v;
-      }
-    }
-    if constexpr (BCOL) {
-#pragma unroll
-      for (int i = 0; i < BC_PER; ++i) {
-        const int q = i * NT + tid;
-        const int r = q >> 3, c = q & 7;
-        const uint16_t* src = p.B + (int64_t)(n0 + r) * p.ldb + 8 * c;
-        if constexpr (FAST) {
-          rb[i] = *reinterpret_cast<const uint4*>(src + k0);
-        } else {
-          rb[i] = (n0 + r < N) ? load8_masked(src - 8 * c, k0 + 8 * c, K) : make_uint4(0, 0, 0, 0);
+        for (int q = tid; q < BK * CPR; q += NT) {
+          const int row = q / CPR, pc = q - (q / CPR) * CPR;
+          const int lc = SWB ? ((((pc >> 2) ^ (row & 3)) << 2) | (pc & 3)) : pc;
+          const int gk = k0 + row;
+          const uint4 v = (gk < K) ? load8_masked(p.B + (int64_t)gk * ldb, n0 + 8 * lc, N)
+                                   : make_uint4(0, 0, 0, 0);
+          dB[row * CPR + pc] = v;
         }
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < BR_BLK; ++i) {
-        const int q = i * NT + tid;
-        if (BN % NT == 0 || q < BN) {
-          const int kb = q / BR_NB, nb = q - (q / BR_NB) * BR_NB;
-          const int gc = n0 + 8 * nb;
-#pragma unroll
-          for (int rr = 0; rr < 8; ++rr) {
-            const int gk = k0 + 8 * kb + rr;
-            const uint16_t* src = p.B + (int64_t)gk * p.ldb;
-            if constexpr (FAST) {
-              rb[8 * i + rr] = *reinterpret_cast<const uint4*>(src + gc);
-            } else {
-              rb[8 * i + rr] = (gk < K) ? load8_masked(src, gc, N) : make_uint4(0, 0, 0, 0);
-            }
-          }
-        }
-      }
+      wait_lgkmcnt0();
     }
   };
 
-  auto store_slab = [&](int buf) {
-    uint4* const dA = sA + buf * A_CH;
-    uint4* const dB = sB + buf * B_CH;
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      const int r = a_r0 + i * A_ROW_STEP;
-      dA[r * 8 + (a_c ^ swz(r))] = ra[i];
-    }
-    if constexpr (BCOL) {
-#pragma unroll
-      for (int i = 0; i < BC_PER; ++i) {
-        const int q = i * NT + tid;
-        const int r = q >> 3, c = q & 7;
-        dB[r * 8 + (c ^ swz(r))] = rb[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < BR_BLK; ++i) {
-        const int q = i * NT + tid;
-        if (BN % NT == 0 || q < BN) {
-          const int kb = q / BR_NB, nb = q - (q / BR_NB) * BR_NB;
-          // rb[8i + rr] holds columns 8nb..8nb+7 of k row 8kb+rr; column c
-          // is dword c/2, half c%2. Regroup into column-major 8-k chunks.
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const bool hi = (c & 1) != 0;
-            uint32_t w[4];
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-              const uint4& x = rb[8 * i + 2 * d];
-              const uint4& y = rb[8 * i + 2 * d + 1];
-              const uint32_t xs = (c >> 1) == 0 ? x.x : (c >> 1) == 1 ? x.y : (c >> 1) == 2 ? x.z : x.w;
-              const uint32_t ys = (c >> 1) == 0 ? y.x : (c >> 1) == 1 ? y.y : (c >> 1) == 2 ? y.z : y.w;
-              w[d] = pack_halves(xs, ys, hi);
-            }
-            const int n = 8 * nb + c;
-            dB[n * 8 + (kb ^ swz(n))] = make_uint4(w[0], w[1], w[2], w[3]);
-          }
-        }
-      }
-    }
+  // vmcnt waits are per wave. Wait until at most SLABS slabs' worth of this
+  // wave's loads remain (waves < B_DMA % NW issue one more B load per slab).
+  auto wait_slabs = [&](auto slabs_c) {
+    constexpr int SL = decltype(slabs_c)::value;
+    if (B_MAX != B_MIN && b_cnt == B_MAX)
+      wait_vmcnt<SL * (A_PER + B_MAX)>();
+    else
+      wait_vmcnt<SL * (A_PER + B_MIN)>();
   };
+  const std::integral_constant<int, 0> k0c{};
+  const std::integral_constant<int, 1> k1c{};
+  const std::integral_constant<int, 2> k2c{};
 
   floatx16 acc[FM][FN];
 #pragma unroll
@@ -186,73 +267,97 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
 
   const int lrow = lane & 31;
   const int lgrp = lane >> 5;
+  // row-major B transposed reads: lane = 16 G + 4 j + q
+  const int tG = lane >> 4, tj = (lane >> 2) & 3, tq = lane & 3;
 
-  // Multiply one staged slab: four 16-k steps; the operands of step kk+1 are
-  // read from LDS while the MFMAs of step kk run.
-  auto compute_slab = [&](int buf) {
-    const uint4* const cA = sA + buf * A_CH;
-    const uint4* const cB = sB + buf * B_CH;
-    bf16x8 af[2][FM], bfr[2][FN];
-    auto read_frags = [&](int kk, int slot) {
-      const int ch = 2 * kk + lgrp;
+  bf16x8 af[2][FM], bfr[2][FN];
+  auto read_frags = [&](int s, int kk, int slot) {
+    const uint32_t sbase = lds0 + (s % kStages) * STAGE;
+    const int ch = 2 * kk + lgrp;
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm * WTM + 32 * i + lrow;
-        af[slot][i] = as_bf16x8(cA[r * 8 + (ch ^ swz(r))]);
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WTM + 32 * i + lrow;
+      af[slot][i] = lds_read16(sbase + r * 64 + ((ch ^ swzA(r)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (BCOL) {
+        const int r = wn * WTN + 32 * j + lrow;
+        bfr[slot][j] = lds_read16(sbase + A_BYTES + r * 64 + ((ch ^ swzA(r)) << 4));
+      } else {
+        const int n = wn * WTN + 32 * j + 16 * (tG & 1) + 4 * tq;
+        i16x4 h[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int row = 16 * kk + 8 * (tG >> 1) + 4 * t + tj;
+          const int col = SWB ? ((((n >> 5) ^ (row & 3)) << 5) | (n & 31)) : n;
+          h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(uintptr_t)(sbase + A_BYTES + row * PITCH +
+                                                                  col * 2));
+        }
+        bfr[slot][j] =
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
       }
+    }
+  };
+  auto mfmas = [&](int slot) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int n = wn * WTN + 32 * j + lrow;
-        bfr[slot][j] = as_bf16x8(cB[n * 8 + (ch ^ swz(n))]);
-      }
-    };
-    read_frags(0, 0);
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      if (kk + 1 < kBK / 16) read_frags(kk + 1, (kk + 1) & 1);
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(af[slot][i], bfr[slot][j], acc[i][j]);
+  };
+  // Scheduling pattern for one 16-k step: each of the next step's operand
+  // reads is issued right after one MFMA of this step, so reads overlap the
+  // MFMAs and never pile up beyond what the LDS counter can track.
+  constexpr int NREAD = FM + (BCOL ? FN : 2 * FN);
+  constexpr int NMFMA = FM * FN;
+  constexpr int RPM = (NREAD + NMFMA - 1) / NMFMA;  // reads issued after each MFMA
+  auto interleave = [&]() {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(af[kk & 1][i], bfr[kk & 1][j], acc[i][j]);
+    for (int k = 0; k < NMFMA; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if (k * RPM < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);  // LDS reads
     }
   };
 
-  const std::integral_constant<bool, true> kFast{};
-  const std::integral_constant<bool, false> kMasked{};
-  const int nk = (K + kBK - 1) / kBK;
-  // slabs [0, nk_fast) need no masking: interior tile and K fully covered
-  const int nk_fast = full_mn ? K / kBK : 0;
-
+  // ---- prologue: slabs 0..kStages-2 in flight, slab 0 ready, its first operands read
   if (nk > 0) {
-    if (nk_fast > 0) load_slab(0, kFast);
-    else load_slab(0, kMasked);
-    store_slab(0);
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+      if (s < nk) issue_slab(s);
+    if (nk >= 3) wait_slabs(k2c);
+    else if (nk == 2) wait_slabs(k1c);
+    else wait_slabs(k0c);
+    block_barrier();
+    read_frags(0, 0, 0);
   }
-  __syncthreads();
 
-  int s = 0;
-  // steady state: the next slab is complete, so its loads are branch-free
-  // (the scheduling barriers keep the compiler from sinking the loads of
-  // slab s+1 below the MFMAs of slab s, which would expose their latency)
-  for (; s + 1 < nk_fast; ++s) {
-    load_slab((s + 1) * kBK, kFast);
+  for (int s = 0; s < nk; ++s) {
     __builtin_amdgcn_sched_barrier(0);
-    compute_slab(s & 1);
+    mfmas(0);
+    read_frags(s, 1, 1);
+    interleave();
     __builtin_amdgcn_sched_barrier(0);
-    store_slab((s & 1) ^ 1);
-    __syncthreads();
-  }
-  for (; s < nk; ++s) {
-    const bool more = (s + 1) < nk;
-    if (more) load_slab((s + 1) * kBK, kMasked);
+    const bool more = s + 1 < nk;
+    if (more) {
+      // this wave's loads of slab s+1 are done once at most the loads of the
+      // slabs issued after it remain (slab s+2, when it exists)
+      if (s + 2 < nk) wait_slabs(k1c);
+      else wait_slabs(k0c);
+      block_barrier();
+      if (s + kStages - 1 < nk) issue_slab(s + kStages - 1);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    compute_slab(s & 1);
+    mfmas(1);
+    // unconditional so it can interleave with the MFMAs; after the last slab
+    // it reads a stale stage (in bounds) whose values are never used
+    read_frags(s + 1, 0, 0);
+    interleave();
     __builtin_amdgcn_sched_barrier(0);
-    if (more) store_slab((s & 1) ^ 1);
-    __syncthreads();
   }
 
   // Epilogue: each accumulator element is stored exactly once, by its owner.
+  const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
