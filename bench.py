@@ -124,12 +124,32 @@ class Bench:
         return ops, res
 
 
+def measured_traffic(workload):
+    """HBM-side bytes per launch recorded by rocprofv3 counter runs
+    (profiles/traffic.json), or None when the kernel sources have changed
+    since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256()
+        for src in rec["kernel_sources"]:
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        if h.hexdigest() != rec["kernel_source_sha256"]:
+            return None
+        w = rec["workloads"][workload]
+        return int(round(1024 * (w["fetch_kib"] * rec["fetch_scale"] + w["write_kib"] * rec["write_scale"])))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def roofline(res, hbm_bound):
+    traffic = measured_traffic(res["workload"])
     if hbm_bound:
         return {"bound": "hbm", "achieved": round(res["gbs"], 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(res["frac_hbm"], 4), "traffic": None}
+                "unit": "GB/s", "frac": round(res["frac_hbm"], 4), "traffic": traffic}
     return {"bound": "mfma", "achieved": round(res["tflops"], 1), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(res["frac_mfma"], 4), "traffic": None}
+            "unit": "TFLOP/s", "frac": round(res["frac_mfma"], 4), "traffic": traffic}
 
 
 def cpu_baseline(w, ops, seconds):
@@ -170,12 +190,18 @@ def cpu_baseline(w, ops, seconds):
 
 
 def copy_calibration(torch, mib):
+    """A plain device copy of `mib` MiB, for scaling the HBM byte counters.
+    A 512 MiB scratch write between the fill and the copy pushes the source
+    out of the last-level cache, so the copy reads it from HBM."""
     n = (mib << 20) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+    flush.fill_(2.0)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
+    del flush
     log(f"[bench] copy calibration: {mib} MiB read + {mib} MiB written")
 
 
