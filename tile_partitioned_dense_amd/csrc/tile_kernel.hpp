@@ -84,8 +84,19 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
 // instructions do not read M0, and nothing else in these kernels sets it.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(uint32_t lds, const i32x4& rsrc, uint32_t voff,
+__device__ __forceinline__ i32x4 uniform_rsrc(const i32x4& r) {
+  i32x4 u;
+  u.x = __builtin_amdgcn_readfirstlane(r.x);
+  u.y = __builtin_amdgcn_readfirstlane(r.y);
+  u.z = __builtin_amdgcn_readfirstlane(r.z);
+  u.w = __builtin_amdgcn_readfirstlane(r.w);
+  return u;
+}
+__device__ __forceinline__ void dma16(uint32_t lds, const i32x4& rsrc_in, uint32_t voff,
                                       uint32_t soff) {
+  const i32x4 rsrc = uniform_rsrc(rsrc_in);
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  soff = __builtin_amdgcn_readfirstlane(soff);
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "buffer_load_dwordx4 %1, %2, %3 offen lds"
@@ -94,6 +105,35 @@ __device__ __forceinline__ void dma16(uint32_t lds, const i32x4& rsrc, uint32_t 
       : "memory", "m0");
 }
 #pragma clang diagnostic pop
+
+// As dma16, with the LDS address formed as an SGPR base plus a constant.
+// The addition happens outside the asm: the asm itself must not touch SCC,
+// which the compiler may hold live across it (a loop condition, a carry).
+template <uint32_t OFF>
+__device__ __forceinline__ void dma16_off(uint32_t lds_base, const i32x4& rsrc, uint32_t voff) {
+  dma16(lds_base + OFF, rsrc, voff, 0u);
+}
+
+// Move a buffer resource `step` bytes forward (base up, extent down, never
+// below zero, so a resource moved past its end only yields out-of-range
+// loads). Exact while the extent never needed clamping (operands < 4 GiB).
+__device__ __forceinline__ void advance_rsrc(i32x4& r, uint32_t step) {
+  uint64_t base = ((uint64_t)((uint32_t)r.y & 0xffffu) << 32) | (uint32_t)r.x;
+  base += step;
+  r.x = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)base);
+  r.y = __builtin_amdgcn_readfirstlane((int32_t)((base >> 32) & 0xffffu));
+  const uint32_t left = (uint32_t)r.z;
+  r.z = __builtin_amdgcn_readfirstlane((int32_t)(left > step ? left - step : 0u));
+}
+
+// Compile-time loop: f(integral_constant<int, I>) for I in [I0, N).
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // s_waitcnt with only the vector-memory counter constrained.
 template <int N>
@@ -332,7 +372,117 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
     read_frags(0, 0, 0);
   }
 
-  for (int s = 0; s < nk; ++s) {
+  // ---- steady state: slabs whose slab-plus-3 is a full slab. No branches,
+  // unrolled by the ring depth so every stage index is a compile-time
+  // constant: LDS addresses are a lane register plus an immediate, DMA
+  // destinations an SGPR plus a constant, and the buffer resources advance by
+  // scalar adds.
+  const int swl = (lrow >> 2) & 3;  // swzA of this lane's rows
+  uint32_t rA[2][2], rB[2][2];      // [kk][stage pair]: K-contiguous operands
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const uint32_t chunk = (uint32_t)(((lgrp ^ swl) ^ (2 * kk)) << 4);
+    const uint32_t a = lds0 + (wm * WTM + lrow) * 64 + chunk;
+    rA[kk][0] = a;
+    rA[kk][1] = a + 2 * STAGE;
+    const uint32_t b = lds0 + A_BYTES + (wn * WTN + lrow) * 64 + chunk;
+    rB[kk][0] = b;
+    rB[kk][1] = b + 2 * STAGE;
+  }
+  uint32_t rT[BCOL ? 1 : FN][2];    // row-major B: per block j, stage pair
+#pragma unroll
+  for (int j = 0; j < (BCOL ? 1 : FN); ++j) {
+    const int n = wn * WTN + 32 * j + 16 * (tG & 1) + 4 * tq;
+    const int col = SWB ? ((((n >> 5) ^ tj) << 5) | (n & 31)) : n;
+    const uint32_t b = lds0 + A_BYTES + (8 * (tG >> 1) + tj) * PITCH + col * 2;
+    rT[j][0] = b;
+    rT[j][1] = b + 2 * STAGE;
+  }
+  const uint32_t ldsw = __builtin_amdgcn_readfirstlane(lds0 + 1024 * wave);
+
+  // operand unit IDX of step KK from stage ST: A block IDX < FM, else B block
+  auto read_fast = [&](auto st_c, auto kk_c, int slot, auto idx_c) {
+    constexpr int ST = decltype(st_c)::value, KK = decltype(kk_c)::value;
+    constexpr int IDX = decltype(idx_c)::value;
+    constexpr int H = ST >> 1;
+    constexpr uint32_t SO = (ST & 1) * STAGE;
+    if constexpr (IDX < FM) {
+      af[slot][IDX] = lds_read16(rA[KK][H] + (SO + IDX * 2048));
+    } else if constexpr (BCOL) {
+      bfr[slot][IDX - FM] = lds_read16(rB[KK][H] + (SO + (IDX - FM) * 2048));
+    } else {
+      constexpr int J = IDX - FM;
+      const i16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(uintptr_t)(rT[J][H] + (SO + KK * 16 * PITCH)));
+      const i16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(uintptr_t)(rT[J][H] +
+                                                              (SO + KK * 16 * PITCH + 4 * PITCH)));
+      bfr[slot][J] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  constexpr int NUNIT = FM + FN;
+  constexpr int UPM = (NUNIT + NMFMA - 1) / NMFMA;  // operand units read after each MFMA
+
+  auto steady = [&](auto bc_c) -> int {
+    constexpr int BC = decltype(bc_c)::value;  // this wave's B loads per slab
+    constexpr int NDMA = A_PER + BC;
+    constexpr int DPMF = (NDMA + NMFMA - 1) / NMFMA;
+    const int n_steady = nk_full - (kStages - 1);
+    int s = 0;
+    if (n_steady < kStages) return 0;
+    i32x4 rsAn = make_rsrc(a_panel + (kStages - 1) * a_step, a_bytes - (kStages - 1) * a_step);
+    i32x4 rsBn = make_rsrc(b_panel + (kStages - 1) * b_step, b_bytes - (kStages - 1) * b_step);
+    for (; s + kStages <= n_steady; s += kStages) {
+      static_for<0, kStages>([&](auto st_c) {
+        constexpr int ST = decltype(st_c)::value;         // stage of slab s + ST
+        constexpr int STN = (ST + 1) % kStages;            // stage of slab s + ST + 1
+        constexpr int STD = (ST + kStages - 1) % kStages;  // stage taking slab s + ST + 3
+        // MFMAs (slab, 0) while reading the operands of (slab, 1)
+        static_for<0, NMFMA>([&](auto k_c) {
+          constexpr int k = decltype(k_c)::value;
+          acc[k / FN][k % FN] = mfma32(af[0][k / FN], bfr[0][k % FN], acc[k / FN][k % FN]);
+          static_for<0, UPM>([&](auto r_c) {
+            constexpr int idx = k * UPM + decltype(r_c)::value;
+            if constexpr (idx < NUNIT)
+              read_fast(st_c, std::integral_constant<int, 1>{}, 1, std::integral_constant<int, idx>{});
+          });
+        });
+        wait_vmcnt<NDMA>();
+        block_barrier();
+        // MFMAs (slab, 1) while reading (slab + 1, 0) and loading slab + 3
+        static_for<0, NMFMA>([&](auto k_c) {
+          constexpr int k = decltype(k_c)::value;
+          acc[k / FN][k % FN] = mfma32(af[1][k / FN], bfr[1][k % FN], acc[k / FN][k % FN]);
+          static_for<0, UPM>([&](auto r_c) {
+            constexpr int idx = k * UPM + decltype(r_c)::value;
+            if constexpr (idx < NUNIT)
+              read_fast(std::integral_constant<int, STN>{}, std::integral_constant<int, 0>{}, 0,
+                        std::integral_constant<int, idx>{});
+          });
+          static_for<0, DPMF>([&](auto d_c) {
+            constexpr int t = k * DPMF + decltype(d_c)::value;
+            if constexpr (t < A_PER)
+              dma16_off<STD * STAGE + 4096 * t>(ldsw, rsAn, voA[t]);
+            else if constexpr (t < NDMA)
+              dma16_off<STD * STAGE + A_BYTES + 4096 * (t - A_PER)>(ldsw, rsBn, voB[t - A_PER]);
+          });
+        });
+        advance_rsrc(rsAn, (uint32_t)a_step);
+        advance_rsrc(rsBn, (uint32_t)b_step);
+      });
+    }
+    return s;
+  };
+  int s0 = 0;
+  if constexpr (B_MAX != B_MIN) {
+    if (b_cnt == B_MAX) s0 = steady(std::integral_constant<int, B_MAX>{});
+    else s0 = steady(std::integral_constant<int, B_MIN>{});
+  } else {
+    s0 = steady(std::integral_constant<int, B_MIN>{});
+  }
+
+  // ---- remaining slabs (and a K tail): the general loop
+  for (int s = s0; s < nk; ++s) {
     __builtin_amdgcn_sched_barrier(0);
     mfmas(0);
     read_frags(s, 1, 1);
