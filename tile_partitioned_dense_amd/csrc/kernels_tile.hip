@@ -14,7 +14,7 @@ hipError_t launch_tile(const TileArgs& a, const Variant& v, hipStream_t stream) 
   const dim3 grid((unsigned)(a.map.tiles_m * a.map.tiles_n));
   const dim3 block(c.wm * c.wn * 64);
 #define TG_TILE_FN(BC, OB, DB) \
-  reinterpret_cast<const void*>(&tile_gemm_kernel<c.bm, c.bn, c.wm, c.wn, BC, OB, DB>)
+  reinterpret_cast<const void*>(&tile_gemm_kernel<c.bm, c.bn, c.wm, c.wn, c.stages, BC, OB, DB>)
   const void* fn;
   if (v.b_col_major) {
     if (v.out_bf16) fn = v.debug ? TG_TILE_FN(true, true, true) : TG_TILE_FN(true, true, false);

@@ -23,7 +23,7 @@
 
 namespace tg {
 
-constexpr int kBK = 64;            // K slab staged per step in the tile kernel
+constexpr int kBK = 32;            // K slab staged per step in the tile kernel
 constexpr int kSkinnyMaxM = 64;    // M at or below this takes the skinny kernel
 constexpr int kSkinnyWaves = 8;    // waves per skinny workgroup, splitting K
 constexpr int kXcds = 8;           // MI355X: 8 accelerator dies share one dispatcher
@@ -34,18 +34,19 @@ constexpr int kXcds = 8;           // MI355X: 8 accelerator dies share one dispa
 struct TileConfig {
   int bm, bn;   // owned tile
   int wm, wn;   // wave grid inside the workgroup (each wave owns (bm/wm) x (bn/wn))
+  int stages;   // depth of the LDS ring of 32-wide K slabs
   float eff;
 };
 
 constexpr int kNumTileConfigs = 7;
 constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
-    {256, 256, 2, 2, 1.00f},  // 0: 4 waves of 128x128
-    {256, 224, 4, 1, 0.93f},  // 1: 4 waves of 64x224
-    {256, 160, 4, 1, 0.85f},  // 2: 4 waves of 64x160
-    {128, 256, 2, 2, 0.85f},  // 3: 4 waves of 64x128
-    {256, 128, 2, 2, 0.85f},  // 4: 4 waves of 128x64
-    {128, 128, 2, 2, 0.70f},  // 5: 4 waves of 64x64
-    {64, 64, 2, 2, 0.35f},    // 6: 4 waves of 32x32
+    {256, 256, 2, 2, 4, 1.00f},  // 0: 4 waves of 128x128
+    {256, 224, 4, 1, 5, 0.93f},  // 1: 4 waves of 64x224
+    {256, 160, 4, 1, 5, 0.85f},  // 2: 4 waves of 64x160
+    {128, 256, 2, 2, 5, 0.85f},  // 3: 4 waves of 64x128
+    {256, 128, 2, 2, 5, 0.85f},  // 4: 4 waves of 128x64
+    {128, 128, 2, 2, 4, 0.70f},  // 5: 4 waves of 64x64
+    {64, 64, 2, 2, 4, 0.35f},    // 6: 4 waves of 32x32
 };
 
 // Skinny-kernel configurations: T output columns per lane (16*T per
@@ -104,7 +105,7 @@ struct Plan {
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-inline int tile_lds_bytes(const TileConfig& c) { return 2 * (c.bm + c.bn) * kBK * 2; }
+inline int tile_lds_bytes(const TileConfig& c) { return c.stages * (c.bm + c.bn) * 32 * 2; }
 inline int skinny_lds_bytes(const SkinnyConfig& c) {
   return (kSkinnyWaves / 2) * c.mg * c.t * 64 * 16;
 }
@@ -161,8 +162,9 @@ inline Plan make_plan(int64_t M, int64_t N, int64_t K, bool b_col_major, int cu_
   if (M <= kSkinnyMaxM) {
     const int mg = (int)ceil_div(M, 16);
     const int mgp = mg <= 1 ? 1 : (mg <= 2 ? 2 : 4);
-    // wide column stripes only when there are still enough workgroups
-    const int t = (ceil_div(N, 128) >= cu_count) ? 8 : 4;
+    // wide column stripes (longer contiguous row segments) unless that
+    // leaves fewer than half as many workgroups as compute units
+    const int t = (2 * ceil_div(N, 128) >= cu_count) ? 8 : 4;
     int idx = 0;
     for (int i = 0; i < kNumSkinnyConfigs; ++i)
       if (kSkinnyConfigs[i].t == t && kSkinnyConfigs[i].mg == mgp) idx = i;

@@ -10,7 +10,8 @@
 // and stores its tile once at the end. A and B are only read, so slabs are
 // fetched up to kStages - 1 ahead; C is never read.
 //
-// Pipeline (per wave, slab s, two 16-k steps kk = 0, 1):
+// Pipeline (per wave, slab s, two 16-k steps kk = 0, 1; shown for a ring of
+// four stages -- the depth NST is a per-configuration constant):
 //   MFMAs(s, 0)  while reading the operands of (s, 1)
 //   wait for this wave's loads of slab s+1, barrier (every wave's loads of
 //   slab s+1 have landed, and every wave is done with slab s-1), then issue
@@ -64,7 +65,6 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTileBK = 32;  // K per slab
-constexpr int kStages = 4;   // LDS ring depth
 
 // Raw buffer resource over [base, base + bytes): loads beyond it return zero
 // and touch no memory.
@@ -157,8 +157,10 @@ __device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
   return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)addr;
 }
 
-template <int BM, int BN, int WM, int WN, bool BCOL, bool OUT_BF16, bool DEBUG>
+template <int BM, int BN, int WM, int WN, int NST, bool BCOL, bool OUT_BF16, bool DEBUG>
 __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) {
+  constexpr int kStages = NST;  // LDS ring depth
+  static_assert(NST >= 3 && NST <= 6, "ring depth");
   constexpr int NW = WM * WN;
   constexpr int NT = NW * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -365,8 +367,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
       if (s < nk) issue_slab(s);
-    if (nk >= 3) wait_slabs(k2c);
-    else if (nk == 2) wait_slabs(k1c);
+    const int after = nk - 1 < kStages - 2 ? nk - 1 : kStages - 2;
+    if (after >= 4) wait_slabs(std::integral_constant<int, 4>{});
+    else if (after == 3) wait_slabs(std::integral_constant<int, 3>{});
+    else if (after == 2) wait_slabs(k2c);
+    else if (after == 1) wait_slabs(k1c);
     else wait_slabs(k0c);
     block_barrier();
     read_frags(0, 0, 0);
@@ -378,25 +383,27 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
   // destinations an SGPR plus a constant, and the buffer resources advance by
   // scalar adds.
   const int swl = (lrow >> 2) & 3;  // swzA of this lane's rows
-  uint32_t rA[2][2], rB[2][2];      // [kk][stage pair]: K-contiguous operands
+  constexpr int NPAIR = (kStages + 1) / 2;  // stage pairs: one base register each
+  uint32_t rA[2][NPAIR], rB[2][NPAIR];      // [kk][pair]: K-contiguous operands
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const uint32_t chunk = (uint32_t)(((lgrp ^ swl) ^ (2 * kk)) << 4);
     const uint32_t a = lds0 + (wm * WTM + lrow) * 64 + chunk;
-    rA[kk][0] = a;
-    rA[kk][1] = a + 2 * STAGE;
     const uint32_t b = lds0 + A_BYTES + (wn * WTN + lrow) * 64 + chunk;
-    rB[kk][0] = b;
-    rB[kk][1] = b + 2 * STAGE;
+#pragma unroll
+    for (int h = 0; h < NPAIR; ++h) {
+      rA[kk][h] = a + 2 * h * STAGE;
+      rB[kk][h] = b + 2 * h * STAGE;
+    }
   }
-  uint32_t rT[BCOL ? 1 : FN][2];    // row-major B: per block j, stage pair
+  uint32_t rT[BCOL ? 1 : FN][NPAIR];        // row-major B: per block j and pair
 #pragma unroll
   for (int j = 0; j < (BCOL ? 1 : FN); ++j) {
     const int n = wn * WTN + 32 * j + 16 * (tG & 1) + 4 * tq;
     const int col = SWB ? ((((n >> 5) ^ tj) << 5) | (n & 31)) : n;
     const uint32_t b = lds0 + A_BYTES + (8 * (tG >> 1) + tj) * PITCH + col * 2;
-    rT[j][0] = b;
-    rT[j][1] = b + 2 * STAGE;
+#pragma unroll
+    for (int h = 0; h < NPAIR; ++h) rT[j][h] = b + 2 * h * STAGE;
   }
   const uint32_t ldsw = __builtin_amdgcn_readfirstlane(lds0 + 1024 * wave);
 
@@ -436,7 +443,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
       static_for<0, kStages>([&](auto st_c) {
         constexpr int ST = decltype(st_c)::value;         // stage of slab s + ST
         constexpr int STN = (ST + 1) % kStages;            // stage of slab s + ST + 1
-        constexpr int STD = (ST + kStages - 1) % kStages;  // stage taking slab s + ST + 3
+        constexpr int STD = (ST + kStages - 1) % kStages;  // stage taking slab s + ST + kStages - 1
         // MFMAs (slab, 0) while reading the operands of (slab, 1)
         static_for<0, NMFMA>([&](auto k_c) {
           constexpr int k = decltype(k_c)::value;
@@ -447,9 +454,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
               read_fast(st_c, std::integral_constant<int, 1>{}, 1, std::integral_constant<int, idx>{});
           });
         });
-        wait_vmcnt<NDMA>();
+        wait_vmcnt<(kStages - 3) * NDMA>();
         block_barrier();
-        // MFMAs (slab, 1) while reading (slab + 1, 0) and loading slab + 3
+        // MFMAs (slab, 1) while reading (slab + 1, 0) and loading slab + kStages - 1
         static_for<0, NMFMA>([&](auto k_c) {
           constexpr int k = decltype(k_c)::value;
           acc[k / FN][k % FN] = mfma32(af[1][k / FN], bfr[1][k % FN], acc[k / FN][k % FN]);
@@ -491,8 +498,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
     const bool more = s + 1 < nk;
     if (more) {
       // this wave's loads of slab s+1 are done once at most the loads of the
-      // slabs issued after it remain (slab s+2, when it exists)
-      if (s + 2 < nk) wait_slabs(k1c);
+      // slabs issued after it remain (slabs s+2 .. s+kStages-2 that exist)
+      const int after = (nk - 2 - s) < (kStages - 3) ? (nk - 2 - s) : (kStages - 3);
+      if (after >= 3) wait_slabs(std::integral_constant<int, 3>{});
+      else if (after == 2) wait_slabs(k2c);
+      else if (after == 1) wait_slabs(k1c);
       else wait_slabs(k0c);
       block_barrier();
       if (s + kStages - 1 < nk) issue_slab(s + kStages - 1);
