@@ -93,7 +93,8 @@ tile_gemm_status_t tile_gemm_create(tile_gemm_t* out, int device);
  *
  * Shapes: M = 0 or N = 0 is a successful no-op (pointers are not checked);
  * K = 0 writes zeros to C (A and B are not read: they may be NULL and their
- * strides are not checked). M, N and K must be below 2^31.
+ * strides are not checked). M, N and K must be below 2^31, and A and B must
+ * each span less than 4 GiB (TILE_GEMM_ERR_BAD_SHAPE otherwise).
  *
  * Errors are returned before anything is enqueued and leave C untouched:
  * NULL_ARG, BAD_SHAPE, BAD_STRIDE, MISALIGNED, ALIAS, DTYPE, DEVICE (the

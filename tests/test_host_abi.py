@@ -100,6 +100,8 @@ def test_check_args_ok_layouts():
     (dict(C=A0 + 1024), Status.ERR_ALIAS),                           # C inside A
     (dict(C=B0 - 1024), Status.ERR_ALIAS),                           # C runs into B
     (dict(s=None), Status.ERR_NULL_ARG),
+    (dict(M=70000, K=32768, s=(32768, 1, 64, 1, 64, 1)), Status.ERR_BAD_SHAPE),   # A >= 4 GiB
+    (dict(N=70000, K=32768, s=(32768, 1, 1, 32768, 70000, 1)), Status.ERR_BAD_SHAPE),  # B >= 4 GiB
 ])
 def test_check_args_errors(kw, want):
     if "s" in kw and kw["s"] is None:

@@ -55,6 +55,20 @@ __device__ __forceinline__ uint4 load8_masked(const uint16_t* row, int c, int le
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
+
+// Streaming (non-temporal) loads for data read exactly once: the hardware
+// keeps them from displacing reused lines in the caches.
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load8_stream(const void* p) {
+  const u32x2_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_nt*>(p));
+  return make_uint2(v.x, v.y);
+}
+
 // Pack the low (hi_half = false) or high halves of two dwords: the result
 // holds x's half in bits 0-15 and y's half in bits 16-31.
 __device__ __forceinline__ uint32_t pack_halves(uint32_t x, uint32_t y, bool hi_half) {

@@ -89,7 +89,85 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(SkinnyArgs p) {
 #pragma unroll
     for (int c = 0; c < T; ++c) acc[g][c] = floatx4{};
 
-  for (int kb = kb0; kb < kb1; kb += U) {
+  // ---- fast path: interior column stripe, full 32-k blocks. Loads are
+  // unconditional (rows of A past M are clamped to row M-1; their products
+  // only reach accumulator rows that are never stored), double-buffered so
+  // the next block's loads are in flight while this block is multiplied.
+  int kb = kb0;
+  const int kb_full = kb1 < (K >> 5) ? kb1 : (K >> 5);  // end of full blocks
+  if (cols_full && kb_full - kb0 >= 2) {
+    struct Blk {
+      bf16x8 a[MG];
+      RowChunk<T> rows[8];  // row-major B: 8 k rows x T columns
+      bf16x8 bc[T];         // column-major B: T columns x 8 k
+    };
+    // per-lane element offsets (32-bit, fixed for the loop) from a uniform
+    // per-block base, so each load is one SGPR base plus one VGPR offset
+    uint32_t offA[MG];
+#pragma unroll
+    for (int g = 0; g < MG; ++g) {
+      const int row = (16 * g + nl) < M ? (16 * g + nl) : (M - 1);
+      offA[g] = (uint32_t)(row * p.lda + 8 * kg);
+    }
+    uint32_t offB[BCOL ? T : 8];
+#pragma unroll
+    for (int r = 0; r < (BCOL ? T : 8); ++r)
+      offB[r] = BCOL ? (uint32_t)((ncol + r) * p.ldb + 8 * kg) : (uint32_t)((8 * kg + r) * p.ldb + ncol);
+    auto load_blk = [&](int b, Blk& x) {
+      const uint16_t* ab = p.A + b * 32;
+      const uint16_t* bb = BCOL ? p.B + b * 32 : p.B + (int64_t)b * 32 * p.ldb;
+#pragma unroll
+      for (int g = 0; g < MG; ++g) x.a[g] = as_bf16x8(*reinterpret_cast<const uint4*>(ab + offA[g]));
+      // B is read exactly once: streaming loads
+      if constexpr (BCOL) {
+#pragma unroll
+        for (int c = 0; c < T; ++c) x.bc[c] = as_bf16x8(load16_stream(bb + offB[c]));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          if constexpr (T == 8) {
+            const uint4 v = load16_stream(bb + offB[r]);
+            x.rows[r].w[0] = v.x; x.rows[r].w[1] = v.y; x.rows[r].w[2] = v.z; x.rows[r].w[3] = v.w;
+          } else {
+            const uint2 v = load8_stream(bb + offB[r]);
+            x.rows[r].w[0] = v.x; x.rows[r].w[1] = v.y;
+          }
+        }
+      }
+    };
+    auto compute_blk = [&](const Blk& x) {
+#pragma unroll
+      for (int c = 0; c < T; ++c) {
+        bf16x8 bv;
+        if constexpr (BCOL) {
+          bv = x.bc[c];
+        } else {
+          uint32_t w[4];
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            w[d] = pack_halves(x.rows[2 * d].w[c >> 1], x.rows[2 * d + 1].w[c >> 1], (c & 1) != 0);
+          bv = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+        }
+#pragma unroll
+        for (int g = 0; g < MG; ++g) acc[g][c] = mfma16(x.a[g], bv, acc[g][c]);
+      }
+    };
+    Blk X, Y;
+    load_blk(kb, X);
+    load_blk(kb + 1, Y);
+    for (; kb + 4 <= kb_full; kb += 2) {
+      compute_blk(X);
+      load_blk(kb + 2, X);
+      compute_blk(Y);
+      load_blk(kb + 3, Y);
+    }
+    compute_blk(X);
+    compute_blk(Y);
+    kb += 2;
+  }
+
+  // ---- general path: the rest of this wave's blocks (edges, K tail)
+  for (; kb < kb1; kb += U) {
     bf16x8 af[U][MG];
     bf16x8 bt[U][T];
     // issue every load of U blocks before the first MFMA

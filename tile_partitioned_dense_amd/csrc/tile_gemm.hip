@@ -109,9 +109,17 @@ tile_gemm_status_t check_args(const void* A, const void* B, const void* C, int64
                 brow ? "b_k" : "b_n", (long long)ldb);
 
   // Byte extents actually touched.
+  const int64_t a_span = 2 * ((M - 1) * s->a_m + K);
+  const int64_t b_span = 2 * (brow ? (K - 1) * s->b_k + N : (N - 1) * s->b_n + K);
+  // the kernels address each operand with 32-bit byte offsets
+  if (a_span >= ((int64_t)1 << 32))
+    return fail(TILE_GEMM_ERR_BAD_SHAPE, "A: spans %lld bytes, must be below 4 GiB", (long long)a_span);
+  if (b_span >= ((int64_t)1 << 32))
+    return fail(TILE_GEMM_ERR_BAD_SHAPE, "B: spans %lld bytes, must be below 4 GiB", (long long)b_span);
+
   const uintptr_t a0 = (uintptr_t)A, b0 = (uintptr_t)B, c0 = (uintptr_t)C;
-  const uintptr_t a1 = a0 + (uintptr_t)(2 * ((M - 1) * s->a_m + K));
-  const uintptr_t b1 = b0 + (uintptr_t)(2 * (brow ? (K - 1) * s->b_k + N : (N - 1) * s->b_n + K));
+  const uintptr_t a1 = a0 + (uintptr_t)a_span;
+  const uintptr_t b1 = b0 + (uintptr_t)b_span;
   const uintptr_t c1 = c0 + (uintptr_t)(esz * ((M - 1) * s->c_m + N));
   if (overlap(c0, c1, a0, a1)) return fail(TILE_GEMM_ERR_ALIAS, "C overlaps A (C is written)");
   if (overlap(c0, c1, b0, b1)) return fail(TILE_GEMM_ERR_ALIAS, "C overlaps B (C is written)");
