@@ -33,6 +33,18 @@ def host_out(C) -> np.ndarray:
     return host_bits(C)
 
 
+def tile_config_table():
+    """(bm, bn, wm, wn, stages) of every compiled tile configuration, read from
+    the planner's table so new configurations are covered automatically."""
+    import os
+    import re
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "tile_partitioned_dense_amd", "csrc", "plan.hpp")).read()
+    body = re.search(r"kTileConfigs\[kNumTileConfigs\]\s*=\s*\{(.*?)\n\};", src, re.S).group(1)
+    rows = re.findall(r"^\s*\{(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),", body, re.M)
+    return [tuple(int(v) for v in r) for r in rows]
+
+
 def round_up(x, m):
     return (x + m - 1) // m * m
 

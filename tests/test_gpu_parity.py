@@ -13,7 +13,7 @@ import oracle
 import tile_partitioned_dense_amd as tg
 from tile_partitioned_dense_amd import synth
 
-from gpu_helpers import Case, check, host_out, workload_case
+from gpu_helpers import Case, check, host_out, tile_config_table, workload_case
 
 pytestmark = pytest.mark.gpu
 
@@ -57,8 +57,7 @@ def _parity(g, case, dtype, flags=0, integer=False):
 # ------------------------------------------------ every compiled configuration
 
 def tile_shape(cfg):
-    bm, bn = {0: (256, 256), 1: (256, 224), 2: (256, 160), 3: (128, 256), 4: (256, 128),
-              5: (128, 128), 6: (64, 64)}[cfg]
+    bm, bn = tile_config_table()[cfg][:2]
     return 2 * bm + 37, 2 * bn + 19     # several tiles plus a ragged edge in M and N
 
 

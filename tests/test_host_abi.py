@@ -125,3 +125,16 @@ def test_alias_adjacent_is_not_overlap():
     a_end = A0 + 2 * (63 * 64 + 64)
     assert chk(C=a_end) == Status.OK
     assert chk(C=a_end - 16) == Status.ERR_ALIAS
+
+
+def test_config_counts_match_the_compiled_tables():
+    """The Python-side counts of compiled configurations (build loop, forced
+    configuration flags) equal the table sizes in plan.hpp."""
+    from tile_partitioned_dense_amd import binding, build
+    plan_src = open(os.path.join(ROOT, "tile_partitioned_dense_amd", "csrc", "plan.hpp")).read()
+    n_tile = int(re.search(r"kNumTileConfigs\s*=\s*(\d+)", plan_src).group(1))
+    n_skinny = int(re.search(r"kNumSkinnyConfigs\s*=\s*(\d+)", plan_src).group(1))
+    assert binding.N_TILE_CONFIGS == build.N_TILE_CONFIGS == n_tile
+    assert binding.N_SKINNY_CONFIGS == build.N_SKINNY_CONFIGS == n_skinny
+    table = re.search(r"kTileConfigs\[kNumTileConfigs\]\s*=\s*\{(.*?)\n\};", plan_src, re.S).group(1)
+    assert len(re.findall(r"^\s*\{\d+,", table, re.M)) == n_tile

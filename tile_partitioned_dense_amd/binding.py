@@ -45,7 +45,7 @@ def DEBUG_FORCE_SKINNY(c: int) -> int:
     return ((c + 1) & 0xFF) << 16
 
 
-N_TILE_CONFIGS = 7
+N_TILE_CONFIGS = 11
 N_SKINNY_CONFIGS = 6
 
 VARIANT_NONE, VARIANT_TILE, VARIANT_SKINNY = 0, 1, 2

@@ -28,9 +28,13 @@ constexpr int kSkinnyMaxM = 64;    // M at or below this takes the skinny kernel
 constexpr int kSkinnyWaves = 8;    // waves per skinny workgroup, splitting K
 constexpr int kXcds = 8;           // MI355X: 8 accelerator dies share one dispatcher
 
-// Tile-kernel configurations compiled into the library. `eff` is the fraction
-// of the MFMA peak a compute unit sustains when running this configuration;
-// the planner uses it only to rank configurations for a shape.
+// Tile-kernel configurations compiled into the library. `eff` is the
+// throughput a compute unit sustains on this configuration relative to
+// configuration 7, measured with random bf16 data on shapes that keep every
+// compute unit busy (a partly idle chip clocks higher and would flatter it);
+// the planner uses it only to rank configurations for a shape. Eight-wave
+// configurations put two waves on each SIMD, so one wave's LDS reads, loads
+// and barrier waits overlap the other's MFMAs.
 struct TileConfig {
   int bm, bn;   // owned tile
   int wm, wn;   // wave grid inside the workgroup (each wave owns (bm/wm) x (bn/wn))
@@ -38,15 +42,19 @@ struct TileConfig {
   float eff;
 };
 
-constexpr int kNumTileConfigs = 7;
+constexpr int kNumTileConfigs = 11;
 constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
-    {256, 256, 2, 2, 4, 1.00f},  // 0: 4 waves of 128x128
-    {256, 224, 4, 1, 5, 0.93f},  // 1: 4 waves of 64x224
-    {256, 160, 4, 1, 5, 0.85f},  // 2: 4 waves of 64x160
+    {256, 256, 2, 2, 4, 0.88f},  // 0: 4 waves of 128x128
+    {256, 224, 4, 1, 5, 1.03f},  // 1: 4 waves of 64x224
+    {256, 160, 4, 1, 5, 0.95f},  // 2: 4 waves of 64x160
     {128, 256, 2, 2, 5, 0.85f},  // 3: 4 waves of 64x128
-    {256, 128, 2, 2, 5, 0.85f},  // 4: 4 waves of 128x64
-    {128, 128, 2, 2, 4, 0.70f},  // 5: 4 waves of 64x64
-    {64, 64, 2, 2, 4, 0.35f},    // 6: 4 waves of 32x32
+    {256, 128, 2, 2, 5, 0.78f},  // 4: 4 waves of 128x64
+    {128, 128, 2, 2, 4, 0.81f},  // 5: 4 waves of 64x64
+    {64, 64, 2, 2, 4, 0.46f},    // 6: 4 waves of 32x32
+    {256, 256, 2, 4, 4, 1.00f},  // 7: 8 waves of 128x64
+    {256, 256, 4, 2, 4, 0.99f},  // 8: 8 waves of 64x128
+    {256, 224, 8, 1, 5, 1.02f},  // 9: 8 waves of 32x224
+    {256, 160, 8, 1, 5, 0.96f},  // 10: 8 waves of 32x160
 };
 
 // Skinny-kernel configurations: T output columns per lane (16*T per

@@ -151,10 +151,14 @@ hipError_t dispatch_tile(int cfg, const tg::TileArgs& a, const tg::Variant& v, h
     case 4: return tg::launch_tile<4>(a, v, st);
     case 5: return tg::launch_tile<5>(a, v, st);
     case 6: return tg::launch_tile<6>(a, v, st);
+    case 7: return tg::launch_tile<7>(a, v, st);
+    case 8: return tg::launch_tile<8>(a, v, st);
+    case 9: return tg::launch_tile<9>(a, v, st);
+    case 10: return tg::launch_tile<10>(a, v, st);
   }
   return hipErrorInvalidValue;
 }
-static_assert(tg::kNumTileConfigs == 7, "dispatch_tile covers every tile configuration");
+static_assert(tg::kNumTileConfigs == 11, "dispatch_tile covers every tile configuration");
 
 hipError_t dispatch_skinny(int cfg, const tg::SkinnyArgs& a, int64_t grid, const tg::Variant& v,
                            hipStream_t st) {

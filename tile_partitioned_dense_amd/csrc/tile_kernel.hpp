@@ -1,24 +1,32 @@
 // tile_kernel.hpp -- the LDS-staged bf16 MFMA tile kernel for gfx950.
 //
 // One workgroup owns one BM x BN tile of C (found with tile_of) and is its
-// only writer. It walks K in 32-wide slabs in ascending order through a ring
-// of kStages LDS buffers:
+// only writer. Four or eight waves (one or two per SIMD) split the tile into
+// WM x WN wave tiles. The workgroup walks K in 32-wide slabs in ascending
+// order through a ring of NST LDS buffers:
 //
 //   global --(buffer load straight into LDS, no registers)--> LDS stage
 //   LDS stage --(ds_read)--> MFMA operands --> fp32 accumulators
 //
 // and stores its tile once at the end. A and B are only read, so slabs are
-// fetched up to kStages - 1 ahead; C is never read.
+// fetched up to NST - 1 ahead; C is never read.
 //
-// Pipeline (per wave, slab s, two 16-k steps kk = 0, 1; shown for a ring of
-// four stages -- the depth NST is a per-configuration constant):
-//   MFMAs(s, 0)  while reading the operands of (s, 1)
-//   wait for this wave's loads of slab s+1, barrier (every wave's loads of
-//   slab s+1 have landed, and every wave is done with slab s-1), then issue
-//   the loads of slab s+3 into slab s-1's stage
-//   MFMAs(s, 1)  while reading the operands of (s+1, 0)
-// The barrier is a bare s_barrier with explicit vmcnt waits: a full fence
-// would also wait for the loads that are meant to stay in flight.
+// Pipeline (per wave, slab s, two 16-k steps kk = 0, 1):
+//   MFMAs(s, 0)  while reading the operands of (s, 1) and issuing the second
+//                half of this wave's loads of slab s + NST - 2
+//   wait for this wave's loads of slab s + 1, barrier (every wave's loads of
+//   slab s + 1 have landed, and every wave is done with slab s - 1)
+//   MFMAs(s, 1)  while reading the operands of (s + 1, 0) and issuing the
+//                first half of the loads of slab s + NST - 1 into the stage
+//                slab s - 1 just freed
+// Splitting each slab's loads over two steps keeps the texture unit's queue
+// from filling (a wave that finds it full stalls, MFMAs included). The
+// barrier is a bare s_barrier with explicit vmcnt waits: a full fence would
+// also wait for the loads that are meant to stay in flight.
+//
+// Accumulators hold each 32 x 32 block of C transposed (see mma), so a lane
+// owns four consecutive columns of one row. The epilogue stages each wave's
+// results through the then idle ring and writes C as 16-byte row chunks.
 //
 // LDS layouts (all reads conflict-free on 64 banks):
 //  * A, and B when column-major (both K-contiguous): a slab row is 32 bf16 =
@@ -63,6 +71,8 @@ struct TileArgs {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kTileBK = 32;  // K per slab
 
@@ -157,6 +167,16 @@ __device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
   return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)addr;
 }
 
+// One 32 x 32 x 16 step of a C block held transposed: the B fragment goes in
+// as the MFMA's row operand and the A fragment as its column operand, so the
+// MFMA computes the block of C^T. Lane l then holds C row (l % 32), columns
+// 8 q + 4 (l / 32) + r in accumulator element 4 q + r: four consecutive
+// columns per q, which the epilogue stores as one vector. Every output element
+// is still the sum over the same 16 products.
+__device__ __forceinline__ floatx16 mma(const bf16x8& a_frag, const bf16x8& b_frag, const floatx16& acc) {
+  return mfma32(b_frag, a_frag, acc);
+}
+
 template <int BM, int BN, int WM, int WN, int NST, bool BCOL, bool OUT_BF16, bool DEBUG>
 __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) {
   constexpr int kStages = NST;  // LDS ring depth
@@ -166,7 +186,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(NW == 4, "four waves per workgroup");
+  static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
   constexpr int BK = kTileBK;
   constexpr int A_BYTES = BM * BK * 2;  // per stage
   constexpr int B_BYTES = BN * BK * 2;
@@ -288,6 +308,21 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
     }
   };
 
+  // Issue DMA units [lo, hi) of full slab s: units 0 .. A_PER-1 are this
+  // wave's A loads, then its b_cnt B loads.
+  auto issue_units = [&](int s, int lo, int hi) {
+    const uint32_t la = lds0 + (s % kStages) * STAGE;
+    const uint32_t lb = la + A_BYTES;
+    const i32x4 rsA = make_rsrc(a_panel + s * a_step, a_bytes - s * a_step);
+    const i32x4 rsB = make_rsrc(b_panel + s * b_step, b_bytes - s * b_step);
+#pragma unroll
+    for (int t = 0; t < A_PER; ++t)
+      if (t >= lo && t < hi) dma16(la + 1024 * (wave + NW * t), rsA, voA[t], 0u);
+#pragma unroll
+    for (int t = 0; t < B_MAX; ++t)
+      if (t < b_cnt && A_PER + t >= lo && A_PER + t < hi) dma16(lb + 1024 * (wave + NW * t), rsB, voB[t], 0u);
+  };
+
   // vmcnt waits are per wave. Wait until at most SLABS slabs' worth of this
   // wave's loads remain (waves < B_DMA % NW issue one more B load per slab).
   auto wait_slabs = [&](auto slabs_c) {
@@ -346,7 +381,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(af[slot][i], bfr[slot][j], acc[i][j]);
+      for (int j = 0; j < FN; ++j) acc[i][j] = mma(af[slot][i], bfr[slot][j], acc[i][j]);
   };
   // Scheduling pattern for one 16-k step: each of the next step's operand
   // reads is issued right after one MFMA of this step, so reads overlap the
@@ -362,17 +397,39 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
     }
   };
 
-  // ---- prologue: slabs 0..kStages-2 in flight, slab 0 ready, its first operands read
+  // The steady loop below spreads each slab's loads over two steps: the
+  // first ceil(n/2) of a wave's n DMA units go out after the barrier of one
+  // slab, the rest in the first step of the next, so the loads of a slab
+  // never arrive at the texture unit faster than it drains them.
+  const int n_steady = nk_full - (kStages - 1);  // slabs the steady loop may cover
+  const bool split = n_steady >= kStages;        // the steady loop runs
+  const int ndma = A_PER + b_cnt;
+  const int nh1 = (ndma + 1) / 2;
+
+  // ---- prologue: slabs 0..kStages-2 in flight (the last one only its first
+  // half when the steady loop runs), slab 0 ready, its first operands read
   if (nk > 0) {
 #pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
-      if (s < nk) issue_slab(s);
-    const int after = nk - 1 < kStages - 2 ? nk - 1 : kStages - 2;
-    if (after >= 4) wait_slabs(std::integral_constant<int, 4>{});
-    else if (after == 3) wait_slabs(std::integral_constant<int, 3>{});
-    else if (after == 2) wait_slabs(k2c);
-    else if (after == 1) wait_slabs(k1c);
-    else wait_slabs(k0c);
+    for (int s = 0; s < kStages - 1; ++s) {
+      if (s < nk) {
+        if (split && s == kStages - 2) issue_units(s, 0, nh1);
+        else issue_slab(s);
+      }
+    }
+    if (split) {
+      // everything issued after slab 0: kStages-3 whole slabs and a first half
+      if (B_MAX != B_MIN && b_cnt == B_MAX)
+        wait_vmcnt<(kStages - 3) * (A_PER + B_MAX) + (A_PER + B_MAX + 1) / 2>();
+      else
+        wait_vmcnt<(kStages - 3) * (A_PER + B_MIN) + (A_PER + B_MIN + 1) / 2>();
+    } else {
+      const int after = nk - 1 < kStages - 2 ? nk - 1 : kStages - 2;
+      if (after >= 4) wait_slabs(std::integral_constant<int, 4>{});
+      else if (after == 3) wait_slabs(std::integral_constant<int, 3>{});
+      else if (after == 2) wait_slabs(k2c);
+      else if (after == 1) wait_slabs(k1c);
+      else wait_slabs(k0c);
+    }
     block_barrier();
     read_frags(0, 0, 0);
   }
@@ -429,55 +486,99 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
   };
   constexpr int NUNIT = FM + FN;
   constexpr int UPM = (NUNIT + NMFMA - 1) / NMFMA;  // operand units read after each MFMA
+  constexpr int RPU = BCOL ? 1 : 2;                  // LDS read instructions per B unit
+  // Hold the scheduler to "one MFMA, then that MFMA's share of the next
+  // step's operand reads": left alone it sinks the reads below the MFMAs that
+  // free their registers, and the next step then waits on LDS latency.
+  auto pin_pattern = [&]() {
+    static_for<0, NMFMA>([&](auto k_c) {
+      constexpr int k = decltype(k_c)::value;
+      constexpr int lo = k * UPM, hi = (k + 1) * UPM < NUNIT ? (k + 1) * UPM : NUNIT;
+      constexpr int n_a = (lo < FM ? (hi < FM ? hi : FM) - lo : 0);
+      constexpr int n_b = (hi > FM ? hi - (lo > FM ? lo : FM) : 0);
+      constexpr int n_rd = lo < NUNIT ? n_a + RPU * n_b : 0;
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (n_rd > 0) __builtin_amdgcn_sched_group_barrier(0x100, n_rd, 0);
+    });
+  };
 
   auto steady = [&](auto bc_c) -> int {
     constexpr int BC = decltype(bc_c)::value;  // this wave's B loads per slab
     constexpr int NDMA = A_PER + BC;
-    constexpr int DPMF = (NDMA + NMFMA - 1) / NMFMA;
-    const int n_steady = nk_full - (kStages - 1);
+    constexpr int NH1 = (NDMA + 1) / 2;        // units issued after a barrier
+    constexpr int NH2 = NDMA - NH1;            // units issued one step later
+    constexpr int D1 = (NH1 + NMFMA - 1) / NMFMA;
+    constexpr int D2 = (NH2 + NMFMA - 1) / NMFMA;
     int s = 0;
-    if (n_steady < kStages) return 0;
-    i32x4 rsAn = make_rsrc(a_panel + (kStages - 1) * a_step, a_bytes - (kStages - 1) * a_step);
-    i32x4 rsBn = make_rsrc(b_panel + (kStages - 1) * b_step, b_bytes - (kStages - 1) * b_step);
+    if (!split) return 0;
+    // Unit U of the slab whose stage is STG, from resources rA_/rB_.
+    auto unit = [&](auto stg_c, auto u_c, const i32x4& rA_, const i32x4& rB_) {
+      constexpr int STG = decltype(stg_c)::value, U = decltype(u_c)::value;
+      if constexpr (U < A_PER)
+        dma16_off<STG * STAGE + 1024 * NW * U>(ldsw, rA_, voA[U]);
+      else
+        dma16_off<STG * STAGE + A_BYTES + 1024 * NW * (U - A_PER)>(ldsw, rB_, voB[U - A_PER]);
+    };
+    // resources of slab kStages-2, whose first half the prologue issued
+    i32x4 rsAn = make_rsrc(a_panel + (kStages - 2) * a_step, a_bytes - (kStages - 2) * a_step);
+    i32x4 rsBn = make_rsrc(b_panel + (kStages - 2) * b_step, b_bytes - (kStages - 2) * b_step);
     for (; s + kStages <= n_steady; s += kStages) {
       static_for<0, kStages>([&](auto st_c) {
         constexpr int ST = decltype(st_c)::value;         // stage of slab s + ST
         constexpr int STN = (ST + 1) % kStages;            // stage of slab s + ST + 1
-        constexpr int STD = (ST + kStages - 1) % kStages;  // stage taking slab s + ST + kStages - 1
-        // MFMAs (slab, 0) while reading the operands of (slab, 1)
+        constexpr int STD = (ST + kStages - 1) % kStages;  // stage of slab s + ST + kStages - 1
+        constexpr int ST2 = (ST + kStages - 2) % kStages;  // stage of slab s + ST + kStages - 2
+        // MFMAs (slab, 0) while reading the operands of (slab, 1) and issuing
+        // the second half of slab + kStages - 2 (its stage was freed by the
+        // barrier of the previous slab)
         static_for<0, NMFMA>([&](auto k_c) {
           constexpr int k = decltype(k_c)::value;
-          acc[k / FN][k % FN] = mfma32(af[0][k / FN], bfr[0][k % FN], acc[k / FN][k % FN]);
+          acc[k / FN][k % FN] = mma(af[0][k / FN], bfr[0][k % FN], acc[k / FN][k % FN]);
           static_for<0, UPM>([&](auto r_c) {
             constexpr int idx = k * UPM + decltype(r_c)::value;
             if constexpr (idx < NUNIT)
               read_fast(st_c, std::integral_constant<int, 1>{}, 1, std::integral_constant<int, idx>{});
           });
+          static_for<0, D2>([&](auto d_c) {
+            constexpr int t = k * D2 + decltype(d_c)::value;
+            if constexpr (t < NH2)
+              unit(std::integral_constant<int, ST2>{}, std::integral_constant<int, NH1 + t>{}, rsAn, rsBn);
+          });
         });
+        pin_pattern();
+        advance_rsrc(rsAn, (uint32_t)a_step);
+        advance_rsrc(rsBn, (uint32_t)b_step);
+        // slab + 1 has landed once at most the loads issued after its last
+        // half remain: halves of later slabs, kStages - 3 slabs' worth
         wait_vmcnt<(kStages - 3) * NDMA>();
         block_barrier();
-        // MFMAs (slab, 1) while reading (slab + 1, 0) and loading slab + kStages - 1
+        // MFMAs (slab, 1) while reading (slab + 1, 0) and issuing the first
+        // half of slab + kStages - 1 into the stage the barrier just freed
         static_for<0, NMFMA>([&](auto k_c) {
           constexpr int k = decltype(k_c)::value;
-          acc[k / FN][k % FN] = mfma32(af[1][k / FN], bfr[1][k % FN], acc[k / FN][k % FN]);
+          acc[k / FN][k % FN] = mma(af[1][k / FN], bfr[1][k % FN], acc[k / FN][k % FN]);
           static_for<0, UPM>([&](auto r_c) {
             constexpr int idx = k * UPM + decltype(r_c)::value;
             if constexpr (idx < NUNIT)
               read_fast(std::integral_constant<int, STN>{}, std::integral_constant<int, 0>{}, 0,
                         std::integral_constant<int, idx>{});
           });
-          static_for<0, DPMF>([&](auto d_c) {
-            constexpr int t = k * DPMF + decltype(d_c)::value;
-            if constexpr (t < A_PER)
-              dma16_off<STD * STAGE + 4096 * t>(ldsw, rsAn, voA[t]);
-            else if constexpr (t < NDMA)
-              dma16_off<STD * STAGE + A_BYTES + 4096 * (t - A_PER)>(ldsw, rsBn, voB[t - A_PER]);
+          static_for<0, D1>([&](auto d_c) {
+            constexpr int t = k * D1 + decltype(d_c)::value;
+            if constexpr (t < NH1)
+              unit(std::integral_constant<int, STD>{}, std::integral_constant<int, t>{}, rsAn, rsBn);
           });
         });
-        advance_rsrc(rsAn, (uint32_t)a_step);
-        advance_rsrc(rsBn, (uint32_t)b_step);
+        pin_pattern();
       });
     }
+    // The second half of slab s + kStages - 2 (stage kStages - 2, as s is a
+    // multiple of kStages) is still due; after it every slab in flight is
+    // whole again, which is what the general loop expects.
+    static_for<0, NH2>([&](auto t_c) {
+      unit(std::integral_constant<int, kStages - 2>{}, std::integral_constant<int, NH1 + decltype(t_c)::value>{},
+           rsAn, rsBn);
+    });
     return s;
   };
   int s0 = 0;
@@ -517,27 +618,86 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
   }
 
   // Epilogue: each accumulator element is stored exactly once, by its owner.
+  // The K loop is over, so the LDS ring is free: each wave stages strips of
+  // its sub-tile there (SH rows x WTN columns, row-major, padded rows) and
+  // reads them back as 16-byte row chunks, so every global store writes whole
+  // row segments instead of scattered 8- or 16-byte pieces.
+  constexpr int ESZ = OUT_BF16 ? 2 : 4;
+  constexpr int RING = kStages * STAGE;
+  constexpr int OPITCH = WTN * ESZ + 16;  // staged row pitch (bytes); /16 is odd
+  constexpr int SH = (NW * 32 * OPITCH <= RING) ? 32 : 16;
+  static_assert(NW * SH * OPITCH <= RING, "a staged strip of every wave fits the ring");
+  constexpr int CH = WTN * ESZ / 16;  // 16-byte chunks per staged row
+  constexpr int EPC = 16 / ESZ;       // elements per chunk
+  static_assert((SH * CH) % 64 == 0, "a strip is a whole number of wave-wide chunk rows");
+  __syncthreads();  // every wave is done reading the ring
+  const uint32_t stg = lds0 + (uint32_t)(wave * SH * OPITCH);
   const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = n0 + wn * WTN + 32 * j + lrow;
+    for (int hs = 0; hs < 32 / SH; ++hs) {
+      // lane l holds row (l % 32) of the block and, for q = 0..3, the four
+      // consecutive columns 8 q + 4 (l / 32) .. + 3 (accumulator 4 q .. 4 q + 3)
+      const int rl = lrow - SH * hs;
+      if (SH == 32 || (lrow >> 4) == hs) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * WTM + 32 * i + 8 * (v >> 2) + 4 * lgrp + (v & 3);
-        if (full_mn || (row < M && col < N)) {
-          const int64_t off = (int64_t)row * p.ldc + col;
-          if constexpr (OUT_BF16) {
-            static_cast<uint16_t*>(p.C)[off] = f32_to_bf16_rne(acc[i][j][v]);
-          } else {
-            static_cast<float*>(p.C)[off] = acc[i][j][v];
-          }
-          if constexpr (DEBUG) {
-            if (p.flags & kDbgCount) atomicAdd(p.counts + (int64_t)row * N + col, 1u);
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t a = stg + (uint32_t)(rl * OPITCH + (32 * j + 8 * q + 4 * lgrp) * ESZ);
+            const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
+            const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+            if constexpr (OUT_BF16) {
+              const u32x2v w = {(uint32_t)f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16),
+                                (uint32_t)f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16)};
+              *(__attribute__((address_space(3))) u32x2v*)(uintptr_t)a = w;
+            } else {
+              const floatx4 w = {v0, v1, v2, v3};
+              *(__attribute__((address_space(3))) floatx4*)(uintptr_t)a = w;
+            }
           }
         }
       }
+      // The strip is private to this wave and one wave's LDS operations run
+      // in order, so its reads below see its writes above.
+      wait_lgkmcnt0();
+      const int grow0 = m0 + wm * WTM + 32 * i + SH * hs;
+      const int gcol0 = n0 + wn * WTN;
+#pragma unroll
+      for (int c0 = 0; c0 < SH * CH; c0 += 64) {
+        const int c = c0 + lane;
+        const int r = c / CH, ch = c - (c / CH) * CH;
+        const u32x4v lv = *(const __attribute__((address_space(3))) u32x4v*)(uintptr_t)(stg + (uint32_t)(r * OPITCH + ch * 16));
+        const uint4 v = make_uint4(lv.x, lv.y, lv.z, lv.w);
+        const int row = grow0 + r, col = gcol0 + ch * EPC;
+        const int64_t off = (int64_t)row * p.ldc + col;
+        char* cbase = static_cast<char*>(p.C) + off * ESZ;
+        if (full_mn || (row < M && col + EPC <= N)) {
+          *reinterpret_cast<uint4*>(cbase) = v;
+          if constexpr (DEBUG) {
+            if (p.flags & kDbgCount)
+#pragma unroll
+              for (int e = 0; e < EPC; ++e) atomicAdd(p.counts + (int64_t)row * N + col + e, 1u);
+          }
+        } else if (row < M) {
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) {
+            if (col + e < N) {
+              if constexpr (OUT_BF16) {
+                reinterpret_cast<uint16_t*>(cbase)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+              } else {
+                reinterpret_cast<uint32_t*>(cbase)[e] = w[e];
+              }
+              if constexpr (DEBUG) {
+                if (p.flags & kDbgCount) atomicAdd(p.counts + (int64_t)row * N + col + e, 1u);
+              }
+            }
+          }
+        }
+      }
+      wait_lgkmcnt0();
     }
   }
 }
