@@ -18,12 +18,17 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest, ties to even: gfx950 converts in hardware
+// (v_cvt_pk_bf16_f32, two values per instruction, NaN -> quiet NaN). The
+// packed form puts `lo` in bits 0-15 and `hi` in bits 16-31.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // 32x32x16 bf16 MFMA, fp32 accumulate. Lane l supplies row (l % 32) of the

@@ -257,7 +257,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(SkinnyArgs p) {
             if (col < N) {
               const int64_t off = (int64_t)row * p.ldc + col;
               if constexpr (OUT_BF16) {
-                static_cast<uint16_t*>(p.C)[off] = f32_to_bf16_rne(acc[g][c][v]);
+                static_cast<uint16_t*>(p.C)[off] = f32_to_bf16(acc[g][c][v]);
               } else {
                 static_cast<float*>(p.C)[off] = acc[g][c][v];
               }

@@ -649,8 +649,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
             const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
             const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
             if constexpr (OUT_BF16) {
-              const u32x2v w = {(uint32_t)f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16),
-                                (uint32_t)f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16)};
+              const u32x2v w = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
               *(__attribute__((address_space(3))) u32x2v*)(uintptr_t)a = w;
             } else {
               const floatx4 w = {v0, v1, v2, v3};
