@@ -8,7 +8,7 @@
  * section "Safety without a visible tax"), built on the partition discipline
  * of the same page (sections "Ownership crosses the launch boundary" and
  * "The useful boundary"): the output is split into disjoint tiles before
- * launch, each workgroup exclusively owns one tile and is the only writer of
+ * launch, each tile is exclusively owned by one workgroup, the only writer of
  * it, and A and B are shared read-only views.
  *
  * Numerics: every output element is the sum of its K products accumulated in
@@ -144,10 +144,15 @@ typedef enum {
 /*
  * The launch plan for a shape: a pure function of (M, N, K, B layout,
  * compute-unit count). The output type never changes it.
- *   tile kernel:   each workgroup owns a bm x bn tile; grid = tiles_m*tiles_n.
+ *   tile kernel:   C is cut into tiles = tiles_m*tiles_n tiles of bm x bn.
+ *                  When they fit in one round on the compute units every
+ *                  workgroup owns one (grid = tiles); otherwise grid is about
+ *                  tiles / ceil(tiles / cu_count) (a multiple of 8) and
+ *                  workgroup w owns tiles w, w + grid, w + 2 grid, ..., each
+ *                  whole, with its own K loop and store.
  *   skinny kernel: each workgroup owns rows [0, M) x bn columns; the waves of
  *                  one workgroup split K and combine their partial sums in a
- *                  fixed order; grid = tiles_n, tiles_m = 1.
+ *                  fixed order; grid = tiles = tiles_n, tiles_m = 1.
  */
 typedef struct {
   int32_t variant;      /* tile_gemm_variant_t */
@@ -160,6 +165,7 @@ typedef struct {
   int32_t xcds;         /* dispatch remap width (XCD count), 1 = identity */
   int32_t k_split;      /* skinny kernel: waves sharing K inside one workgroup */
   int64_t grid;         /* workgroups launched */
+  int64_t tiles;        /* owned tiles (each owned by exactly one workgroup) */
 } tile_gemm_plan_t;
 
 /* b_col_major: 0 for row-major B, 1 for column-major B. cu_count > 0. */
@@ -167,10 +173,11 @@ tile_gemm_status_t tile_gemm_plan(int64_t M, int64_t N, int64_t K, int b_col_maj
                                   int cu_count, tile_gemm_plan_t* out);
 
 /*
- * The owned tile of workgroup `wg` under `plan`: rows [m0, m0 + rows) and
- * columns [n0, n0 + cols) of C, clipped to M x N. This is the very function
- * the kernels run, compiled for the host, so tests can check that the map is
- * a bijection onto the tiles and that the tiles exactly cover C.
+ * Tile number `wg` (0 <= wg < plan->tiles) under `plan`: rows [m0, m0 + rows)
+ * and columns [n0, n0 + cols) of C, clipped to M x N. Workgroup w of the
+ * launch owns tile numbers w, w + grid, ... This is the very function the
+ * kernels run, compiled for the host, so tests can check that the map is a
+ * bijection onto the tiles and that the tiles exactly cover C.
  */
 tile_gemm_status_t tile_gemm_tile_of(const tile_gemm_plan_t* plan, int64_t M, int64_t N,
                                      int64_t wg, int64_t* m0, int64_t* n0,
@@ -188,6 +195,11 @@ enum {
  * needs M <= its row capacity (16 * row groups). */
 #define TILE_GEMM_DEBUG_FORCE_TILE(c) ((((c) + 1) & 0xff) << 8)
 #define TILE_GEMM_DEBUG_FORCE_SKINNY(c) ((((c) + 1) & 0xff) << 16)
+/* Launch g workgroups (1 <= g <= 126, at most the tile count) for the tile
+ * kernel instead of the planner's grid, so each takes several tiles; or, with
+ * TILE_GEMM_DEBUG_ONE_TILE_PER_WG, one workgroup per tile. */
+#define TILE_GEMM_DEBUG_FORCE_GRID(g) (((g) & 0x7f) << 24)
+#define TILE_GEMM_DEBUG_ONE_TILE_PER_WG (0x7f << 24)
 
 /*
  * As tile_gemm_run, with instrumentation. `counts` is a device array of M*N

@@ -20,7 +20,7 @@ import pytest
 import tile_partitioned_dense_amd as tg
 from tile_partitioned_dense_amd import synth
 
-from gpu_helpers import Case, host_out, workload_case
+from gpu_helpers import Case, check, host_out, workload_case
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +86,36 @@ def test_every_config_writes_once(g, cfg):
     store, C, counts = _counts_run(g, case, torch.float32,
                                    tg.DEBUG_COUNT_WRITES | tg.DEBUG_FORCE_TILE(cfg))
     assert int(counts.min()) == 1 and int(counts.max()) == 1
+
+
+@pytest.mark.parametrize("cfg,grid", [(1, 1), (1, 3), (7, 2), (9, 5), (6, 8), (10, 3)])
+def test_workgroups_owning_several_tiles(g, cfg, grid):
+    """A launch with fewer workgroups than tiles (workgroup w owns tile
+    numbers w, w + grid, ...): every element still written once, and the
+    result bit-identical to one workgroup per tile, since each tile keeps its
+    own K loop and K order whichever workgroup runs it."""
+    case = Case(700, 900, 300, cfg in (1, 9), seed=40 + cfg, pad=8)  # steady loop + K tail
+    print(f"[several tiles per workgroup cfg {cfg} grid {grid}]", flush=True)
+    for dt in (torch.float32, torch.bfloat16):
+        store, C, counts = _counts_run(g, case, dt, tg.DEBUG_COUNT_WRITES | tg.DEBUG_FORCE_TILE(cfg)
+                                       | tg.DEBUG_FORCE_GRID(grid))
+        assert int(counts.min()) == 1 and int(counts.max()) == 1
+        assert not torch.isnan(C.float()).any()
+        assert torch.isnan(store[:, case.N:].float()).all()
+        _, C1, _ = _counts_run(g, case, dt, tg.DEBUG_FORCE_TILE(cfg) | tg.DEBUG_ONE_TILE_PER_WG)
+        assert torch.equal(_as_int(C), _as_int(C1))
+        Cr, Dr = case.ref()
+        rep = check(host_out(C), Cr, Dr, dt == torch.bfloat16, False)
+        assert rep.ok, rep
+
+
+def test_forced_grid_rejected_for_the_skinny_kernel(g):
+    case = Case(16, 512, 64, False, seed=3)
+    store, C = case.out(torch.float32)
+    with pytest.raises(tg.TileGemmError):
+        g.run_debug(case.A_dev, case.B_dev, C, flags=tg.DEBUG_FORCE_GRID(2))
+    torch.cuda.synchronize()
+    assert torch.isnan(C).all()
 
 
 @pytest.mark.parametrize("cfg", range(tg.N_SKINNY_CONFIGS))

@@ -1,11 +1,12 @@
 """Host-side checks of the planner and the owned-tile map.
 
-The output is partitioned into disjoint tiles before launch and each
-workgroup owns exactly one ("GPU speed, without leaving Rust's safety model",
-section "Ownership crosses the launch boundary"). tile_gemm_tile_of runs the
-same tile_of function the kernels run, compiled for the host, so these tests
-check the device map itself: a bijection from workgroup ids onto the tile
-grid whose tiles cover C exactly once.
+The output is partitioned into disjoint tiles before launch and each tile
+has exactly one owning workgroup ("GPU speed, without leaving Rust's safety
+model", section "Ownership crosses the launch boundary"). tile_gemm_tile_of
+runs the same tile_of function the kernels run, compiled for the host, so
+these tests check the device map itself: a bijection from tile numbers onto
+the tile grid whose tiles cover C exactly once, and workgroup w owning tile
+numbers w, w + grid, ...
 """
 
 import itertools
@@ -22,11 +23,12 @@ CU = 256
 def cover_check(M, N, K, bcol=False, cu=CU):
     plan = tg.tile_gemm_plan(M, N, K, bcol, cu)
     if M == 0 or N == 0:
-        assert plan.variant == tg.VARIANT_NONE and plan.grid == 0
+        assert plan.variant == tg.VARIANT_NONE and plan.grid == 0 and plan.tiles == 0
         return plan
+    check_grid(plan, cu)
     seen = set()
     area = 0
-    for wg in range(plan.grid):
+    for wg in range(plan.tiles):
         m0, n0, rows, cols = tg.tile_gemm_tile_of(plan, M, N, wg)
         assert (m0, n0) not in seen, f"tile ({m0},{n0}) owned twice"
         seen.add((m0, n0))
@@ -37,8 +39,29 @@ def cover_check(M, N, K, bcol=False, cu=CU):
         area += rows * cols
     # distinct grid-aligned tiles whose clipped areas sum to M*N cover C exactly
     assert area == M * N
-    assert len(seen) == plan.grid
+    assert len(seen) == plan.tiles
     return plan
+
+
+def check_grid(plan, cu):
+    """Workgroup w owns tile numbers w, w + grid, ...: every tile has one owner
+    by construction. One round of tiles gets one workgroup each; more rounds
+    share the tiles out evenly, never needing more rounds than one tile per
+    compute unit would, and keep a workgroup's tiles on one XCD."""
+    T, G = plan.tiles, plan.grid
+    assert 1 <= G <= T
+    if plan.variant == tg.VARIANT_SKINNY or T <= cu:
+        assert G == T
+        return
+    rounds = -(-T // cu)
+    g0 = -(-T // rounds)
+    g8 = -(-g0 // 8) * 8
+    assert G == (g8 if g8 <= cu else g0)
+    per_wg = [len(range(w, T, G)) for w in range(G)]
+    assert max(per_wg) == rounds and max(per_wg) - min(per_wg) <= 1
+    if G % 8 == 0:
+        for w in range(0, G, max(1, G // 17)):
+            assert all(t % 8 == w % 8 for t in range(w, T, G))
 
 
 @pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
@@ -51,14 +74,23 @@ def test_workload_partitions(name):
 def test_expected_plans_for_workloads():
     W = synth.WORKLOADS
     p = tg.tile_gemm_plan(W["qkv_shard"].M, W["qkv_shard"].N, W["qkv_shard"].K, False, CU)
-    assert (p.variant, p.bm, p.bn, p.grid) == (tg.VARIANT_TILE, 256, 160, 256)
+    assert (p.variant, p.bm, p.bn, p.tiles, p.grid) == (tg.VARIANT_TILE, 256, 160, 256, 256)
     p = tg.tile_gemm_plan(8192, 7168, 8192, True, CU)
-    assert (p.variant, p.bm, p.bn, p.grid) == (tg.VARIANT_TILE, 256, 224, 1024)
+    assert (p.variant, p.bm, p.bn, p.tiles, p.grid) == (tg.VARIANT_TILE, 256, 224, 1024, 256)
     p = tg.tile_gemm_plan(4096, 4096, 4096, False, CU)
-    assert (p.variant, p.bm, p.bn, p.grid) == (tg.VARIANT_TILE, 256, 256, 256)
+    assert (p.variant, p.bm, p.bn, p.tiles, p.grid) == (tg.VARIANT_TILE, 256, 256, 256, 256)
     p = tg.tile_gemm_plan(16, 28672, 8192, False, CU)
     assert p.variant == tg.VARIANT_SKINNY and p.k_split == 8 and p.bm == 16
-    assert p.grid * p.bn >= 28672 and (p.grid - 1) * p.bn < 28672
+    assert p.grid == p.tiles and p.grid * p.bn >= 28672 and (p.grid - 1) * p.bn < 28672
+
+
+def test_persistent_grid_shares_tiles_evenly():
+    # 8192^3: 1024 tiles of 256x256 -> 4 rounds of 256 workgroups;
+    # 7168 x 6144: 28 x 24 = 672 tiles of 256x256 -> 3 rounds of 224
+    p = tg.tile_gemm_plan(8192, 8192, 8192, False, CU)
+    assert (p.bm, p.bn, p.tiles, p.grid) == (256, 256, 1024, 256)
+    p = tg.tile_gemm_plan(7168, 6144, 8192, True, CU)
+    assert (p.bm, p.bn, p.tiles, p.grid) == (256, 256, 672, 224)
 
 
 def test_plan_is_a_pure_function_of_shape():
@@ -95,7 +127,7 @@ def test_xcd_remap_keeps_neighbours_on_one_xcd():
     plan = tg.tile_gemm_plan(8192, 7168, 8192, True, CU)
     assert plan.xcds == 8
     by_xcd = {}
-    for wg in range(plan.grid):
+    for wg in range(plan.tiles):
         m0, n0, _, _ = tg.tile_gemm_tile_of(plan, 8192, 7168, wg)
         by_xcd.setdefault(wg % 8, []).append((m0 // plan.bm, n0 // plan.bn))
     for x, tiles in by_xcd.items():
@@ -112,7 +144,7 @@ def test_plan_rejects_bad_input():
         tg.tile_gemm_plan(4, 4, 4, cu_count=0)
     plan = tg.tile_gemm_plan(512, 512, 64)
     with pytest.raises(tg.TileGemmError):
-        tg.tile_gemm_tile_of(plan, 512, 512, plan.grid)
+        tg.tile_gemm_tile_of(plan, 512, 512, plan.tiles)
 
 
 def _colliding_tile_of(plan, M, N, wg):
@@ -125,8 +157,8 @@ def test_negative_control_map_is_caught_by_cover_check():
     plan = tg.tile_gemm_plan(1024, 1024, 64)
     seen = set()
     dup = False
-    for wg in range(plan.grid):
+    for wg in range(plan.tiles):
         t = _colliding_tile_of(plan, 1024, 1024, wg)[:2]
         dup |= t in seen
         seen.add(t)
-    assert dup and len(seen) == plan.grid - 1
+    assert dup and len(seen) == plan.tiles - 1

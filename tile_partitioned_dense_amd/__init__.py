@@ -1,8 +1,8 @@
 """tile_partitioned_dense_amd -- tile-partitioned dense GEMM C = A.B on AMD
 Instinct MI355X (gfx950).
 
-Every workgroup exclusively owns one disjoint output tile and reads A and B as
-shared read-only views (the partition discipline of "GPU speed, without
+Every output tile is exclusively owned by one workgroup, which reads A and B
+as shared read-only views (the partition discipline of "GPU speed, without
 leaving Rust's safety model", sections "Ownership crosses the launch
 boundary" and "The useful boundary"). The compute runs in hand-written HIP
 kernels behind a C ABI (``include/tile_gemm.h``); this package is the thin
@@ -19,7 +19,7 @@ __all__ = ["tile_gemm_create", "tile_gemm_run", "tile_gemm_run_debug", "tile_gem
            "tile_gemm_tile_of", "TileGemm", "TileGemmError", "Status", "Dtype",
            "Strides", "Plan", "library_path", "load_library", "last_error_detail",
            "DEBUG_COUNT_WRITES", "DEBUG_COLLIDE", "DEBUG_FORCE_TILE",
-           "DEBUG_FORCE_SKINNY", "N_TILE_CONFIGS", "N_SKINNY_CONFIGS", "VARIANT_NONE", "VARIANT_TILE",
+           "DEBUG_FORCE_SKINNY", "DEBUG_FORCE_GRID", "DEBUG_ONE_TILE_PER_WG", "N_TILE_CONFIGS", "N_SKINNY_CONFIGS", "VARIANT_NONE", "VARIANT_TILE",
            "VARIANT_SKINNY"]
 
 

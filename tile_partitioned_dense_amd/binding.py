@@ -45,6 +45,13 @@ def DEBUG_FORCE_SKINNY(c: int) -> int:
     return ((c + 1) & 0xFF) << 16
 
 
+def DEBUG_FORCE_GRID(g: int) -> int:
+    return (g & 0x7F) << 24
+
+
+DEBUG_ONE_TILE_PER_WG = 0x7F << 24
+
+
 N_TILE_CONFIGS = 11
 N_SKINNY_CONFIGS = 6
 
@@ -63,7 +70,8 @@ class Plan(ctypes.Structure):
                 ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("tiles_m", ctypes.c_int32), ("tiles_n", ctypes.c_int32),
                 ("group_m", ctypes.c_int32), ("xcds", ctypes.c_int32),
-                ("k_split", ctypes.c_int32), ("grid", ctypes.c_int64)]
+                ("k_split", ctypes.c_int32), ("grid", ctypes.c_int64),
+                ("tiles", ctypes.c_int64)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

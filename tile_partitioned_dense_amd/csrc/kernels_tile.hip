@@ -9,9 +9,9 @@
 namespace tg {
 
 template <int CFG>
-hipError_t launch_tile(const TileArgs& a, const Variant& v, hipStream_t stream) {
+hipError_t launch_tile(const TileArgs& a, int64_t grid_wgs, const Variant& v, hipStream_t stream) {
   constexpr TileConfig c = kTileConfigs[CFG];
-  const dim3 grid((unsigned)(a.map.tiles_m * a.map.tiles_n));
+  const dim3 grid((unsigned)grid_wgs);
   const dim3 block(c.wm * c.wn * 64);
 #define TG_TILE_FN(BC, OB, DB) \
   reinterpret_cast<const void*>(&tile_gemm_kernel<c.bm, c.bn, c.wm, c.wn, c.stages, BC, OB, DB>)
@@ -27,6 +27,6 @@ hipError_t launch_tile(const TileArgs& a, const Variant& v, hipStream_t stream) 
   return launch_raw(fn, grid, block, a, stream);
 }
 
-template hipError_t launch_tile<TG_TILE_CONFIG>(const TileArgs&, const Variant&, hipStream_t);
+template hipError_t launch_tile<TG_TILE_CONFIG>(const TileArgs&, int64_t, const Variant&, hipStream_t);
 
 }  // namespace tg

@@ -17,7 +17,7 @@ struct Variant {
 };
 
 template <int CFG>
-hipError_t launch_tile(const TileArgs& a, const Variant& v, hipStream_t stream);
+hipError_t launch_tile(const TileArgs& a, int64_t grid, const Variant& v, hipStream_t stream);
 
 template <int CFG>
 hipError_t launch_skinny(const SkinnyArgs& a, int64_t grid, const Variant& v, hipStream_t stream);

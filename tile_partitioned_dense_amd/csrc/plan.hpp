@@ -1,7 +1,7 @@
 // plan.hpp -- output-tile partitioner and launch planner.
 //
-// The output C is split into disjoint tiles before launch and each workgroup
-// exclusively owns one of them: the host-side partition that "GPU speed,
+// The output C is split into disjoint tiles before launch and each tile is
+// exclusively owned by one workgroup: the host-side partition that "GPU speed,
 // without leaving Rust's safety model" describes in "Ownership crosses the
 // launch boundary" (a mutable output partitioned into exclusive
 // sub-tensors, inputs broadcast as shared views) and "Disjointness outside.
@@ -108,7 +108,8 @@ struct Plan {
   int bm, bn, bk, threads, lds_bytes;
   TileMap map;
   int k_split;
-  int64_t grid;
+  int64_t tiles;  // owned tiles
+  int64_t grid;   // workgroups launched
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -127,8 +128,25 @@ inline int32_t pick_group_m(int32_t tiles_m, int32_t tiles_n) {
   return g < 1 ? 1 : g;
 }
 
+// Workgroups for `tiles` tiles on `cu_count` compute units: as many as one
+// round of tiles needs when the tiles fit in one round; otherwise the tiles
+// are shared out evenly over ceil(tiles / cu_count) rounds, each workgroup
+// taking tiles t, t + grid, t + 2 grid, ... Every workgroup then runs the same
+// number of tiles (give or take one), instead of a last round that leaves
+// part of the chip idle, and the idle units' power budget goes to the busy
+// ones. The count is rounded up to a multiple of the XCD count where that
+// still fits the compute units, so all tiles of a workgroup stay on its XCD
+// (t and t + grid share t % kXcds).
+inline int64_t persistent_grid(int64_t tiles, int cu_count) {
+  if (tiles <= cu_count) return tiles;
+  const int64_t rounds = ceil_div(tiles, cu_count);
+  const int64_t g0 = ceil_div(tiles, rounds);
+  const int64_t g = ceil_div(g0, kXcds) * kXcds;
+  return g <= cu_count ? g : g0;
+}
+
 // The launch geometry of one configuration for an M x N output.
-inline Plan plan_for(int variant, int config, int64_t M, int64_t N) {
+inline Plan plan_for(int variant, int config, int64_t M, int64_t N, int cu_count) {
   Plan p{};
   p.bk = kBK;
   p.map.xcds = 1;
@@ -144,7 +162,8 @@ inline Plan plan_for(int variant, int config, int64_t M, int64_t N) {
     p.map.tiles_m = 1;
     p.map.tiles_n = (int32_t)ceil_div(N, p.bn);
     p.map.group_m = 1;
-    p.grid = p.map.tiles_n;
+    p.tiles = p.map.tiles_n;
+    p.grid = p.tiles;
   } else if (variant == 1) {
     const TileConfig& c = kTileConfigs[config];
     p.bm = c.bm;
@@ -156,7 +175,8 @@ inline Plan plan_for(int variant, int config, int64_t M, int64_t N) {
     p.map.tiles_n = (int32_t)ceil_div(N, c.bn);
     p.map.group_m = pick_group_m(p.map.tiles_m, p.map.tiles_n);
     p.map.xcds = kXcds;
-    p.grid = (int64_t)ceil_div(M, c.bm) * ceil_div(N, c.bn);
+    p.tiles = (int64_t)ceil_div(M, c.bm) * ceil_div(N, c.bn);
+    p.grid = persistent_grid(p.tiles, cu_count);
   }
   return p;
 }
@@ -166,7 +186,7 @@ inline Plan plan_for(int variant, int config, int64_t M, int64_t N) {
 inline Plan make_plan(int64_t M, int64_t N, int64_t K, bool b_col_major, int cu_count) {
   (void)K;
   (void)b_col_major;
-  if (M <= 0 || N <= 0) return plan_for(0, 0, M, N);
+  if (M <= 0 || N <= 0) return plan_for(0, 0, M, N, cu_count);
   if (M <= kSkinnyMaxM) {
     const int mg = (int)ceil_div(M, 16);
     const int mgp = mg <= 1 ? 1 : (mg <= 2 ? 2 : 4);
@@ -176,7 +196,7 @@ inline Plan make_plan(int64_t M, int64_t N, int64_t K, bool b_col_major, int cu_
     int idx = 0;
     for (int i = 0; i < kNumSkinnyConfigs; ++i)
       if (kSkinnyConfigs[i].t == t && kSkinnyConfigs[i].mg == mgp) idx = i;
-    return plan_for(2, idx, M, N);
+    return plan_for(2, idx, M, N, cu_count);
   }
   // Tile kernel: minimise (tiles on the busiest CU) x (tile area) / efficiency.
   int best = 0;
@@ -190,7 +210,7 @@ inline Plan make_plan(int64_t M, int64_t N, int64_t K, bool b_col_major, int cu_
       best_cost = cost;
     }
   }
-  return plan_for(1, best, M, N);
+  return plan_for(1, best, M, N, cu_count);
 }
 
 }  // namespace tg

@@ -140,21 +140,23 @@ void fill_plan(const tg::Plan& p, tile_gemm_plan_t* out) {
   out->xcds = p.map.xcds;
   out->k_split = p.k_split;
   out->grid = p.grid;
+  out->tiles = p.tiles;
 }
 
-hipError_t dispatch_tile(int cfg, const tg::TileArgs& a, const tg::Variant& v, hipStream_t st) {
+hipError_t dispatch_tile(int cfg, const tg::TileArgs& a, int64_t grid, const tg::Variant& v,
+                         hipStream_t st) {
   switch (cfg) {
-    case 0: return tg::launch_tile<0>(a, v, st);
-    case 1: return tg::launch_tile<1>(a, v, st);
-    case 2: return tg::launch_tile<2>(a, v, st);
-    case 3: return tg::launch_tile<3>(a, v, st);
-    case 4: return tg::launch_tile<4>(a, v, st);
-    case 5: return tg::launch_tile<5>(a, v, st);
-    case 6: return tg::launch_tile<6>(a, v, st);
-    case 7: return tg::launch_tile<7>(a, v, st);
-    case 8: return tg::launch_tile<8>(a, v, st);
-    case 9: return tg::launch_tile<9>(a, v, st);
-    case 10: return tg::launch_tile<10>(a, v, st);
+    case 0: return tg::launch_tile<0>(a, grid, v, st);
+    case 1: return tg::launch_tile<1>(a, grid, v, st);
+    case 2: return tg::launch_tile<2>(a, grid, v, st);
+    case 3: return tg::launch_tile<3>(a, grid, v, st);
+    case 4: return tg::launch_tile<4>(a, grid, v, st);
+    case 5: return tg::launch_tile<5>(a, grid, v, st);
+    case 6: return tg::launch_tile<6>(a, grid, v, st);
+    case 7: return tg::launch_tile<7>(a, grid, v, st);
+    case 8: return tg::launch_tile<8>(a, grid, v, st);
+    case 9: return tg::launch_tile<9>(a, grid, v, st);
+    case 10: return tg::launch_tile<10>(a, grid, v, st);
   }
   return hipErrorInvalidValue;
 }
@@ -196,19 +198,25 @@ tile_gemm_status_t run_impl(tile_gemm_t h, const void* A, const void* B, void* C
   if (force_tile) {
     if (force_tile > tg::kNumTileConfigs)
       return fail(TILE_GEMM_ERR_BAD_SHAPE, "debug: no tile configuration %d", force_tile - 1);
-    p = tg::plan_for(1, force_tile - 1, M, N);
+    p = tg::plan_for(1, force_tile - 1, M, N, h->cu_count);
   } else if (force_skinny) {
     if (force_skinny > tg::kNumSkinnyConfigs)
       return fail(TILE_GEMM_ERR_BAD_SHAPE, "debug: no skinny configuration %d", force_skinny - 1);
     if (M > 16 * tg::kSkinnyConfigs[force_skinny - 1].mg)
       return fail(TILE_GEMM_ERR_BAD_SHAPE, "debug: M=%lld exceeds skinny configuration %d",
                   (long long)M, force_skinny - 1);
-    p = tg::plan_for(2, force_skinny - 1, M, N);
+    p = tg::plan_for(2, force_skinny - 1, M, N, h->cu_count);
   }
   if (p.grid > 0x7fffffff)
     return fail(TILE_GEMM_ERR_BAD_SHAPE, "shape: %lld workgroups exceed the launch limit",
                 (long long)p.grid);
-  if ((flags & TILE_GEMM_DEBUG_COLLIDE) && (p.variant != 1 || p.grid < 2))
+  const int force_grid = (flags >> 24) & 0x7f;
+  if (force_grid) {
+    if (p.variant != 1)
+      return fail(TILE_GEMM_ERR_BAD_SHAPE, "debug: a forced grid applies to the tile kernel only");
+    p.grid = (force_grid == 0x7f || force_grid > p.tiles) ? p.tiles : force_grid;
+  }
+  if ((flags & TILE_GEMM_DEBUG_COLLIDE) && (p.variant != 1 || p.tiles < 2))
     return fail(TILE_GEMM_ERR_BAD_SHAPE, "debug collide: needs the tile kernel and >= 2 tiles");
 
   const tg::Variant v{!brow, dtype == TILE_GEMM_BF16_TO_BF16, flags != 0};
@@ -228,7 +236,7 @@ tile_gemm_status_t run_impl(tile_gemm_t h, const void* A, const void* B, void* C
     a.map = p.map;
     a.counts = counts;
     a.flags = flags;
-    e = dispatch_tile(p.config, a, v, hs);
+    e = dispatch_tile(p.config, a, p.grid, v, hs);
   } else {
     tg::SkinnyArgs a{};
     a.A = static_cast<const uint16_t*>(A);
@@ -305,7 +313,7 @@ tile_gemm_status_t tile_gemm_run_debug(tile_gemm_t h, const void* A, const void*
                                        int64_t M, int64_t N, int64_t K,
                                        const tile_gemm_strides_t* strides, tile_gemm_dtype_t dtype,
                                        void* stream, uint32_t* counts, int flags) {
-  if (flags & ~(TILE_GEMM_DEBUG_COUNT_WRITES | TILE_GEMM_DEBUG_COLLIDE | 0x00ffff00))
+  if (flags & ~(TILE_GEMM_DEBUG_COUNT_WRITES | TILE_GEMM_DEBUG_COLLIDE | 0x7fffff00))
     return fail(TILE_GEMM_ERR_BAD_SHAPE, "flags: unknown bits 0x%x", flags);
   return run_impl(h, A, B, C, M, N, K, strides, dtype, stream, counts, flags);
 }
@@ -332,7 +340,7 @@ tile_gemm_status_t tile_gemm_tile_of(const tile_gemm_plan_t* plan, int64_t M, in
                                      int64_t* cols) {
   g_detail[0] = '\0';
   if (!plan || !m0 || !n0 || !rows || !cols) return fail(TILE_GEMM_ERR_NULL_ARG, "NULL argument");
-  if (wg < 0 || wg >= plan->grid) return fail(TILE_GEMM_ERR_BAD_SHAPE, "wg out of range");
+  if (wg < 0 || wg >= plan->tiles) return fail(TILE_GEMM_ERR_BAD_SHAPE, "tile index out of range");
   int64_t r0, c0;
   if (plan->variant == TILE_GEMM_VARIANT_TILE) {
     tg::TileMap mp{plan->tiles_m, plan->tiles_n, plan->group_m, plan->xcds};
