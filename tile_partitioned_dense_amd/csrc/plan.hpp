@@ -44,17 +44,17 @@ struct TileConfig {
 
 constexpr int kNumTileConfigs = 11;
 constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
-    {256, 256, 2, 2, 4, 0.88f},  // 0: 4 waves of 128x128
-    {256, 224, 4, 1, 5, 1.03f},  // 1: 4 waves of 64x224
-    {256, 160, 4, 1, 5, 0.95f},  // 2: 4 waves of 64x160
+    {256, 256, 2, 2, 4, 0.94f},  // 0: 4 waves of 128x128
+    {256, 224, 4, 1, 5, 0.85f},  // 1: 4 waves of 64x224
+    {256, 160, 4, 1, 5, 0.81f},  // 2: 4 waves of 64x160
     {128, 256, 2, 2, 5, 0.85f},  // 3: 4 waves of 64x128
     {256, 128, 2, 2, 5, 0.78f},  // 4: 4 waves of 128x64
     {128, 128, 2, 2, 4, 0.81f},  // 5: 4 waves of 64x64
     {64, 64, 2, 2, 4, 0.46f},    // 6: 4 waves of 32x32
     {256, 256, 2, 4, 4, 1.00f},  // 7: 8 waves of 128x64
     {256, 256, 4, 2, 4, 0.99f},  // 8: 8 waves of 64x128
-    {256, 224, 8, 1, 5, 1.02f},  // 9: 8 waves of 32x224
-    {256, 160, 8, 1, 5, 0.96f},  // 10: 8 waves of 32x160
+    {256, 224, 8, 1, 5, 0.85f},  // 9: 8 waves of 32x224
+    {256, 160, 8, 1, 5, 0.82f},  // 10: 8 waves of 32x160
 };
 
 // Skinny-kernel configurations: T output columns per lane (16*T per
