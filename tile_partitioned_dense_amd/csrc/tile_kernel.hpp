@@ -514,8 +514,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
       constexpr int NDMA = A_PER + BC;
       constexpr int NH1 = (NDMA + 1) / 2;        // units issued after a barrier
       constexpr int NH2 = NDMA - NH1;            // units issued one step later
-      constexpr int D1 = (NH1 + NMFMA - 1) / NMFMA;
-      constexpr int D2 = (NH2 + NMFMA - 1) / NMFMA;
+      // Unit t of n goes out after MFMA (2t + 1) NMFMA / (2n) of its step: spread
+      // evenly, so the waves' loads do not all reach the texture unit at once.
+      auto dma_slot = [](int t, int n) constexpr { return ((2 * t + 1) * NMFMA) / (2 * n); };
       int s = 0;
       if (!split) return 0;
       // Unit U of the slab whose stage is STG, from resources rA_/rB_.
@@ -546,9 +547,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
               if constexpr (idx < NUNIT)
                 read_fast(st_c, std::integral_constant<int, 1>{}, 1, std::integral_constant<int, idx>{});
             });
-            static_for<0, D2>([&](auto d_c) {
-              constexpr int t = k * D2 + decltype(d_c)::value;
-              if constexpr (t < NH2)
+            static_for<0, NH2>([&](auto t_c) {
+              constexpr int t = decltype(t_c)::value;
+              if constexpr (dma_slot(t, NH2) == k)
                 unit(std::integral_constant<int, ST2>{}, std::integral_constant<int, NH1 + t>{}, rsAn, rsBn);
             });
           });
@@ -570,9 +571,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
                 read_fast(std::integral_constant<int, STN>{}, std::integral_constant<int, 0>{}, 0,
                           std::integral_constant<int, idx>{});
             });
-            static_for<0, D1>([&](auto d_c) {
-              constexpr int t = k * D1 + decltype(d_c)::value;
-              if constexpr (t < NH1)
+            static_for<0, NH1>([&](auto t_c) {
+              constexpr int t = decltype(t_c)::value;
+              if constexpr (dma_slot(t, NH1) == k)
                 unit(std::integral_constant<int, STD>{}, std::integral_constant<int, t>{}, rsAn, rsBn);
             });
           });
