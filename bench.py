@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mlp_gate_up_shard")
-    ap.add_argument("--secondary", default="qkv_shard,square4096,decode,gemm256",
+    ap.add_argument("--secondary", default="qkv_shard,square4096,decode,decode_colB,gemm256",
                     help="comma-separated extra workloads reported on the same line ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -78,6 +78,49 @@ class Bench:
         log(f"[bench] {w.name}: {w.M}x{w.N}x{w.K} out={out} copies={copies} "
             f"(operands ready in {time.time() - t0:.1f}s)")
         return ops, sets
+
+    def launch_overhead(self, abc, n=400, per_graph=20):
+        """Host-visible cost per call for a launch-bound shape: each call
+        followed by a synchronisation; calls chained on the stream with one
+        synchronisation at the end; and the same calls captured into a HIP
+        graph (per_graph per graph) and replayed."""
+        torch, g = self.torch, self.g
+        A, B, C = abc
+        for _ in range(10):
+            g(A, B, C)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            g(A, B, C)
+            torch.cuda.synchronize()
+        synced = (time.perf_counter() - t0) / n
+        t0 = time.perf_counter()
+        for _ in range(n):
+            g(A, B, C)
+        torch.cuda.synchronize()
+        chained = (time.perf_counter() - t0) / n
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            g(A, B, C)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(per_graph):
+                g(A, B, C)
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, n // per_graph)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        replay = (time.perf_counter() - t0) / (reps * per_graph)
+        out = {"synced": round(synced * 1e6, 2), "chained": round(chained * 1e6, 2),
+               "graph_replay": round(replay * 1e6, 2)}
+        log(f"[bench] per-call cost (us): {out}")
+        return out
 
     def time_workload(self, w, out, steps, warmup):
         torch = self.torch
@@ -115,6 +158,8 @@ class Bench:
         res["gbs"] = w.algorithmic_bytes(out) / mean_s / 1e9
         res["frac_mfma"] = res["tflops"] / PEAK_BF16_TFLOPS
         res["frac_hbm"] = res["gbs"] / PEAK_HBM_GBS
+        if w.flops < 1e9:
+            res["launch_us"] = self.launch_overhead(sets[0])
         log(f"[bench] {w.name}: mean {res['kernel_ms_mean'] * 1e3:.1f} us "
             f"(median {res['kernel_ms_median'] * 1e3:.1f}, min {res['kernel_ms_min'] * 1e3:.1f}) "
             f"-> {res['tflops']:.1f} TFLOP/s ({100 * res['frac_mfma']:.1f}% MFMA), "
@@ -227,12 +272,12 @@ def main():
     for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
         w = synth.WORKLOADS[name]
         _, r = b.time_workload(w, w.outs[0], args.steps, args.warmup)
-        r["roofline"] = roofline(r, hbm_bound=(name == "decode"))
+        r["roofline"] = roofline(r, hbm_bound=name.startswith("decode"))
         secondary.append(r)
     if args.copy_calibration_mib:
         copy_calibration(torch, args.copy_calibration_mib)
 
-    hbm_head = head.name == "decode"
+    hbm_head = head.name.startswith("decode")
     line = {
         "metric": METRIC,
         "value": round(res["gbs"] if hbm_head else res["tflops"], 2),

@@ -121,6 +121,11 @@ WORKLOADS = {
         "decode", 5, 16, 28672, 8192, False, ("bf16",), "normal", "normal",
         b_scale=_S,
         note="decode-shaped skinny GEMM, 16 tokens, HBM-bound"),
+    "decode_colB": Workload(
+        "decode_colB", 6, 16, 28672, 8192, True, ("bf16",), "normal", "normal",
+        b_scale=_S,
+        note="the decode shape with B stored column-major (each output column's weights "
+             "contiguous, the usual layout of a projection's weight matrix)"),
 }
 
 
