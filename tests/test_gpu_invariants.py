@@ -88,7 +88,7 @@ def test_every_config_writes_once(g, cfg):
     assert int(counts.min()) == 1 and int(counts.max()) == 1
 
 
-@pytest.mark.parametrize("cfg,grid", [(1, 1), (1, 3), (7, 2), (9, 5), (6, 8), (10, 3)])
+@pytest.mark.parametrize("cfg,grid", [(1, 1), (1, 3), (7, 2), (9, 5), (6, 8), (10, 3), (11, 5), (12, 3)])
 def test_workgroups_owning_several_tiles(g, cfg, grid):
     """A launch with fewer workgroups than tiles (workgroup w owns tile
     numbers w, w + grid, ...): every element still written once, and the

@@ -52,7 +52,7 @@ def DEBUG_FORCE_GRID(g: int) -> int:
 DEBUG_ONE_TILE_PER_WG = 0x7F << 24
 
 
-N_TILE_CONFIGS = 11
+N_TILE_CONFIGS = 14
 N_SKINNY_CONFIGS = 6
 
 VARIANT_NONE, VARIANT_TILE, VARIANT_SKINNY = 0, 1, 2

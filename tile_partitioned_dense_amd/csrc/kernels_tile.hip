@@ -8,22 +8,30 @@
 
 namespace tg {
 
+// The kernel instance of configuration CFG: the tile kernel, or the K-split
+// kernel for configurations whose waves share K.
+template <int CFG, bool BC, bool OB, bool DB>
+const void* tile_fn() {
+  constexpr TileConfig c = kTileConfigs[CFG];
+  if constexpr (c.ks > 1)
+    return reinterpret_cast<const void*>(&ksplit_gemm_kernel<c.bm, c.bn, c.ks, c.stages, BC, OB, DB>);
+  else
+    return reinterpret_cast<const void*>(&tile_gemm_kernel<c.bm, c.bn, c.wm, c.wn, c.stages, BC, OB, DB>);
+}
+
 template <int CFG>
 hipError_t launch_tile(const TileArgs& a, int64_t grid_wgs, const Variant& v, hipStream_t stream) {
   constexpr TileConfig c = kTileConfigs[CFG];
   const dim3 grid((unsigned)grid_wgs);
-  const dim3 block(c.wm * c.wn * 64);
-#define TG_TILE_FN(BC, OB, DB) \
-  reinterpret_cast<const void*>(&tile_gemm_kernel<c.bm, c.bn, c.wm, c.wn, c.stages, BC, OB, DB>)
+  const dim3 block(c.wm * c.wn * c.ks * 64);
   const void* fn;
   if (v.b_col_major) {
-    if (v.out_bf16) fn = v.debug ? TG_TILE_FN(true, true, true) : TG_TILE_FN(true, true, false);
-    else fn = v.debug ? TG_TILE_FN(true, false, true) : TG_TILE_FN(true, false, false);
+    if (v.out_bf16) fn = v.debug ? tile_fn<CFG, true, true, true>() : tile_fn<CFG, true, true, false>();
+    else fn = v.debug ? tile_fn<CFG, true, false, true>() : tile_fn<CFG, true, false, false>();
   } else {
-    if (v.out_bf16) fn = v.debug ? TG_TILE_FN(false, true, true) : TG_TILE_FN(false, true, false);
-    else fn = v.debug ? TG_TILE_FN(false, false, true) : TG_TILE_FN(false, false, false);
+    if (v.out_bf16) fn = v.debug ? tile_fn<CFG, false, true, true>() : tile_fn<CFG, false, true, false>();
+    else fn = v.debug ? tile_fn<CFG, false, false, true>() : tile_fn<CFG, false, false, false>();
   }
-#undef TG_TILE_FN
   return launch_raw(fn, grid, block, a, stream);
 }
 

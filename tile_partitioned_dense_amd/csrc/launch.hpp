@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "ksplit_kernel.hpp"
 #include "skinny_kernel.hpp"
 #include "tile_kernel.hpp"
 

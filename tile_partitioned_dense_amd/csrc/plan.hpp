@@ -28,33 +28,51 @@ constexpr int kSkinnyMaxM = 64;    // M at or below this takes the skinny kernel
 constexpr int kSkinnyWaves = 8;    // waves per skinny workgroup, splitting K
 constexpr int kXcds = 8;           // MI355X: 8 accelerator dies share one dispatcher
 
-// Tile-kernel configurations compiled into the library. `eff` is the
-// throughput a compute unit sustains on this configuration relative to
-// configuration 7, measured with random bf16 data on shapes that keep every
-// compute unit busy (a partly idle chip clocks higher and would flatter it);
-// the planner uses it only to rank configurations for a shape. Eight-wave
-// configurations put two waves on each SIMD, so one wave's LDS reads, loads
-// and barrier waits overlap the other's MFMAs.
+// Tile-kernel configurations compiled into the library. `eff` (and `eff1`
+// for a workgroup alone on its compute unit) is the throughput a compute
+// unit sustains on this configuration relative to configuration 7, measured
+// with random bf16 data in interleaved cold-cache runs; the planner uses it
+// only to rank configurations for a shape. Eight-wave configurations put two
+// waves on each SIMD, so one wave's LDS reads, loads and barrier waits overlap
+// the other's MFMAs. K-split configurations (ks > 1) serve outputs with few
+// or small tiles and a long K.
 struct TileConfig {
   int bm, bn;   // owned tile
   int wm, wn;   // wave grid inside the workgroup (each wave owns (bm/wm) x (bn/wn))
-  int stages;   // depth of the LDS ring of 32-wide K slabs
-  float eff;
+  int stages;   // depth of the LDS ring of 32-wide K slabs (per wave when ks > 1)
+  float eff;    // rate with `occ` workgroups sharing each compute unit
+  int ks = 1;   // > 1: that many waves each take the whole tile over a share of
+                // K and combine in a fixed tree (ksplit_kernel.hpp)
+  float eff1 = 0.0f;  // rate of a workgroup alone on its compute unit (0: = eff)
+  int occ = 1;        // workgroups that fit on one compute unit at once
 };
 
-constexpr int kNumTileConfigs = 11;
+// Rate of configuration c when each compute unit has `per_cu` of its tiles:
+// small-LDS configurations hide load latency only with several workgroups on
+// one compute unit (alone, a 64 x 64 tile's four waves wait on every slab).
+inline double tile_eff(const TileConfig& c, int64_t per_cu) {
+  const double e1 = c.eff1 > 0.0f ? c.eff1 : c.eff;
+  if (c.occ <= 1 || per_cu <= 1) return per_cu <= 1 ? e1 : c.eff;
+  const int64_t n = per_cu < c.occ ? per_cu : c.occ;
+  return e1 + (c.eff - e1) * (double)(n - 1) / (double)(c.occ - 1);
+}
+
+constexpr int kNumTileConfigs = 14;
 constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
     {256, 256, 2, 2, 4, 0.94f},  // 0: 4 waves of 128x128
     {256, 224, 4, 1, 5, 0.85f},  // 1: 4 waves of 64x224
     {256, 160, 4, 1, 5, 0.81f},  // 2: 4 waves of 64x160
     {128, 256, 2, 2, 5, 0.85f},  // 3: 4 waves of 64x128
     {256, 128, 2, 2, 5, 0.78f},  // 4: 4 waves of 128x64
-    {128, 128, 2, 2, 4, 0.81f},  // 5: 4 waves of 64x64
-    {64, 64, 2, 2, 4, 0.46f},    // 6: 4 waves of 32x32
+    {128, 128, 2, 2, 4, 0.81f, 1, 0.59f, 2},  // 5: 4 waves of 64x64
+    {64, 64, 2, 2, 4, 0.46f, 1, 0.17f, 4},    // 6: 4 waves of 32x32
     {256, 256, 2, 4, 4, 1.00f},  // 7: 8 waves of 128x64
     {256, 256, 4, 2, 4, 0.99f},  // 8: 8 waves of 64x128
     {256, 224, 8, 1, 5, 0.85f},  // 9: 8 waves of 32x224
     {256, 160, 8, 1, 5, 0.82f},  // 10: 8 waves of 32x160
+    {64, 64, 1, 1, 4, 0.28f, 4},    // 11: 4 waves, each 64x64 over a quarter of K
+    {64, 128, 1, 1, 3, 0.42f, 4},   // 12: 4 waves, each 64x128 over a quarter of K
+    {128, 64, 1, 1, 3, 0.39f, 4},   // 13: 4 waves, each 128x64 over a quarter of K
 };
 
 // Skinny-kernel configurations: T output columns per lane (16*T per
@@ -114,7 +132,11 @@ struct Plan {
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-inline int tile_lds_bytes(const TileConfig& c) { return c.stages * (c.bm + c.bn) * 32 * 2; }
+inline int tile_lds_bytes(const TileConfig& c) {
+  const int ring = c.ks * c.stages * (c.bm + c.bn) * 32 * 2;
+  const int tree = (c.ks / 2) * c.bm * c.bn * 4;
+  return ring > tree ? ring : tree;
+}
 inline int skinny_lds_bytes(const SkinnyConfig& c) {
   return (kSkinnyWaves / 2) * c.mg * c.t * 64 * 16;
 }
@@ -168,9 +190,9 @@ inline Plan plan_for(int variant, int config, int64_t M, int64_t N, int cu_count
     const TileConfig& c = kTileConfigs[config];
     p.bm = c.bm;
     p.bn = c.bn;
-    p.threads = c.wm * c.wn * 64;
+    p.threads = c.wm * c.wn * c.ks * 64;
     p.lds_bytes = tile_lds_bytes(c);
-    p.k_split = 1;
+    p.k_split = c.ks;
     p.map.tiles_m = (int32_t)ceil_div(M, c.bm);
     p.map.tiles_n = (int32_t)ceil_div(N, c.bn);
     p.map.group_m = pick_group_m(p.map.tiles_m, p.map.tiles_n);
@@ -198,13 +220,14 @@ inline Plan make_plan(int64_t M, int64_t N, int64_t K, bool b_col_major, int cu_
       if (kSkinnyConfigs[i].t == t && kSkinnyConfigs[i].mg == mgp) idx = i;
     return plan_for(2, idx, M, N, cu_count);
   }
-  // Tile kernel: minimise (tiles on the busiest CU) x (tile area) / efficiency.
+  // Tile kernel: minimise (tiles on the busiest CU) x (tile area) / rate.
   int best = 0;
   double best_cost = 0.0;
   for (int i = 0; i < kNumTileConfigs; ++i) {
     const TileConfig& c = kTileConfigs[i];
     const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
-    const double cost = (double)ceil_div(tiles, cu_count) * c.bm * c.bn / c.eff;
+    const int64_t per_cu = ceil_div(tiles, cu_count);
+    const double cost = (double)per_cu * c.bm * c.bn / tile_eff(c, per_cu);
     if (i == 0 || cost < best_cost * 0.999) {
       best = i;
       best_cost = cost;

@@ -157,10 +157,13 @@ hipError_t dispatch_tile(int cfg, const tg::TileArgs& a, int64_t grid, const tg:
     case 8: return tg::launch_tile<8>(a, grid, v, st);
     case 9: return tg::launch_tile<9>(a, grid, v, st);
     case 10: return tg::launch_tile<10>(a, grid, v, st);
+    case 11: return tg::launch_tile<11>(a, grid, v, st);
+    case 12: return tg::launch_tile<12>(a, grid, v, st);
+    case 13: return tg::launch_tile<13>(a, grid, v, st);
   }
   return hipErrorInvalidValue;
 }
-static_assert(tg::kNumTileConfigs == 11, "dispatch_tile covers every tile configuration");
+static_assert(tg::kNumTileConfigs == 14, "dispatch_tile covers every tile configuration");
 
 hipError_t dispatch_skinny(int cfg, const tg::SkinnyArgs& a, int64_t grid, const tg::Variant& v,
                            hipStream_t st) {
