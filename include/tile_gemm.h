@@ -138,7 +138,7 @@ tile_gemm_status_t tile_gemm_check_args(const void* A, const void* B, const void
 typedef enum {
   TILE_GEMM_VARIANT_NONE = 0,   /* M == 0 or N == 0: nothing to launch */
   TILE_GEMM_VARIANT_TILE = 1,   /* LDS-staged MFMA tile kernel */
-  TILE_GEMM_VARIANT_SKINNY = 2  /* HBM-streaming kernel for M <= 64 */
+  TILE_GEMM_VARIANT_SKINNY = 2  /* HBM-streaming kernel, chosen for M <= 16 */
 } tile_gemm_variant_t;
 
 /*

@@ -24,7 +24,8 @@
 namespace tg {
 
 constexpr int kBK = 32;            // K slab staged per step in the tile kernel
-constexpr int kSkinnyMaxM = 64;    // M at or below this takes the skinny kernel
+constexpr int kSkinnyMaxM = 16;    // M at or below this takes the skinny kernel; above
+                                   // it the K-split tile kernel measured faster
 constexpr int kSkinnyWaves = 8;    // waves per skinny workgroup, splitting K
 constexpr int kXcds = 8;           // MI355X: 8 accelerator dies share one dispatcher
 

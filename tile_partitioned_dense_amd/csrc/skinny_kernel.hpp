@@ -1,5 +1,6 @@
 // skinny_kernel.hpp -- bandwidth-oriented kernel for decode-shaped GEMMs
-// (M <= 64), where streaming B from HBM is the whole cost: with M rows the
+// (M up to 64; the planner uses it for M <= 16), where streaming B from HBM
+// is the whole cost: with M rows the
 // arithmetic intensity is about M flops per byte of B, far below the MFMA
 // ridge point, the memory-bound regime the tensor-parallel page describes
 // for small GEMMs ("Implementing Tensor Parallelism Communication Overlays
