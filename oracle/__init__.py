@@ -18,6 +18,8 @@ Contents
 * ``bf16_to_f64`` / ``rne_bf16`` -- the oracle's own bf16 decode and
   round-to-nearest-even encode (directly from fp64, no double rounding).
 * ``check_f32`` / ``check_bf16`` / ``check_exact`` -- the acceptance rules.
+* ``epilogue`` / ``check_epilogue`` -- the fused epilogue act(C + bias) in
+  fp64 and its acceptance rule (``fused_epilogue.py``).
 
 Parity pins (tests/test_oracle_pins.py) tie every function here to
 something other than itself: exact rational brute force, identity and
@@ -42,4 +44,11 @@ from .numerics import (  # noqa: F401
     check_bf16,
     check_exact,
     CheckReport,
+)
+from .fused_epilogue import (  # noqa: F401
+    ACTS,
+    act_f64,
+    epilogue,
+    epilogue_bound,
+    check_epilogue,
 )
