@@ -44,7 +44,8 @@ typedef enum {
   TILE_GEMM_ERR_ALIAS = 5,      /* C's bytes overlap A's or B's */
   TILE_GEMM_ERR_DTYPE = 6,      /* unknown tile_gemm_dtype_t */
   TILE_GEMM_ERR_DEVICE = 7,     /* no such device, not gfx950, or not the current device */
-  TILE_GEMM_ERR_HIP = 8         /* the HIP runtime refused a call or a launch */
+  TILE_GEMM_ERR_HIP = 8,        /* the HIP runtime refused a call or a launch */
+  TILE_GEMM_ERR_EPILOGUE = 9    /* unknown activation in a fused epilogue */
 } tile_gemm_status_t;
 
 /* Input is always bf16 with fp32 accumulation; the enum picks the output. */
@@ -107,6 +108,39 @@ tile_gemm_status_t tile_gemm_run(tile_gemm_t h, const void* A, const void* B, vo
                                  const tile_gemm_strides_t* strides,
                                  tile_gemm_dtype_t dtype, void* stream);
 
+/*
+ * Fused epilogue: the store applies act(C + bias) to each element of the owned
+ * tile before writing it, in the spirit of the epilogue fusion the TorchInductor
+ * page describes ("TorchInductor ganha suporte a GEMMs de alta performance com
+ * CuteDSL": a bias addition or an activation folded into the GEMM's store;
+ * element-wise operations and ReLU, sigmoid, tanh in its roadmap paragraph).
+ * SiLU is x * sigmoid(x).
+ */
+typedef enum {
+  TILE_GEMM_ACT_NONE = 0,
+  TILE_GEMM_ACT_RELU = 1,     /* max(x, 0) */
+  TILE_GEMM_ACT_SIGMOID = 2,  /* 1 / (1 + e^-x) */
+  TILE_GEMM_ACT_TANH = 3,     /* tanh x */
+  TILE_GEMM_ACT_SILU = 4      /* x / (1 + e^-x) */
+} tile_gemm_act_t;
+
+/*
+ * As tile_gemm_run, storing C[i][j] = act(sum_k A[i][k] B[k][j] + bias[j]).
+ * The sum is accumulated exactly as in tile_gemm_run (same kernels, tiles and
+ * K order); bias[j] is added and act evaluated in fp32, then the value is
+ * stored as dtype says (a bf16 output is the round-to-nearest-even of that
+ * fp32 value). `bias` is a device pointer to N fp32 values, read-only, 16-byte
+ * aligned, not overlapping C; NULL means no bias. With K = 0 the result is
+ * act(bias[j]) (act(0) without a bias).
+ * Errors: as tile_gemm_run, plus TILE_GEMM_ERR_EPILOGUE (unknown act),
+ * TILE_GEMM_ERR_MISALIGNED (bias) and TILE_GEMM_ERR_ALIAS (bias overlaps C).
+ */
+tile_gemm_status_t tile_gemm_run_epilogue(tile_gemm_t h, const void* A, const void* B, void* C,
+                                          int64_t M, int64_t N, int64_t K,
+                                          const tile_gemm_strides_t* strides,
+                                          tile_gemm_dtype_t dtype, const float* bias,
+                                          tile_gemm_act_t act, void* stream);
+
 /* Release a handle (host memory only). NULL is accepted and returns OK. */
 tile_gemm_status_t tile_gemm_destroy(tile_gemm_t h);
 
@@ -133,6 +167,15 @@ tile_gemm_status_t tile_gemm_check_args(const void* A, const void* B, const void
                                         int64_t M, int64_t N, int64_t K,
                                         const tile_gemm_strides_t* strides,
                                         tile_gemm_dtype_t dtype);
+
+/*
+ * The checks tile_gemm_run_epilogue adds for its epilogue arguments (after
+ * those of tile_gemm_check_args), with the same results.
+ */
+tile_gemm_status_t tile_gemm_check_epilogue(const void* C, int64_t M, int64_t N,
+                                            const tile_gemm_strides_t* strides,
+                                            tile_gemm_dtype_t dtype, const float* bias,
+                                            tile_gemm_act_t act);
 
 /* Kernel variants the planner chooses between. */
 typedef enum {
@@ -209,13 +252,17 @@ enum {
  * tile map (two workgroups own one tile, another tile has no owner) so tests
  * can show that their checks catch a partition error. The collision needs at
  * least two tiles and applies to the tile kernel only. Unknown flag bits or an
- * unknown forced configuration return TILE_GEMM_ERR_BAD_SHAPE.
+ * unknown forced configuration return TILE_GEMM_ERR_BAD_SHAPE. `bias` and `act`
+ * are the fused epilogue of tile_gemm_run_epilogue (NULL and
+ * TILE_GEMM_ACT_NONE for the plain product), so tests can run it on every
+ * configuration.
  */
 tile_gemm_status_t tile_gemm_run_debug(tile_gemm_t h, const void* A, const void* B, void* C,
                                        int64_t M, int64_t N, int64_t K,
                                        const tile_gemm_strides_t* strides,
                                        tile_gemm_dtype_t dtype, void* stream,
-                                       uint32_t* counts, int flags);
+                                       uint32_t* counts, int flags, const float* bias,
+                                       tile_gemm_act_t act);
 
 #ifdef __cplusplus
 }

@@ -138,3 +138,35 @@ def test_config_counts_match_the_compiled_tables():
     assert binding.N_SKINNY_CONFIGS == build.N_SKINNY_CONFIGS == n_skinny
     table = re.search(r"kTileConfigs\[kNumTileConfigs\]\s*=\s*\{(.*?)\n\};", plan_src, re.S).group(1)
     assert len(re.findall(r"^\s*\{\d+,", table, re.M)) == n_tile
+
+
+# --- fused epilogue argument checks
+def chk_epi(bias=0x400000, act=0, C=C0, M=64, N=64, s=(64, 1, 64, 1, 64, 1), dtype=Dtype.BF16_TO_F32):
+    return tg.tile_gemm_check_epilogue(C, M, N, s, dtype, bias, act)
+
+
+def test_check_epilogue():
+    from tile_partitioned_dense_amd.binding import Act
+    for a in Act:
+        assert chk_epi(act=a) == Status.OK
+        assert chk_epi(bias=None, act=a) == Status.OK          # bias is optional
+    assert chk_epi(act=5) == Status.ERR_EPILOGUE
+    assert chk_epi(act=-1) == Status.ERR_EPILOGUE
+    assert "activation" in tg.last_error_detail()
+    assert chk_epi(bias=0x400004) == Status.ERR_MISALIGNED
+    assert chk_epi(bias=C0 + 64) == Status.ERR_ALIAS            # bias inside C
+    # fp32 C of 64 x 64 ends at C0 + 16384: a bias right there is fine, 16 bytes earlier is not
+    assert chk_epi(bias=C0 + 4 * 64 * 64) == Status.OK
+    assert chk_epi(bias=C0 + 4 * 64 * 64 - 16) == Status.ERR_ALIAS
+    # bf16 C is half as long
+    assert chk_epi(bias=C0 + 2 * 64 * 64, dtype=Dtype.BF16_TO_BF16) == Status.OK
+    assert chk_epi(bias=C0 - 4 * 64) == Status.OK               # bias ends where C starts
+    assert chk_epi(bias=C0 - 4 * 64 + 16) == Status.ERR_ALIAS
+    assert chk_epi(M=0, bias=0x400004) == Status.OK             # empty output: nothing read
+
+
+def test_run_epilogue_null_handle_and_bad_act():
+    lib = tg.load_library()
+    s = Strides(64, 1, 64, 1, 64, 1)
+    assert lib.tile_gemm_run_epilogue(None, A0, B0, C0, 64, 64, 64, ctypes.byref(s), 0, None, 0,
+                                      None) == Status.ERR_NULL_ARG

@@ -26,11 +26,20 @@ class Status(enum.IntEnum):
     ERR_DTYPE = 6
     ERR_DEVICE = 7
     ERR_HIP = 8
+    ERR_EPILOGUE = 9
 
 
 class Dtype(enum.IntEnum):
     BF16_TO_F32 = 0
     BF16_TO_BF16 = 1
+
+
+class Act(enum.IntEnum):
+    NONE = 0
+    RELU = 1
+    SIGMOID = 2
+    TANH = 3
+    SILU = 4
 
 
 DEBUG_COUNT_WRITES = 1
@@ -108,8 +117,13 @@ def load_library():
     lib.tile_gemm_run.argtypes = [vp, vp, vp, vp, i64, i64, i64, P(Strides), i32, vp]
     lib.tile_gemm_run.restype = i32
     lib.tile_gemm_run_debug.argtypes = [vp, vp, vp, vp, i64, i64, i64, P(Strides), i32, vp,
-                                        vp, i32]
+                                        vp, i32, vp, i32]
     lib.tile_gemm_run_debug.restype = i32
+    lib.tile_gemm_run_epilogue.argtypes = [vp, vp, vp, vp, i64, i64, i64, P(Strides), i32, vp, i32,
+                                           vp]
+    lib.tile_gemm_run_epilogue.restype = i32
+    lib.tile_gemm_check_epilogue.argtypes = [vp, i64, i64, P(Strides), i32, vp, i32]
+    lib.tile_gemm_check_epilogue.restype = i32
     lib.tile_gemm_status_str.argtypes = [i32]
     lib.tile_gemm_status_str.restype = ctypes.c_char_p
     lib.tile_gemm_last_error_detail.argtypes = []
@@ -212,13 +226,28 @@ def tile_gemm_run(h, A, B, C, M=None, N=None, K=None, strides=None, dtype=None, 
     return Status(st)
 
 
+def tile_gemm_run_epilogue(h, A, B, C, bias=None, act=Act.NONE, M=None, N=None, K=None,
+                           strides=None, dtype=None, stream=None, check: bool = True):
+    """Enqueue C := act(A.B + bias) (bias: N fp32 values on the device, or None)."""
+    a, b, c, M_, N_, K_, s, dt = _operands(A, B, C, M, N, K, strides, dtype)
+    bp = bias.data_ptr() if _is_tensor(bias) else bias
+    st = load_library().tile_gemm_run_epilogue(h, a, b, c, M_, N_, K_, ctypes.byref(s), dt, bp,
+                                               int(act), _stream_ptr(stream, C))
+    if check:
+        _raise_if(st)
+    return Status(st)
+
+
 def tile_gemm_run_debug(h, A, B, C, counts=None, flags=0, M=None, N=None, K=None, strides=None,
-                        dtype=None, stream=None, check: bool = True):
-    """tile_gemm_run with test instrumentation (write counts, collision)."""
+                        dtype=None, stream=None, check: bool = True, bias=None, act=Act.NONE):
+    """tile_gemm_run (or, with bias/act, tile_gemm_run_epilogue) with test
+    instrumentation (write counts, collision, forced configuration or grid)."""
     a, b, c, M_, N_, K_, s, dt = _operands(A, B, C, M, N, K, strides, dtype)
     cnt = counts.data_ptr() if _is_tensor(counts) else counts
+    bp = bias.data_ptr() if _is_tensor(bias) else bias
     st = load_library().tile_gemm_run_debug(h, a, b, c, M_, N_, K_, ctypes.byref(s), dt,
-                                            _stream_ptr(stream, C), cnt, int(flags))
+                                            _stream_ptr(stream, C), cnt, int(flags), bp,
+                                            int(act))
     if check:
         _raise_if(st)
     return Status(st)
@@ -229,6 +258,13 @@ def tile_gemm_check_args(A, B, C, M, N, K, strides, dtype) -> Status:
     s = strides if isinstance(strides, Strides) else Strides(*strides)
     return Status(load_library().tile_gemm_check_args(A, B, C, int(M), int(N), int(K),
                                                       ctypes.byref(s), int(dtype)))
+
+
+def tile_gemm_check_epilogue(C, M, N, strides, dtype, bias, act) -> Status:
+    """Host-only checks of the fused epilogue's arguments."""
+    s = strides if isinstance(strides, Strides) else Strides(*strides)
+    return Status(load_library().tile_gemm_check_epilogue(C, int(M), int(N), ctypes.byref(s),
+                                                          int(dtype), bias, int(act)))
 
 
 def tile_gemm_plan(M, N, K, b_col_major=False, cu_count=256) -> Plan:
@@ -251,12 +287,16 @@ class TileGemm:
     def __init__(self, device: int = 0):
         self.handle = tile_gemm_create(device)
 
-    def __call__(self, A, B, C, stream=None):
-        return tile_gemm_run(self.handle, A, B, C, stream=stream)
+    def __call__(self, A, B, C, stream=None, bias=None, act=None):
+        if bias is None and act is None:
+            return tile_gemm_run(self.handle, A, B, C, stream=stream)
+        return tile_gemm_run_epilogue(self.handle, A, B, C, bias=bias,
+                                      act=Act.NONE if act is None else act, stream=stream)
 
-    def run_debug(self, A, B, C, counts=None, flags=0, stream=None):
+    def run_debug(self, A, B, C, counts=None, flags=0, stream=None, bias=None, act=None):
         return tile_gemm_run_debug(self.handle, A, B, C, counts=counts, flags=flags,
-                                   stream=stream)
+                                   stream=stream, bias=bias,
+                                   act=Act.NONE if act is None else act)
 
     def close(self):
         if self.handle is not None:

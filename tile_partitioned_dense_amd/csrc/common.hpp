@@ -10,6 +10,39 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
+// Fused-epilogue activations (mirror TILE_GEMM_ACT_* in tile_gemm.h).
+constexpr int kActNone = 0, kActRelu = 1, kActSigmoid = 2, kActTanh = 3, kActSilu = 4;
+
+// act(x) in fp32 with the device math library.
+__device__ __forceinline__ float apply_act(float x, int act) {
+  switch (act) {
+    case kActRelu: return fmaxf(x, 0.0f);
+    case kActSigmoid: return 1.0f / (1.0f + expf(-x));
+    case kActTanh: return tanhf(x);
+    case kActSilu: return x / (1.0f + expf(-x));
+    default: return x;
+  }
+}
+
+// The fused epilogue on four consecutive columns col..col+3 of one row:
+// v[e] = act(v[e] + bias[col + e]) for the columns below N (bias may be NULL).
+__device__ __forceinline__ void apply_epilogue4(float v[4], const float* bias, int act, int col, int N) {
+  if (bias) {
+    if (col + 3 < N) {
+      const float4 b = *reinterpret_cast<const float4*>(bias + col);
+      v[0] += b.x; v[1] += b.y; v[2] += b.z; v[3] += b.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (col + e < N) v[e] += bias[col + e];
+    }
+  }
+  if (act != kActNone) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = apply_act(v[e], act);
+  }
+}
+
 // Debug flags (mirror TILE_GEMM_DEBUG_* in tile_gemm.h).
 constexpr int kDbgCount = 1;
 constexpr int kDbgCollide = 2;
@@ -78,6 +111,82 @@ __device__ __forceinline__ uint2 load8_stream(const void* p) {
 // holds x's half in bits 0-15 and y's half in bits 16-31.
 __device__ __forceinline__ uint32_t pack_halves(uint32_t x, uint32_t y, bool hi_half) {
   return hi_half ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+}
+
+// Destination and epilogue of store_staged_fused.
+struct EpiOut {
+  void* C;
+  int64_t ldc;
+  int32_t M, N;
+  const float* bias;
+  int32_t act;
+  uint32_t* counts;  // debug instrumentation only
+  int32_t flags;
+};
+
+__device__ __forceinline__ floatx4 lds_load_f4(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) floatx4*)(uintptr_t)addr;
+}
+__device__ __forceinline__ void lds_store_f4(uint32_t addr, const floatx4& v) {
+  *(__attribute__((address_space(3))) floatx4*)(uintptr_t)addr = v;
+}
+
+// Fused-epilogue store of an fp32 block staged row-major in LDS: `rows` x
+// `cols` values at LDS byte address `src` (row pitch `pitch` bytes, both
+// multiples of 16) belong at C[grow0 + r][gcol0 + c]. Thread `tid` of `nthr`
+// takes 16-byte output chunks tid, tid + nthr, ... (4 fp32 or 8 bf16 columns;
+// `cols` is a multiple of 8), forms act(x + bias) in fp32, rounds to bf16
+// (nearest even) for a bf16 output and writes each element of C once, rows
+// and columns past M and N masked. The loop stays rolled, so the activation
+// code is emitted once however large the block.
+template <bool OUT_BF16, bool DEBUG>
+__device__ __forceinline__ void store_staged_fused(uint32_t src, int pitch, int rows, int cols,
+                                                   int grow0, int gcol0, int tid, int nthr,
+                                                   const EpiOut& o) {
+  constexpr int EPC = OUT_BF16 ? 8 : 4;  // elements per 16-byte output chunk
+  constexpr int ESZ = OUT_BF16 ? 2 : 4;
+  const int cho = cols / EPC;
+  const int total = rows * cho;
+#pragma unroll 1
+  for (int c = tid; c < total; c += nthr) {
+    const int r = c / cho, ch = c - r * cho;
+    const int row = grow0 + r, col = gcol0 + ch * EPC;
+    if (row >= o.M || col >= o.N) continue;
+    float v[EPC];
+#pragma unroll
+    for (int h = 0; h < EPC / 4; ++h) {
+      const floatx4 x = lds_load_f4(src + (uint32_t)(r * pitch + (ch * EPC + 4 * h) * 4));
+      v[4 * h] = x[0]; v[4 * h + 1] = x[1]; v[4 * h + 2] = x[2]; v[4 * h + 3] = x[3];
+    }
+#pragma unroll
+    for (int h = 0; h < EPC / 4; ++h) apply_epilogue4(v + 4 * h, o.bias, o.act, col + 4 * h, o.N);
+    char* cb = static_cast<char*>(o.C) + ((int64_t)row * o.ldc + col) * ESZ;
+    if (col + EPC <= o.N) {
+      if constexpr (OUT_BF16) {
+        *reinterpret_cast<uint4*>(cb) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                   pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+      } else {
+        *reinterpret_cast<float4*>(cb) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        if (col + e < o.N) {
+          if constexpr (OUT_BF16) {
+            reinterpret_cast<uint16_t*>(cb)[e] = f32_to_bf16(v[e]);
+          } else {
+            reinterpret_cast<float*>(cb)[e] = v[e];
+          }
+        }
+      }
+    }
+    if constexpr (DEBUG) {
+      if (o.flags & kDbgCount)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+          if (col + e < o.N) atomicAdd(o.counts + (int64_t)row * o.N + col + e, 1u);
+    }
+  }
 }
 
 }  // namespace tg

@@ -231,6 +231,30 @@ __global__ __launch_bounds__(KS * 64, 1) void ksplit_gemm_kernel(TileArgs p) {
       __syncthreads();
     }
 
+    if (p.bias != nullptr || p.act != kActNone) {
+      // Fused epilogue: wave 0 stages the summed tile as fp32 rows in LDS and
+      // every wave takes a share of the bias / activation / store pass, one
+      // rolled loop (the activation code is emitted once).
+      constexpr int OPF = BN * 4 + 16;
+      static_assert(BM * OPF <= LDS, "the fp32 tile fits the workgroup's LDS");
+      if (wave == 0) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              lds_store_f4(lds0 + (uint32_t)((32 * i + lrow) * OPF + (32 * j + 8 * q + 4 * lgrp) * 4),
+                           floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                   acc[i][j][4 * q + 3]});
+      }
+      __syncthreads();
+      const EpiOut eo{p.C, p.ldc, M, N, p.bias, p.act, p.counts, p.flags};
+      store_staged_fused<OUT_BF16, DEBUG>(lds0, OPF, BM, BN, m0, n0, threadIdx.x, KS * 64, eo);
+      __syncthreads();
+      continue;
+    }
+
     // Wave 0 stores the tile: lane l holds row (l % 32) of each 32 x 32 block
     // and, for q = 0..3, its four consecutive columns 8 q + 4 (l / 32) .. + 3.
     if (wave == 0) {

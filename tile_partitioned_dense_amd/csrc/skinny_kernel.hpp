@@ -35,6 +35,8 @@ struct SkinnyArgs {
   int64_t lda, ldb, ldc;
   uint32_t* counts;  // debug instrumentation only
   int32_t flags;
+  const float* bias;  // fused epilogue: N fp32 values or NULL
+  int32_t act;        // fused epilogue: kAct*
 };
 
 template <int T>
@@ -249,6 +251,29 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(SkinnyArgs p) {
         for (int c = 0; c < T; ++c) acc[g][c] += red[wave][g * T + c][lane];
     }
     __syncthreads();
+  }
+
+  if (p.bias != nullptr || p.act != kActNone) {
+    // Fused epilogue: wave 0 stages the summed block as fp32 rows in LDS (the
+    // tree's buffer is free again) and all waves share one rolled
+    // bias / activation / store pass.
+    constexpr int OPF = 16 * T * 4 + 16;
+    static_assert(16 * MG * OPF <= (int)sizeof(red), "the fp32 block fits the tree's buffer");
+    const uint32_t stf = (uint32_t)(uintptr_t)&red[0][0][0];
+    if (wave == 0) {
+#pragma unroll
+      for (int g = 0; g < MG; ++g)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int c = 0; c < T; c += 4)
+            lds_store_f4(stf + (uint32_t)((16 * g + 4 * kg + v) * OPF + (T * nl + c) * 4),
+                         floatx4{acc[g][c][v], acc[g][c + 1][v], acc[g][c + 2][v], acc[g][c + 3][v]});
+    }
+    __syncthreads();
+    const EpiOut eo{p.C, p.ldc, M, N, p.bias, p.act, p.counts, p.flags};
+    store_staged_fused<OUT_BF16, DEBUG>(stf, OPF, 16 * MG, 16 * T, 0, n0, threadIdx.x, NW * 64, eo);
+    return;
   }
 
   if (wave == 0) {

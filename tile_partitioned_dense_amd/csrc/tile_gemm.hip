@@ -126,6 +126,21 @@ tile_gemm_status_t check_args(const void* A, const void* B, const void* C, int64
   return TILE_GEMM_OK;
 }
 
+// Checks of the fused epilogue's arguments (C and its strides already checked).
+tile_gemm_status_t check_epilogue(const void* C, int64_t M, int64_t N,
+                                  const tile_gemm_strides_t* s, int dtype, const float* bias,
+                                  int act) {
+  if (act < TILE_GEMM_ACT_NONE || act > TILE_GEMM_ACT_SILU)
+    return fail(TILE_GEMM_ERR_EPILOGUE, "act: unknown activation %d", act);
+  if (!bias || M == 0 || N == 0) return TILE_GEMM_OK;
+  if ((uintptr_t)bias % 16) return fail(TILE_GEMM_ERR_MISALIGNED, "bias: pointer not 16-byte aligned");
+  const int64_t esz = dtype == TILE_GEMM_BF16_TO_BF16 ? 2 : 4;
+  const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)(esz * ((M - 1) * s->c_m + N));
+  const uintptr_t q0 = (uintptr_t)bias, q1 = q0 + (uintptr_t)(4 * N);
+  if (overlap(c0, c1, q0, q1)) return fail(TILE_GEMM_ERR_ALIAS, "bias overlaps C (C is written)");
+  return TILE_GEMM_OK;
+}
+
 void fill_plan(const tg::Plan& p, tile_gemm_plan_t* out) {
   out->variant = p.variant;
   out->config = p.config;
@@ -181,9 +196,12 @@ static_assert(tg::kNumSkinnyConfigs == 6, "dispatch_skinny covers every skinny c
 
 tile_gemm_status_t run_impl(tile_gemm_t h, const void* A, const void* B, void* C, int64_t M,
                             int64_t N, int64_t K, const tile_gemm_strides_t* s,
-                            tile_gemm_dtype_t dtype, void* stream, uint32_t* counts, int flags) {
+                            tile_gemm_dtype_t dtype, void* stream, uint32_t* counts, int flags,
+                            const float* bias = nullptr, int act = TILE_GEMM_ACT_NONE) {
   if (!h) return fail(TILE_GEMM_ERR_NULL_ARG, "handle: NULL");
-  const tile_gemm_status_t st = check_args(A, B, C, M, N, K, s, (int)dtype);
+  tile_gemm_status_t st = check_args(A, B, C, M, N, K, s, (int)dtype);
+  if (st != TILE_GEMM_OK) return st;
+  st = check_epilogue(C, M, N, s, (int)dtype, bias, act);
   if (st != TILE_GEMM_OK) return st;
   if (M == 0 || N == 0) return TILE_GEMM_OK;
   int cur = -1;
@@ -239,6 +257,8 @@ tile_gemm_status_t run_impl(tile_gemm_t h, const void* A, const void* B, void* C
     a.map = p.map;
     a.counts = counts;
     a.flags = flags;
+    a.bias = bias;
+    a.act = act;
     e = dispatch_tile(p.config, a, p.grid, v, hs);
   } else {
     tg::SkinnyArgs a{};
@@ -253,6 +273,8 @@ tile_gemm_status_t run_impl(tile_gemm_t h, const void* A, const void* B, void* C
     a.ldc = s->c_m;
     a.counts = counts;
     a.flags = flags;
+    a.bias = bias;
+    a.act = act;
     e = dispatch_skinny(p.config, a, p.grid, v, hs);
   }
   if (e != hipSuccess) return fail(TILE_GEMM_ERR_HIP, "launch: %s", hipGetErrorString(e));
@@ -274,6 +296,7 @@ const char* tile_gemm_status_str(tile_gemm_status_t s) {
     case TILE_GEMM_ERR_DTYPE: return "unknown dtype";
     case TILE_GEMM_ERR_DEVICE: return "device unavailable, not gfx950, or not current";
     case TILE_GEMM_ERR_HIP: return "HIP runtime error";
+    case TILE_GEMM_ERR_EPILOGUE: return "unknown activation";
   }
   return "unknown status";
 }
@@ -312,19 +335,37 @@ tile_gemm_status_t tile_gemm_run(tile_gemm_t h, const void* A, const void* B, vo
   return run_impl(h, A, B, C, M, N, K, strides, dtype, stream, nullptr, 0);
 }
 
+tile_gemm_status_t tile_gemm_run_epilogue(tile_gemm_t h, const void* A, const void* B, void* C,
+                                          int64_t M, int64_t N, int64_t K,
+                                          const tile_gemm_strides_t* strides,
+                                          tile_gemm_dtype_t dtype, const float* bias,
+                                          tile_gemm_act_t act, void* stream) {
+  return run_impl(h, A, B, C, M, N, K, strides, dtype, stream, nullptr, 0, bias, (int)act);
+}
+
 tile_gemm_status_t tile_gemm_run_debug(tile_gemm_t h, const void* A, const void* B, void* C,
                                        int64_t M, int64_t N, int64_t K,
                                        const tile_gemm_strides_t* strides, tile_gemm_dtype_t dtype,
-                                       void* stream, uint32_t* counts, int flags) {
+                                       void* stream, uint32_t* counts, int flags,
+                                       const float* bias, tile_gemm_act_t act) {
   if (flags & ~(TILE_GEMM_DEBUG_COUNT_WRITES | TILE_GEMM_DEBUG_COLLIDE | 0x7fffff00))
     return fail(TILE_GEMM_ERR_BAD_SHAPE, "flags: unknown bits 0x%x", flags);
-  return run_impl(h, A, B, C, M, N, K, strides, dtype, stream, counts, flags);
+  return run_impl(h, A, B, C, M, N, K, strides, dtype, stream, counts, flags, bias, (int)act);
 }
 
 tile_gemm_status_t tile_gemm_check_args(const void* A, const void* B, const void* C, int64_t M,
                                         int64_t N, int64_t K, const tile_gemm_strides_t* strides,
                                         tile_gemm_dtype_t dtype) {
   return check_args(A, B, C, M, N, K, strides, (int)dtype);
+}
+
+tile_gemm_status_t tile_gemm_check_epilogue(const void* C, int64_t M, int64_t N,
+                                            const tile_gemm_strides_t* strides,
+                                            tile_gemm_dtype_t dtype, const float* bias,
+                                            tile_gemm_act_t act) {
+  g_detail[0] = '\0';
+  if (!strides) return fail(TILE_GEMM_ERR_NULL_ARG, "strides: NULL");
+  return check_epilogue(C, M, N, strides, (int)dtype, bias, (int)act);
 }
 
 tile_gemm_status_t tile_gemm_plan(int64_t M, int64_t N, int64_t K, int b_col_major, int cu_count,

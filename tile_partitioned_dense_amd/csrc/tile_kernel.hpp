@@ -69,6 +69,8 @@ struct TileArgs {
   TileMap map;
   uint32_t* counts;  // debug instrumentation only
   int32_t flags;     // debug instrumentation only
+  const float* bias;  // fused epilogue: N fp32 values or NULL
+  int32_t act;        // fused epilogue: kAct*
 };
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -639,6 +641,39 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
     constexpr int EPC = 16 / ESZ;       // elements per chunk
     static_assert((SH * CH) % 64 == 0, "a strip is a whole number of wave-wide chunk rows");
     __syncthreads();  // every wave is done reading the ring
+    if (p.bias != nullptr || p.act != kActNone) {
+      // Fused epilogue: strips are staged as fp32 whatever the output type and
+      // read back by a rolled loop that adds the bias, applies the activation
+      // and then converts, so the activation code is emitted once.
+      constexpr int OPF = WTN * 4 + 16;
+      constexpr int SHF = (NW * 32 * OPF <= RING) ? 32 : 16;
+      static_assert(NW * SHF * OPF <= RING, "an fp32 strip of every wave fits the ring");
+      const uint32_t stf = lds0 + (uint32_t)(wave * SHF * OPF);
+      const EpiOut eo{p.C, p.ldc, M, N, p.bias, p.act, p.counts, p.flags};
+  #pragma unroll
+      for (int i = 0; i < FM; ++i) {
+  #pragma unroll
+        for (int hs = 0; hs < 32 / SHF; ++hs) {
+          const int rl = lrow - SHF * hs;
+          if (SHF == 32 || (lrow >> 4) == hs) {
+  #pragma unroll
+            for (int j = 0; j < FN; ++j)
+  #pragma unroll
+              for (int q = 0; q < 4; ++q)
+                lds_store_f4(stf + (uint32_t)(rl * OPF + (32 * j + 8 * q + 4 * lgrp) * 4),
+                             floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                     acc[i][j][4 * q + 3]});
+          }
+          wait_lgkmcnt0();
+          store_staged_fused<OUT_BF16, DEBUG>(stf, OPF, SHF, WTN, m0 + wm * WTM + 32 * i + SHF * hs,
+                                              n0 + wn * WTN, lane, 64, eo);
+          wait_lgkmcnt0();
+        }
+      }
+      wait_lgkmcnt0();
+      block_barrier();
+      continue;
+    }
     const uint32_t stg = lds0 + (uint32_t)(wave * SH * OPITCH);
     const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
   #pragma unroll

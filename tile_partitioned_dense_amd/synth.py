@@ -10,6 +10,8 @@ weights exist here, so every operand is synthetic):
 
 * generator: numpy PCG64 ``default_rng(seed)`` with seed = 1000 * case + op,
   op = 1 for A, 2 for B, 3 and 4 for the integer-valued A and B;
+* a fused-epilogue bias is N(0, 1) (or scaled) drawn in float64 and rounded
+  once to float32;
 * real-valued entries are drawn in float64, scaled in float64 and rounded
   once to bf16 (round to nearest, ties to even);
 * N(0, s2) names the variance: N(0, 1/8192) has standard deviation 8192^-1/2,
@@ -73,6 +75,13 @@ def draw(rows: int, cols: int, dist: str, seed: int, scale: float = 1.0) -> np.n
             x = rng.integers(-3, 4, n).astype(np.float64)
         flat[s:s + n] = f64_to_bf16_bits(x)
     return out
+
+
+def draw_bias(n: int, seed: int, scale: float = 1.0) -> np.ndarray:
+    """A length-n float32 bias vector: N(0, scale^2) drawn in float64 with
+    ``default_rng(seed)`` and rounded once to float32."""
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal(int(n)) * float(scale)).astype(np.float32)
 
 
 @dataclass(frozen=True)
