@@ -43,8 +43,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mlp_gate_up_shard")
-    ap.add_argument("--secondary", default="qkv_shard,square4096,decode,decode_colB,gemm256",
-                    help="comma-separated extra workloads reported on the same line ('' for none)")
+    ap.add_argument("--secondary", default="qkv_shard,square4096,decode,decode_colB,gemm256,"
+                    "mlp_gate_up_shard:bias+silu,decode:bias+silu",
+                    help="comma-separated extra workloads reported on the same line; NAME:EPI adds a "
+                    "fused epilogue, e.g. decode:bias+silu ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time for the oracle baseline sample")
@@ -122,13 +124,25 @@ class Bench:
         log(f"[bench] per-call cost (us): {out}")
         return out
 
-    def time_workload(self, w, out, steps, warmup):
+    def time_workload(self, w, out, steps, warmup, epi=None):
+        """Time `steps` launches of the product over rotating operand sets. `epi`
+        names a fused epilogue ("bias+silu", "relu", ...): the timed call is
+        then tile_gemm_run_epilogue, and the same product followed by torch's
+        separate bias-add and activation pass is timed beside it."""
         torch = self.torch
         ops, sets = self.make(w, out)
         g = self.g
+        kw = {}
+        if epi:
+            parts = epi.split("+")
+            acts = [p for p in parts if p != "bias"]
+            act = self.tg.Act[acts[0].upper()] if acts else self.tg.Act.NONE
+            bias = (torch.from_numpy(self.synth.draw_bias(w.N, 760)).cuda()
+                    if "bias" in parts else None)
+            kw = {"bias": bias, "act": act}
         for i in range(warmup):
             A, B, C = sets[i % len(sets)]
-            g(A, B, C)
+            g(A, B, C, **kw)
         torch.cuda.synchronize()
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -137,14 +151,30 @@ class Bench:
         for i in range(steps):
             A, B, C = sets[i % len(sets)]
             starts[i].record()
-            g(A, B, C)
+            g(A, B, C, **kw)
             ends[i].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms per launch
+        unfused = None
+        if epi:
+            fn = {"none": lambda x: x, "relu": torch.relu, "sigmoid": torch.sigmoid,
+                  "tanh": torch.tanh, "silu": torch.nn.functional.silu}[kw["act"].name.lower()]
+            t = []
+            for i in range(steps + warmup):
+                A, B, C = sets[i % len(sets)]
+                s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s0.record()
+                g(A, B, C)
+                y = fn(C + kw["bias"]) if kw["bias"] is not None else fn(C)
+                s1.record()
+                t.append((s0, s1))
+            torch.cuda.synchronize()
+            unfused = float(np.mean([a.elapsed_time(b) for a, b in t[warmup:]]))
+            del y
         plan = self.tg.tile_gemm_plan(w.M, w.N, w.K, w.b_col_major, 256)
         res = {
-            "workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+            "workload": w.name + (f":{epi}" if epi else ""), "M": w.M, "N": w.N, "K": w.K,
             "b_layout": "column-major" if w.b_col_major else "row-major", "out": out,
             "wall_ms_per_step": 1e3 * wall / steps,
             "kernel_ms_mean": float(per.mean()), "kernel_ms_median": float(np.median(per)),
@@ -153,6 +183,8 @@ class Bench:
             "plan": {"variant": "tile" if plan.variant == 1 else "skinny", "bm": plan.bm,
                      "bn": plan.bn, "grid": int(plan.grid), "k_split": plan.k_split},
         }
+        if unfused is not None:
+            res["unfused_torch_ms_mean"] = unfused
         mean_s = res["kernel_ms_mean"] * 1e-3
         res["tflops"] = w.flops / mean_s / 1e12
         res["gbs"] = w.algorithmic_bytes(out) / mean_s / 1e9
@@ -270,8 +302,9 @@ def main():
     ops, res = b.time_workload(head, head_out, args.steps, args.warmup)
     secondary = []
     for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
-        w = synth.WORKLOADS[name]
-        _, r = b.time_workload(w, w.outs[0], args.steps, args.warmup)
+        base, _, epi = name.partition(":")
+        w = synth.WORKLOADS[base]
+        _, r = b.time_workload(w, w.outs[0], args.steps, args.warmup, epi or None)
         r["roofline"] = roofline(r, hbm_bound=name.startswith("decode"))
         secondary.append(r)
     if args.copy_calibration_mib:

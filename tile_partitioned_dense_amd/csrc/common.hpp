@@ -13,34 +13,50 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 // Fused-epilogue activations (mirror TILE_GEMM_ACT_* in tile_gemm.h).
 constexpr int kActNone = 0, kActRelu = 1, kActSigmoid = 2, kActTanh = 3, kActSilu = 4;
 
-// act(x) in fp32 with the device math library.
-__device__ __forceinline__ float apply_act(float x, int act) {
-  switch (act) {
-    case kActRelu: return fmaxf(x, 0.0f);
-    case kActSigmoid: return 1.0f / (1.0f + expf(-x));
-    case kActTanh: return tanhf(x);
-    case kActSilu: return x / (1.0f + expf(-x));
-    default: return x;
-  }
+// e^x as 2^(x log2 e) on the hardware exponential (v_exp_f32, about 1 ulp):
+// rounding x log2 e adds a relative error of about 2^-24 |x| to the result,
+// the size of the rounding already present in an fp32 x.
+__device__ __forceinline__ float exp_hw(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
 }
 
-// The fused epilogue on four consecutive columns col..col+3 of one row:
-// v[e] = act(v[e] + bias[col + e]) for the columns below N (bias may be NULL).
-__device__ __forceinline__ void apply_epilogue4(float v[4], const float* bias, int act, int col, int N) {
-  if (bias) {
-    if (col + 3 < N) {
-      const float4 b = *reinterpret_cast<const float4*>(bias + col);
-      v[0] += b.x; v[1] += b.y; v[2] += b.z; v[3] += b.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (col + e < N) v[e] += bias[col + e];
-    }
-  }
-  if (act != kActNone) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = apply_act(v[e], act);
-  }
+// 1 / (1 + e^-x) with the hardware reciprocal (about 1 ulp); saturates to
+// exactly 0 and 1 where e^-x overflows or underflows.
+__device__ __forceinline__ float sigmoid_hw(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + exp_hw(-x));
+}
+
+// tanh x. For |x| >= 1/2, 1 - 2 / (e^(2|x|) + 1) with the sign of x: the
+// hardware exponential and reciprocal keep the absolute error near 1e-7,
+// small against |tanh x| >= 0.46. Below 1/2 that difference would cancel, so
+// the odd Taylor series of tanh (coefficients 2^(2n) (2^(2n) - 1) B_2n / (2n)!
+// from the Bernoulli numbers: 1, -1/3, 2/15, -17/315, 62/2835,
+// -1382/155925, 21844/6081075) through x^13 takes over; its truncation error
+// there is below 1e-7 relative. Both are evaluated and one selected, so
+// lanes on either side of 1/2 do not diverge.
+__device__ __forceinline__ float tanh_hw(float x) {
+  const float a = fabsf(x);
+  const float z = a * a;
+  float p = 21844.0f / 6081075.0f;
+  p = p * z - 1382.0f / 155925.0f;
+  p = p * z + 62.0f / 2835.0f;
+  p = p * z - 17.0f / 315.0f;
+  p = p * z + 2.0f / 15.0f;
+  p = p * z - 1.0f / 3.0f;
+  p = p * z + 1.0f;
+  const float small = a * p;
+  const float large = 1.0f - 2.0f * __builtin_amdgcn_rcpf(exp_hw(2.0f * a) + 1.0f);
+  return copysignf(a < 0.5f ? small : large, x);
+}
+
+// act(x) in fp32 for a compile-time activation.
+template <int ACT>
+__device__ __forceinline__ float act_fn(float x) {
+  if constexpr (ACT == kActRelu) return fmaxf(x, 0.0f);
+  else if constexpr (ACT == kActSigmoid) return sigmoid_hw(x);
+  else if constexpr (ACT == kActTanh) return tanh_hw(x);
+  else if constexpr (ACT == kActSilu) return x * sigmoid_hw(x);
+  else return x;
 }
 
 // Debug flags (mirror TILE_GEMM_DEBUG_* in tile_gemm.h).
@@ -131,37 +147,33 @@ __device__ __forceinline__ void lds_store_f4(uint32_t addr, const floatx4& v) {
   *(__attribute__((address_space(3))) floatx4*)(uintptr_t)addr = v;
 }
 
-// Fused-epilogue store of an fp32 block staged row-major in LDS: `rows` x
-// `cols` values at LDS byte address `src` (row pitch `pitch` bytes, both
-// multiples of 16) belong at C[grow0 + r][gcol0 + c]. Thread `tid` of `nthr`
-// takes 16-byte output chunks tid, tid + nthr, ... (4 fp32 or 8 bf16 columns;
-// `cols` is a multiple of 8), forms act(x + bias) in fp32, rounds to bf16
-// (nearest even) for a bf16 output and writes each element of C once, rows
-// and columns past M and N masked. The loop stays rolled, so the activation
-// code is emitted once however large the block.
-template <bool OUT_BF16, bool DEBUG>
-__device__ __forceinline__ void store_staged_fused(uint32_t src, int pitch, int rows, int cols,
-                                                   int grow0, int gcol0, int tid, int nthr,
-                                                   const EpiOut& o) {
-  constexpr int EPC = OUT_BF16 ? 8 : 4;  // elements per 16-byte output chunk
+// The row loop of store_staged_fused for one activation (the activation is
+// a template argument, so the loop carries no per-element dispatch).
+template <bool OUT_BF16, bool DEBUG, int ACT>
+__device__ __forceinline__ void store_staged_rows(uint32_t src, int pitch, int rows, int grow0,
+                                                  int r0, int rstep, int ch, int col, bool full,
+                                                  const float (&b)[OUT_BF16 ? 8 : 4],
+                                                  const EpiOut& o) {
+  constexpr int EPC = OUT_BF16 ? 8 : 4;
   constexpr int ESZ = OUT_BF16 ? 2 : 4;
-  const int cho = cols / EPC;
-  const int total = rows * cho;
-#pragma unroll 1
-  for (int c = tid; c < total; c += nthr) {
-    const int r = c / cho, ch = c - r * cho;
-    const int row = grow0 + r, col = gcol0 + ch * EPC;
-    if (row >= o.M || col >= o.N) continue;
+  const int rend = rows < o.M - grow0 ? rows : o.M - grow0;
+#pragma unroll 2
+  for (int r = r0; r < rend; r += rstep) {
     float v[EPC];
 #pragma unroll
     for (int h = 0; h < EPC / 4; ++h) {
       const floatx4 x = lds_load_f4(src + (uint32_t)(r * pitch + (ch * EPC + 4 * h) * 4));
       v[4 * h] = x[0]; v[4 * h + 1] = x[1]; v[4 * h + 2] = x[2]; v[4 * h + 3] = x[3];
     }
+    if (o.bias) {
 #pragma unroll
-    for (int h = 0; h < EPC / 4; ++h) apply_epilogue4(v + 4 * h, o.bias, o.act, col + 4 * h, o.N);
+      for (int e = 0; e < EPC; ++e) v[e] += b[e];
+    }
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) v[e] = act_fn<ACT>(v[e]);
+    const int row = grow0 + r;
     char* cb = static_cast<char*>(o.C) + ((int64_t)row * o.ldc + col) * ESZ;
-    if (col + EPC <= o.N) {
+    if (full) {
       if constexpr (OUT_BF16) {
         *reinterpret_cast<uint4*>(cb) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                                                    pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
@@ -186,6 +198,62 @@ __device__ __forceinline__ void store_staged_fused(uint32_t src, int pitch, int 
         for (int e = 0; e < EPC; ++e)
           if (col + e < o.N) atomicAdd(o.counts + (int64_t)row * o.N + col + e, 1u);
     }
+  }
+}
+
+// Fused-epilogue store of an fp32 block staged row-major in LDS: `rows` x
+// `cols` values at LDS byte address `src` (row pitch `pitch` bytes, both
+// multiples of 16) belong at C[grow0 + r][gcol0 + c]. The block is cut into
+// 16-byte output chunks (4 fp32 or 8 bf16 columns; `cols` is a multiple of 8
+// and at most 8 * nthr) and thread `tid` of `nthr` keeps one chunk column
+// for every row it visits, so it loads its bias once. Each element is formed
+// as act(x + bias) in fp32, rounded to bf16 (nearest even) for a bf16 output
+// and written once; rows and columns past M and N are masked. The row loop
+// stays rolled (unrolled twice to overlap its LDS reads), so the activation
+// code is emitted a fixed number of times however large the block.
+template <bool OUT_BF16, bool DEBUG>
+__device__ __forceinline__ void store_staged_fused(uint32_t src, int pitch, int rows, int cols,
+                                                   int grow0, int gcol0, int tid, int nthr,
+                                                   const EpiOut& o) {
+  constexpr int EPC = OUT_BF16 ? 8 : 4;  // elements per 16-byte output chunk
+  const int cho = cols / EPC;             // chunks per row
+  const int rstep = nthr / cho;           // rows one pass of the threads covers
+  if (tid >= rstep * cho) return;         // threads past a whole number of rows idle
+  const int ch = tid % cho;
+  const int col = gcol0 + ch * EPC;
+  if (col >= o.N) return;
+  const bool full = col + EPC <= o.N;
+  float b[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) b[e] = 0.0f;
+  if (o.bias) {
+    if (full) {
+#pragma unroll
+      for (int h = 0; h < EPC / 4; ++h) {
+        const float4 x = *reinterpret_cast<const float4*>(o.bias + col + 4 * h);
+        b[4 * h] = x.x; b[4 * h + 1] = x.y; b[4 * h + 2] = x.z; b[4 * h + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e)
+        if (col + e < o.N) b[e] = o.bias[col + e];
+    }
+  }
+  switch (o.act) {
+    case kActRelu:
+      store_staged_rows<OUT_BF16, DEBUG, kActRelu>(src, pitch, rows, grow0, tid / cho, rstep, ch, col, full, b, o);
+      break;
+    case kActSigmoid:
+      store_staged_rows<OUT_BF16, DEBUG, kActSigmoid>(src, pitch, rows, grow0, tid / cho, rstep, ch, col, full, b, o);
+      break;
+    case kActTanh:
+      store_staged_rows<OUT_BF16, DEBUG, kActTanh>(src, pitch, rows, grow0, tid / cho, rstep, ch, col, full, b, o);
+      break;
+    case kActSilu:
+      store_staged_rows<OUT_BF16, DEBUG, kActSilu>(src, pitch, rows, grow0, tid / cho, rstep, ch, col, full, b, o);
+      break;
+    default:
+      store_staged_rows<OUT_BF16, DEBUG, kActNone>(src, pitch, rows, grow0, tid / cho, rstep, ch, col, full, b, o);
   }
 }
 

@@ -237,6 +237,7 @@ __global__ __launch_bounds__(KS * 64, 1) void ksplit_gemm_kernel(TileArgs p) {
       // rolled loop (the activation code is emitted once).
       constexpr int OPF = BN * 4 + 16;
       static_assert(BM * OPF <= LDS, "the fp32 tile fits the workgroup's LDS");
+      static_assert(BN / 4 <= KS * 64, "the workgroup covers a staged row in 16-byte chunks");
       if (wave == 0) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)

@@ -259,6 +259,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(SkinnyArgs p) {
     // bias / activation / store pass.
     constexpr int OPF = 16 * T * 4 + 16;
     static_assert(16 * MG * OPF <= (int)sizeof(red), "the fp32 block fits the tree's buffer");
+    static_assert(16 * T / 4 <= NW * 64, "the workgroup covers a staged row in 16-byte chunks");
     const uint32_t stf = (uint32_t)(uintptr_t)&red[0][0][0];
     if (wave == 0) {
 #pragma unroll

@@ -648,6 +648,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
       constexpr int OPF = WTN * 4 + 16;
       constexpr int SHF = (NW * 32 * OPF <= RING) ? 32 : 16;
       static_assert(NW * SHF * OPF <= RING, "an fp32 strip of every wave fits the ring");
+      static_assert(WTN / 4 <= 64, "one wave covers a staged row in 16-byte chunks");
       const uint32_t stf = lds0 + (uint32_t)(wave * SHF * OPF);
       const EpiOut eo{p.C, p.ldc, M, N, p.bias, p.act, p.counts, p.flags};
   #pragma unroll
