@@ -51,4 +51,7 @@ from .fused_epilogue import (  # noqa: F401
     epilogue,
     epilogue_bound,
     check_epilogue,
+    swiglu,
+    swiglu_bound,
+    check_swiglu,
 )
