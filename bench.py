@@ -140,6 +140,12 @@ class Bench:
             bias = (torch.from_numpy(self.synth.draw_bias(w.N, 760)).cuda()
                     if "bias" in parts else None)
             kw = {"bias": bias, "act": act}
+            if act == self.tg.Act.SWIGLU:
+                # the output is M x N/2; keep the full-width C for the unfused leg
+                sets = [(A, B, torch.empty((w.M, w.N // 2), dtype=C.dtype, device="cuda"), C)
+                        for A, B, C in sets]
+        full_c = {i: (s[3] if len(s) > 3 else s[2]) for i, s in enumerate(sets)}
+        sets = [s[:3] for s in sets]
         for i in range(warmup):
             A, B, C = sets[i % len(sets)]
             g(A, B, C, **kw)
@@ -158,11 +164,15 @@ class Bench:
         per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms per launch
         unfused = None
         if epi:
+            silu = torch.nn.functional.silu
             fn = {"none": lambda x: x, "relu": torch.relu, "sigmoid": torch.sigmoid,
-                  "tanh": torch.tanh, "silu": torch.nn.functional.silu}[kw["act"].name.lower()]
+                  "tanh": torch.tanh, "silu": silu,
+                  "swiglu": lambda x: silu(x[:, :w.N // 2]) * x[:, w.N // 2:]}[
+                      kw["act"].name.lower()]
             t = []
             for i in range(steps + warmup):
-                A, B, C = sets[i % len(sets)]
+                A, B, _ = sets[i % len(sets)]
+                C = full_c[i % len(sets)]
                 s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 s0.record()
                 g(A, B, C)

@@ -115,13 +115,23 @@ tile_gemm_status_t tile_gemm_run(tile_gemm_t h, const void* A, const void* B, vo
  * CuteDSL": a bias addition or an activation folded into the GEMM's store;
  * element-wise operations and ReLU, sigmoid, tanh in its roadmap paragraph).
  * SiLU is x * sigmoid(x).
+ *
+ * TILE_GEMM_ACT_SWIGLU is the gated step that follows a merged gate+up
+ * projection (the column-sharded MLP of the tensor-parallel page,
+ * "Implementing Tensor Parallelism Communication Overlays for Distributed LLM
+ * Inference in Rust"): B's first N/2 columns are the gate, its last N/2 the
+ * up projection, and the output is the M x N/2 matrix
+ * silu(x[i][j]) * x[i][j + N/2], x = A.B + bias. Each output element is
+ * owned and written once by the workgroup that computes both of its product
+ * columns, so the single-writer rule holds for the narrower output too.
  */
 typedef enum {
   TILE_GEMM_ACT_NONE = 0,
   TILE_GEMM_ACT_RELU = 1,     /* max(x, 0) */
   TILE_GEMM_ACT_SIGMOID = 2,  /* 1 / (1 + e^-x) */
   TILE_GEMM_ACT_TANH = 3,     /* tanh x */
-  TILE_GEMM_ACT_SILU = 4      /* x / (1 + e^-x) */
+  TILE_GEMM_ACT_SILU = 4,     /* x / (1 + e^-x) */
+  TILE_GEMM_ACT_SWIGLU = 5    /* silu(gate) * up over the two halves of B's columns */
 } tile_gemm_act_t;
 
 /*
@@ -132,6 +142,9 @@ typedef enum {
  * fp32 value). `bias` is a device pointer to N fp32 values, read-only, 16-byte
  * aligned, not overlapping C; NULL means no bias. With K = 0 the result is
  * act(bias[j]) (act(0) without a bias).
+ * With TILE_GEMM_ACT_SWIGLU, N counts B's columns (gate and up; a multiple of
+ * 16, else TILE_GEMM_ERR_BAD_SHAPE), C is M x N/2 (c_m >= N/2) and bias, if
+ * given, holds N values (gate biases, then up biases).
  * Errors: as tile_gemm_run, plus TILE_GEMM_ERR_EPILOGUE (unknown act),
  * TILE_GEMM_ERR_MISALIGNED (bias) and TILE_GEMM_ERR_ALIAS (bias overlaps C).
  */
@@ -170,7 +183,8 @@ tile_gemm_status_t tile_gemm_check_args(const void* A, const void* B, const void
 
 /*
  * The checks tile_gemm_run_epilogue adds for its epilogue arguments (after
- * those of tile_gemm_check_args), with the same results.
+ * those of tile_gemm_check_args, which for TILE_GEMM_ACT_SWIGLU it applies
+ * with C's width N/2), with the same results.
  */
 tile_gemm_status_t tile_gemm_check_epilogue(const void* C, int64_t M, int64_t N,
                                             const tile_gemm_strides_t* strides,

@@ -26,7 +26,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-ACTS = list(tg.Act)
+ACTS = [a for a in tg.Act if a != tg.Act.SWIGLU]     # elementwise activations
 SKINNY_MG = [1, 1, 2, 2, 4, 4]
 
 
@@ -169,4 +169,104 @@ def test_workload_epilogue_sampled(g, name, act):
         rep = oracle.check_epilogue(out[None, :], c[None, :], d[None, :], b_np[jj],
                                     _name(act), out_bf16=dt == torch.bfloat16)
         assert rep.ok, f"{name} {dt}: {rep}"
+        del C
+
+
+# ------------------------------------------------------ SiLU(gate) * up
+
+def _glu_out(case, dtype, pad=8):
+    h = case.N // 2
+    store = torch.full((case.M, h + pad), float("nan"), dtype=dtype, device="cuda")
+    return store, store[:, :h]
+
+
+def _check_glu(g, case, flags, bias_np, bias_dev, label, counts=False):
+    Cr, Dr = case.ref()
+    h = case.N // 2
+    for with_bias in (True, False):
+        for dt in (torch.float32, torch.bfloat16):
+            store, C = _glu_out(case, dt)
+            cnt = torch.zeros((case.M, h), dtype=torch.int32, device="cuda") if counts else None
+            g.run_debug(case.A_dev, case.B_dev, C, counts=cnt,
+                        flags=flags | (tg.DEBUG_COUNT_WRITES if counts else 0),
+                        bias=bias_dev if with_bias else None, act=tg.Act.SWIGLU)
+            torch.cuda.synchronize()
+            rep = oracle.check_swiglu(host_out(C), Cr, Dr, bias_np if with_bias else None,
+                                      out_bf16=dt == torch.bfloat16)
+            assert rep.ok, f"{label} swiglu bias={with_bias} {dt}: {rep}"
+            assert torch.isnan(store[:, h:].float()).all(), f"{label}: store outside C's columns"
+            if counts:
+                assert bool((cnt == 1).all()), f"{label}: an element not written exactly once"
+
+
+@pytest.mark.parametrize("cfg", range(tg.N_TILE_CONFIGS))
+@pytest.mark.parametrize("bcol", [False, True], ids=["Brow", "Bcol"])
+def test_swiglu_tile_configs(g, cfg, bcol):
+    bm, bn = tile_config_table()[cfg][:2]
+    M, N, K = 2 * bm + 37, 2 * (bn + 24), 200      # half = bn + 24: a ragged last tile
+    print(f"[swiglu tile cfg {cfg} bcol={bcol} {M}x{N}x{K}]", flush=True)
+    case = Case(M, N, K, bcol, seed=100 + cfg, pad=8, b_scale=K ** -0.5)
+    b_np, b_dev = _bias(N, 800 + cfg)
+    _check_glu(g, case, tg.DEBUG_FORCE_TILE(cfg), b_np, b_dev, f"tile cfg {cfg}", counts=True)
+
+
+@pytest.mark.parametrize("cfg", range(tg.N_SKINNY_CONFIGS))
+@pytest.mark.parametrize("bcol", [False, True], ids=["Brow", "Bcol"])
+def test_swiglu_skinny_configs(g, cfg, bcol):
+    M, N, K = 16 * SKINNY_MG[cfg] - 3, 2 * (8 * 8 * 3 + 8), 8 * 32 * 3 + 24 + 5
+    print(f"[swiglu skinny cfg {cfg} bcol={bcol} {M}x{N}x{K}]", flush=True)
+    case = Case(M, N, K, bcol, seed=120 + cfg, pad=8, b_scale=K ** -0.5)
+    b_np, b_dev = _bias(N, 820 + cfg)
+    _check_glu(g, case, tg.DEBUG_FORCE_SKINNY(cfg), b_np, b_dev, f"skinny cfg {cfg}",
+               counts=True)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 272, 0), (5, 304, 0), (1000, 1024, 1000),
+                                   (64, 28672 // 8, 1024)], ids=["K0-tile", "K0-skinny",
+                                                                  "square", "k-split"])
+def test_swiglu_planner_path(g, M, N, K):
+    print(f"[swiglu planner {M}x{N}x{K}]", flush=True)
+    case = Case(M, N, K, seed=140, b_scale=max(K, 1) ** -0.5)
+    b_np, b_dev = _bias(N, 840, scale=2.0)
+    _check_glu(g, case, 0, b_np, b_dev, f"{M}x{N}x{K}")
+
+
+def test_swiglu_rejects_bad_widths(g):
+    case = Case(64, 72, 64, seed=141)                  # 72 is even but not a multiple of 16
+    _, C = _glu_out(case, torch.float32)
+    st = tg.tile_gemm_run_epilogue(g.handle, case.A_dev, case.B_dev, C, act=tg.Act.SWIGLU,
+                                   check=False)
+    assert st == tg.Status.ERR_BAD_SHAPE
+    case = Case(64, 64, 64, seed=142)
+    wrong = torch.empty((64, 64), dtype=torch.float32, device="cuda")   # must be 64 x 32
+    with pytest.raises(ValueError):
+        g(case.A_dev, case.B_dev, wrong, act=tg.Act.SWIGLU)
+
+
+@pytest.mark.parametrize("name", ["mlp_gate_up_shard", "decode", "decode_colB"])
+def test_swiglu_workload_sampled(g, name):
+    """The gate+up workloads at full size with their SiLU(gate) * up: sampled
+    output elements against the oracle's one-element products of both the
+    gate and the up column."""
+    w, ops, A, B = workload_case(name)
+    h = w.N // 2
+    print(f"[swiglu workload {name} {w.M}x{w.N}x{w.K}]", flush=True)
+    b_np, b_dev = _bias(w.N, 860)
+    rng = np.random.default_rng(12)
+    ii = np.concatenate([rng.integers(0, w.M, 300), [0, w.M - 1, 0, w.M - 1]])
+    jj = np.concatenate([rng.integers(0, h, 300), [0, 0, h - 1, h - 1]])
+    cg, dg = oracle.gemm_at(ops.A, ops.B, ii, jj)
+    cu, du = oracle.gemm_at(ops.A, ops.B, ii, jj + h)
+    C2 = np.stack([cg, cu], axis=1)                     # n x 2: [gate, up] per sample
+    D2 = np.stack([dg, du], axis=1)
+    for dt in (torch.float32, torch.bfloat16):
+        C = torch.full((w.M, h), float("nan"), dtype=dt, device="cuda")
+        g(A, B, C, bias=b_dev, act=tg.Act.SWIGLU)
+        torch.cuda.synchronize()
+        out = host_out(C)[ii, jj]
+        for t in range(len(ii)):
+            bias2 = np.array([b_np[jj[t]], b_np[jj[t] + h]])
+            rep = oracle.check_swiglu(out[t:t + 1, None], C2[t:t + 1], D2[t:t + 1], bias2,
+                                      out_bf16=dt == torch.bfloat16)
+            assert rep.ok, f"{name} {dt} sample ({ii[t]}, {jj[t]}): {rep}"
         del C

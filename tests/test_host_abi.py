@@ -150,7 +150,7 @@ def test_check_epilogue():
     for a in Act:
         assert chk_epi(act=a) == Status.OK
         assert chk_epi(bias=None, act=a) == Status.OK          # bias is optional
-    assert chk_epi(act=5) == Status.ERR_EPILOGUE
+    assert chk_epi(act=6) == Status.ERR_EPILOGUE
     assert chk_epi(act=-1) == Status.ERR_EPILOGUE
     assert "activation" in tg.last_error_detail()
     assert chk_epi(bias=0x400004) == Status.ERR_MISALIGNED
@@ -170,3 +170,13 @@ def test_run_epilogue_null_handle_and_bad_act():
     s = Strides(64, 1, 64, 1, 64, 1)
     assert lib.tile_gemm_run_epilogue(None, A0, B0, C0, 64, 64, 64, ctypes.byref(s), 0, None, 0,
                                       None) == Status.ERR_NULL_ARG
+
+
+def test_check_swiglu_widths():
+    from tile_partitioned_dense_amd.binding import Act
+    # N counts gate + up columns and must be a multiple of 16; C is M x N/2
+    assert chk_epi(act=Act.SWIGLU, N=64) == Status.OK
+    assert chk_epi(act=Act.SWIGLU, N=72, s=(64, 1, 72, 1, 72, 1)) == Status.ERR_BAD_SHAPE
+    # the bias (N values) may sit right after C's M x N/2 fp32 elements
+    assert chk_epi(act=Act.SWIGLU, bias=C0 + 4 * (63 * 64 + 32)) == Status.OK
+    assert chk_epi(act=Act.SWIGLU, bias=C0 + 4 * (63 * 64 + 32) - 16) == Status.ERR_ALIAS

@@ -40,6 +40,7 @@ class Act(enum.IntEnum):
     SIGMOID = 2
     TANH = 3
     SILU = 4
+    SWIGLU = 5
 
 
 DEBUG_COUNT_WRITES = 1
@@ -174,8 +175,9 @@ def _is_tensor(x):
     return hasattr(x, "data_ptr") and hasattr(x, "stride")
 
 
-def _operands(A, B, C, M, N, K, strides, dtype):
-    """Pointers, shape, strides and dtype from torch tensors or raw values."""
+def _operands(A, B, C, M, N, K, strides, dtype, c_cols_div=1):
+    """Pointers, shape, strides and dtype from torch tensors or raw values.
+    C has N / c_cols_div columns (2 for SiLU(gate) * up)."""
     if _is_tensor(A) and _is_tensor(B) and _is_tensor(C):
         import torch
         if A.dim() != 2 or B.dim() != 2 or C.dim() != 2:
@@ -184,7 +186,7 @@ def _operands(A, B, C, M, N, K, strides, dtype):
             raise TypeError("A and B must be bfloat16")
         M_, K_ = A.shape
         K2, N_ = B.shape
-        if K2 != K_ or tuple(C.shape) != (M_, N_):
+        if K2 != K_ or N_ % c_cols_div or tuple(C.shape) != (M_, N_ // c_cols_div):
             raise ValueError(f"shapes do not chain: A{tuple(A.shape)} B{tuple(B.shape)} "
                              f"C{tuple(C.shape)}")
         if dtype is None:
@@ -228,8 +230,11 @@ def tile_gemm_run(h, A, B, C, M=None, N=None, K=None, strides=None, dtype=None, 
 
 def tile_gemm_run_epilogue(h, A, B, C, bias=None, act=Act.NONE, M=None, N=None, K=None,
                            strides=None, dtype=None, stream=None, check: bool = True):
-    """Enqueue C := act(A.B + bias) (bias: N fp32 values on the device, or None)."""
-    a, b, c, M_, N_, K_, s, dt = _operands(A, B, C, M, N, K, strides, dtype)
+    """Enqueue C := act(A.B + bias) (bias: N fp32 values on the device, or None).
+    With act=Act.SWIGLU, C is M x N/2: silu of B's first N/2 columns' results
+    times its last N/2."""
+    div = 2 if int(act) == Act.SWIGLU else 1
+    a, b, c, M_, N_, K_, s, dt = _operands(A, B, C, M, N, K, strides, dtype, div)
     bp = bias.data_ptr() if _is_tensor(bias) else bias
     st = load_library().tile_gemm_run_epilogue(h, a, b, c, M_, N_, K_, ctypes.byref(s), dt, bp,
                                                int(act), _stream_ptr(stream, C))
@@ -242,7 +247,8 @@ def tile_gemm_run_debug(h, A, B, C, counts=None, flags=0, M=None, N=None, K=None
                         dtype=None, stream=None, check: bool = True, bias=None, act=Act.NONE):
     """tile_gemm_run (or, with bias/act, tile_gemm_run_epilogue) with test
     instrumentation (write counts, collision, forced configuration or grid)."""
-    a, b, c, M_, N_, K_, s, dt = _operands(A, B, C, M, N, K, strides, dtype)
+    div = 2 if int(act) == Act.SWIGLU else 1
+    a, b, c, M_, N_, K_, s, dt = _operands(A, B, C, M, N, K, strides, dtype, div)
     cnt = counts.data_ptr() if _is_tensor(counts) else counts
     bp = bias.data_ptr() if _is_tensor(bias) else bias
     st = load_library().tile_gemm_run_debug(h, a, b, c, M_, N_, K_, ctypes.byref(s), dt,

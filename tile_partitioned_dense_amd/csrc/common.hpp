@@ -11,7 +11,8 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // Fused-epilogue activations (mirror TILE_GEMM_ACT_* in tile_gemm.h).
-constexpr int kActNone = 0, kActRelu = 1, kActSigmoid = 2, kActTanh = 3, kActSilu = 4;
+constexpr int kActNone = 0, kActRelu = 1, kActSigmoid = 2, kActTanh = 3, kActSilu = 4,
+              kActSwiglu = 5;
 
 // e^x as 2^(x log2 e) on the hardware exponential (v_exp_f32, about 1 ulp):
 // rounding x log2 e adds a relative error of about 2^-24 |x| to the result,
@@ -254,6 +255,92 @@ __device__ __forceinline__ void store_staged_fused(uint32_t src, int pitch, int 
       break;
     default:
       store_staged_rows<OUT_BF16, DEBUG, kActNone>(src, pitch, rows, grow0, tid / cho, rstep, ch, col, full, b, o);
+  }
+}
+
+// SiLU(gate) * up store of an fp32 gate+up block staged in LDS: block row r
+// (0 <= r < rows) holds `cols` gate values followed by the `cols` matching up
+// values, at LDS byte address src + r * pitch. Block row r is output row
+// grow0 + (r / rgroup) * rgap + r % rgroup (several waves' strips side by
+// side); block column c < cols is output column gcol0 + c of an output o.N
+// (= half the product's columns) wide. The gate's bias is bias[j], the up
+// value's bias[half + j]. Threads split the work as in store_staged_fused.
+template <bool OUT_BF16, bool DEBUG>
+__device__ __forceinline__ void store_staged_glu(uint32_t src, int pitch, int rows, int cols,
+                                                 int rgroup, int rgap, int grow0, int gcol0,
+                                                 int tid, int nthr, const EpiOut& o) {
+  constexpr int EPC = OUT_BF16 ? 8 : 4;
+  constexpr int ESZ = OUT_BF16 ? 2 : 4;
+  const int cho = cols / EPC;
+  const int rstep = nthr / cho;
+  if (tid >= rstep * cho) return;
+  const int ch = tid % cho;
+  const int col = gcol0 + ch * EPC;
+  if (col >= o.N) return;
+  const bool full = col + EPC <= o.N;
+  float bg[EPC], bu[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) {
+    bg[e] = 0.0f;
+    bu[e] = 0.0f;
+  }
+  if (o.bias) {
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      if (full || col + e < o.N) {
+        bg[e] = o.bias[col + e];
+        bu[e] = o.bias[o.N + col + e];
+      }
+    }
+  }
+#pragma unroll 2
+  for (int r = tid / cho; r < rows; r += rstep) {
+    const int row = grow0 + (r / rgroup) * rgap + (r - (r / rgroup) * rgroup);
+    if (row >= o.M) continue;
+    float g[EPC], u[EPC];
+#pragma unroll
+    for (int h = 0; h < EPC / 4; ++h) {
+      const uint32_t a = src + (uint32_t)(r * pitch + (ch * EPC + 4 * h) * 4);
+      const floatx4 x = lds_load_f4(a);
+      const floatx4 y = lds_load_f4(a + (uint32_t)(cols * 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        g[4 * h + e] = x[e];
+        u[4 * h + e] = y[e];
+      }
+    }
+    float v[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      const float gv = g[e] + bg[e], uv = u[e] + bu[e];
+      v[e] = gv * sigmoid_hw(gv) * uv;
+    }
+    char* cb = static_cast<char*>(o.C) + ((int64_t)row * o.ldc + col) * ESZ;
+    if (full) {
+      if constexpr (OUT_BF16) {
+        *reinterpret_cast<uint4*>(cb) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                   pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+      } else {
+        *reinterpret_cast<float4*>(cb) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        if (col + e < o.N) {
+          if constexpr (OUT_BF16) {
+            reinterpret_cast<uint16_t*>(cb)[e] = f32_to_bf16(v[e]);
+          } else {
+            reinterpret_cast<float*>(cb)[e] = v[e];
+          }
+        }
+      }
+    }
+    if constexpr (DEBUG) {
+      if (o.flags & kDbgCount)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+          if (col + e < o.N) atomicAdd(o.counts + (int64_t)row * o.N + col + e, 1u);
+    }
   }
 }
 

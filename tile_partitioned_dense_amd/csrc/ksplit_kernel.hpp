@@ -51,6 +51,10 @@ __global__ __launch_bounds__(KS * 64, 1) void ksplit_gemm_kernel(TileArgs p) {
   const uint32_t ring = lds0 + (uint32_t)(wave * RING);
   const int M = p.M, N = p.N, K = p.K;
   const int64_t lda = p.lda, ldb = p.ldb;
+  // SiLU(gate) * up: the tile's last BN/2 columns are the up columns of its
+  // first BN/2 gate columns (B column shift glu - BN/2), as in the tile kernel
+  const int glu = p.glu_half;
+  const int gshift = glu ? glu - BN / 2 : 0;
   const int lrow = lane & 31, lgrp = lane >> 5;
   const int tG = lane >> 4, tj = (lane >> 2) & 3, tq = lane & 3;
 
@@ -70,12 +74,12 @@ __global__ __launch_bounds__(KS * 64, 1) void ksplit_gemm_kernel(TileArgs p) {
   for (int u = 0; u < B_UNITS; ++u) {
     if constexpr (BCOL) {
       const int r = 16 * u + (lane >> 2);
-      voB[u] = (uint32_t)(r * ldb * 2) + (((lane & 3) ^ swzA(r)) << 4);
+      voB[u] = (uint32_t)((r + (r >= BN / 2 ? gshift : 0)) * ldb * 2) + (((lane & 3) ^ swzA(r)) << 4);
     } else {
       const int q = 64 * u + lane;
       const int row = q / CPR, pc = q - (q / CPR) * CPR;
       const int lc = SWB ? ((((pc >> 2) ^ (row & 3)) << 2) | (pc & 3)) : pc;
-      voB[u] = (uint32_t)(row * ldb * 2) + lc * 16;
+      voB[u] = (uint32_t)(row * ldb * 2) + lc * 16 + (lc >= CPR / 2 ? 2 * gshift : 0);
     }
   }
   const uint32_t ldsw = __builtin_amdgcn_readfirstlane(ring);
@@ -88,7 +92,7 @@ __global__ __launch_bounds__(KS * 64, 1) void ksplit_gemm_kernel(TileArgs p) {
     }
     int32_t tm, tn;
     tile_of(p.map, wg, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int m0 = tm * BM, n0 = tn * (glu ? BN / 2 : BN);
     const char* a_panel = reinterpret_cast<const char*>(p.A + (int64_t)m0 * lda);
     const int64_t a_bytes = K > 0 ? (((int64_t)(M - 1) * lda + K) - (int64_t)m0 * lda) * 2 : 0;
     const char* b_panel = reinterpret_cast<const char*>(BCOL ? p.B + (int64_t)n0 * ldb : p.B + n0);
@@ -123,8 +127,9 @@ __global__ __launch_bounds__(KS * 64, 1) void ksplit_gemm_kernel(TileArgs p) {
         if constexpr (BCOL) {
           for (int q = lane; q < BN * 4; q += 64) {
             const int r = q >> 2, c = q & 3;
-            const uint4 v = (n0 + r < N) ? load8_masked(p.B + (int64_t)(n0 + r) * ldb, k0 + 8 * c, K)
-                                         : make_uint4(0, 0, 0, 0);
+            const int col = n0 + r + (r >= BN / 2 ? gshift : 0);
+            const uint4 v = (col < N) ? load8_masked(p.B + (int64_t)col * ldb, k0 + 8 * c, K)
+                                      : make_uint4(0, 0, 0, 0);
             dB[r * 4 + (c ^ swzA(r))] = v;
           }
         } else {
@@ -132,7 +137,8 @@ __global__ __launch_bounds__(KS * 64, 1) void ksplit_gemm_kernel(TileArgs p) {
             const int row = q / CPR, pc = q - (q / CPR) * CPR;
             const int lc = SWB ? ((((pc >> 2) ^ (row & 3)) << 2) | (pc & 3)) : pc;
             const int gk = k0 + row;
-            const uint4 v = (gk < K) ? load8_masked(p.B + (int64_t)gk * ldb, n0 + 8 * lc, N)
+            const int col = n0 + 8 * lc + (lc >= CPR / 2 ? gshift : 0);
+            const uint4 v = (gk < K) ? load8_masked(p.B + (int64_t)gk * ldb, col, N)
                                      : make_uint4(0, 0, 0, 0);
             dB[row * CPR + pc] = v;
           }
@@ -250,8 +256,15 @@ __global__ __launch_bounds__(KS * 64, 1) void ksplit_gemm_kernel(TileArgs p) {
                                    acc[i][j][4 * q + 3]});
       }
       __syncthreads();
-      const EpiOut eo{p.C, p.ldc, M, N, p.bias, p.act, p.counts, p.flags};
-      store_staged_fused<OUT_BF16, DEBUG>(lds0, OPF, BM, BN, m0, n0, threadIdx.x, KS * 64, eo);
+      if (glu) {
+        static_assert(BN / 2 % 8 == 0, "whole output chunks per row");
+        const EpiOut eo{p.C, p.ldc, M, glu, p.bias, p.act, p.counts, p.flags};
+        store_staged_glu<OUT_BF16, DEBUG>(lds0, OPF, BM, BN / 2, BM, 0, m0, n0, threadIdx.x,
+                                          KS * 64, eo);
+      } else {
+        const EpiOut eo{p.C, p.ldc, M, N, p.bias, p.act, p.counts, p.flags};
+        store_staged_fused<OUT_BF16, DEBUG>(lds0, OPF, BM, BN, m0, n0, threadIdx.x, KS * 64, eo);
+      }
       __syncthreads();
       continue;
     }

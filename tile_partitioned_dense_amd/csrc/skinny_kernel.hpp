@@ -37,6 +37,7 @@ struct SkinnyArgs {
   int32_t flags;
   const float* bias;  // fused epilogue: N fp32 values or NULL
   int32_t act;        // fused epilogue: kAct*
+  int32_t glu_half;   // SiLU(gate) * up: N / 2 (the gate's width), else 0
 };
 
 template <int T>
@@ -78,9 +79,15 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(SkinnyArgs p) {
   const int wave = threadIdx.x >> 6;
   const int kg = lane >> 4, nl = lane & 15;
   const int M = p.M, N = p.N, K = p.K;
-  const int n0 = blockIdx.x * (16 * T);
-  const int ncol = n0 + T * nl;  // first of this lane's T columns
-  const bool cols_full = (n0 + 16 * T) <= N;
+  // With SiLU(gate) * up a workgroup owns 8 T output columns n0 ..: lanes
+  // nl < 8 read their gate columns, lanes nl >= 8 the matching up columns
+  // glu + n0 + .., so both halves of an output column meet in one block.
+  const int glu = p.glu_half;
+  const int n0 = blockIdx.x * (glu ? 8 * T : 16 * T);      // first output column
+  const int lcol = n0 + T * (glu ? (nl & 7) : nl);         // this lane's first logical column
+  const int ncol = lcol + ((glu && nl >= 8) ? glu : 0);    // ... and its first column of B
+  const int climit = glu ? glu : N;                        // logical columns end here
+  const bool cols_full = n0 + (glu ? 8 * T : 16 * T) <= climit;
 
   const int nkb = (K + 31) >> 5;
   const int kb0 = (wave * nkb) / NW;
@@ -197,7 +204,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(SkinnyArgs p) {
         for (int c = 0; c < T; ++c) {
           const int col = ncol + c;
           uint4 v = make_uint4(0, 0, 0, 0);
-          if (valid && col < N) v = load8_masked(p.B + (int64_t)col * p.ldb, kbase, K);
+          if (valid && lcol + c < climit) v = load8_masked(p.B + (int64_t)col * p.ldb, kbase, K);
           bt[u][c] = as_bf16x8(v);
         }
       } else {
@@ -206,8 +213,8 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(SkinnyArgs p) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           const int gk = kbase + r;
-          if (valid && gk < K && ncol < N) {
-            rows[r] = load_row_chunk<T>(p.B + (int64_t)gk * p.ldb, ncol, N, fast);
+          if (valid && gk < K && lcol < climit) {
+            rows[r] = load_row_chunk<T>(p.B + (int64_t)gk * p.ldb, ncol, ncol - lcol + climit, fast);
           } else {
 #pragma unroll
             for (int d = 0; d < T / 2; ++d) rows[r].w[d] = 0u;
@@ -272,8 +279,14 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(SkinnyArgs p) {
                          floatx4{acc[g][c][v], acc[g][c + 1][v], acc[g][c + 2][v], acc[g][c + 3][v]});
     }
     __syncthreads();
-    const EpiOut eo{p.C, p.ldc, M, N, p.bias, p.act, p.counts, p.flags};
-    store_staged_fused<OUT_BF16, DEBUG>(stf, OPF, 16 * MG, 16 * T, 0, n0, threadIdx.x, NW * 64, eo);
+    if (glu) {
+      const EpiOut eo{p.C, p.ldc, M, glu, p.bias, p.act, p.counts, p.flags};
+      store_staged_glu<OUT_BF16, DEBUG>(stf, OPF, 16 * MG, 8 * T, 16 * MG, 0, 0, n0, threadIdx.x,
+                                        NW * 64, eo);
+    } else {
+      const EpiOut eo{p.C, p.ldc, M, N, p.bias, p.act, p.counts, p.flags};
+      store_staged_fused<OUT_BF16, DEBUG>(stf, OPF, 16 * MG, 16 * T, 0, n0, threadIdx.x, NW * 64, eo);
+    }
     return;
   }
 

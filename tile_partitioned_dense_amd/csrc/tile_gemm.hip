@@ -56,8 +56,11 @@ bool overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
   return a0 < a1 && b0 < b1 && a0 < b1 && b0 < a1;
 }
 
+// n_out: C's width (N, or N/2 for SiLU(gate) * up); -1 means N.
 tile_gemm_status_t check_args(const void* A, const void* B, const void* C, int64_t M, int64_t N,
-                              int64_t K, const tile_gemm_strides_t* s, int dtype) {
+                              int64_t K, const tile_gemm_strides_t* s, int dtype,
+                              int64_t n_out = -1) {
+  if (n_out < 0) n_out = N;
   g_detail[0] = '\0';
   if (dtype != TILE_GEMM_BF16_TO_F32 && dtype != TILE_GEMM_BF16_TO_BF16)
     return fail(TILE_GEMM_ERR_DTYPE, "dtype: unknown value %d", dtype);
@@ -87,10 +90,10 @@ tile_gemm_status_t check_args(const void* A, const void* B, const void* C, int64
                   "or b_k == 1 and b_n >= K=%lld (column-major)",
                   (long long)s->b_k, (long long)s->b_n, (long long)N, (long long)K);
   }
-  if (s->c_n != 1 || s->c_m < N)
+  if (s->c_n != 1 || s->c_m < n_out)
     return fail(TILE_GEMM_ERR_BAD_STRIDE,
-                "C strides (c_m=%lld, c_n=%lld): need c_n == 1 and c_m >= N=%lld",
-                (long long)s->c_m, (long long)s->c_n, (long long)N);
+                "C strides (c_m=%lld, c_n=%lld): need c_n == 1 and c_m >= %lld (C's width)",
+                (long long)s->c_m, (long long)s->c_n, (long long)n_out);
 
   const int64_t esz = (dtype == TILE_GEMM_BF16_TO_F32) ? 4 : 2;
   if ((uintptr_t)C % 16) return fail(TILE_GEMM_ERR_MISALIGNED, "C: base pointer not 16-byte aligned");
@@ -120,7 +123,7 @@ tile_gemm_status_t check_args(const void* A, const void* B, const void* C, int64
   const uintptr_t a0 = (uintptr_t)A, b0 = (uintptr_t)B, c0 = (uintptr_t)C;
   const uintptr_t a1 = a0 + (uintptr_t)a_span;
   const uintptr_t b1 = b0 + (uintptr_t)b_span;
-  const uintptr_t c1 = c0 + (uintptr_t)(esz * ((M - 1) * s->c_m + N));
+  const uintptr_t c1 = c0 + (uintptr_t)(esz * ((M - 1) * s->c_m + n_out));
   if (overlap(c0, c1, a0, a1)) return fail(TILE_GEMM_ERR_ALIAS, "C overlaps A (C is written)");
   if (overlap(c0, c1, b0, b1)) return fail(TILE_GEMM_ERR_ALIAS, "C overlaps B (C is written)");
   return TILE_GEMM_OK;
@@ -130,12 +133,18 @@ tile_gemm_status_t check_args(const void* A, const void* B, const void* C, int64
 tile_gemm_status_t check_epilogue(const void* C, int64_t M, int64_t N,
                                   const tile_gemm_strides_t* s, int dtype, const float* bias,
                                   int act) {
-  if (act < TILE_GEMM_ACT_NONE || act > TILE_GEMM_ACT_SILU)
+  if (act < TILE_GEMM_ACT_NONE || act > TILE_GEMM_ACT_SWIGLU)
     return fail(TILE_GEMM_ERR_EPILOGUE, "act: unknown activation %d", act);
+  const bool glu = act == TILE_GEMM_ACT_SWIGLU;
+  if (glu && N % 16)
+    return fail(TILE_GEMM_ERR_BAD_SHAPE,
+                "N=%lld: SiLU(gate) * up needs B's column count (gate + up) a multiple of 16",
+                (long long)N);
   if (!bias || M == 0 || N == 0) return TILE_GEMM_OK;
   if ((uintptr_t)bias % 16) return fail(TILE_GEMM_ERR_MISALIGNED, "bias: pointer not 16-byte aligned");
   const int64_t esz = dtype == TILE_GEMM_BF16_TO_BF16 ? 2 : 4;
-  const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)(esz * ((M - 1) * s->c_m + N));
+  const int64_t n_out = glu ? N / 2 : N;
+  const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)(esz * ((M - 1) * s->c_m + n_out));
   const uintptr_t q0 = (uintptr_t)bias, q1 = q0 + (uintptr_t)(4 * N);
   if (overlap(c0, c1, q0, q1)) return fail(TILE_GEMM_ERR_ALIAS, "bias overlaps C (C is written)");
   return TILE_GEMM_OK;
@@ -199,7 +208,8 @@ tile_gemm_status_t run_impl(tile_gemm_t h, const void* A, const void* B, void* C
                             tile_gemm_dtype_t dtype, void* stream, uint32_t* counts, int flags,
                             const float* bias = nullptr, int act = TILE_GEMM_ACT_NONE) {
   if (!h) return fail(TILE_GEMM_ERR_NULL_ARG, "handle: NULL");
-  tile_gemm_status_t st = check_args(A, B, C, M, N, K, s, (int)dtype);
+  const bool glu = act == TILE_GEMM_ACT_SWIGLU;
+  tile_gemm_status_t st = check_args(A, B, C, M, N, K, s, (int)dtype, glu ? N / 2 : N);
   if (st != TILE_GEMM_OK) return st;
   st = check_epilogue(C, M, N, s, (int)dtype, bias, act);
   if (st != TILE_GEMM_OK) return st;
@@ -259,6 +269,7 @@ tile_gemm_status_t run_impl(tile_gemm_t h, const void* A, const void* B, void* C
     a.flags = flags;
     a.bias = bias;
     a.act = act;
+    a.glu_half = glu ? (int32_t)(N / 2) : 0;
     e = dispatch_tile(p.config, a, p.grid, v, hs);
   } else {
     tg::SkinnyArgs a{};
@@ -275,6 +286,7 @@ tile_gemm_status_t run_impl(tile_gemm_t h, const void* A, const void* B, void* C
     a.flags = flags;
     a.bias = bias;
     a.act = act;
+    a.glu_half = glu ? (int32_t)(N / 2) : 0;
     e = dispatch_skinny(p.config, a, p.grid, v, hs);
   }
   if (e != hipSuccess) return fail(TILE_GEMM_ERR_HIP, "launch: %s", hipGetErrorString(e));

@@ -71,6 +71,7 @@ struct TileArgs {
   int32_t flags;     // debug instrumentation only
   const float* bias;  // fused epilogue: N fp32 values or NULL
   int32_t act;        // fused epilogue: kAct*
+  int32_t glu_half;   // SiLU(gate) * up: N / 2 (the gate's width), else 0
 };
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -225,9 +226,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
     }
     int32_t tm, tn;
     tile_of(p.map, wg, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, N = p.N, K = p.K;
     const int64_t lda = p.lda, ldb = p.ldb;
+    // With SiLU(gate) * up the tile's first BN/2 columns are gate columns
+    // n0 .. and its last BN/2 the up columns glu + n0 ..: B column n0 + c for
+    // c < BN/2, glu - BN/2 + n0 + c above. Otherwise plain columns n0 + c.
+    const int glu = p.glu_half;
+    const int gshift = glu ? glu - BN / 2 : 0;
+    const int m0 = tm * BM, n0 = tn * (glu ? BN / 2 : BN);
 
     // ---- this tile's panels and their valid extents in bytes (to the last
     // valid element of the operand)
@@ -258,12 +264,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
       if constexpr (BCOL) {
         const int r = 16 * ins + (lane >> 2);
         const int c = (lane & 3) ^ swzA(r);
-        voB[t] = (uint32_t)(r * ldb * 2) + c * 16;
+        voB[t] = (uint32_t)((r + (r >= BN / 2 ? gshift : 0)) * ldb * 2) + c * 16;
       } else {
         const int q = 64 * ins + lane;
         const int row = q / CPR, pc = q - (q / CPR) * CPR;
         const int lc = SWB ? ((((pc >> 2) ^ (row & 3)) << 2) | (pc & 3)) : pc;
-        voB[t] = (uint32_t)(row * ldb * 2) + lc * 16;
+        voB[t] = (uint32_t)(row * ldb * 2) + lc * 16 + (lc >= CPR / 2 ? 2 * gshift : 0);
       }
     }
 
@@ -299,8 +305,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
         if constexpr (BCOL) {
           for (int q = tid; q < BN * 4; q += NT) {
             const int r = q >> 2, c = q & 3;
-            const uint4 v = (n0 + r < N) ? load8_masked(p.B + (int64_t)(n0 + r) * ldb, k0 + 8 * c, K)
-                                         : make_uint4(0, 0, 0, 0);
+            const int col = n0 + r + (r >= BN / 2 ? gshift : 0);
+            const uint4 v = (col < N) ? load8_masked(p.B + (int64_t)col * ldb, k0 + 8 * c, K)
+                                      : make_uint4(0, 0, 0, 0);
             dB[r * 4 + (c ^ swzA(r))] = v;
           }
         } else {
@@ -308,7 +315,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
             const int row = q / CPR, pc = q - (q / CPR) * CPR;
             const int lc = SWB ? ((((pc >> 2) ^ (row & 3)) << 2) | (pc & 3)) : pc;
             const int gk = k0 + row;
-            const uint4 v = (gk < K) ? load8_masked(p.B + (int64_t)gk * ldb, n0 + 8 * lc, N)
+            const int col = n0 + 8 * lc + (lc >= CPR / 2 ? gshift : 0);
+            const uint4 v = (gk < K) ? load8_masked(p.B + (int64_t)gk * ldb, col, N)
                                      : make_uint4(0, 0, 0, 0);
             dB[row * CPR + pc] = v;
           }
@@ -641,6 +649,38 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
     constexpr int EPC = 16 / ESZ;       // elements per chunk
     static_assert((SH * CH) % 64 == 0, "a strip is a whole number of wave-wide chunk rows");
     __syncthreads();  // every wave is done reading the ring
+    if (glu) {
+      // SiLU(gate) * up: a gate column and its up column sit in different
+      // waves' sub-tiles, so every wave stages its strip of 32 (or 16) rows
+      // into one block-wide fp32 strip, and after a barrier all threads form
+      // silu(gate) * up for the BN/2 output columns and store them.
+      constexpr int OPG = BN * 4 + 16;
+      constexpr int SHG = (WM * 32 * OPG <= RING) ? 32 : 16;
+      static_assert(WM * SHG * OPG <= RING, "a block-wide fp32 strip fits the ring");
+      static_assert(BN / 2 % 8 == 0 && BN / 2 / 4 <= NT, "whole output chunks per block row");
+      const EpiOut eo{p.C, p.ldc, M, glu, p.bias, p.act, p.counts, p.flags};
+  #pragma unroll
+      for (int i = 0; i < FM; ++i) {
+  #pragma unroll
+        for (int hs = 0; hs < 32 / SHG; ++hs) {
+          const int rl = lrow - SHG * hs;
+          if (SHG == 32 || (lrow >> 4) == hs) {
+  #pragma unroll
+            for (int j = 0; j < FN; ++j)
+  #pragma unroll
+              for (int q = 0; q < 4; ++q)
+                lds_store_f4(lds0 + (uint32_t)((wm * SHG + rl) * OPG + (wn * WTN + 32 * j + 8 * q + 4 * lgrp) * 4),
+                             floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                     acc[i][j][4 * q + 3]});
+          }
+          __syncthreads();
+          store_staged_glu<OUT_BF16, DEBUG>(lds0, OPG, WM * SHG, BN / 2, SHG, WTM,
+                                            m0 + 32 * i + SHG * hs, n0, tid, NT, eo);
+          __syncthreads();
+        }
+      }
+      continue;
+    }
     if (p.bias != nullptr || p.act != kActNone) {
       // Fused epilogue: strips are staged as fp32 whatever the output type and
       // read back by a rolled loop that adds the bias, applies the activation
