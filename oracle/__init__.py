@@ -19,7 +19,11 @@ Contents
   round-to-nearest-even encode (directly from fp64, no double rounding).
 * ``check_f32`` / ``check_bf16`` / ``check_exact`` -- the acceptance rules.
 * ``epilogue`` / ``check_epilogue`` -- the fused epilogue act(C + bias) in
-  fp64 and its acceptance rule (``fused_epilogue.py``).
+  fp64 and its acceptance rule (``fused_epilogue.py``); ``swiglu`` /
+  ``check_swiglu`` -- SiLU(gate) * up on a merged gate+up product.
+* ``mx`` -- the microscaled (MXFP8 / MXFP4) product: E4M3, E2M1 and E8M0
+  decoding and the scaled sum in fp64 (``mx.py``); its results are checked
+  with ``check_f32`` / ``check_bf16`` like the bf16 product's.
 
 Parity pins (tests/test_oracle_pins.py) tie every function here to
 something other than itself: exact rational brute force, identity and
@@ -55,3 +59,4 @@ from .fused_epilogue import (  # noqa: F401
     swiglu_bound,
     check_swiglu,
 )
+from . import mx  # noqa: F401,E402

@@ -1,0 +1,121 @@
+"""Microscaled (MX) low-precision product, written for the oracle only.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The TorchInductor page measures MXFP8 and FP4 GEMMs beside bf16 ("TorchInductor
+ganha suporte a GEMMs de alta performance com CuteDSL", the benchmark
+paragraphs on the MXFP8 and NVFP4 regimes) without defining the formats. The
+reading taken here is the OCP Microscaling Formats (MX) v1.0 definition, the
+format family those names refer to:
+
+* an MX block is 32 consecutive elements along K sharing one scale;
+* the scale is E8M0: an unsigned 8-bit exponent e, value 2^(e - 127);
+  e = 255 is NaN;
+* MXFP8 elements are FP8 E4M3 (OCP): sign, 4 exponent bits (bias 7), 3
+  mantissa bits; exponent 0 holds subnormals m/8 * 2^-6; S.1111.111 is NaN;
+  there is no infinity, so the largest finite value is 1.75 * 2^8 = 448;
+* MXFP4 elements are FP4 E2M1: sign, 2 exponent bits (bias 1), 1 mantissa
+  bit, values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives; no NaN or
+  infinity; two elements per byte, the element with the lower K index in the
+  low nibble.
+
+The product of an M x K MX matrix A (row-major elements, scales sA[i][k/32])
+and a K x N MX matrix B given as its N x K transpose (the K-contiguous layout,
+scales sB[j][k/32]) is
+
+    C[i][j] = sum_k (sA[i][k/32] * a[i][k]) * (sB[j][k/32] * b[j][k]),
+
+computed here exactly in fp64 terms (every decoded value and every product
+of two is exact in fp64; only the sum rounds, within K * 2^-53 * D), with
+D[i][j] = sum_k |sA a| * |sB b| for the tolerance rule of the bf16 product
+(the GPU accumulates in fp32 within 1e-5 * D).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 32
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Decode FP8 E4M3 (OCP) bytes to fp64, by the field definition."""
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    normal = s * (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    sub = s * (m / 8.0) * 2.0 ** -6
+    out = np.where(e == 0, sub, normal)
+    return np.where((e == 0xF) & ((b & 0x7) == 0x7), np.nan, out)
+
+
+def e2m1_to_f64(nibbles) -> np.ndarray:
+    """Decode FP4 E2M1 codes (one per entry, 0..15) to fp64."""
+    c = np.asarray(nibbles, dtype=np.uint8).astype(np.int64) & 0xF
+    s = np.where(c >> 3, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = (c & 0x1).astype(np.float64)
+    normal = (1.0 + m / 2.0) * np.exp2(e.astype(np.float64) - 1.0)
+    sub = m / 2.0
+    return s * np.where(e == 0, sub, normal)
+
+
+def unpack_fp4(packed, k: int) -> np.ndarray:
+    """rows x ceil(k/2) bytes -> rows x k E2M1 codes (low nibble first)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty((p.shape[0], 2 * p.shape[1]), np.uint8)
+    out[:, 0::2] = p & 0xF
+    out[:, 1::2] = p >> 4
+    return out[:, :k]
+
+
+def e8m0_to_f64(codes) -> np.ndarray:
+    """Decode E8M0 scale bytes: 2^(e - 127), NaN for 255."""
+    e = np.asarray(codes, dtype=np.uint8).astype(np.float64)
+    return np.where(e == 255, np.nan, np.exp2(e - 127.0))
+
+
+def mx_decode(elems, scales, k: int, fmt: str = "e4m3") -> np.ndarray:
+    """The rows x k fp64 matrix an MX operand stands for: element times the
+    scale of its block of 32 along K. `elems` is rows x k bytes (e4m3) or rows
+    x k/2 packed bytes (e2m1); `scales` is rows x ceil(k/32) E8M0 bytes."""
+    if fmt == "e4m3":
+        v = e4m3_to_f64(np.asarray(elems)[:, :k])
+    elif fmt == "e2m1":
+        v = e2m1_to_f64(unpack_fp4(elems, k))
+    else:
+        raise ValueError(f"unknown MX element format {fmt!r}")
+    sc = e8m0_to_f64(np.asarray(scales))
+    block = np.arange(k) // BLOCK
+    return v * sc[:, block]
+
+
+def mx_gemm(A, sA, Bt, sB, k: int, fmt: str = "e4m3", want_d: bool = True):
+    """(C, D) of the MX product: A is M x K, Bt is B's N x K transpose, with
+    their scales (module docstring). The fp64 matrix product is a library
+    primitive used as one step."""
+    a = mx_decode(A, sA, k, fmt)
+    b = mx_decode(Bt, sB, k, fmt)
+    C = a @ b.T
+    D = np.abs(a) @ np.abs(b).T if want_d else None
+    return C, D
+
+
+def mx_gemm_at(A, sA, Bt, sB, k: int, ii, jj, fmt: str = "e4m3"):
+    """C[ii[t], jj[t]] and D[ii[t], jj[t]] one element at a time: the plain
+    sum over k of the decoded, scaled products, in ascending k."""
+    ii = np.asarray(ii, dtype=np.int64)
+    jj = np.asarray(jj, dtype=np.int64)
+    c = np.empty(ii.size)
+    d = np.empty(ii.size)
+    for t in range(ii.size):
+        a = mx_decode(np.asarray(A)[ii[t]:ii[t] + 1], np.asarray(sA)[ii[t]:ii[t] + 1], k, fmt)[0]
+        b = mx_decode(np.asarray(Bt)[jj[t]:jj[t] + 1], np.asarray(sB)[jj[t]:jj[t] + 1], k, fmt)[0]
+        p = a * b
+        acc = 0.0
+        for v in p:
+            acc += v
+        c[t] = acc
+        d[t] = float(np.sum(np.abs(p)))
+    return c, d
