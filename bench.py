@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GEMM TFLOP/s & % MFMA peak (large); HBM GB/s & % peak (decode shape)"
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA (twice the bf16 rate)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 MIN_ROTATION_BYTES = 600 << 20  # > 2x the 256 MB last-level cache
 
@@ -44,7 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mlp_gate_up_shard")
     ap.add_argument("--secondary", default="qkv_shard,square4096,decode,decode_colB,gemm256,"
-                    "mlp_gate_up_shard:bias+silu,decode:bias+silu",
+                    "mlp_gate_up_shard:bias+silu,decode:bias+silu,mx_mlp_gate_up_shard,mx_square4096,"
+                    "mx_decode",
                     help="comma-separated extra workloads reported on the same line; NAME:EPI adds a "
                     "fused epilogue, e.g. decode:bias+silu ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -211,6 +213,65 @@ class Bench:
         return ops, res
 
 
+def time_mx_workload(b, w, steps, warmup):
+    """Time the MXFP8 product on an MX workload (operands rotated like the
+    bf16 ones; elements, scales and C resident in HBM)."""
+    torch, synth, g = b.torch, b.synth, b.g
+    t0 = time.time()
+    ops = synth.mx_operands(w)
+    A = torch.from_numpy(ops.A).cuda()
+    Bt = torch.from_numpy(ops.Bt).cuda()
+    sA = torch.from_numpy(ops.sA).cuda()
+    sB = torch.from_numpy(ops.sB).cuda()
+    out = w.outs[0]
+    odt = torch.float32 if out == "f32" else torch.bfloat16
+    copies = max(1, min(8, -(-MIN_ROTATION_BYTES // w.algorithmic_bytes(out))))
+    sets = [(A, Bt, sA, sB) if i == 0 else (A.clone(), Bt.clone(), sA.clone(), sB.clone())
+            for i in range(copies)]
+    Cs = [torch.empty((w.M, w.N), dtype=odt, device="cuda") for _ in range(copies)]
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: {w.M}x{w.N}x{w.K} MXFP8 out={out} copies={copies} "
+        f"(operands ready in {time.time() - t0:.1f}s)")
+    for i in range(warmup):
+        a, bt, sa, sb = sets[i % copies]
+        g.mx(a, bt, Cs[i % copies], sa, sb)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        a, bt, sa, sb = sets[i % copies]
+        ev[i][0].record()
+        g.mx(a, bt, Cs[i % copies], sa, sb)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([x.elapsed_time(y) for x, y in ev])
+    plan = b.tg.tile_gemm_plan_mx(w.M, w.N, w.K, 256)
+    res = {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "format": "MXFP8 (E4M3, E8M0 / 32)",
+           "out": out, "wall_ms_per_step": 1e3 * wall / steps,
+           "kernel_ms_mean": float(per.mean()), "kernel_ms_median": float(np.median(per)),
+           "kernel_ms_min": float(per.min()), "kernel_ms_max": float(per.max()),
+           "flop": w.flops, "bytes": w.algorithmic_bytes(out),
+           "plan": {"variant": "mx", "bm": plan.bm, "bn": plan.bn, "grid": int(plan.grid)}}
+    mean_s = res["kernel_ms_mean"] * 1e-3
+    res["tflops"] = w.flops / mean_s / 1e12
+    res["gbs"] = w.algorithmic_bytes(out) / mean_s / 1e9
+    hbm = w.name.startswith("mx_decode")
+    res["roofline"] = ({"bound": "hbm", "achieved": round(res["gbs"], 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(res["gbs"] / PEAK_HBM_GBS, 4),
+                        "traffic": measured_traffic(w.name)} if hbm else
+                       {"bound": "mfma", "achieved": round(res["tflops"], 1),
+                        "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(res["tflops"] / PEAK_FP8_TFLOPS, 4),
+                        "traffic": measured_traffic(w.name)})
+    log(f"[bench] {w.name}: mean {res['kernel_ms_mean'] * 1e3:.1f} us -> {res['tflops']:.1f} "
+        f"TFLOP/s ({100 * res['tflops'] / PEAK_FP8_TFLOPS:.1f}% of fp8 MFMA), {res['gbs']:.0f} GB/s")
+    del sets, Cs
+    torch.cuda.empty_cache()
+    return res
+
+
 def measured_traffic(workload):
     """HBM-side bytes per launch recorded by rocprofv3 counter runs
     (profiles/traffic.json), or None when the kernel sources have changed
@@ -312,6 +373,9 @@ def main():
     ops, res = b.time_workload(head, head_out, args.steps, args.warmup)
     secondary = []
     for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
+        if name in synth.MX_WORKLOADS:
+            secondary.append(time_mx_workload(b, synth.MX_WORKLOADS[name], args.steps, args.warmup))
+            continue
         base, _, epi = name.partition(":")
         w = synth.WORKLOADS[base]
         _, r = b.time_workload(w, w.outs[0], args.steps, args.warmup, epi or None)

@@ -154,6 +154,39 @@ tile_gemm_status_t tile_gemm_run_epilogue(tile_gemm_t h, const void* A, const vo
                                           tile_gemm_dtype_t dtype, const float* bias,
                                           tile_gemm_act_t act, void* stream);
 
+/*
+ * Microscaled FP8 product (MXFP8), the low-precision GEMM the TorchInductor
+ * page measures beside bf16 ("TorchInductor ganha suporte a GEMMs de alta
+ * performance com CuteDSL", its MXFP8 benchmark paragraph). The format is
+ * read as OCP Microscaling (MX) v1.0: elements are FP8 E4M3 bytes, and every
+ * 32 consecutive elements of a row along K share one E8M0 scale byte (value
+ * 2^(e - 127); 255 is NaN).
+ *
+ *   C[i][j] = sum_k (sa[i][k/32] * a[i][k]) * (sb[j][k/32] * b[j][k])
+ *
+ * A is M x K bytes, row-major (strides a_m >= K, a_k = 1, in bytes). B is
+ * given as its N x K transpose, K-contiguous (b_k = 1, b_n >= K, in bytes):
+ * the layout in which weight matrices are usually stored. a_scale is M rows
+ * and b_scale N rows of `scale_stride` bytes (a multiple of 4, >= K/32), the
+ * scale of element k of a row at byte k/32. K must be a multiple of 64
+ * (TILE_GEMM_ERR_BAD_SHAPE otherwise). C, dtype, bias and act (not
+ * TILE_GEMM_ACT_SWIGLU) are as for tile_gemm_run_epilogue; accumulation is
+ * fp32 in ascending K, one owner per output tile, each element written once.
+ * A, B 16-byte aligned with 16-byte leading dimensions; scales 4-byte aligned.
+ * All inputs are borrowed read-only until the stream reaches the work; C may
+ * overlap none of them. Enqueue-only, allocates nothing.
+ */
+typedef enum {
+  TILE_GEMM_MX_E4M3 = 0  /* MXFP8: E4M3 elements, E8M0 scales per 32 */
+} tile_gemm_mx_format_t;
+
+tile_gemm_status_t tile_gemm_run_mx(tile_gemm_t h, const void* A, const void* B, void* C,
+                                    int64_t M, int64_t N, int64_t K,
+                                    const tile_gemm_strides_t* strides, const void* a_scale,
+                                    const void* b_scale, int64_t scale_stride,
+                                    tile_gemm_mx_format_t fmt, tile_gemm_dtype_t dtype,
+                                    const float* bias, tile_gemm_act_t act, void* stream);
+
 /* Release a handle (host memory only). NULL is accepted and returns OK. */
 tile_gemm_status_t tile_gemm_destroy(tile_gemm_t h);
 
@@ -191,11 +224,20 @@ tile_gemm_status_t tile_gemm_check_epilogue(const void* C, int64_t M, int64_t N,
                                             tile_gemm_dtype_t dtype, const float* bias,
                                             tile_gemm_act_t act);
 
+/* The checks tile_gemm_run_mx performs before any launch, with the same results. */
+tile_gemm_status_t tile_gemm_check_mx(const void* A, const void* B, const void* C, int64_t M,
+                                      int64_t N, int64_t K, const tile_gemm_strides_t* strides,
+                                      const void* a_scale, const void* b_scale,
+                                      int64_t scale_stride, tile_gemm_mx_format_t fmt,
+                                      tile_gemm_dtype_t dtype, const float* bias,
+                                      tile_gemm_act_t act);
+
 /* Kernel variants the planner chooses between. */
 typedef enum {
   TILE_GEMM_VARIANT_NONE = 0,   /* M == 0 or N == 0: nothing to launch */
   TILE_GEMM_VARIANT_TILE = 1,   /* LDS-staged MFMA tile kernel */
-  TILE_GEMM_VARIANT_SKINNY = 2  /* HBM-streaming kernel, chosen for M <= 16 */
+  TILE_GEMM_VARIANT_SKINNY = 2, /* HBM-streaming kernel, chosen for M <= 16 */
+  TILE_GEMM_VARIANT_MX = 3      /* MXFP8 tile kernel (tile_gemm_run_mx) */
 } tile_gemm_variant_t;
 
 /*
@@ -228,6 +270,10 @@ typedef struct {
 /* b_col_major: 0 for row-major B, 1 for column-major B. cu_count > 0. */
 tile_gemm_status_t tile_gemm_plan(int64_t M, int64_t N, int64_t K, int b_col_major,
                                   int cu_count, tile_gemm_plan_t* out);
+
+/* The plan of tile_gemm_run_mx for a shape (variant TILE_GEMM_VARIANT_MX). */
+tile_gemm_status_t tile_gemm_plan_mx(int64_t M, int64_t N, int64_t K, int cu_count,
+                                     tile_gemm_plan_t* out);
 
 /*
  * Tile number `wg` (0 <= wg < plan->tiles) under `plan`: rows [m0, m0 + rows)
@@ -277,6 +323,19 @@ tile_gemm_status_t tile_gemm_run_debug(tile_gemm_t h, const void* A, const void*
                                        tile_gemm_dtype_t dtype, void* stream,
                                        uint32_t* counts, int flags, const float* bias,
                                        tile_gemm_act_t act);
+
+/*
+ * As tile_gemm_run_mx, with the instrumentation of tile_gemm_run_debug
+ * (TILE_GEMM_DEBUG_FORCE_TILE(c) forces MX configuration c).
+ */
+tile_gemm_status_t tile_gemm_run_mx_debug(tile_gemm_t h, const void* A, const void* B, void* C,
+                                          int64_t M, int64_t N, int64_t K,
+                                          const tile_gemm_strides_t* strides,
+                                          const void* a_scale, const void* b_scale,
+                                          int64_t scale_stride, tile_gemm_mx_format_t fmt,
+                                          tile_gemm_dtype_t dtype, const float* bias,
+                                          tile_gemm_act_t act, void* stream, uint32_t* counts,
+                                          int flags);
 
 #ifdef __cplusplus
 }

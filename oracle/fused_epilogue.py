@@ -86,21 +86,24 @@ def epilogue(C, bias=None, act: str = "none") -> np.ndarray:
     return act_f64(x, act)
 
 
-def epilogue_bound(C, D, bias=None, act: str = "none", rel: float = 1e-5) -> np.ndarray:
-    """The per-element tolerance t of the acceptance rule above."""
+def epilogue_bound(C, D, bias=None, act: str = "none", rel: float = 1e-5,
+                   tau=None) -> np.ndarray:
+    """The per-element tolerance t of the acceptance rule above. `tau`, when
+    given, replaces rel * D as the product's own bound (a product computed
+    with another arithmetic, such as the MX one, brings its own)."""
     C = np.asarray(C, dtype=np.float64)
     x = C if bias is None else C + np.asarray(bias, dtype=np.float64)[None, :]
     y = act_f64(x, act)
-    tau = rel * np.asarray(D, dtype=np.float64)
+    tau = rel * np.asarray(D, dtype=np.float64) if tau is None else np.asarray(tau, dtype=np.float64)
     return LIPSCHITZ[act] * (tau + 2.0 ** -22 * np.abs(x)) + 2.0 ** -20 * np.abs(y) + 2.0 ** -126
 
 
 def check_epilogue(g, C, D, bias=None, act: str = "none", out_bf16: bool = False,
-                   rel: float = 1e-5) -> CheckReport:
+                   rel: float = 1e-5, tau=None) -> CheckReport:
     """Check a GPU result g (fp32 values, or bf16 bit patterns when out_bf16)
     against act(C + bias) within epilogue_bound."""
     y = epilogue(C, bias, act)
-    t = epilogue_bound(C, D, bias, act, rel)
+    t = epilogue_bound(C, D, bias, act, rel, tau)
     if out_bf16:
         gb = np.asarray(g)
         lo = bf16_to_f64(rne_bf16(y - t))

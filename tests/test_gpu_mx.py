@@ -1,0 +1,198 @@
+"""GPU parity of the MXFP8 product (tile_gemm_run_mx) against the oracle's
+microscaled product (oracle/mx.py), through the C ABI.
+
+Acceptance: fp32 output within the oracle's per-element MX bound T of the
+fp64 sum (T follows the instruction's grouped fixed-point summation, see
+oracle/mx.py), bf16 output inside the RNE bracket of that interval,
+integer-valued inputs exactly equal. Outputs start as NaN
+(padding columns included) and a write counter checks that every element is
+written exactly once.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import tile_partitioned_dense_amd as tg
+from tile_partitioned_dense_amd import synth
+
+from gpu_helpers import host_out
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    with tg.TileGemm(0) as gg:
+        yield gg
+
+
+def mx_config_table():
+    import os
+    import re
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "tile_partitioned_dense_amd", "csrc", "plan.hpp")).read()
+    body = re.search(r"kMxConfigs\[kNumMxConfigs\]\s*=\s*\{(.*?)\n\};", src, re.S).group(1)
+    rows = re.findall(r"^\s*\{(\d+),\s*(\d+),", body, re.M)
+    return [tuple(int(v) for v in r) for r in rows]
+
+
+class MxCase:
+    def __init__(self, M, N, K, dist="normal", seed=0, pad=16, b_scale=1.0):
+        self.M, self.N, self.K = M, N, K
+        lk = K + pad                                   # padded rows (a multiple of 16)
+        A, sA = synth.draw_mx(M, lk, dist, 2 * seed + 1)
+        Bt, sB = synth.draw_mx(N, lk, dist, 2 * seed + 2, b_scale)
+        ls = synth.mx_scale_stride(K)
+        self.A, self.Bt = A[:, :K], Bt[:, :K]
+        self.sA, self.sB = sA[:, :ls], sB[:, :ls]
+        dA = torch.from_numpy(A).cuda()
+        dB = torch.from_numpy(Bt).cuda()
+        self.A_dev, self.Bt_dev = dA[:, :K], dB[:, :K]
+        self.sA_dev = torch.from_numpy(np.ascontiguousarray(self.sA)).cuda()
+        self.sB_dev = torch.from_numpy(np.ascontiguousarray(self.sB)).cuda()
+        self._ref = None
+
+    def ref(self):
+        if self._ref is None:
+            self._ref = oracle.mx.mx_gemm(self.A, self.sA, self.Bt, self.sB, self.K)
+        return self._ref
+
+    def bound(self):
+        if getattr(self, "_bound", None) is None:
+            self._bound = oracle.mx.mx_bound(self.A, self.sA, self.Bt, self.sB, self.K)
+        return self._bound
+
+    def out(self, dtype, pad=8):
+        ld = (self.N + 7) // 8 * 8 + pad                # 16-byte rows for both output types
+        store = torch.full((self.M, ld), float("nan"), dtype=dtype, device="cuda")
+        return store, store[:, : self.N]
+
+
+def _check(out, C, T, bf16, integer=False):
+    if integer:
+        return oracle.check_exact(out, C, bf16)
+    return oracle.mx.check_mx(out, C, T, out_bf16=bf16)
+
+
+def _run_and_check(g, case, flags=0, integer=False, label=""):
+    C, _ = case.ref()
+    D = case.bound()
+    for dt in (torch.float32, torch.bfloat16):
+        store, out = case.out(dt)
+        cnt = torch.zeros((case.M, case.N), dtype=torch.int32, device="cuda")
+        g.mx(case.A_dev, case.Bt_dev, out, case.sA_dev, case.sB_dev, counts=cnt,
+             flags=flags | tg.DEBUG_COUNT_WRITES)
+        torch.cuda.synchronize()
+        rep = _check(host_out(out), C, D, dt == torch.bfloat16, integer)
+        assert rep.ok, f"{label} {dt}: {rep}"
+        assert bool((cnt == 1).all()), f"{label} {dt}: an element not written exactly once"
+        assert torch.isnan(store[:, case.N:].float()).all(), f"{label}: store outside C"
+
+
+@pytest.mark.parametrize("cfg", range(tg.N_MX_CONFIGS))
+@pytest.mark.parametrize("K", [64, 192, 256])
+def test_mx_configs(g, cfg, K):
+    bm, bn = mx_config_table()[cfg]
+    M, N = 2 * bm + 37, 2 * bn + 19
+    print(f"[mx cfg {cfg} {M}x{N}x{K}]", flush=True)
+    _run_and_check(g, MxCase(M, N, K, seed=cfg * 10 + K), tg.DEBUG_FORCE_TILE(cfg),
+                   label=f"cfg {cfg}")
+
+
+@pytest.mark.parametrize("cfg", range(tg.N_MX_CONFIGS))
+def test_mx_configs_integer_exact(g, cfg):
+    bm, bn = mx_config_table()[cfg]
+    M, N, K = bm + 5, bn + 3, 320
+    print(f"[mx int cfg {cfg} {M}x{N}x{K}]", flush=True)
+    _run_and_check(g, MxCase(M, N, K, dist="int3", seed=50 + cfg), tg.DEBUG_FORCE_TILE(cfg),
+                   integer=True, label=f"int cfg {cfg}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (17, 33, 128), (300, 520, 576), (16, 4096, 1024),
+                                   (1000, 1000, 1024), (130, 130, 0)])
+def test_mx_planner_shapes(g, M, N, K):
+    print(f"[mx planner {M}x{N}x{K}]", flush=True)
+    case = MxCase(M, N, K, seed=M + N + K)
+    _run_and_check(g, case, label=f"{M}x{N}x{K}")
+
+
+def test_mx_several_tiles_per_workgroup(g):
+    case = MxCase(600, 700, 256, seed=61)
+    print("[mx forced grid]", flush=True)
+    for cfg, grid in ((0, 3), (1, 5)):
+        _run_and_check(g, case, tg.DEBUG_FORCE_TILE(cfg) | tg.DEBUG_FORCE_GRID(grid),
+                       label=f"cfg {cfg} grid {grid}")
+
+
+def test_mx_fused_epilogue(g):
+    case = MxCase(300, 264, 512, seed=62, b_scale=512 ** -0.5)
+    C, D = case.ref()
+    b = synth.draw_bias(case.N, 900)
+    bd = torch.from_numpy(b).cuda()
+    for act in (tg.Act.RELU, tg.Act.SILU, tg.Act.TANH):
+        for dt in (torch.float32, torch.bfloat16):
+            _, out = case.out(dt)
+            g.mx(case.A_dev, case.Bt_dev, out, case.sA_dev, case.sB_dev, bias=bd, act=act)
+            torch.cuda.synchronize()
+            rep = oracle.check_epilogue(host_out(out), C, D, b, act.name.lower(),
+                                        out_bf16=dt == torch.bfloat16, tau=case.bound())
+            assert rep.ok, f"{act.name} {dt}: {rep}"
+
+
+def test_mx_deterministic_and_bf16_is_rne_of_fp32(g):
+    case = MxCase(1024, 1024, 2048, seed=63)
+    outs = []
+    for _ in range(5):
+        _, out = case.out(torch.float32)
+        g.mx(case.A_dev, case.Bt_dev, out, case.sA_dev, case.sB_dev)
+        torch.cuda.synchronize()
+        outs.append(out.clone())
+    assert all(torch.equal(outs[0].view(torch.int32), o.view(torch.int32)) for o in outs[1:])
+    _, o16 = case.out(torch.bfloat16)
+    g.mx(case.A_dev, case.Bt_dev, o16, case.sA_dev, case.sB_dev)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_out(o16), oracle.rne_bf16(host_out(outs[0]).astype(np.float64)))
+
+
+def test_mx_rejects_bad_arguments(g):
+    case = MxCase(64, 64, 128, seed=64)
+    _, out = case.out(torch.float32)
+    A96 = case.A_dev[:, :96]
+    B96 = case.Bt_dev[:, :96]
+    st = tg.tile_gemm_run_mx(g.handle, A96, B96, out, case.sA_dev, case.sB_dev, check=False)
+    assert st == tg.Status.ERR_BAD_SHAPE                 # K not a multiple of 64
+    st = tg.tile_gemm_run_mx(g.handle, case.A_dev, case.Bt_dev, out, case.sA_dev, case.sB_dev,
+                             act=tg.Act.SWIGLU, check=False)
+    assert st == tg.Status.ERR_EPILOGUE
+    assert torch.isnan(out).all()
+
+
+@pytest.mark.parametrize("name", sorted(synth.MX_WORKLOADS))
+def test_mx_workload_sampled(g, name):
+    """Full size, in the launch configuration the benchmark times: sampled
+    elements against the oracle's one-element sums."""
+    w = synth.MX_WORKLOADS[name]
+    ops = synth.mx_operands(w)
+    print(f"[mx workload {name} {w.M}x{w.N}x{w.K}]", flush=True)
+    A, Bt = torch.from_numpy(ops.A).cuda(), torch.from_numpy(ops.Bt).cuda()
+    sA, sB = torch.from_numpy(ops.sA).cuda(), torch.from_numpy(ops.sB).cuda()
+    rng = np.random.default_rng(13)
+    ii = np.concatenate([rng.integers(0, w.M, 200), [0, w.M - 1, 0, w.M - 1]])
+    jj = np.concatenate([rng.integers(0, w.N, 200), [0, 0, w.N - 1, w.N - 1]])
+    c, d = oracle.mx.mx_gemm_at(ops.A, ops.sA, ops.Bt, ops.sB, w.K, ii, jj)
+    t = oracle.mx.mx_bound_at(ops.A, ops.sA, ops.Bt, ops.sB, w.K, ii, jj)
+    for dt in (torch.float32, torch.bfloat16):
+        C = torch.full((w.M, w.N), float("nan"), dtype=dt, device="cuda")
+        g.mx(A, Bt, C, sA, sB)
+        torch.cuda.synchronize()
+        out = host_out(C)
+        assert not np.isnan(out.astype(np.float32) if dt == torch.float32 else
+                            oracle.bf16_to_f64(out)).any(), "an element was not written"
+        rep = oracle.mx.check_mx(out[ii, jj], c, t, out_bf16=dt == torch.bfloat16)
+        assert rep.ok, f"{name} {dt}: {rep}"
+        del C

@@ -180,3 +180,41 @@ def test_check_swiglu_widths():
     # the bias (N values) may sit right after C's M x N/2 fp32 elements
     assert chk_epi(act=Act.SWIGLU, bias=C0 + 4 * (63 * 64 + 32)) == Status.OK
     assert chk_epi(act=Act.SWIGLU, bias=C0 + 4 * (63 * 64 + 32) - 16) == Status.ERR_ALIAS
+
+
+# --- MX argument checks
+SA0, SB0 = 0x500000, 0x600000
+
+
+def chk_mx(A=A0, B=B0, C=C0, M=64, N=64, K=128, s=(128, 1, 1, 128, 64, 1), sa=SA0, sb=SB0,
+           ls=4, dtype=Dtype.BF16_TO_F32, bias=None, act=0, fmt=0):
+    return tg.tile_gemm_check_mx(A, B, C, M, N, K, s, sa, sb, ls, dtype, bias, act, fmt)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(), Status.OK),
+    (dict(K=0, A=0, B=0, sa=0, sb=0), Status.OK),
+    (dict(M=0), Status.OK),
+    (dict(K=96, s=(128, 1, 1, 128, 64, 1)), Status.ERR_BAD_SHAPE),      # K % 64
+    (dict(fmt=1), Status.ERR_DTYPE),
+    (dict(dtype=5), Status.ERR_DTYPE),
+    (dict(sa=0), Status.ERR_NULL_ARG),
+    (dict(s=(128, 1, 128, 1, 64, 1)), Status.ERR_BAD_STRIDE),           # B not K-contiguous
+    (dict(s=(64, 1, 1, 128, 64, 1)), Status.ERR_BAD_STRIDE),            # a_m < K
+    (dict(ls=2), Status.ERR_BAD_STRIDE),                                # ls not a multiple of 4
+    (dict(ls=0), Status.ERR_BAD_STRIDE),                                # ls < K/32
+    (dict(A=A0 + 8), Status.ERR_MISALIGNED),
+    (dict(sa=SA0 + 2), Status.ERR_MISALIGNED),
+    (dict(s=(136, 1, 1, 128, 64, 1)), Status.ERR_MISALIGNED),           # a_m not /16
+    (dict(C=SA0 + 64), Status.ERR_ALIAS),                               # C over a_scale
+    (dict(act=5), Status.ERR_EPILOGUE),                                 # no SiLU(gate)*up
+    (dict(bias=0x700004, act=1), Status.ERR_MISALIGNED),
+])
+def test_check_mx(kw, want):
+    assert chk_mx(**kw) == want, tg.last_error_detail()
+
+
+def test_mx_plan():
+    p = tg.tile_gemm_plan_mx(8192, 7168, 8192)
+    assert p.variant == tg.VARIANT_MX and p.bm == 256 and p.bn == 256 and p.bk == 64
+    assert p.tiles == 32 * 28 and p.grid == 224

@@ -276,3 +276,41 @@ def test_the_unmodified_product_passes_through_the_same_driver():
     good = _gemm_with()
     for pin in PINS:
         pin(good)
+
+
+# ------------------------------------------------------------- tolerance
+
+def test_mx_bound_closed_form():
+    """One run of 8 with products 1, 2^-14 and zeros: T = 7 * 2^-13 plus the
+    fp32 term; integer-valued products keep every bit (T far below 1)."""
+    A = np.zeros((1, 64), np.uint8)
+    Bt = np.zeros((1, 64), np.uint8)
+    A[0, 0] = 0x38                                     # 1
+    Bt[0, 0] = 0x38
+    one = np.full((1, 2), 127, np.uint8)
+    T = mx.mx_bound(A, one, Bt, one, 64)
+    assert T[0, 0] == 7 * 2.0 ** -13 + 10 * 2.0 ** -24 * 1.0
+    # two runs: maxima 448 * 1 (E = 8) and 1 (E = 0)
+    A[0, 8] = 0x7e
+    Bt[0, 8] = 0x38
+    T = mx.mx_bound(A, one, Bt, one, 64)
+    assert T[0, 0] == 7 * (2.0 ** -13 + 2.0 ** -5) + 10 * 2.0 ** -24 * 449.0
+
+
+def test_check_mx_accepts_within_and_rejects_beyond():
+    rng = np.random.default_rng(9)
+    M, N, K = 5, 6, 128
+    A, sA = _rand_mx(rng, M, K, "e4m3")
+    Bt, sB = _rand_mx(rng, N, K, "e4m3")
+    C, D = mx.mx_gemm(A, sA, Bt, sB, K)
+    T = mx.mx_bound(A, sA, Bt, sB, K)
+    assert np.all(T > 0)
+    assert mx.check_mx(C.astype(np.float32), C, T).ok
+    off = C.copy()
+    off[1, 2] += 2 * T[1, 2]
+    rep = mx.check_mx(off, C, T)
+    assert not rep.ok and rep.first_bad == (1, 2)
+    from oracle import rne_bf16
+    assert mx.check_mx(rne_bf16(C), C, T, out_bf16=True).ok
+    t = mx.mx_bound_at(A, sA, Bt, sB, K, [1, 4], [2, 0])
+    assert np.array_equal(t, T[[1, 4], [2, 0]])

@@ -63,9 +63,11 @@ DEBUG_ONE_TILE_PER_WG = 0x7F << 24
 
 
 N_TILE_CONFIGS = 14
+N_MX_CONFIGS = 2
+MX_E4M3 = 0
 N_SKINNY_CONFIGS = 6
 
-VARIANT_NONE, VARIANT_TILE, VARIANT_SKINNY = 0, 1, 2
+VARIANT_NONE, VARIANT_TILE, VARIANT_SKINNY, VARIANT_MX = 0, 1, 2, 3
 
 
 class Strides(ctypes.Structure):
@@ -133,6 +135,17 @@ def load_library():
     lib.tile_gemm_check_args.restype = i32
     lib.tile_gemm_plan.argtypes = [i64, i64, i64, i32, i32, P(Plan)]
     lib.tile_gemm_plan.restype = i32
+    lib.tile_gemm_plan_mx.argtypes = [i64, i64, i64, i32, P(Plan)]
+    lib.tile_gemm_plan_mx.restype = i32
+    lib.tile_gemm_run_mx.argtypes = [vp, vp, vp, vp, i64, i64, i64, P(Strides), vp, vp, i64, i32,
+                                     i32, vp, i32, vp]
+    lib.tile_gemm_run_mx.restype = i32
+    lib.tile_gemm_run_mx_debug.argtypes = [vp, vp, vp, vp, i64, i64, i64, P(Strides), vp, vp, i64,
+                                           i32, i32, vp, i32, vp, vp, i32]
+    lib.tile_gemm_run_mx_debug.restype = i32
+    lib.tile_gemm_check_mx.argtypes = [vp, vp, vp, i64, i64, i64, P(Strides), vp, vp, i64, i32, i32,
+                                       vp, i32]
+    lib.tile_gemm_check_mx.restype = i32
     lib.tile_gemm_tile_of.argtypes = [P(Plan), i64, i64, i64, P(i64), P(i64), P(i64), P(i64)]
     lib.tile_gemm_tile_of.restype = i32
     _lib = lib
@@ -259,6 +272,64 @@ def tile_gemm_run_debug(h, A, B, C, counts=None, flags=0, M=None, N=None, K=None
     return Status(st)
 
 
+def _mx_operands(A, Bt, C, a_scale, b_scale):
+    """Pointers, shape and strides of an MX call from torch tensors: A (M x K)
+    and Bt (N x K) uint8 E4M3 codes, scales uint8 (M x ls) and (N x ls)."""
+    import torch
+    for name, t in (("A", A), ("Bt", Bt), ("a_scale", a_scale), ("b_scale", b_scale)):
+        if t.dtype != torch.uint8 or t.dim() != 2:
+            raise TypeError(f"{name} must be a 2-D uint8 tensor")
+    M, K = A.shape
+    N, K2 = Bt.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shapes do not chain: A{tuple(A.shape)} Bt{tuple(Bt.shape)} C{tuple(C.shape)}")
+    if a_scale.shape[0] != M or b_scale.shape[0] != N or a_scale.stride(1) != 1 \
+            or b_scale.stride(1) != 1 or a_scale.stride(0) != b_scale.stride(0):
+        raise ValueError("scales: M and N rows with one common row stride and unit column stride")
+    if C.dtype == torch.float32:
+        dtype = Dtype.BF16_TO_F32
+    elif C.dtype == torch.bfloat16:
+        dtype = Dtype.BF16_TO_BF16
+    else:
+        raise TypeError("C must be float32 or bfloat16")
+    s = Strides(A.stride(0), A.stride(1), Bt.stride(1), Bt.stride(0), C.stride(0), C.stride(1))
+    return M, N, K, s, a_scale.stride(0), int(dtype)
+
+
+def tile_gemm_run_mx(h, A, Bt, C, a_scale, b_scale, bias=None, act=Act.NONE, stream=None,
+                     counts=None, flags=0, check: bool = True):
+    """Enqueue the MXFP8 product C := act((sa * A) . (sb * Bt)^T + bias) (torch tensors)."""
+    M, N, K, s, ls, dt = _mx_operands(A, Bt, C, a_scale, b_scale)
+    bp = bias.data_ptr() if _is_tensor(bias) else bias
+    lib = load_library()
+    args = (h, A.data_ptr(), Bt.data_ptr(), C.data_ptr(), M, N, K, ctypes.byref(s),
+            a_scale.data_ptr(), b_scale.data_ptr(), ls, MX_E4M3, dt, bp, int(act),
+            _stream_ptr(stream, C))
+    if flags or counts is not None:
+        cnt = counts.data_ptr() if _is_tensor(counts) else counts
+        st = lib.tile_gemm_run_mx_debug(*args, cnt, int(flags))
+    else:
+        st = lib.tile_gemm_run_mx(*args)
+    if check:
+        _raise_if(st)
+    return Status(st)
+
+
+def tile_gemm_check_mx(A, B, C, M, N, K, strides, a_scale, b_scale, scale_stride, dtype,
+                       bias=None, act=Act.NONE, fmt=MX_E4M3) -> Status:
+    """Host-only checks of tile_gemm_run_mx's arguments (pointers are integers)."""
+    s = strides if isinstance(strides, Strides) else Strides(*strides)
+    return Status(load_library().tile_gemm_check_mx(A, B, C, int(M), int(N), int(K), ctypes.byref(s),
+                                                    a_scale, b_scale, int(scale_stride), int(fmt),
+                                                    int(dtype), bias, int(act)))
+
+
+def tile_gemm_plan_mx(M, N, K, cu_count=256) -> Plan:
+    p = Plan()
+    _raise_if(load_library().tile_gemm_plan_mx(int(M), int(N), int(K), int(cu_count), ctypes.byref(p)))
+    return p
+
+
 def tile_gemm_check_args(A, B, C, M, N, K, strides, dtype) -> Status:
     """Host-only argument checks (pointers are plain integers here)."""
     s = strides if isinstance(strides, Strides) else Strides(*strides)
@@ -303,6 +374,13 @@ class TileGemm:
         return tile_gemm_run_debug(self.handle, A, B, C, counts=counts, flags=flags,
                                    stream=stream, bias=bias,
                                    act=Act.NONE if act is None else act)
+
+    def mx(self, A, Bt, C, a_scale, b_scale, bias=None, act=None, stream=None, counts=None,
+           flags=0):
+        """MXFP8 product (tile_gemm_run_mx) into C."""
+        return tile_gemm_run_mx(self.handle, A, Bt, C, a_scale, b_scale, bias=bias,
+                                act=Act.NONE if act is None else act, stream=stream,
+                                counts=counts, flags=flags)
 
     def close(self):
         if self.handle is not None:

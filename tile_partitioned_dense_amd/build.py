@@ -27,6 +27,7 @@ ARCH = "gfx950"
 
 N_TILE_CONFIGS = 14
 N_SKINNY_CONFIGS = 6
+N_MX_CONFIGS = 2
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -45,6 +46,9 @@ def _units():
     for i in range(N_SKINNY_CONFIGS):
         units.append((f"kernels_skinny_{i}", os.path.join(CSRC, "kernels_skinny.hip"),
                       [f"-DTG_SKINNY_CONFIG={i}"]))
+    for i in range(N_MX_CONFIGS):
+        units.append((f"kernels_mx_{i}", os.path.join(CSRC, "kernels_mx.hip"),
+                      [f"-DTG_MX_CONFIG={i}"]))
     return units
 
 

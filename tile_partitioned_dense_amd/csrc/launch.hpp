@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include "ksplit_kernel.hpp"
+#include "mx_kernel.hpp"
 #include "skinny_kernel.hpp"
 #include "tile_kernel.hpp"
 
@@ -22,6 +23,9 @@ hipError_t launch_tile(const TileArgs& a, int64_t grid, const Variant& v, hipStr
 
 template <int CFG>
 hipError_t launch_skinny(const SkinnyArgs& a, int64_t grid, const Variant& v, hipStream_t stream);
+
+template <int CFG>
+hipError_t launch_mx(const MxArgs& a, int64_t grid, const Variant& v, hipStream_t stream);
 
 // Launch through hipLaunchKernel so the launch status comes back directly
 // rather than through the thread's sticky last-error slot.

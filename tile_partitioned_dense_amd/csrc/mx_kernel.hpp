@@ -1,0 +1,293 @@
+// mx_kernel.hpp -- microscaled FP8 (MXFP8) tile kernel for gfx950.
+//
+// The low-precision GEMMs the TorchInductor page measures beside bf16
+// ("TorchInductor ganha suporte a GEMMs de alta performance com CuteDSL", its
+// MXFP8 benchmark paragraph), read as the OCP MX format: E4M3 elements, one
+// E8M0 scale per 32 consecutive elements along K. A is M x K (row-major,
+// bytes), B is given as its N x K transpose (K-contiguous), scales are
+// row-major [rows][ls] bytes with ls >= K / 32 a multiple of 4.
+//
+// Partition and ownership are the tile kernel's: every BM x BN output tile is
+// owned by one workgroup (a persistent grid walks tiles wg, wg + grid, ...),
+// which reads A and B as shared immutable views and writes its tile once.
+// A slab is 64 K values = 64 bytes per row, the same LDS row as the bf16
+// kernel's 32-element slab, so staging (direct buffer -> LDS loads through
+// range-checked resources), the swizzled layout and the operand reads are
+// those of the tile kernel. Each 64-K slab is one v_mfma_scale_f32_32x32x64
+// per 32 x 32 block: lane l holds row (l % 32), bytes 0-15 from the slab's
+// first 32-element block and bytes 16-31 from its second (LDS chunks l / 32
+// and 2 + l / 32), and the scale of block b of row r sits in lane r + 32 b
+// (measured on the device with a one-wave probe). Each lane therefore needs
+// the scale of its row for block 2 s + l / 32: one dword of the scale row
+// covers two slabs; it is shifted by 8 (l / 32) bits per lane and the
+// instruction's byte select picks byte 0 or 2 by slab parity.
+//
+// K advances in ascending order (fp32 accumulation, no split-K), so results
+// are bit-identical run to run.
+#pragma once
+
+#include "tile_kernel.hpp"
+
+namespace tg {
+
+struct MxArgs {
+  const uint8_t* A;   // M x K E4M3, lda bytes between rows
+  const uint8_t* B;   // N x K E4M3 (B transposed), ldb bytes between rows
+  const uint8_t* sA;  // M x ls E8M0
+  const uint8_t* sB;  // N x ls E8M0
+  void* C;
+  int32_t M, N, K;
+  int64_t lda, ldb, ldc;
+  int32_t ls;  // scale row stride in bytes (multiple of 4)
+  TileMap map;
+  uint32_t* counts;  // debug instrumentation only
+  int32_t flags;
+  const float* bias;
+  int32_t act;
+};
+
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+// One 32 x 32 x 64 scaled step of a C block held transposed (as mma()): the B
+// fragment is the instruction's first operand. OPSEL picks the scale byte.
+template <int OPSEL>
+__device__ __forceinline__ floatx16 mma_mx(const i32x8& a_frag, const i32x8& b_frag, int a_scale,
+                                           int b_scale, const floatx16& acc) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b_frag, a_frag, acc, 0, 0, OPSEL, b_scale,
+                                                         OPSEL, a_scale);
+}
+
+template <int BM, int BN, int WM, int WN, int NST, bool OUT_BF16, bool DEBUG>
+__global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
+  static_assert(NST >= 3 && NST <= 6, "ring depth");
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+  constexpr int BKB = 64;                 // K bytes (= elements) per slab
+  constexpr int A_BYTES = BM * BKB;
+  constexpr int B_BYTES = BN * BKB;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_DMA = A_BYTES / 1024, B_DMA = B_BYTES / 1024;
+  static_assert(A_DMA % NW == 0 && B_DMA % NW == 0, "slabs split evenly over the waves");
+  constexpr int A_PER = A_DMA / NW, B_PER = B_DMA / NW;
+  constexpr int NDMA = A_PER + B_PER;     // DMA instructions per wave and slab
+  constexpr int RING = NST * STAGE;
+
+  __shared__ __attribute__((aligned(1024))) uint4 smem[RING / 16];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave - (wave / WN) * WN;
+  const int lrow = lane & 31, lgrp = lane >> 5;
+  const int M = p.M, N = p.N, K = p.K;
+  const int64_t lda = p.lda, ldb = p.ldb;
+  const int nk = K / BKB;                 // K is a multiple of 64
+
+  // per-lane DMA source offsets within a slab (bytes), fixed for the kernel
+  uint32_t voA[A_PER], voB[B_PER];
+#pragma unroll
+  for (int t = 0; t < A_PER; ++t) {
+    const int r = 16 * (wave + NW * t) + (lane >> 2);
+    voA[t] = (uint32_t)(r * lda) + (((lane & 3) ^ swzA(r)) << 4);
+  }
+#pragma unroll
+  for (int t = 0; t < B_PER; ++t) {
+    const int r = 16 * (wave + NW * t) + (lane >> 2);
+    voB[t] = (uint32_t)(r * ldb) + (((lane & 3) ^ swzA(r)) << 4);
+  }
+  const uint32_t ldsw = __builtin_amdgcn_readfirstlane(lds0 + 1024 * wave);
+  // this lane's LDS read addresses of stage 0 (chunk lgrp and 2 + lgrp)
+  const int swl = (lrow >> 2) & 3;
+  const uint32_t rA0 = lds0 + (wm * WTM + lrow) * 64 + (((lgrp ^ swl)) << 4);
+  const uint32_t rA1 = lds0 + (wm * WTM + lrow) * 64 + (((lgrp ^ swl) ^ 2) << 4);
+  const uint32_t rB0 = lds0 + A_BYTES + (wn * WTN + lrow) * 64 + (((lgrp ^ swl)) << 4);
+  const uint32_t rB1 = lds0 + A_BYTES + (wn * WTN + lrow) * 64 + (((lgrp ^ swl) ^ 2) << 4);
+
+  const int n_tiles = p.map.tiles_m * p.map.tiles_n;
+  for (int wg_it = blockIdx.x; wg_it < n_tiles; wg_it += gridDim.x) {
+    int wg = wg_it;
+    if constexpr (DEBUG) {
+      if ((p.flags & kDbgCollide) && wg == 1) wg = 0;  // negative control only
+    }
+    int32_t tm, tn;
+    tile_of(p.map, wg, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const char* a_panel = reinterpret_cast<const char*>(p.A + (int64_t)m0 * lda);
+    const int64_t a_bytes = K > 0 ? ((int64_t)(M - 1) * lda + K) - (int64_t)m0 * lda : 0;
+    const char* b_panel = reinterpret_cast<const char*>(p.B + (int64_t)n0 * ldb);
+    const int64_t b_bytes = K > 0 ? ((int64_t)(N - 1) * ldb + K) - (int64_t)n0 * ldb : 0;
+
+    // this lane's scale rows (rows past the edge repeat the last row; their
+    // products only reach accumulator rows that are never stored)
+    const uint32_t* sa_row[FM];
+    const uint32_t* sb_row[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = m0 + wm * WTM + 32 * i + lrow;
+      sa_row[i] = reinterpret_cast<const uint32_t*>(p.sA + (int64_t)(r < M ? r : M - 1) * p.ls);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = n0 + wn * WTN + 32 * j + lrow;
+      sb_row[j] = reinterpret_cast<const uint32_t*>(p.sB + (int64_t)(r < N ? r : N - 1) * p.ls);
+    }
+    const int sh = 8 * lgrp;
+
+    auto issue_slab = [&](int s) {
+      const uint32_t st = (uint32_t)(s % NST) * STAGE;
+      const i32x4 rsA = make_rsrc(a_panel + (int64_t)s * BKB, a_bytes - (int64_t)s * BKB);
+      const i32x4 rsB = make_rsrc(b_panel + (int64_t)s * BKB, b_bytes - (int64_t)s * BKB);
+#pragma unroll
+      for (int t = 0; t < A_PER; ++t) dma16(ldsw + st + 1024 * NW * t, rsA, voA[t], 0u);
+#pragma unroll
+      for (int t = 0; t < B_PER; ++t) dma16(ldsw + st + A_BYTES + 1024 * NW * t, rsB, voB[t], 0u);
+    };
+    // wait until this wave's loads of slab s have landed, given the slabs
+    // issued after it (whole slabs only: scale loads make the real count
+    // larger, so this waits at least as long as needed)
+    auto wait_after = [&](int after) {
+      switch (after) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<1 * NDMA>(); break;
+        case 2: wait_vmcnt<(2 * NDMA < 63 ? 2 * NDMA : 63)>(); break;
+        default: wait_vmcnt<(3 * NDMA < 63 ? 3 * NDMA : 63)>(); break;
+      }
+    };
+
+    floatx16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = floatx16{};
+
+    i32x8 af[2][FM], bfr[2][FN];
+    // scales of the current slab pair (pre-shifted per lane) and of the next
+    // one, loaded a pair ahead so their latency hides behind two slabs
+    int sca[FM], scb[FN];
+    uint32_t nsa[FM], nsb[FN];
+    const int npairs = (nk + 1) >> 1;
+    auto read_frags = [&](int s, int slot) {
+      const uint32_t so = (uint32_t)(s % NST) * STAGE;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const uint4 x = __builtin_bit_cast(uint4, lds_read16(rA0 + so + i * 2048));
+        const uint4 y = __builtin_bit_cast(uint4, lds_read16(rA1 + so + i * 2048));
+        af[slot][i] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const uint4 x = __builtin_bit_cast(uint4, lds_read16(rB0 + so + j * 2048));
+        const uint4 y = __builtin_bit_cast(uint4, lds_read16(rB1 + so + j * 2048));
+        bfr[slot][j] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+      }
+    };
+    auto fetch_scales = [&](int pair) {
+      if (pair < npairs) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) nsa[i] = sa_row[i][pair];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) nsb[j] = sb_row[j][pair];
+      }
+    };
+    auto take_scales = [&]() {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sca[i] = (int)(nsa[i] >> sh);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) scb[j] = (int)(nsb[j] >> sh);
+    };
+    auto mfmas = [&](auto opsel_c, int slot) {
+      constexpr int OPSEL = decltype(opsel_c)::value;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = mma_mx<OPSEL>(af[slot][i], bfr[slot][j], sca[i], scb[j], acc[i][j]);
+    };
+    constexpr int NREAD = 2 * (FM + FN);
+    constexpr int NMFMA = FM * FN;
+    constexpr int RPM = (NREAD + NMFMA - 1) / NMFMA;
+    auto interleave = [&]() {
+#pragma unroll
+      for (int k = 0; k < NMFMA; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (k * RPM < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+      }
+    };
+
+    // prologue: slabs 0 .. NST-2 in flight, slab 0 landed and read
+    if (nk > 0) {
+      for (int s = 0; s < NST - 1 && s < nk; ++s) issue_slab(s);
+      fetch_scales(0);
+      wait_after((nk - 1 < NST - 2 ? nk - 1 : NST - 2));
+      block_barrier();
+      read_frags(0, 0);
+    }
+    // Slab s: its operands are in registers (slot s % 2); slab s + 1 must land
+    // before its operands are read during slab s's MFMAs; the stage of slab
+    // s - 1 (read before the last barrier) takes slab s + NST - 1.
+    auto step = [&](int s, auto par_c) {
+      constexpr int PAR = decltype(par_c)::value;  // s % 2
+      if (PAR == 0) {
+        take_scales();
+        fetch_scales((s >> 1) + 1);
+      }
+      if (s + 1 < nk) {
+        const int issued_after = (nk - 1 < s + NST - 2 ? nk - 1 : s + NST - 2) - (s + 1);
+        wait_after(issued_after);
+        block_barrier();
+        if (s + NST - 1 < nk) issue_slab(s + NST - 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(std::integral_constant<int, 2 * PAR>{}, PAR);
+      // unconditional so it interleaves with the MFMAs; after the last slab
+      // it reads a stale stage (in bounds) whose values are never used
+      read_frags(s + 1, PAR ^ 1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int s = 0;
+    for (; s + 2 <= nk; s += 2) {
+      step(s, std::integral_constant<int, 0>{});
+      step(s + 1, std::integral_constant<int, 1>{});
+    }
+    if (s < nk) step(s, std::integral_constant<int, 0>{});
+
+    // Store: the summed tile is staged in the free ring as fp32 strips and
+    // written once per element (with the fused epilogue when asked).
+    __syncthreads();
+    {
+      constexpr int OPF = WTN * 4 + 16;
+      constexpr int SHF = (NW * 32 * OPF <= RING) ? 32 : 16;
+      static_assert(NW * SHF * OPF <= RING, "an fp32 strip of every wave fits the ring");
+      static_assert(WTN / 4 <= 64, "one wave covers a staged row in 16-byte chunks");
+      const uint32_t stf = lds0 + (uint32_t)(wave * SHF * OPF);
+      const EpiOut eo{p.C, p.ldc, M, N, p.bias, p.act, p.counts, p.flags};
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int hs = 0; hs < 32 / SHF; ++hs) {
+          const int rl = lrow - SHF * hs;
+          if (SHF == 32 || (lrow >> 4) == hs) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                lds_store_f4(stf + (uint32_t)(rl * OPF + (32 * j + 8 * q + 4 * lgrp) * 4),
+                             floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                     acc[i][j][4 * q + 3]});
+          }
+          wait_lgkmcnt0();
+          store_staged_fused<OUT_BF16, DEBUG>(stf, OPF, SHF, WTN, m0 + wm * WTM + 32 * i + SHF * hs,
+                                              n0 + wn * WTN, lane, 64, eo);
+          wait_lgkmcnt0();
+        }
+      }
+    }
+    wait_lgkmcnt0();
+    block_barrier();
+  }
+}
+
+}  // namespace tg

@@ -86,6 +86,19 @@ constexpr SkinnyConfig kSkinnyConfigs[kNumSkinnyConfigs] = {
     {4, 1}, {8, 1}, {4, 2}, {8, 2}, {4, 4}, {8, 4},
 };
 
+// MXFP8 tile-kernel configurations (mx_kernel.hpp); `eff` ranks them as in
+// the bf16 table.
+struct MxConfig {
+  int bm, bn, wm, wn, stages;
+  float eff;
+};
+constexpr int kNumMxConfigs = 2;
+constexpr MxConfig kMxConfigs[kNumMxConfigs] = {
+    {256, 256, 2, 2, 4, 1.00f},  // 0: 4 waves of 128x128
+    {128, 128, 2, 2, 4, 0.70f},  // 1: 4 waves of 64x64
+};
+constexpr int kMxBK = 64;  // K per slab of the MX kernel (a multiple of it is required)
+
 // Owned-tile map parameters (kernel argument; plain data).
 struct TileMap {
   int32_t tiles_m, tiles_n;
@@ -122,7 +135,7 @@ TG_HD void tile_of(const TileMap& mp, int32_t wg, int32_t& tm, int32_t& tn) {
 }
 
 struct Plan {
-  int variant;  // 0 none, 1 tile, 2 skinny
+  int variant;  // 0 none, 1 tile, 2 skinny, 3 MXFP8 tile
   int config;
   int bm, bn, bk, threads, lds_bytes;
   TileMap map;
@@ -202,6 +215,46 @@ inline Plan plan_for(int variant, int config, int64_t M, int64_t N, int cu_count
     p.grid = persistent_grid(p.tiles, cu_count);
   }
   return p;
+}
+
+// The launch geometry of MX configuration `config` for an M x N output.
+inline Plan plan_for_mx(int config, int64_t M, int64_t N, int cu_count) {
+  Plan p{};
+  const MxConfig& c = kMxConfigs[config];
+  p.variant = 3;
+  p.config = config;
+  p.bm = c.bm;
+  p.bn = c.bn;
+  p.bk = kMxBK;
+  p.threads = c.wm * c.wn * 64;
+  p.lds_bytes = c.stages * (c.bm + c.bn) * kMxBK;
+  p.k_split = 1;
+  p.map.tiles_m = (int32_t)ceil_div(M, c.bm);
+  p.map.tiles_n = (int32_t)ceil_div(N, c.bn);
+  p.map.group_m = pick_group_m(p.map.tiles_m, p.map.tiles_n);
+  p.map.xcds = kXcds;
+  p.tiles = (int64_t)p.map.tiles_m * p.map.tiles_n;
+  p.grid = persistent_grid(p.tiles, cu_count);
+  return p;
+}
+
+// MX plan: the configuration minimising (tiles on the busiest CU) x (tile
+// area) / rate, as for the bf16 tile kernel.
+inline Plan make_plan_mx(int64_t M, int64_t N, int64_t K, int cu_count) {
+  (void)K;
+  if (M <= 0 || N <= 0) return plan_for(0, 0, M, N, cu_count);
+  int best = 0;
+  double best_cost = 0.0;
+  for (int i = 0; i < kNumMxConfigs; ++i) {
+    const MxConfig& c = kMxConfigs[i];
+    const int64_t per_cu = ceil_div(ceil_div(M, c.bm) * ceil_div(N, c.bn), cu_count);
+    const double cost = (double)per_cu * c.bm * c.bn / c.eff;
+    if (i == 0 || cost < best_cost * 0.999) {
+      best = i;
+      best_cost = cost;
+    }
+  }
+  return plan_for_mx(best, M, N, cu_count);
 }
 
 // Pure function of (M, N, K, B layout, CU count). The output type is not an

@@ -203,6 +203,135 @@ hipError_t dispatch_skinny(int cfg, const tg::SkinnyArgs& a, int64_t grid, const
 }
 static_assert(tg::kNumSkinnyConfigs == 6, "dispatch_skinny covers every skinny configuration");
 
+hipError_t dispatch_mx(int cfg, const tg::MxArgs& a, int64_t grid, const tg::Variant& v,
+                       hipStream_t st) {
+  switch (cfg) {
+    case 0: return tg::launch_mx<0>(a, grid, v, st);
+    case 1: return tg::launch_mx<1>(a, grid, v, st);
+  }
+  return hipErrorInvalidValue;
+}
+static_assert(tg::kNumMxConfigs == 2, "dispatch_mx covers every MX configuration");
+
+// Checks of tile_gemm_run_mx's arguments (see the header).
+tile_gemm_status_t check_mx(const void* A, const void* B, const void* C, int64_t M, int64_t N,
+                            int64_t K, const tile_gemm_strides_t* s, const void* sa,
+                            const void* sb, int64_t ls, int fmt, int dtype, const float* bias,
+                            int act) {
+  g_detail[0] = '\0';
+  if (dtype != TILE_GEMM_BF16_TO_F32 && dtype != TILE_GEMM_BF16_TO_BF16)
+    return fail(TILE_GEMM_ERR_DTYPE, "dtype: unknown value %d", dtype);
+  if (fmt != TILE_GEMM_MX_E4M3) return fail(TILE_GEMM_ERR_DTYPE, "fmt: unknown MX format %d", fmt);
+  if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+    return fail(TILE_GEMM_ERR_BAD_SHAPE, "shape: M=%lld N=%lld K=%lld, each must be in [0, 2^31)",
+                (long long)M, (long long)N, (long long)K);
+  if (K % tg::kMxBK)
+    return fail(TILE_GEMM_ERR_BAD_SHAPE, "K=%lld: the MX product needs K a multiple of %d",
+                (long long)K, tg::kMxBK);
+  if (!s) return fail(TILE_GEMM_ERR_NULL_ARG, "strides: NULL");
+  if (act < TILE_GEMM_ACT_NONE || act > TILE_GEMM_ACT_SILU)
+    return fail(TILE_GEMM_ERR_EPILOGUE, "act: %d is not available for the MX product", act);
+  if (M == 0 || N == 0) return TILE_GEMM_OK;
+  if (!C) return fail(TILE_GEMM_ERR_NULL_ARG, "C: NULL");
+  if (K > 0) {
+    if (!A) return fail(TILE_GEMM_ERR_NULL_ARG, "A: NULL");
+    if (!B) return fail(TILE_GEMM_ERR_NULL_ARG, "B: NULL");
+    if (!sa) return fail(TILE_GEMM_ERR_NULL_ARG, "a_scale: NULL");
+    if (!sb) return fail(TILE_GEMM_ERR_NULL_ARG, "b_scale: NULL");
+    if (s->a_k != 1 || s->a_m < K)
+      return fail(TILE_GEMM_ERR_BAD_STRIDE, "A strides (a_m=%lld, a_k=%lld): need a_k == 1, a_m >= K",
+                  (long long)s->a_m, (long long)s->a_k);
+    if (s->b_k != 1 || s->b_n < K)
+      return fail(TILE_GEMM_ERR_BAD_STRIDE,
+                  "B strides (b_k=%lld, b_n=%lld): the MX product takes B as N x K, b_k == 1, b_n >= K",
+                  (long long)s->b_k, (long long)s->b_n);
+    if (ls < K / 32 || ls % 4)
+      return fail(TILE_GEMM_ERR_BAD_STRIDE,
+                  "scale_stride=%lld: need a multiple of 4 bytes and >= K/32=%lld", (long long)ls,
+                  (long long)(K / 32));
+  }
+  if (s->c_n != 1 || s->c_m < N)
+    return fail(TILE_GEMM_ERR_BAD_STRIDE, "C strides (c_m=%lld, c_n=%lld): need c_n == 1, c_m >= N",
+                (long long)s->c_m, (long long)s->c_n);
+  const int64_t esz = dtype == TILE_GEMM_BF16_TO_F32 ? 4 : 2;
+  if ((uintptr_t)C % 16) return fail(TILE_GEMM_ERR_MISALIGNED, "C: base pointer not 16-byte aligned");
+  if ((s->c_m * esz) % 16)
+    return fail(TILE_GEMM_ERR_MISALIGNED, "C: c_m=%lld elements is not a multiple of 16 bytes",
+                (long long)s->c_m);
+  const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)(esz * ((M - 1) * s->c_m + N));
+  if (K > 0) {
+    if ((uintptr_t)A % 16 || s->a_m % 16)
+      return fail(TILE_GEMM_ERR_MISALIGNED, "A: base or a_m not a multiple of 16 bytes");
+    if ((uintptr_t)B % 16 || s->b_n % 16)
+      return fail(TILE_GEMM_ERR_MISALIGNED, "B: base or b_n not a multiple of 16 bytes");
+    if ((uintptr_t)sa % 4 || (uintptr_t)sb % 4)
+      return fail(TILE_GEMM_ERR_MISALIGNED, "scales: base pointers must be 4-byte aligned");
+    const int64_t a_span = (M - 1) * s->a_m + K, b_span = (N - 1) * s->b_n + K;
+    if (a_span >= ((int64_t)1 << 32) || b_span >= ((int64_t)1 << 32))
+      return fail(TILE_GEMM_ERR_BAD_SHAPE, "A or B spans 4 GiB or more");
+    const uintptr_t a0 = (uintptr_t)A, b0 = (uintptr_t)B, s0 = (uintptr_t)sa, t0 = (uintptr_t)sb;
+    if (overlap(c0, c1, a0, a0 + a_span)) return fail(TILE_GEMM_ERR_ALIAS, "C overlaps A");
+    if (overlap(c0, c1, b0, b0 + b_span)) return fail(TILE_GEMM_ERR_ALIAS, "C overlaps B");
+    if (overlap(c0, c1, s0, s0 + (uintptr_t)(M * ls)))
+      return fail(TILE_GEMM_ERR_ALIAS, "C overlaps a_scale");
+    if (overlap(c0, c1, t0, t0 + (uintptr_t)(N * ls)))
+      return fail(TILE_GEMM_ERR_ALIAS, "C overlaps b_scale");
+  }
+  return check_epilogue(C, M, N, s, dtype, bias, act);
+}
+
+tile_gemm_status_t run_mx_impl(tile_gemm_t h, const void* A, const void* B, void* C, int64_t M,
+                               int64_t N, int64_t K, const tile_gemm_strides_t* s, const void* sa,
+                               const void* sb, int64_t ls, int fmt, int dtype, const float* bias,
+                               int act, void* stream, uint32_t* counts, int flags) {
+  if (!h) return fail(TILE_GEMM_ERR_NULL_ARG, "handle: NULL");
+  tile_gemm_status_t st = check_mx(A, B, C, M, N, K, s, sa, sb, ls, fmt, dtype, bias, act);
+  if (st != TILE_GEMM_OK) return st;
+  if (flags & ~(TILE_GEMM_DEBUG_COUNT_WRITES | TILE_GEMM_DEBUG_COLLIDE | 0x7f00ff00))
+    return fail(TILE_GEMM_ERR_BAD_SHAPE, "flags: unknown bits 0x%x", flags);
+  if (M == 0 || N == 0) return TILE_GEMM_OK;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != h->device)
+    return fail(TILE_GEMM_ERR_DEVICE, "current device %d is not the handle's device %d", cur,
+                h->device);
+  if ((flags & TILE_GEMM_DEBUG_COUNT_WRITES) && !counts)
+    return fail(TILE_GEMM_ERR_NULL_ARG, "counts: NULL with TILE_GEMM_DEBUG_COUNT_WRITES");
+  tg::Plan p = tg::make_plan_mx(M, N, K, h->cu_count);
+  const int force = (flags >> 8) & 0xff;
+  if (force) {
+    if (force > tg::kNumMxConfigs)
+      return fail(TILE_GEMM_ERR_BAD_SHAPE, "debug: no MX configuration %d", force - 1);
+    p = tg::plan_for_mx(force - 1, M, N, h->cu_count);
+  }
+  const int force_grid = (flags >> 24) & 0x7f;
+  if (force_grid) p.grid = (force_grid == 0x7f || force_grid > p.tiles) ? p.tiles : force_grid;
+  if ((flags & TILE_GEMM_DEBUG_COLLIDE) && p.tiles < 2)
+    return fail(TILE_GEMM_ERR_BAD_SHAPE, "debug collide: needs >= 2 tiles");
+  if (p.grid > 0x7fffffff) return fail(TILE_GEMM_ERR_BAD_SHAPE, "shape: too many workgroups");
+  tg::MxArgs a{};
+  a.A = static_cast<const uint8_t*>(A);
+  a.B = static_cast<const uint8_t*>(B);
+  a.sA = static_cast<const uint8_t*>(sa);
+  a.sB = static_cast<const uint8_t*>(sb);
+  a.C = C;
+  a.M = (int32_t)M;
+  a.N = (int32_t)N;
+  a.K = (int32_t)K;
+  a.lda = s->a_m;
+  a.ldb = s->b_n;
+  a.ldc = s->c_m;
+  a.ls = (int32_t)ls;
+  a.map = p.map;
+  a.counts = counts;
+  a.flags = flags;
+  a.bias = bias;
+  a.act = act;
+  const tg::Variant v{true, dtype == TILE_GEMM_BF16_TO_BF16, flags != 0};
+  const hipError_t e = dispatch_mx(p.config, a, p.grid, v, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(TILE_GEMM_ERR_HIP, "launch: %s", hipGetErrorString(e));
+  return TILE_GEMM_OK;
+}
+
 tile_gemm_status_t run_impl(tile_gemm_t h, const void* A, const void* B, void* C, int64_t M,
                             int64_t N, int64_t K, const tile_gemm_strides_t* s,
                             tile_gemm_dtype_t dtype, void* stream, uint32_t* counts, int flags,
@@ -308,7 +437,7 @@ const char* tile_gemm_status_str(tile_gemm_status_t s) {
     case TILE_GEMM_ERR_DTYPE: return "unknown dtype";
     case TILE_GEMM_ERR_DEVICE: return "device unavailable, not gfx950, or not current";
     case TILE_GEMM_ERR_HIP: return "HIP runtime error";
-    case TILE_GEMM_ERR_EPILOGUE: return "unknown activation";
+    case TILE_GEMM_ERR_EPILOGUE: return "activation unknown or not available here";
   }
   return "unknown status";
 }
@@ -380,6 +509,49 @@ tile_gemm_status_t tile_gemm_check_epilogue(const void* C, int64_t M, int64_t N,
   return check_epilogue(C, M, N, strides, (int)dtype, bias, (int)act);
 }
 
+tile_gemm_status_t tile_gemm_run_mx(tile_gemm_t h, const void* A, const void* B, void* C,
+                                    int64_t M, int64_t N, int64_t K,
+                                    const tile_gemm_strides_t* strides, const void* a_scale,
+                                    const void* b_scale, int64_t scale_stride,
+                                    tile_gemm_mx_format_t fmt, tile_gemm_dtype_t dtype,
+                                    const float* bias, tile_gemm_act_t act, void* stream) {
+  return run_mx_impl(h, A, B, C, M, N, K, strides, a_scale, b_scale, scale_stride, (int)fmt,
+                     (int)dtype, bias, (int)act, stream, nullptr, 0);
+}
+
+tile_gemm_status_t tile_gemm_run_mx_debug(tile_gemm_t h, const void* A, const void* B, void* C,
+                                          int64_t M, int64_t N, int64_t K,
+                                          const tile_gemm_strides_t* strides,
+                                          const void* a_scale, const void* b_scale,
+                                          int64_t scale_stride, tile_gemm_mx_format_t fmt,
+                                          tile_gemm_dtype_t dtype, const float* bias,
+                                          tile_gemm_act_t act, void* stream, uint32_t* counts,
+                                          int flags) {
+  return run_mx_impl(h, A, B, C, M, N, K, strides, a_scale, b_scale, scale_stride, (int)fmt,
+                     (int)dtype, bias, (int)act, stream, counts, flags);
+}
+
+tile_gemm_status_t tile_gemm_check_mx(const void* A, const void* B, const void* C, int64_t M,
+                                      int64_t N, int64_t K, const tile_gemm_strides_t* strides,
+                                      const void* a_scale, const void* b_scale,
+                                      int64_t scale_stride, tile_gemm_mx_format_t fmt,
+                                      tile_gemm_dtype_t dtype, const float* bias,
+                                      tile_gemm_act_t act) {
+  return check_mx(A, B, C, M, N, K, strides, a_scale, b_scale, scale_stride, (int)fmt, (int)dtype,
+                  bias, (int)act);
+}
+
+tile_gemm_status_t tile_gemm_plan_mx(int64_t M, int64_t N, int64_t K, int cu_count,
+                                     tile_gemm_plan_t* out) {
+  g_detail[0] = '\0';
+  if (!out) return fail(TILE_GEMM_ERR_NULL_ARG, "out: NULL");
+  if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+    return fail(TILE_GEMM_ERR_BAD_SHAPE, "shape out of range");
+  if (cu_count <= 0) return fail(TILE_GEMM_ERR_DEVICE, "cu_count: %d", cu_count);
+  fill_plan(tg::make_plan_mx(M, N, K, cu_count), out);
+  return TILE_GEMM_OK;
+}
+
 tile_gemm_status_t tile_gemm_plan(int64_t M, int64_t N, int64_t K, int b_col_major, int cu_count,
                                   tile_gemm_plan_t* out) {
   g_detail[0] = '\0';
@@ -398,7 +570,7 @@ tile_gemm_status_t tile_gemm_tile_of(const tile_gemm_plan_t* plan, int64_t M, in
   if (!plan || !m0 || !n0 || !rows || !cols) return fail(TILE_GEMM_ERR_NULL_ARG, "NULL argument");
   if (wg < 0 || wg >= plan->tiles) return fail(TILE_GEMM_ERR_BAD_SHAPE, "tile index out of range");
   int64_t r0, c0;
-  if (plan->variant == TILE_GEMM_VARIANT_TILE) {
+  if (plan->variant == TILE_GEMM_VARIANT_TILE || plan->variant == TILE_GEMM_VARIANT_MX) {
     tg::TileMap mp{plan->tiles_m, plan->tiles_n, plan->group_m, plan->xcds};
     int32_t tm, tn;
     tg::tile_of(mp, (int32_t)wg, tm, tn);

@@ -161,3 +161,123 @@ def operands(w: Workload, integer: bool = False, M: int | None = None,
             draw(K, N, w.b_dist, 1000 * w.case + 2, w.b_scale)
     B = Bs.T if w.b_col_major else Bs
     return Operands(A, B, Bs)
+
+
+# ------------------------------------------------------------------ MX (MXFP8)
+#
+# MX operands are quantised from the same kind of random values: per row,
+# blocks of 32 consecutive K values share a power-of-two scale 2^e (stored as
+# the E8M0 byte e + 127) chosen the OCP MX way, e = floor(log2(max |x|)) - 8
+# (8 being E4M3's largest exponent), and each x / 2^e is rounded to the
+# nearest E4M3 value (ties to even), saturating at +-448. The integer variant
+# uses the E4M3 codes of -3..3 with unit scales, so products are exact.
+
+MX_BLOCK = 32
+_E4M3_INT_CODES = {-3: 0xC4, -2: 0xC0, -1: 0xB8, 0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44}
+
+
+def f64_to_e4m3(y) -> np.ndarray:
+    """Round float64 values to E4M3 codes (nearest, ties to even; saturating
+    at +-448; no NaN is produced)."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.minimum(np.abs(y), 448.0)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    q = np.exp2(e - 3.0)                         # spacing of E4M3 values in [2^e, 2^(e+1))
+    v = np.minimum(np.rint(a / q) * q, 448.0)    # np.rint rounds half to even
+    sub = v < 2.0 ** -6
+    E = np.floor(np.log2(np.where(sub, 1.0, v)))
+    m = np.where(sub, 0.0, (v / np.exp2(E) - 1.0) * 8.0)
+    code = np.where(sub, np.rint(v / 2.0 ** -9), (E + 7.0) * 8.0 + m).astype(np.uint8)
+    return code | np.signbit(y).astype(np.uint8) << 7
+
+
+def mx_scale_stride(k: int) -> int:
+    """Bytes per scale row: one per 32 K values, rounded up to a multiple of 4."""
+    return (((k + MX_BLOCK - 1) // MX_BLOCK) + 3) // 4 * 4
+
+
+def draw_mx(rows: int, k: int, dist: str, seed: int, scale: float = 1.0):
+    """(codes, scales): rows x k E4M3 codes and rows x mx_scale_stride(k) E8M0
+    bytes (padding bytes 127). Values are drawn like draw() (row-major, in
+    chunks of rows), then quantised per block of 32 as described above."""
+    if dist not in ("normal", "uniform", "int3"):
+        raise ValueError(f"unknown distribution {dist!r}")
+    rng = np.random.default_rng(seed)
+    ls = mx_scale_stride(k)
+    codes = np.empty((rows, k), np.uint8)
+    scales = np.full((rows, ls), 127, np.uint8)
+    nb = (k + MX_BLOCK - 1) // MX_BLOCK
+    step = max(1, (1 << 20) // max(k, 1))
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        n = (r1 - r0) * k
+        if dist == "int3":
+            v = rng.integers(-3, 4, n).reshape(r1 - r0, k)
+            codes[r0:r1] = np.vectorize(_E4M3_INT_CODES.get, otypes=[np.uint8])(v)
+            continue
+        x = (rng.standard_normal(n) if dist == "normal" else rng.uniform(-1.0, 1.0, n))
+        x = (x * float(scale)).reshape(r1 - r0, k)
+        pad = np.zeros((r1 - r0, nb * MX_BLOCK))
+        pad[:, :k] = x
+        blocks = pad.reshape(r1 - r0, nb, MX_BLOCK)
+        amax = np.abs(blocks).max(axis=2)
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8.0, -127.0)
+        e = np.clip(e, -127.0, 127.0)
+        scales[r0:r1, :nb] = (e + 127.0).astype(np.uint8)
+        q = blocks / np.exp2(e)[:, :, None]
+        codes[r0:r1] = f64_to_e4m3(q).reshape(r1 - r0, nb * MX_BLOCK)[:, :k]
+    return codes, scales
+
+
+@dataclass(frozen=True)
+class MxWorkload:
+    name: str
+    case: int
+    M: int
+    N: int
+    K: int
+    outs: tuple
+    b_scale: float = 1.0
+    note: str = ""
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    def algorithmic_bytes(self, out: str) -> int:
+        """Elements and scales read once, C written once."""
+        esz = 4 if out == "f32" else 2
+        ls = mx_scale_stride(self.K)
+        return (self.M + self.N) * (self.K + ls) + esz * self.M * self.N
+
+
+MX_WORKLOADS = {
+    "mx_mlp_gate_up_shard": MxWorkload(
+        "mx_mlp_gate_up_shard", 14, 8192, 7168, 8192, ("bf16",), b_scale=_S,
+        note="the MLP gate+up shard in MXFP8 (weights N x K), bf16 output"),
+    "mx_square4096": MxWorkload(
+        "mx_square4096", 12, 4096, 4096, 4096, ("bf16",),
+        note="4096^3 in MXFP8"),
+    "mx_decode": MxWorkload(
+        "mx_decode", 15, 16, 28672, 8192, ("bf16",), b_scale=_S,
+        note="the decode shape in MXFP8, HBM-bound"),
+}
+
+
+@dataclass
+class MxOperands:
+    A: np.ndarray    # (M, K) E4M3 codes
+    sA: np.ndarray   # (M, ls) E8M0
+    Bt: np.ndarray   # (N, K) E4M3 codes of B's transpose
+    sB: np.ndarray   # (N, ls)
+
+
+def mx_operands(w: MxWorkload, integer: bool = False, M: int | None = None,
+                N: int | None = None, K: int | None = None) -> MxOperands:
+    M = w.M if M is None else M
+    N = w.N if N is None else N
+    K = w.K if K is None else K
+    da, db = ("int3", "int3") if integer else ("normal", "normal")
+    A, sA = draw_mx(M, K, da, 1000 * w.case + (3 if integer else 1))
+    Bt, sB = draw_mx(N, K, db, 1000 * w.case + (4 if integer else 2), w.b_scale)
+    return MxOperands(A, sA, Bt, sB)
