@@ -20,7 +20,11 @@
 // (measured on the device with a one-wave probe). Each lane therefore needs
 // the scale of its row for block 2 s + l / 32: one dword of the scale row
 // covers two slabs; it is shifted by 8 (l / 32) bits per lane and the
-// instruction's byte select picks byte 0 or 2 by slab parity.
+// instruction's byte select picks byte 0 or 2 by slab parity. Scales travel
+// like the operands: 16 bytes of every row of the tile (the scales of 8
+// slabs) are loaded straight into a double-buffered LDS window together with
+// the first slab they cover, so their loads are ordered with the slabs'
+// and need no wait of their own.
 //
 // K advances in ascending order (fp32 accumulation, no split-K), so results
 // are bit-identical run to run.
@@ -73,8 +77,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
   constexpr int A_PER = A_DMA / NW, B_PER = B_DMA / NW;
   constexpr int NDMA = A_PER + B_PER;     // DMA instructions per wave and slab
   constexpr int RING = NST * STAGE;
+  constexpr int SWIN = (BM + BN) * 16;    // one scale window: 16 bytes per row
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "scale windows are whole KiB per wave instruction");
+  constexpr int SA_DMA = BM / 64, SB_DMA = BN / 64;   // window loads (1 KiB each)
 
-  __shared__ __attribute__((aligned(1024))) uint4 smem[RING / 16];
+  __shared__ __attribute__((aligned(1024))) uint4 smem[(RING + 2 * SWIN) / 16];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -119,23 +126,30 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
     const char* b_panel = reinterpret_cast<const char*>(p.B + (int64_t)n0 * ldb);
     const int64_t b_bytes = K > 0 ? ((int64_t)(N - 1) * ldb + K) - (int64_t)n0 * ldb : 0;
 
-    // this lane's scale rows (rows past the edge repeat the last row; their
-    // products only reach accumulator rows that are never stored)
-    const uint32_t* sa_row[FM];
-    const uint32_t* sb_row[FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int r = m0 + wm * WTM + 32 * i + lrow;
-      sa_row[i] = reinterpret_cast<const uint32_t*>(p.sA + (int64_t)(r < M ? r : M - 1) * p.ls);
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int r = n0 + wn * WTN + 32 * j + lrow;
-      sb_row[j] = reinterpret_cast<const uint32_t*>(p.sB + (int64_t)(r < N ? r : N - 1) * p.ls);
-    }
     const int sh = 8 * lgrp;
+    // scale windows: rows of both scale arrays with exact extents (rows past
+    // the edge read as zero and are never used)
+    const i32x4 rsSA = make_rsrc(p.sA, (int64_t)M * p.ls);
+    const i32x4 rsSB = make_rsrc(p.sB, (int64_t)N * p.ls);
+    const uint32_t swin0 = lds0 + RING;
+    // Load window w (16 bytes of each of the tile's rows, scales of slabs
+    // 8 w .. 8 w + 7) into buffer w % 2: instruction q covers rows 64 q ..
+    auto issue_window = [&](int w) {
+      const uint32_t dst = swin0 + (uint32_t)((w & 1) * SWIN);
+#pragma unroll
+      for (int q = 0; q < SA_DMA; ++q)
+        if (q % NW == wave)
+          dma16(dst + 1024 * q, rsSA, (uint32_t)((m0 + 64 * q + lane) * p.ls + 16 * w), 0u);
+#pragma unroll
+      for (int q = 0; q < SB_DMA; ++q)
+        if (q % NW == wave)
+          dma16(dst + BM * 16 + 1024 * q, rsSB, (uint32_t)((n0 + 64 * q + lane) * p.ls + 16 * w), 0u);
+    };
 
+    // The window of slabs 8 w .. goes out just before slab 8 w's own loads, so
+    // any wait that covers slab 8 w covers it too.
     auto issue_slab = [&](int s) {
+      if ((s & 7) == 0) issue_window(s >> 3);
       const uint32_t st = (uint32_t)(s % NST) * STAGE;
       const i32x4 rsA = make_rsrc(a_panel + (int64_t)s * BKB, a_bytes - (int64_t)s * BKB);
       const i32x4 rsB = make_rsrc(b_panel + (int64_t)s * BKB, b_bytes - (int64_t)s * BKB);
@@ -163,11 +177,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
       for (int j = 0; j < FN; ++j) acc[i][j] = floatx16{};
 
     i32x8 af[2][FM], bfr[2][FN];
-    // scales of the current slab pair (pre-shifted per lane) and of the next
-    // one, loaded a pair ahead so their latency hides behind two slabs
-    int sca[FM], scb[FN];
-    uint32_t nsa[FM], nsb[FN];
-    const int npairs = (nk + 1) >> 1;
+    int sca[FM], scb[FN];  // scales of the current slab pair, pre-shifted per lane
     auto read_frags = [&](int s, int slot) {
       const uint32_t so = (uint32_t)(s % NST) * STAGE;
 #pragma unroll
@@ -183,19 +193,22 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
         bfr[slot][j] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
       }
     };
-    auto fetch_scales = [&](int pair) {
-      if (pair < npairs) {
+    // scales of slabs s, s + 1 (s even) from window s / 8, landed with slab
+    // 8 (s / 8) before the barrier that made that slab readable
+    auto take_scales = [&](int s) {
+      const uint32_t wb = swin0 + (uint32_t)(((s >> 3) & 1) * SWIN) + (uint32_t)(4 * ((s & 7) >> 1));
 #pragma unroll
-        for (int i = 0; i < FM; ++i) nsa[i] = sa_row[i][pair];
-#pragma unroll
-        for (int j = 0; j < FN; ++j) nsb[j] = sb_row[j][pair];
+      for (int i = 0; i < FM; ++i) {
+        const uint32_t v = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
+            wb + (uint32_t)((wm * WTM + 32 * i + lrow) * 16));
+        sca[i] = (int)(v >> sh);
       }
-    };
-    auto take_scales = [&]() {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) sca[i] = (int)(nsa[i] >> sh);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) scb[j] = (int)(nsb[j] >> sh);
+      for (int j = 0; j < FN; ++j) {
+        const uint32_t v = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
+            wb + (uint32_t)(BM * 16 + (wn * WTN + 32 * j + lrow) * 16));
+        scb[j] = (int)(v >> sh);
+      }
     };
     auto mfmas = [&](auto opsel_c, int slot) {
       constexpr int OPSEL = decltype(opsel_c)::value;
@@ -219,7 +232,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
     // prologue: slabs 0 .. NST-2 in flight, slab 0 landed and read
     if (nk > 0) {
       for (int s = 0; s < NST - 1 && s < nk; ++s) issue_slab(s);
-      fetch_scales(0);
       wait_after((nk - 1 < NST - 2 ? nk - 1 : NST - 2));
       block_barrier();
       read_frags(0, 0);
@@ -229,10 +241,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
     // s - 1 (read before the last barrier) takes slab s + NST - 1.
     auto step = [&](int s, auto par_c) {
       constexpr int PAR = decltype(par_c)::value;  // s % 2
-      if (PAR == 0) {
-        take_scales();
-        fetch_scales((s >> 1) + 1);
-      }
+      if (PAR == 0) take_scales(s);
       if (s + 1 < nk) {
         const int issued_after = (nk - 1 < s + NST - 2 ? nk - 1 : s + NST - 2) - (s + 1);
         wait_after(issued_after);
@@ -247,7 +256,71 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
       interleave();
       __builtin_amdgcn_sched_barrier(0);
     };
+    // Steady state (slab s + NST - 1 exists): the same step with compile-time
+    // waits, each MFMA followed by its share of the next slab's operand reads,
+    // and the DMA loads of slab s + NST - 1 spread evenly among the MFMAs so
+    // they never reach the texture unit as one burst.
+    constexpr int NUNIT = FM + FN;
+    constexpr int UPM = (NUNIT + NMFMA - 1) / NMFMA;
+    auto read_unit = [&](uint32_t so, int slot, auto idx_c) {
+      constexpr int IDX = decltype(idx_c)::value;
+      if constexpr (IDX < FM) {
+        const uint4 x = __builtin_bit_cast(uint4, lds_read16(rA0 + so + IDX * 2048));
+        const uint4 y = __builtin_bit_cast(uint4, lds_read16(rA1 + so + IDX * 2048));
+        af[slot][IDX] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+      } else {
+        const uint4 x = __builtin_bit_cast(uint4, lds_read16(rB0 + so + (IDX - FM) * 2048));
+        const uint4 y = __builtin_bit_cast(uint4, lds_read16(rB1 + so + (IDX - FM) * 2048));
+        bfr[slot][IDX - FM] =
+            i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+      }
+    };
+    auto dma_slot = [](int t, int n) constexpr { return ((2 * t + 1) * NMFMA) / (2 * n); };
+    auto step_full = [&](int s, auto par_c) {
+      constexpr int PAR = decltype(par_c)::value;
+      if (PAR == 0) take_scales(s);
+      wait_vmcnt<((NST - 3) * NDMA < 63 ? (NST - 3) * NDMA : 63)>();
+      block_barrier();
+      const int sn = s + NST - 1;
+      if ((sn & 7) == 0) issue_window(sn >> 3);
+      const uint32_t stn = (uint32_t)(sn % NST) * STAGE;
+      const i32x4 rsA = make_rsrc(a_panel + (int64_t)sn * BKB, a_bytes - (int64_t)sn * BKB);
+      const i32x4 rsB = make_rsrc(b_panel + (int64_t)sn * BKB, b_bytes - (int64_t)sn * BKB);
+      const uint32_t so = (uint32_t)((s + 1) % NST) * STAGE;
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, NMFMA>([&](auto k_c) {
+        constexpr int k = decltype(k_c)::value;
+        acc[k / FN][k % FN] = mma_mx<2 * PAR>(af[PAR][k / FN], bfr[PAR][k % FN], sca[k / FN],
+                                             scb[k % FN], acc[k / FN][k % FN]);
+        static_for<0, UPM>([&](auto r_c) {
+          constexpr int idx = k * UPM + decltype(r_c)::value;
+          if constexpr (idx < NUNIT) read_unit(so, PAR ^ 1, std::integral_constant<int, idx>{});
+        });
+        static_for<0, NDMA>([&](auto t_c) {
+          constexpr int t = decltype(t_c)::value;
+          if constexpr (dma_slot(t, NDMA) == k) {
+            if constexpr (t < A_PER)
+              dma16(ldsw + stn + 1024 * NW * t, rsA, voA[t], 0u);
+            else
+              dma16(ldsw + stn + A_BYTES + 1024 * NW * (t - A_PER), rsB, voB[t - A_PER], 0u);
+          }
+        });
+      });
+      static_for<0, NMFMA>([&](auto k_c) {
+        constexpr int k = decltype(k_c)::value;
+        constexpr int lo = k * UPM, hi = (k + 1) * UPM < NUNIT ? (k + 1) * UPM : NUNIT;
+        constexpr int n_rd = lo < NUNIT ? 2 * (hi - lo) : 0;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (n_rd > 0) __builtin_amdgcn_sched_group_barrier(0x100, n_rd, 0);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    };
     int s = 0;
+    const int n_full = nk - (NST - 1);  // slabs whose slab + NST - 1 exists
+    for (; s + 2 <= n_full; s += 2) {
+      step_full(s, std::integral_constant<int, 0>{});
+      step_full(s + 1, std::integral_constant<int, 1>{});
+    }
     for (; s + 2 <= nk; s += 2) {
       step(s, std::integral_constant<int, 0>{});
       step(s + 1, std::integral_constant<int, 1>{});

@@ -249,6 +249,10 @@ tile_gemm_status_t check_mx(const void* A, const void* B, const void* C, int64_t
       return fail(TILE_GEMM_ERR_BAD_STRIDE,
                   "scale_stride=%lld: need a multiple of 4 bytes and >= K/32=%lld", (long long)ls,
                   (long long)(K / 32));
+    // the kernel addresses scale rows (up to one tile past the edge) with
+    // 32-bit byte offsets
+    if ((M + 256) * ls >= ((int64_t)1 << 32) || (N + 256) * ls >= ((int64_t)1 << 32))
+      return fail(TILE_GEMM_ERR_BAD_SHAPE, "scales: rows x scale_stride must stay below 4 GiB");
   }
   if (s->c_n != 1 || s->c_m < N)
     return fail(TILE_GEMM_ERR_BAD_STRIDE, "C strides (c_m=%lld, c_n=%lld): need c_n == 1, c_m >= N",
