@@ -295,7 +295,9 @@ enum {
 };
 /* Run a given compiled configuration instead of the planner's choice, so tests
  * can cover every configuration at small sizes. A forced skinny configuration
- * needs M <= its row capacity (16 * row groups). */
+ * needs M <= its row capacity (16 * row groups). Forced configurations and
+ * grids run the production kernel instances; only TILE_GEMM_DEBUG_COUNT_WRITES
+ * and TILE_GEMM_DEBUG_COLLIDE select the instrumented ones. */
 #define TILE_GEMM_DEBUG_FORCE_TILE(c) ((((c) + 1) & 0xff) << 8)
 #define TILE_GEMM_DEBUG_FORCE_SKINNY(c) ((((c) + 1) & 0xff) << 16)
 /* Launch g workgroups (1 <= g <= 126, at most the tile count) for the tile

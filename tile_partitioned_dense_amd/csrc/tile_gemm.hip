@@ -52,6 +52,13 @@ bool b_is_col_major(const tile_gemm_strides_t* s, int64_t K) {
   return s->b_k == 1 && s->b_n >= K;
 }
 
+// The instrumented kernel instances (write counter, colliding map) are needed
+// only for those two flags; a forced configuration or grid runs the
+// production instance, so forced runs time exactly what the planner launches.
+bool instrumented(int flags) {
+  return (flags & (TILE_GEMM_DEBUG_COUNT_WRITES | TILE_GEMM_DEBUG_COLLIDE)) != 0;
+}
+
 bool overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
   return a0 < a1 && b0 < b1 && a0 < b1 && b0 < a1;
 }
@@ -330,7 +337,7 @@ tile_gemm_status_t run_mx_impl(tile_gemm_t h, const void* A, const void* B, void
   a.flags = flags;
   a.bias = bias;
   a.act = act;
-  const tg::Variant v{true, dtype == TILE_GEMM_BF16_TO_BF16, flags != 0};
+  const tg::Variant v{true, dtype == TILE_GEMM_BF16_TO_BF16, instrumented(flags)};
   const hipError_t e = dispatch_mx(p.config, a, p.grid, v, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(TILE_GEMM_ERR_HIP, "launch: %s", hipGetErrorString(e));
   return TILE_GEMM_OK;
@@ -383,7 +390,7 @@ tile_gemm_status_t run_impl(tile_gemm_t h, const void* A, const void* B, void* C
   if ((flags & TILE_GEMM_DEBUG_COLLIDE) && (p.variant != 1 || p.tiles < 2))
     return fail(TILE_GEMM_ERR_BAD_SHAPE, "debug collide: needs the tile kernel and >= 2 tiles");
 
-  const tg::Variant v{!brow, dtype == TILE_GEMM_BF16_TO_BF16, flags != 0};
+  const tg::Variant v{!brow, dtype == TILE_GEMM_BF16_TO_BF16, instrumented(flags)};
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (p.variant == 1) {
