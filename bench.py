@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GEMM TFLOP/s & % MFMA peak (large); HBM GB/s & % peak (decode shape)"
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA (twice the bf16 rate)
+PEAK_FP4_TFLOPS = 10066.3      # MI355X dense fp4 / fp6 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 MIN_ROTATION_BYTES = 600 << 20  # > 2x the 256 MB last-level cache
 
@@ -232,11 +233,13 @@ def time_mx_workload(b, w, steps, warmup):
             for i in range(copies)]
     Cs = [torch.empty((w.M, w.N), dtype=odt, device="cuda") for _ in range(copies)]
     torch.cuda.synchronize()
-    log(f"[bench] {w.name}: {w.M}x{w.N}x{w.K} MXFP8 out={out} copies={copies} "
+    log(f"[bench] {w.name}: {w.M}x{w.N}x{w.K} {w.fmt} out={out} copies={copies} "
         f"(operands ready in {time.time() - t0:.1f}s)")
+    fmt = b.tg.MX_E2M1 if w.fmt == "e2m1" else b.tg.MX_E4M3
+    peak = PEAK_FP4_TFLOPS if w.fmt == "e2m1" else PEAK_FP8_TFLOPS
     for i in range(warmup):
         a, bt, sa, sb = sets[i % copies]
-        g.mx(a, bt, Cs[i % copies], sa, sb)
+        g.mx(a, bt, Cs[i % copies], sa, sb, fmt=fmt)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
@@ -244,13 +247,14 @@ def time_mx_workload(b, w, steps, warmup):
     for i in range(steps):
         a, bt, sa, sb = sets[i % copies]
         ev[i][0].record()
-        g.mx(a, bt, Cs[i % copies], sa, sb)
+        g.mx(a, bt, Cs[i % copies], sa, sb, fmt=fmt)
         ev[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = np.array([x.elapsed_time(y) for x, y in ev])
     plan = b.tg.tile_gemm_plan_mx(w.M, w.N, w.K, 256)
-    res = {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "format": "MXFP8 (E4M3, E8M0 / 32)",
+    res = {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+           "format": "MXFP4 (E2M1, E8M0 / 32)" if w.fmt == "e2m1" else "MXFP8 (E4M3, E8M0 / 32)",
            "out": out, "wall_ms_per_step": 1e3 * wall / steps,
            "kernel_ms_mean": float(per.mean()), "kernel_ms_median": float(np.median(per)),
            "kernel_ms_min": float(per.min()), "kernel_ms_max": float(per.max()),
@@ -259,16 +263,16 @@ def time_mx_workload(b, w, steps, warmup):
     mean_s = res["kernel_ms_mean"] * 1e-3
     res["tflops"] = w.flops / mean_s / 1e12
     res["gbs"] = w.algorithmic_bytes(out) / mean_s / 1e9
-    hbm = w.name.startswith("mx_decode")
+    hbm = w.name.endswith("decode")
     res["roofline"] = ({"bound": "hbm", "achieved": round(res["gbs"], 1), "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": round(res["gbs"] / PEAK_HBM_GBS, 4),
                         "traffic": measured_traffic(w.name)} if hbm else
                        {"bound": "mfma", "achieved": round(res["tflops"], 1),
-                        "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(res["tflops"] / PEAK_FP8_TFLOPS, 4),
+                        "peak": peak, "unit": "TFLOP/s",
+                        "frac": round(res["tflops"] / peak, 4),
                         "traffic": measured_traffic(w.name)})
     log(f"[bench] {w.name}: mean {res['kernel_ms_mean'] * 1e3:.1f} us -> {res['tflops']:.1f} "
-        f"TFLOP/s ({100 * res['tflops'] / PEAK_FP8_TFLOPS:.1f}% of fp8 MFMA), {res['gbs']:.0f} GB/s")
+        f"TFLOP/s ({100 * res['tflops'] / peak:.1f}% of {w.fmt} MFMA), {res['gbs']:.0f} GB/s")
     del sets, Cs
     torch.cuda.empty_cache()
     return res

@@ -155,21 +155,21 @@ tile_gemm_status_t tile_gemm_run_epilogue(tile_gemm_t h, const void* A, const vo
                                           tile_gemm_act_t act, void* stream);
 
 /*
- * Microscaled FP8 product (MXFP8), the low-precision GEMM the TorchInductor
- * page measures beside bf16 ("TorchInductor ganha suporte a GEMMs de alta
+ * Microscaled FP8 / FP4 product (MXFP8, MXFP4), the low-precision GEMMs the
+ * TorchInductor page measures beside bf16 ("TorchInductor ganha suporte a GEMMs de alta
  * performance com CuteDSL", its MXFP8 benchmark paragraph). The format is
- * read as OCP Microscaling (MX) v1.0: elements are FP8 E4M3 bytes, and every
- * 32 consecutive elements of a row along K share one E8M0 scale byte (value
- * 2^(e - 127); 255 is NaN).
+ * read as OCP Microscaling (MX) v1.0: elements are FP8 E4M3 bytes (or FP4
+ * E2M1 nibbles, see TILE_GEMM_MX_E2M1), and every 32 consecutive elements of a
+ * row along K share one E8M0 scale byte (value 2^(e - 127); 255 is NaN).
  *
  *   C[i][j] = sum_k (sa[i][k/32] * a[i][k]) * (sb[j][k/32] * b[j][k])
  *
- * A is M x K bytes, row-major (strides a_m >= K, a_k = 1, in bytes). B is
+ * For E4M3, A is M x K bytes, row-major (strides a_m >= K, a_k = 1, in bytes). B is
  * given as its N x K transpose, K-contiguous (b_k = 1, b_n >= K, in bytes):
  * the layout in which weight matrices are usually stored. a_scale is M rows
  * and b_scale N rows of `scale_stride` bytes (a multiple of 4, >= K/32), the
- * scale of element k of a row at byte k/32. K must be a multiple of 64
- * (TILE_GEMM_ERR_BAD_SHAPE otherwise). C, dtype, bias and act (not
+ * scale of element k of a row at byte k/32. K must be a multiple of 64 for
+ * E4M3 and of 128 for E2M1 (TILE_GEMM_ERR_BAD_SHAPE otherwise). C, dtype, bias and act (not
  * TILE_GEMM_ACT_SWIGLU) are as for tile_gemm_run_epilogue; accumulation is
  * fp32 in ascending K, one owner per output tile, each element written once.
  * A, B 16-byte aligned with 16-byte leading dimensions; scales 4-byte aligned.
@@ -177,7 +177,10 @@ tile_gemm_status_t tile_gemm_run_epilogue(tile_gemm_t h, const void* A, const vo
  * overlap none of them. Enqueue-only, allocates nothing.
  */
 typedef enum {
-  TILE_GEMM_MX_E4M3 = 0  /* MXFP8: E4M3 elements, E8M0 scales per 32 */
+  TILE_GEMM_MX_E4M3 = 0, /* MXFP8: E4M3 elements, E8M0 scales per 32 */
+  TILE_GEMM_MX_E2M1 = 1  /* MXFP4: E2M1 elements, two per byte (the lower K index in
+                            the low nibble), E8M0 scales per 32; rows of A and B are
+                            K/2 bytes, strides in bytes; K a multiple of 128 */
 } tile_gemm_mx_format_t;
 
 tile_gemm_status_t tile_gemm_run_mx(tile_gemm_t h, const void* A, const void* B, void* C,

@@ -41,14 +41,20 @@ def mx_config_table():
     return [tuple(int(v) for v in r) for r in rows]
 
 
+FMTS = {"e4m3": tg.MX_E4M3, "e2m1": tg.MX_E2M1}
+
+
 class MxCase:
-    def __init__(self, M, N, K, dist="normal", seed=0, pad=16, b_scale=1.0):
-        self.M, self.N, self.K = M, N, K
-        lk = K + pad                                   # padded rows (a multiple of 16)
-        A, sA = synth.draw_mx(M, lk, dist, 2 * seed + 1)
-        Bt, sB = synth.draw_mx(N, lk, dist, 2 * seed + 2, b_scale)
+    def __init__(self, M, N, K, dist="normal", seed=0, pad=16, b_scale=1.0, fmt="e4m3"):
+        self.M, self.N, self.K, self.fmt = M, N, K, fmt
+        fp4 = fmt == "e2m1"
+        kb = K // 2 if fp4 else K                      # bytes of K in a row
+        lk = K + (2 * pad if fp4 else pad)             # padded rows (16 more bytes)
+        A, sA = synth.draw_mx(M, lk, dist, 2 * seed + 1, fmt=fmt)
+        Bt, sB = synth.draw_mx(N, lk, dist, 2 * seed + 2, b_scale, fmt=fmt)
         ls = synth.mx_scale_stride(K)
-        self.A, self.Bt = A[:, :K], Bt[:, :K]
+        self.A, self.Bt = A[:, :kb], Bt[:, :kb]
+        K = kb
         self.sA, self.sB = sA[:, :ls], sB[:, :ls]
         dA = torch.from_numpy(A).cuda()
         dB = torch.from_numpy(Bt).cuda()
@@ -59,12 +65,12 @@ class MxCase:
 
     def ref(self):
         if self._ref is None:
-            self._ref = oracle.mx.mx_gemm(self.A, self.sA, self.Bt, self.sB, self.K)
+            self._ref = oracle.mx.mx_gemm(self.A, self.sA, self.Bt, self.sB, self.K, self.fmt)
         return self._ref
 
     def bound(self):
         if getattr(self, "_bound", None) is None:
-            self._bound = oracle.mx.mx_bound(self.A, self.sA, self.Bt, self.sB, self.K)
+            self._bound = oracle.mx.mx_bound(self.A, self.sA, self.Bt, self.sB, self.K, self.fmt)
         return self._bound
 
     def out(self, dtype, pad=8):
@@ -86,7 +92,7 @@ def _run_and_check(g, case, flags=0, integer=False, label=""):
         store, out = case.out(dt)
         cnt = torch.zeros((case.M, case.N), dtype=torch.int32, device="cuda")
         g.mx(case.A_dev, case.Bt_dev, out, case.sA_dev, case.sB_dev, counts=cnt,
-             flags=flags | tg.DEBUG_COUNT_WRITES)
+             flags=flags | tg.DEBUG_COUNT_WRITES, fmt=FMTS[case.fmt])
         torch.cuda.synchronize()
         rep = _check(host_out(out), C, D, dt == torch.bfloat16, integer)
         assert rep.ok, f"{label} {dt}: {rep}"
@@ -94,31 +100,37 @@ def _run_and_check(g, case, flags=0, integer=False, label=""):
         assert torch.isnan(store[:, case.N:].float()).all(), f"{label}: store outside C"
 
 
+@pytest.mark.parametrize("fmt", sorted(FMTS))
 @pytest.mark.parametrize("cfg", range(tg.N_MX_CONFIGS))
-@pytest.mark.parametrize("K", [64, 192, 256])
-def test_mx_configs(g, cfg, K):
+@pytest.mark.parametrize("slabs", [1, 3, 4, 19])
+def test_mx_configs(g, fmt, cfg, slabs):
+    """Every configuration and format; 19 slabs run the steady loop and reuse
+    the LDS scale windows."""
     bm, bn = mx_config_table()[cfg]
     M, N = 2 * bm + 37, 2 * bn + 19
-    print(f"[mx cfg {cfg} {M}x{N}x{K}]", flush=True)
-    _run_and_check(g, MxCase(M, N, K, seed=cfg * 10 + K), tg.DEBUG_FORCE_TILE(cfg),
-                   label=f"cfg {cfg}")
+    K = slabs * (128 if fmt == "e2m1" else 64)
+    print(f"[mx {fmt} cfg {cfg} {M}x{N}x{K}]", flush=True)
+    _run_and_check(g, MxCase(M, N, K, seed=cfg * 10 + slabs, fmt=fmt), tg.DEBUG_FORCE_TILE(cfg),
+                   label=f"{fmt} cfg {cfg}")
 
 
+@pytest.mark.parametrize("fmt", sorted(FMTS))
 @pytest.mark.parametrize("cfg", range(tg.N_MX_CONFIGS))
-def test_mx_configs_integer_exact(g, cfg):
+def test_mx_configs_integer_exact(g, fmt, cfg):
     bm, bn = mx_config_table()[cfg]
-    M, N, K = bm + 5, bn + 3, 320
-    print(f"[mx int cfg {cfg} {M}x{N}x{K}]", flush=True)
-    _run_and_check(g, MxCase(M, N, K, dist="int3", seed=50 + cfg), tg.DEBUG_FORCE_TILE(cfg),
-                   integer=True, label=f"int cfg {cfg}")
+    M, N, K = bm + 5, bn + 3, 640
+    print(f"[mx int {fmt} cfg {cfg} {M}x{N}x{K}]", flush=True)
+    _run_and_check(g, MxCase(M, N, K, dist="int3", seed=50 + cfg, fmt=fmt),
+                   tg.DEBUG_FORCE_TILE(cfg), integer=True, label=f"int {fmt} cfg {cfg}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (17, 33, 128), (300, 520, 576), (16, 4096, 1024),
+@pytest.mark.parametrize("fmt", sorted(FMTS))
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (17, 33, 128), (300, 520, 640), (16, 4096, 1024),
                                    (1000, 1000, 1024), (130, 130, 0)])
-def test_mx_planner_shapes(g, M, N, K):
-    print(f"[mx planner {M}x{N}x{K}]", flush=True)
-    case = MxCase(M, N, K, seed=M + N + K)
-    _run_and_check(g, case, label=f"{M}x{N}x{K}")
+def test_mx_planner_shapes(g, fmt, M, N, K):
+    print(f"[mx planner {fmt} {M}x{N}x{K}]", flush=True)
+    case = MxCase(M, N, K, seed=M + N + K, fmt=fmt)
+    _run_and_check(g, case, label=f"{fmt} {M}x{N}x{K}")
 
 
 def test_mx_several_tiles_per_workgroup(g):
@@ -174,6 +186,7 @@ def test_mx_rejects_bad_arguments(g):
 
 @pytest.mark.parametrize("name", sorted(synth.MX_WORKLOADS))
 def test_mx_workload_sampled(g, name):
+    fmt = synth.MX_WORKLOADS[name].fmt
     """Full size, in the launch configuration the benchmark times: sampled
     elements against the oracle's one-element sums."""
     w = synth.MX_WORKLOADS[name]
@@ -184,11 +197,11 @@ def test_mx_workload_sampled(g, name):
     rng = np.random.default_rng(13)
     ii = np.concatenate([rng.integers(0, w.M, 200), [0, w.M - 1, 0, w.M - 1]])
     jj = np.concatenate([rng.integers(0, w.N, 200), [0, 0, w.N - 1, w.N - 1]])
-    c, d = oracle.mx.mx_gemm_at(ops.A, ops.sA, ops.Bt, ops.sB, w.K, ii, jj)
-    t = oracle.mx.mx_bound_at(ops.A, ops.sA, ops.Bt, ops.sB, w.K, ii, jj)
+    c, d = oracle.mx.mx_gemm_at(ops.A, ops.sA, ops.Bt, ops.sB, w.K, ii, jj, fmt)
+    t = oracle.mx.mx_bound_at(ops.A, ops.sA, ops.Bt, ops.sB, w.K, ii, jj, fmt)
     for dt in (torch.float32, torch.bfloat16):
         C = torch.full((w.M, w.N), float("nan"), dtype=dt, device="cuda")
-        g.mx(A, Bt, C, sA, sB)
+        g.mx(A, Bt, C, sA, sB, fmt=FMTS[fmt])
         torch.cuda.synchronize()
         out = host_out(C)
         assert not np.isnan(out.astype(np.float32) if dt == torch.float32 else

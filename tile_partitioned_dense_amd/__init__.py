@@ -16,7 +16,7 @@ fallback path.
 
 __all__ = ["tile_gemm_create", "tile_gemm_run", "tile_gemm_run_debug", "tile_gemm_run_epilogue",
            "tile_gemm_check_epilogue", "Act", "tile_gemm_destroy", "tile_gemm_run_mx",
-           "tile_gemm_check_mx", "tile_gemm_plan_mx", "N_MX_CONFIGS", "MX_E4M3", "VARIANT_MX",
+           "tile_gemm_check_mx", "tile_gemm_plan_mx", "N_MX_CONFIGS", "MX_E4M3", "MX_E2M1", "VARIANT_MX",
            "tile_gemm_status_str", "tile_gemm_check_args", "tile_gemm_plan",
            "tile_gemm_tile_of", "TileGemm", "TileGemmError", "Status", "Dtype",
            "Strides", "Plan", "library_path", "load_library", "last_error_detail",

@@ -63,8 +63,9 @@ DEBUG_ONE_TILE_PER_WG = 0x7F << 24
 
 
 N_TILE_CONFIGS = 14
-N_MX_CONFIGS = 2
+N_MX_CONFIGS = 3
 MX_E4M3 = 0
+MX_E2M1 = 1
 N_SKINNY_CONFIGS = 6
 
 VARIANT_NONE, VARIANT_TILE, VARIANT_SKINNY, VARIANT_MX = 0, 1, 2, 3
@@ -272,15 +273,18 @@ def tile_gemm_run_debug(h, A, B, C, counts=None, flags=0, M=None, N=None, K=None
     return Status(st)
 
 
-def _mx_operands(A, Bt, C, a_scale, b_scale):
+def _mx_operands(A, Bt, C, a_scale, b_scale, fmt=MX_E4M3):
     """Pointers, shape and strides of an MX call from torch tensors: A (M x K)
-    and Bt (N x K) uint8 E4M3 codes, scales uint8 (M x ls) and (N x ls)."""
+    and Bt (N x K) uint8 E4M3 codes (E2M1: M x K/2 and N x K/2 packed bytes),
+    scales uint8 (M x ls) and (N x ls)."""
     import torch
     for name, t in (("A", A), ("Bt", Bt), ("a_scale", a_scale), ("b_scale", b_scale)):
         if t.dtype != torch.uint8 or t.dim() != 2:
             raise TypeError(f"{name} must be a 2-D uint8 tensor")
     M, K = A.shape
     N, K2 = Bt.shape
+    if fmt == MX_E2M1:
+        K, K2 = 2 * K, 2 * K2
     if K2 != K or tuple(C.shape) != (M, N):
         raise ValueError(f"shapes do not chain: A{tuple(A.shape)} Bt{tuple(Bt.shape)} C{tuple(C.shape)}")
     if a_scale.shape[0] != M or b_scale.shape[0] != N or a_scale.stride(1) != 1 \
@@ -297,13 +301,13 @@ def _mx_operands(A, Bt, C, a_scale, b_scale):
 
 
 def tile_gemm_run_mx(h, A, Bt, C, a_scale, b_scale, bias=None, act=Act.NONE, stream=None,
-                     counts=None, flags=0, check: bool = True):
-    """Enqueue the MXFP8 product C := act((sa * A) . (sb * Bt)^T + bias) (torch tensors)."""
-    M, N, K, s, ls, dt = _mx_operands(A, Bt, C, a_scale, b_scale)
+                     counts=None, flags=0, check: bool = True, fmt=MX_E4M3):
+    """Enqueue the MX product C := act((sa * A) . (sb * Bt)^T + bias) (torch tensors)."""
+    M, N, K, s, ls, dt = _mx_operands(A, Bt, C, a_scale, b_scale, fmt)
     bp = bias.data_ptr() if _is_tensor(bias) else bias
     lib = load_library()
     args = (h, A.data_ptr(), Bt.data_ptr(), C.data_ptr(), M, N, K, ctypes.byref(s),
-            a_scale.data_ptr(), b_scale.data_ptr(), ls, MX_E4M3, dt, bp, int(act),
+            a_scale.data_ptr(), b_scale.data_ptr(), ls, int(fmt), dt, bp, int(act),
             _stream_ptr(stream, C))
     if flags or counts is not None:
         cnt = counts.data_ptr() if _is_tensor(counts) else counts
@@ -376,11 +380,11 @@ class TileGemm:
                                    act=Act.NONE if act is None else act)
 
     def mx(self, A, Bt, C, a_scale, b_scale, bias=None, act=None, stream=None, counts=None,
-           flags=0):
-        """MXFP8 product (tile_gemm_run_mx) into C."""
+           flags=0, fmt=MX_E4M3):
+        """MX product (tile_gemm_run_mx) into C."""
         return tile_gemm_run_mx(self.handle, A, Bt, C, a_scale, b_scale, bias=bias,
                                 act=Act.NONE if act is None else act, stream=stream,
-                                counts=counts, flags=flags)
+                                counts=counts, flags=flags, fmt=fmt)
 
     def close(self):
         if self.handle is not None:

@@ -8,23 +8,28 @@
 
 namespace tg {
 
-template <int CFG, bool OB, bool DB>
+template <int CFG, int FMT, bool OB, bool DB>
 const void* mx_fn() {
   constexpr MxConfig c = kMxConfigs[CFG];
-  return reinterpret_cast<const void*>(&mx_gemm_kernel<c.bm, c.bn, c.wm, c.wn, c.stages, OB, DB>);
+  return reinterpret_cast<const void*>(&mx_gemm_kernel<c.bm, c.bn, c.wm, c.wn, c.stages, FMT, OB, DB>);
+}
+
+template <int CFG, int FMT>
+const void* mx_fn_out(const Variant& v) {
+  if (v.out_bf16) return v.debug ? mx_fn<CFG, FMT, true, true>() : mx_fn<CFG, FMT, true, false>();
+  return v.debug ? mx_fn<CFG, FMT, false, true>() : mx_fn<CFG, FMT, false, false>();
 }
 
 template <int CFG>
-hipError_t launch_mx(const MxArgs& a, int64_t grid_wgs, const Variant& v, hipStream_t stream) {
+hipError_t launch_mx(const MxArgs& a, int fmt, int64_t grid_wgs, const Variant& v,
+                     hipStream_t stream) {
   constexpr MxConfig c = kMxConfigs[CFG];
   const dim3 grid((unsigned)grid_wgs);
   const dim3 block(c.wm * c.wn * 64);
-  const void* fn;
-  if (v.out_bf16) fn = v.debug ? mx_fn<CFG, true, true>() : mx_fn<CFG, true, false>();
-  else fn = v.debug ? mx_fn<CFG, false, true>() : mx_fn<CFG, false, false>();
+  const void* fn = fmt == kMxE2M1 ? mx_fn_out<CFG, kMxE2M1>(v) : mx_fn_out<CFG, kMxE4M3>(v);
   return launch_raw(fn, grid, block, a, stream);
 }
 
-template hipError_t launch_mx<TG_MX_CONFIG>(const MxArgs&, int64_t, const Variant&, hipStream_t);
+template hipError_t launch_mx<TG_MX_CONFIG>(const MxArgs&, int, int64_t, const Variant&, hipStream_t);
 
 }  // namespace tg

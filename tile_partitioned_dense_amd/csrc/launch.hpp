@@ -25,7 +25,7 @@ template <int CFG>
 hipError_t launch_skinny(const SkinnyArgs& a, int64_t grid, const Variant& v, hipStream_t stream);
 
 template <int CFG>
-hipError_t launch_mx(const MxArgs& a, int64_t grid, const Variant& v, hipStream_t stream);
+hipError_t launch_mx(const MxArgs& a, int fmt, int64_t grid, const Variant& v, hipStream_t stream);
 
 // Launch through hipLaunchKernel so the launch status comes back directly
 // rather than through the thread's sticky last-error slot.

@@ -1,4 +1,4 @@
-// mx_kernel.hpp -- microscaled FP8 (MXFP8) tile kernel for gfx950.
+// mx_kernel.hpp -- microscaled FP8 / FP4 (MXFP8, MXFP4) tile kernel for gfx950.
 //
 // The low-precision GEMMs the TorchInductor page measures beside bf16
 // ("TorchInductor ganha suporte a GEMMs de alta performance com CuteDSL", its
@@ -22,9 +22,15 @@
 // covers two slabs; it is shifted by 8 (l / 32) bits per lane and the
 // instruction's byte select picks byte 0 or 2 by slab parity. Scales travel
 // like the operands: 16 bytes of every row of the tile (the scales of 8
-// slabs) are loaded straight into a double-buffered LDS window together with
-// the first slab they cover, so their loads are ordered with the slabs'
-// and need no wait of their own.
+// slabs) are loaded straight into a ring of LDS windows together with the
+// first slab they cover, so their loads are ordered with the slabs' and need
+// no wait of their own.
+//
+// MXFP4 (E2M1, two elements per byte, the lower K index in the low nibble)
+// uses the same 64-byte rows, now 128 K values per slab: each 16-byte LDS
+// chunk is one 32-element block and one instruction operand, so a slab is two
+// instructions per 32 x 32 block (chunks l / 32, then 2 + l / 32), and a scale
+// dword covers one slab (byte 2 m + l / 32 for its instruction m).
 //
 // K advances in ascending order (fp32 accumulation, no split-K), so results
 // are bit-identical run to run.
@@ -52,23 +58,40 @@ struct MxArgs {
 
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
+// Element formats of the MX kernel (the C ABI's tile_gemm_mx_format_t).
+constexpr int kMxE4M3 = 0, kMxE2M1 = 1;
+
 // One 32 x 32 x 64 scaled step of a C block held transposed (as mma()): the B
-// fragment is the instruction's first operand. OPSEL picks the scale byte.
-template <int OPSEL>
+// fragment is the instruction's first operand. OPSEL picks the scale byte;
+// HW is the instruction's element-format code (0 E4M3, 4 E2M1).
+template <int OPSEL, int HW>
 __device__ __forceinline__ floatx16 mma_mx(const i32x8& a_frag, const i32x8& b_frag, int a_scale,
                                            int b_scale, const floatx16& acc) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b_frag, a_frag, acc, 0, 0, OPSEL, b_scale,
-                                                         OPSEL, a_scale);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b_frag, a_frag, acc, HW, HW, OPSEL,
+                                                         b_scale, OPSEL, a_scale);
 }
 
-template <int BM, int BN, int WM, int WN, int NST, bool OUT_BF16, bool DEBUG>
+// The 16 bytes of half H (0: LDS chunk l / 32, 1: chunk 2 + l / 32) of a
+// staged fragment as an E2M1 operand: 32 four-bit elements, one MX block.
+template <int H>
+__device__ __forceinline__ i32x8 fp4_half(const i32x8& f) {
+  if constexpr (H == 0) return i32x8{f[0], f[1], f[2], f[3], 0, 0, 0, 0};
+  else return i32x8{f[4], f[5], f[6], f[7], 0, 0, 0, 0};
+}
+
+template <int BM, int BN, int WM, int WN, int NST, int FMT, bool OUT_BF16, bool DEBUG>
 __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
-  static_assert(NST >= 3 && NST <= 6, "ring depth");
+  static_assert(NST >= 4 && NST <= 12, "ring depth");
+  static_assert(FMT == 0 || FMT == 1, "E4M3 or E2M1 elements");
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
-  constexpr int BKB = 64;                 // K bytes (= elements) per slab
+  constexpr bool FP4 = FMT == kMxE2M1;
+  constexpr int HW = FP4 ? 4 : 0;         // the instruction's format code
+  constexpr int BKB = 64;                 // bytes per row and slab
+  constexpr int KPS = FP4 ? 128 : 64;     // K elements per slab
+  constexpr int SPW = FP4 ? 4 : 8;        // slabs per scale window (16 scale bytes per row)
   constexpr int A_BYTES = BM * BKB;
   constexpr int B_BYTES = BN * BKB;
   constexpr int STAGE = A_BYTES + B_BYTES;
@@ -78,10 +101,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
   constexpr int NDMA = A_PER + B_PER;     // DMA instructions per wave and slab
   constexpr int RING = NST * STAGE;
   constexpr int SWIN = (BM + BN) * 16;    // one scale window: 16 bytes per row
+  // Window w + NWB reuses window w's buffer. It is loaded with slab SPW (w +
+  // NWB), issued at step SPW (w + NWB) - (NST - 1), which must come after the
+  // step that last reads window w (SPW (w + 1) - 1 at the latest).
+  constexpr int NWB = 1 + (NST - 1 + SPW - 1) / SPW;
+  static_assert(SPW * (NWB - 1) >= NST - 1, "a scale window is reloaded only after its last use");
   static_assert(BM % 64 == 0 && BN % 64 == 0, "scale windows are whole KiB per wave instruction");
   constexpr int SA_DMA = BM / 64, SB_DMA = BN / 64;   // window loads (1 KiB each)
 
-  __shared__ __attribute__((aligned(1024))) uint4 smem[(RING + 2 * SWIN) / 16];
+  __shared__ __attribute__((aligned(1024))) uint4 smem[(RING + NWB * SWIN) / 16];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -90,7 +118,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
   const int lrow = lane & 31, lgrp = lane >> 5;
   const int M = p.M, N = p.N, K = p.K;
   const int64_t lda = p.lda, ldb = p.ldb;
-  const int nk = K / BKB;                 // K is a multiple of 64
+  const int nk = K / KPS;                 // K is a multiple of KPS
+  const int kbytes = FP4 ? K / 2 : K;     // bytes of K in a row
 
   // per-lane DMA source offsets within a slab (bytes), fixed for the kernel
   uint32_t voA[A_PER], voB[B_PER];
@@ -122,9 +151,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
     tile_of(p.map, wg, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const char* a_panel = reinterpret_cast<const char*>(p.A + (int64_t)m0 * lda);
-    const int64_t a_bytes = K > 0 ? ((int64_t)(M - 1) * lda + K) - (int64_t)m0 * lda : 0;
+    const int64_t a_bytes = K > 0 ? ((int64_t)(M - 1) * lda + kbytes) - (int64_t)m0 * lda : 0;
     const char* b_panel = reinterpret_cast<const char*>(p.B + (int64_t)n0 * ldb);
-    const int64_t b_bytes = K > 0 ? ((int64_t)(N - 1) * ldb + K) - (int64_t)n0 * ldb : 0;
+    const int64_t b_bytes = K > 0 ? ((int64_t)(N - 1) * ldb + kbytes) - (int64_t)n0 * ldb : 0;
 
     const int sh = 8 * lgrp;
     // scale windows: rows of both scale arrays with exact extents (rows past
@@ -132,10 +161,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
     const i32x4 rsSA = make_rsrc(p.sA, (int64_t)M * p.ls);
     const i32x4 rsSB = make_rsrc(p.sB, (int64_t)N * p.ls);
     const uint32_t swin0 = lds0 + RING;
-    // Load window w (16 bytes of each of the tile's rows, scales of slabs
-    // 8 w .. 8 w + 7) into buffer w % 2: instruction q covers rows 64 q ..
+    // Load window w (16 bytes of each of the tile's rows, the scales of slabs
+    // SPW w .. SPW w + SPW - 1) into buffer w % NWB: instruction q covers rows
+    // 64 q ..
     auto issue_window = [&](int w) {
-      const uint32_t dst = swin0 + (uint32_t)((w & 1) * SWIN);
+      const uint32_t dst = swin0 + (uint32_t)((w % NWB) * SWIN);
 #pragma unroll
       for (int q = 0; q < SA_DMA; ++q)
         if (q % NW == wave)
@@ -149,7 +179,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
     // The window of slabs 8 w .. goes out just before slab 8 w's own loads, so
     // any wait that covers slab 8 w covers it too.
     auto issue_slab = [&](int s) {
-      if ((s & 7) == 0) issue_window(s >> 3);
+      if (s % SPW == 0) issue_window(s / SPW);
       const uint32_t st = (uint32_t)(s % NST) * STAGE;
       const i32x4 rsA = make_rsrc(a_panel + (int64_t)s * BKB, a_bytes - (int64_t)s * BKB);
       const i32x4 rsB = make_rsrc(b_panel + (int64_t)s * BKB, b_bytes - (int64_t)s * BKB);
@@ -193,10 +223,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
         bfr[slot][j] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
       }
     };
-    // scales of slabs s, s + 1 (s even) from window s / 8, landed with slab
-    // 8 (s / 8) before the barrier that made that slab readable
+    // Scales from window s / SPW, landed with its first slab before the
+    // barrier that made that slab readable. E4M3: the dword of slabs s, s + 1
+    // (s even), byte 2 (s % 2) + l / 32 after the shift; E2M1: the dword of
+    // slab s (its four blocks), byte 2 m + l / 32 for the slab's MFMA m.
     auto take_scales = [&](int s) {
-      const uint32_t wb = swin0 + (uint32_t)(((s >> 3) & 1) * SWIN) + (uint32_t)(4 * ((s & 7) >> 1));
+      const int dw = FP4 ? (s % SPW) : ((s % SPW) >> 1);
+      const uint32_t wb = swin0 + (uint32_t)(((s / SPW) % NWB) * SWIN) + (uint32_t)(4 * dw);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const uint32_t v = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
@@ -210,16 +243,24 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
         scb[j] = (int)(v >> sh);
       }
     };
-    auto mfmas = [&](auto opsel_c, int slot) {
-      constexpr int OPSEL = decltype(opsel_c)::value;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = mma_mx<OPSEL>(af[slot][i], bfr[slot][j], sca[i], scb[j], acc[i][j]);
+    // MFMA k of a slab (k < NMFMA): block (i, j) and, for E2M1, half m
+    constexpr int NBLK = FM * FN;
+    constexpr int NMFMA = FP4 ? 2 * NBLK : NBLK;
+    auto mfma_k = [&](auto k_c, auto par_c, int slot) {
+      constexpr int k = decltype(k_c)::value, PAR = decltype(par_c)::value;
+      constexpr int b = k % NBLK, i = b / FN, j = b % FN;
+      if constexpr (FP4) {
+        constexpr int m = k / NBLK;
+        acc[i][j] = mma_mx<2 * m, HW>(fp4_half<m>(af[slot][i]), fp4_half<m>(bfr[slot][j]), sca[i],
+                                      scb[j], acc[i][j]);
+      } else {
+        acc[i][j] = mma_mx<2 * PAR, HW>(af[slot][i], bfr[slot][j], sca[i], scb[j], acc[i][j]);
+      }
+    };
+    auto mfmas = [&](auto par_c, int slot) {
+      static_for<0, NMFMA>([&](auto k_c) { mfma_k(k_c, par_c, slot); });
     };
     constexpr int NREAD = 2 * (FM + FN);
-    constexpr int NMFMA = FM * FN;
     constexpr int RPM = (NREAD + NMFMA - 1) / NMFMA;
     auto interleave = [&]() {
 #pragma unroll
@@ -241,7 +282,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
     // s - 1 (read before the last barrier) takes slab s + NST - 1.
     auto step = [&](int s, auto par_c) {
       constexpr int PAR = decltype(par_c)::value;  // s % 2
-      if (PAR == 0) take_scales(s);
+      if (FP4 || PAR == 0) take_scales(s);
       if (s + 1 < nk) {
         const int issued_after = (nk - 1 < s + NST - 2 ? nk - 1 : s + NST - 2) - (s + 1);
         wait_after(issued_after);
@@ -249,7 +290,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
         if (s + NST - 1 < nk) issue_slab(s + NST - 1);
       }
       __builtin_amdgcn_sched_barrier(0);
-      mfmas(std::integral_constant<int, 2 * PAR>{}, PAR);
+      mfmas(par_c, PAR);
       // unconditional so it interleaves with the MFMAs; after the last slab
       // it reads a stale stage (in bounds) whose values are never used
       read_frags(s + 1, PAR ^ 1);
@@ -278,11 +319,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
     auto dma_slot = [](int t, int n) constexpr { return ((2 * t + 1) * NMFMA) / (2 * n); };
     auto step_full = [&](int s, auto par_c) {
       constexpr int PAR = decltype(par_c)::value;
-      if (PAR == 0) take_scales(s);
+      if (FP4 || PAR == 0) take_scales(s);
       wait_vmcnt<((NST - 3) * NDMA < 63 ? (NST - 3) * NDMA : 63)>();
       block_barrier();
       const int sn = s + NST - 1;
-      if ((sn & 7) == 0) issue_window(sn >> 3);
+      if (sn % SPW == 0) issue_window(sn / SPW);
       const uint32_t stn = (uint32_t)(sn % NST) * STAGE;
       const i32x4 rsA = make_rsrc(a_panel + (int64_t)sn * BKB, a_bytes - (int64_t)sn * BKB);
       const i32x4 rsB = make_rsrc(b_panel + (int64_t)sn * BKB, b_bytes - (int64_t)sn * BKB);
@@ -290,8 +331,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, NMFMA>([&](auto k_c) {
         constexpr int k = decltype(k_c)::value;
-        acc[k / FN][k % FN] = mma_mx<2 * PAR>(af[PAR][k / FN], bfr[PAR][k % FN], sca[k / FN],
-                                             scb[k % FN], acc[k / FN][k % FN]);
+        mfma_k(k_c, par_c, PAR);
         static_for<0, UPM>([&](auto r_c) {
           constexpr int idx = k * UPM + decltype(r_c)::value;
           if constexpr (idx < NUNIT) read_unit(so, PAR ^ 1, std::integral_constant<int, idx>{});

@@ -92,10 +92,11 @@ struct MxConfig {
   int bm, bn, wm, wn, stages;
   float eff;
 };
-constexpr int kNumMxConfigs = 2;
+constexpr int kNumMxConfigs = 3;
 constexpr MxConfig kMxConfigs[kNumMxConfigs] = {
     {256, 256, 2, 2, 4, 1.00f},  // 0: 4 waves of 128x128
     {128, 128, 2, 2, 4, 0.70f},  // 1: 4 waves of 64x64
+    {64, 128, 2, 2, 12, 0.50f},  // 2: 4 waves of 32x64, 12 stages: few rows, weight streaming
 };
 constexpr int kMxBK = 64;  // K per slab of the MX kernel (a multiple of it is required)
 

@@ -210,15 +210,16 @@ hipError_t dispatch_skinny(int cfg, const tg::SkinnyArgs& a, int64_t grid, const
 }
 static_assert(tg::kNumSkinnyConfigs == 6, "dispatch_skinny covers every skinny configuration");
 
-hipError_t dispatch_mx(int cfg, const tg::MxArgs& a, int64_t grid, const tg::Variant& v,
+hipError_t dispatch_mx(int cfg, const tg::MxArgs& a, int fmt, int64_t grid, const tg::Variant& v,
                        hipStream_t st) {
   switch (cfg) {
-    case 0: return tg::launch_mx<0>(a, grid, v, st);
-    case 1: return tg::launch_mx<1>(a, grid, v, st);
+    case 0: return tg::launch_mx<0>(a, fmt, grid, v, st);
+    case 1: return tg::launch_mx<1>(a, fmt, grid, v, st);
+    case 2: return tg::launch_mx<2>(a, fmt, grid, v, st);
   }
   return hipErrorInvalidValue;
 }
-static_assert(tg::kNumMxConfigs == 2, "dispatch_mx covers every MX configuration");
+static_assert(tg::kNumMxConfigs == 3, "dispatch_mx covers every MX configuration");
 
 // Checks of tile_gemm_run_mx's arguments (see the header).
 tile_gemm_status_t check_mx(const void* A, const void* B, const void* C, int64_t M, int64_t N,
@@ -228,13 +229,17 @@ tile_gemm_status_t check_mx(const void* A, const void* B, const void* C, int64_t
   g_detail[0] = '\0';
   if (dtype != TILE_GEMM_BF16_TO_F32 && dtype != TILE_GEMM_BF16_TO_BF16)
     return fail(TILE_GEMM_ERR_DTYPE, "dtype: unknown value %d", dtype);
-  if (fmt != TILE_GEMM_MX_E4M3) return fail(TILE_GEMM_ERR_DTYPE, "fmt: unknown MX format %d", fmt);
+  if (fmt != TILE_GEMM_MX_E4M3 && fmt != TILE_GEMM_MX_E2M1)
+    return fail(TILE_GEMM_ERR_DTYPE, "fmt: unknown MX format %d", fmt);
+  const bool fp4 = fmt == TILE_GEMM_MX_E2M1;
+  const int kps = fp4 ? 2 * tg::kMxBK : tg::kMxBK;  // K elements per 64-byte slab
   if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
     return fail(TILE_GEMM_ERR_BAD_SHAPE, "shape: M=%lld N=%lld K=%lld, each must be in [0, 2^31)",
                 (long long)M, (long long)N, (long long)K);
-  if (K % tg::kMxBK)
-    return fail(TILE_GEMM_ERR_BAD_SHAPE, "K=%lld: the MX product needs K a multiple of %d",
-                (long long)K, tg::kMxBK);
+  if (K % kps)
+    return fail(TILE_GEMM_ERR_BAD_SHAPE, "K=%lld: this MX format needs K a multiple of %d",
+                (long long)K, kps);
+  const int64_t kb = fp4 ? K / 2 : K;  // bytes of K in a row
   if (!s) return fail(TILE_GEMM_ERR_NULL_ARG, "strides: NULL");
   if (act < TILE_GEMM_ACT_NONE || act > TILE_GEMM_ACT_SILU)
     return fail(TILE_GEMM_ERR_EPILOGUE, "act: %d is not available for the MX product", act);
@@ -245,13 +250,15 @@ tile_gemm_status_t check_mx(const void* A, const void* B, const void* C, int64_t
     if (!B) return fail(TILE_GEMM_ERR_NULL_ARG, "B: NULL");
     if (!sa) return fail(TILE_GEMM_ERR_NULL_ARG, "a_scale: NULL");
     if (!sb) return fail(TILE_GEMM_ERR_NULL_ARG, "b_scale: NULL");
-    if (s->a_k != 1 || s->a_m < K)
-      return fail(TILE_GEMM_ERR_BAD_STRIDE, "A strides (a_m=%lld, a_k=%lld): need a_k == 1, a_m >= K",
-                  (long long)s->a_m, (long long)s->a_k);
-    if (s->b_k != 1 || s->b_n < K)
+    if (s->a_k != 1 || s->a_m < kb)
       return fail(TILE_GEMM_ERR_BAD_STRIDE,
-                  "B strides (b_k=%lld, b_n=%lld): the MX product takes B as N x K, b_k == 1, b_n >= K",
-                  (long long)s->b_k, (long long)s->b_n);
+                  "A strides (a_m=%lld, a_k=%lld): need a_k == 1, a_m >= %lld bytes",
+                  (long long)s->a_m, (long long)s->a_k, (long long)kb);
+    if (s->b_k != 1 || s->b_n < kb)
+      return fail(TILE_GEMM_ERR_BAD_STRIDE,
+                  "B strides (b_k=%lld, b_n=%lld): the MX product takes B as N x K, b_k == 1, "
+                  "b_n >= %lld bytes",
+                  (long long)s->b_k, (long long)s->b_n, (long long)kb);
     if (ls < K / 32 || ls % 4)
       return fail(TILE_GEMM_ERR_BAD_STRIDE,
                   "scale_stride=%lld: need a multiple of 4 bytes and >= K/32=%lld", (long long)ls,
@@ -277,7 +284,7 @@ tile_gemm_status_t check_mx(const void* A, const void* B, const void* C, int64_t
       return fail(TILE_GEMM_ERR_MISALIGNED, "B: base or b_n not a multiple of 16 bytes");
     if ((uintptr_t)sa % 4 || (uintptr_t)sb % 4)
       return fail(TILE_GEMM_ERR_MISALIGNED, "scales: base pointers must be 4-byte aligned");
-    const int64_t a_span = (M - 1) * s->a_m + K, b_span = (N - 1) * s->b_n + K;
+    const int64_t a_span = (M - 1) * s->a_m + kb, b_span = (N - 1) * s->b_n + kb;
     if (a_span >= ((int64_t)1 << 32) || b_span >= ((int64_t)1 << 32))
       return fail(TILE_GEMM_ERR_BAD_SHAPE, "A or B spans 4 GiB or more");
     const uintptr_t a0 = (uintptr_t)A, b0 = (uintptr_t)B, s0 = (uintptr_t)sa, t0 = (uintptr_t)sb;
@@ -338,7 +345,8 @@ tile_gemm_status_t run_mx_impl(tile_gemm_t h, const void* A, const void* B, void
   a.bias = bias;
   a.act = act;
   const tg::Variant v{true, dtype == TILE_GEMM_BF16_TO_BF16, instrumented(flags)};
-  const hipError_t e = dispatch_mx(p.config, a, p.grid, v, static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      dispatch_mx(p.config, a, fmt, p.grid, v, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(TILE_GEMM_ERR_HIP, "launch: %s", hipGetErrorString(e));
   return TILE_GEMM_OK;
 }

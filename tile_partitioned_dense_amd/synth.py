@@ -191,17 +191,49 @@ def f64_to_e4m3(y) -> np.ndarray:
     return code | np.signbit(y).astype(np.uint8) << 7
 
 
+_E2M1_INT_CODES = {-3: 0xD, -2: 0xC, -1: 0xA, 0: 0x0, 1: 0x2, 2: 0x4, 3: 0x5}
+
+
+def f64_to_e2m1(y) -> np.ndarray:
+    """Round float64 values to E2M1 codes 0..15 (nearest, ties to even;
+    saturating at +-6). The spacing of E2M1 values is 0.5 below 2, 1 in
+    [2, 4) and 2 in [4, 6]."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.minimum(np.abs(y), 6.0)
+    e = np.maximum(np.floor(np.log2(np.maximum(a, 1.0))), 0.0)
+    q = np.exp2(e - 1.0)
+    v = np.minimum(np.rint(a / q) * q, 6.0)
+    idx = np.searchsorted(np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]), v)
+    return (idx.astype(np.uint8) | (np.signbit(y).astype(np.uint8) << 3)).astype(np.uint8)
+
+
+def pack_fp4(codes) -> np.ndarray:
+    """rows x k E2M1 codes -> rows x ceil(k/2) bytes, the lower K index in the
+    low nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    if c.shape[1] % 2:
+        c = np.pad(c, ((0, 0), (0, 1)))
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
 def mx_scale_stride(k: int) -> int:
     """Bytes per scale row: one per 32 K values, rounded up to a multiple of 4."""
     return (((k + MX_BLOCK - 1) // MX_BLOCK) + 3) // 4 * 4
 
 
-def draw_mx(rows: int, k: int, dist: str, seed: int, scale: float = 1.0):
-    """(codes, scales): rows x k E4M3 codes and rows x mx_scale_stride(k) E8M0
-    bytes (padding bytes 127). Values are drawn like draw() (row-major, in
-    chunks of rows), then quantised per block of 32 as described above."""
+def draw_mx(rows: int, k: int, dist: str, seed: int, scale: float = 1.0, fmt: str = "e4m3"):
+    """(codes, scales): rows x k E4M3 codes (E2M1: rows x k/2 packed bytes) and
+    rows x mx_scale_stride(k) E8M0 bytes (padding bytes 127). Values are drawn
+    like draw() (row-major, in chunks of rows), then quantised per block of 32
+    as described above (E2M1: largest exponent 2, so e = floor(log2 max) - 2)."""
     if dist not in ("normal", "uniform", "int3"):
         raise ValueError(f"unknown distribution {dist!r}")
+    if fmt not in ("e4m3", "e2m1"):
+        raise ValueError(f"unknown MX element format {fmt!r}")
+    fp4 = fmt == "e2m1"
+    emax = 2.0 if fp4 else 8.0
+    encode = f64_to_e2m1 if fp4 else f64_to_e4m3
+    int_codes = _E2M1_INT_CODES if fp4 else _E4M3_INT_CODES
     rng = np.random.default_rng(seed)
     ls = mx_scale_stride(k)
     codes = np.empty((rows, k), np.uint8)
@@ -213,7 +245,7 @@ def draw_mx(rows: int, k: int, dist: str, seed: int, scale: float = 1.0):
         n = (r1 - r0) * k
         if dist == "int3":
             v = rng.integers(-3, 4, n).reshape(r1 - r0, k)
-            codes[r0:r1] = np.vectorize(_E4M3_INT_CODES.get, otypes=[np.uint8])(v)
+            codes[r0:r1] = np.vectorize(int_codes.get, otypes=[np.uint8])(v)
             continue
         x = (rng.standard_normal(n) if dist == "normal" else rng.uniform(-1.0, 1.0, n))
         x = (x * float(scale)).reshape(r1 - r0, k)
@@ -221,12 +253,12 @@ def draw_mx(rows: int, k: int, dist: str, seed: int, scale: float = 1.0):
         pad[:, :k] = x
         blocks = pad.reshape(r1 - r0, nb, MX_BLOCK)
         amax = np.abs(blocks).max(axis=2)
-        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8.0, -127.0)
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - emax, -127.0)
         e = np.clip(e, -127.0, 127.0)
         scales[r0:r1, :nb] = (e + 127.0).astype(np.uint8)
         q = blocks / np.exp2(e)[:, :, None]
-        codes[r0:r1] = f64_to_e4m3(q).reshape(r1 - r0, nb * MX_BLOCK)[:, :k]
-    return codes, scales
+        codes[r0:r1] = encode(q).reshape(r1 - r0, nb * MX_BLOCK)[:, :k]
+    return (pack_fp4(codes) if fp4 else codes), scales
 
 
 @dataclass(frozen=True)
@@ -239,6 +271,7 @@ class MxWorkload:
     outs: tuple
     b_scale: float = 1.0
     note: str = ""
+    fmt: str = "e4m3"
 
     @property
     def flops(self) -> int:
@@ -248,7 +281,8 @@ class MxWorkload:
         """Elements and scales read once, C written once."""
         esz = 4 if out == "f32" else 2
         ls = mx_scale_stride(self.K)
-        return (self.M + self.N) * (self.K + ls) + esz * self.M * self.N
+        kb = self.K // 2 if self.fmt == "e2m1" else self.K
+        return (self.M + self.N) * (kb + ls) + esz * self.M * self.N
 
 
 MX_WORKLOADS = {
@@ -261,12 +295,18 @@ MX_WORKLOADS = {
     "mx_decode": MxWorkload(
         "mx_decode", 15, 16, 28672, 8192, ("bf16",), b_scale=_S,
         note="the decode shape in MXFP8, HBM-bound"),
+    "mxfp4_mlp_gate_up_shard": MxWorkload(
+        "mxfp4_mlp_gate_up_shard", 16, 8192, 7168, 8192, ("bf16",), b_scale=_S,
+        note="the MLP gate+up shard in MXFP4 (weights N x K), bf16 output", fmt="e2m1"),
+    "mxfp4_decode": MxWorkload(
+        "mxfp4_decode", 17, 16, 28672, 8192, ("bf16",), b_scale=_S,
+        note="the decode shape in MXFP4, HBM-bound", fmt="e2m1"),
 }
 
 
 @dataclass
 class MxOperands:
-    A: np.ndarray    # (M, K) E4M3 codes
+    A: np.ndarray    # (M, K) E4M3 codes (E2M1: (M, K/2) packed)
     sA: np.ndarray   # (M, ls) E8M0
     Bt: np.ndarray   # (N, K) E4M3 codes of B's transpose
     sB: np.ndarray   # (N, ls)
@@ -278,6 +318,6 @@ def mx_operands(w: MxWorkload, integer: bool = False, M: int | None = None,
     N = w.N if N is None else N
     K = w.K if K is None else K
     da, db = ("int3", "int3") if integer else ("normal", "normal")
-    A, sA = draw_mx(M, K, da, 1000 * w.case + (3 if integer else 1))
-    Bt, sB = draw_mx(N, K, db, 1000 * w.case + (4 if integer else 2), w.b_scale)
+    A, sA = draw_mx(M, K, da, 1000 * w.case + (3 if integer else 1), fmt=w.fmt)
+    Bt, sB = draw_mx(N, K, db, 1000 * w.case + (4 if integer else 2), w.b_scale, fmt=w.fmt)
     return MxOperands(A, sA, Bt, sB)
