@@ -196,7 +196,10 @@ def chk_mx(A=A0, B=B0, C=C0, M=64, N=64, K=128, s=(128, 1, 1, 128, 64, 1), sa=SA
     (dict(K=0, A=0, B=0, sa=0, sb=0), Status.OK),
     (dict(M=0), Status.OK),
     (dict(K=96, s=(128, 1, 1, 128, 64, 1)), Status.ERR_BAD_SHAPE),      # K % 64
-    (dict(fmt=1), Status.ERR_DTYPE),
+    (dict(fmt=2), Status.ERR_DTYPE),
+    (dict(fmt=1), Status.OK),                                           # E2M1: K = 128 fits
+    (dict(fmt=1, K=64, s=(64, 1, 1, 64, 64, 1), ls=4), Status.ERR_BAD_SHAPE),   # E2M1 K % 128
+    (dict(fmt=1, s=(48, 1, 1, 64, 64, 1)), Status.ERR_BAD_STRIDE),      # E2M1 a_m < K/2 bytes
     (dict(dtype=5), Status.ERR_DTYPE),
     (dict(sa=0), Status.ERR_NULL_ARG),
     (dict(s=(128, 1, 128, 1, 64, 1)), Status.ERR_BAD_STRIDE),           # B not K-contiguous
