@@ -302,7 +302,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
     // and the DMA loads of slab s + NST - 1 spread evenly among the MFMAs so
     // they never reach the texture unit as one burst.
     constexpr int NUNIT = FM + FN;
-    constexpr int UPM = (NUNIT + NMFMA - 1) / NMFMA;
     auto read_unit = [&](uint32_t so, int slot, auto idx_c) {
       constexpr int IDX = decltype(idx_c)::value;
       if constexpr (IDX < FM) {
@@ -317,11 +316,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
       }
     };
     auto dma_slot = [](int t, int n) constexpr { return ((2 * t + 1) * NMFMA) / (2 * n); };
+    // Steady step s (slab s + NST - 1 exists): the first half of slab s's
+    // MFMAs needs nothing new, so they run while this wave issues slab s + NST
+    // - 1 (into the stage of slab s - 1, whose reads every wave completed
+    // before the previous step's barrier) and while slab s + 1 is still
+    // landing; then the wait and the barrier for slab s + 1, and the second
+    // half of the MFMAs each followed by its share of slab s + 1's reads.
+    constexpr int HALF = NMFMA / 2;
+    constexpr int UPH = (NUNIT + HALF - 1) / HALF;  // operand units read after each MFMA
     auto step_full = [&](int s, auto par_c) {
       constexpr int PAR = decltype(par_c)::value;
       if (FP4 || PAR == 0) take_scales(s);
-      wait_vmcnt<((NST - 3) * NDMA < 63 ? (NST - 3) * NDMA : 63)>();
-      block_barrier();
       const int sn = s + NST - 1;
       if (sn % SPW == 0) issue_window(sn / SPW);
       const uint32_t stn = (uint32_t)(sn % NST) * STAGE;
@@ -329,16 +334,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
       const i32x4 rsB = make_rsrc(b_panel + (int64_t)sn * BKB, b_bytes - (int64_t)sn * BKB);
       const uint32_t so = (uint32_t)((s + 1) % NST) * STAGE;
       __builtin_amdgcn_sched_barrier(0);
-      static_for<0, NMFMA>([&](auto k_c) {
+      static_for<0, HALF>([&](auto k_c) {
         constexpr int k = decltype(k_c)::value;
         mfma_k(k_c, par_c, PAR);
-        static_for<0, UPM>([&](auto r_c) {
-          constexpr int idx = k * UPM + decltype(r_c)::value;
-          if constexpr (idx < NUNIT) read_unit(so, PAR ^ 1, std::integral_constant<int, idx>{});
-        });
         static_for<0, NDMA>([&](auto t_c) {
           constexpr int t = decltype(t_c)::value;
-          if constexpr (dma_slot(t, NDMA) == k) {
+          if constexpr (dma_slot(t, NDMA) / 2 == k) {
             if constexpr (t < A_PER)
               dma16(ldsw + stn + 1024 * NW * t, rsA, voA[t], 0u);
             else
@@ -346,9 +347,25 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
           }
         });
       });
-      static_for<0, NMFMA>([&](auto k_c) {
+      __builtin_amdgcn_sched_barrier(0);
+      // slab s + 1 has landed once at most the loads of slabs s + 2 .. s + NST - 1
+      // remain (scale windows among them only make the wait longer); this
+      // wave's LDS reads (of slab s, issued last step) are complete before the
+      // barrier, so the next step may load slab s + NST into slab s's stage
+      wait_vmcnt<((NST - 2) * NDMA < 63 ? (NST - 2) * NDMA : 63)>();
+      wait_lgkmcnt0();
+      block_barrier();
+      static_for<HALF, NMFMA>([&](auto k_c) {
         constexpr int k = decltype(k_c)::value;
-        constexpr int lo = k * UPM, hi = (k + 1) * UPM < NUNIT ? (k + 1) * UPM : NUNIT;
+        mfma_k(k_c, par_c, PAR);
+        static_for<0, UPH>([&](auto r_c) {
+          constexpr int idx = (k - HALF) * UPH + decltype(r_c)::value;
+          if constexpr (idx < NUNIT) read_unit(so, PAR ^ 1, std::integral_constant<int, idx>{});
+        });
+      });
+      static_for<HALF, NMFMA>([&](auto k_c) {
+        constexpr int k = decltype(k_c)::value;
+        constexpr int lo = (k - HALF) * UPH, hi = (k - HALF + 1) * UPH < NUNIT ? (k - HALF + 1) * UPH : NUNIT;
         constexpr int n_rd = lo < NUNIT ? 2 * (hi - lo) : 0;
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if constexpr (n_rd > 0) __builtin_amdgcn_sched_group_barrier(0x100, n_rd, 0);
