@@ -297,10 +297,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
       interleave();
       __builtin_amdgcn_sched_barrier(0);
     };
-    // Steady state (slab s + NST - 1 exists): the same step with compile-time
-    // waits, each MFMA followed by its share of the next slab's operand reads,
-    // and the DMA loads of slab s + NST - 1 spread evenly among the MFMAs so
-    // they never reach the texture unit as one burst.
+    // Operand units of the steady step: A fragment IDX < FM, else B fragment
+    // IDX - FM, each two 16-byte LDS reads. The DMA loads of a slab are spread
+    // evenly among the MFMAs so they never reach the texture unit as one burst.
     constexpr int NUNIT = FM + FN;
     auto read_unit = [&](uint32_t so, int slot, auto idx_c) {
       constexpr int IDX = decltype(idx_c)::value;
