@@ -176,8 +176,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
           dma16(dst + BM * 16 + 1024 * q, rsSB, (uint32_t)((n0 + 64 * q + lane) * p.ls + 16 * w), 0u);
     };
 
-    // The window of slabs 8 w .. goes out just before slab 8 w's own loads, so
-    // any wait that covers slab 8 w covers it too.
+    // The window of slabs SPW w .. goes out just before slab SPW w's own loads,
+    // so any wait that covers slab SPW w covers it too.
     auto issue_slab = [&](int s) {
       if (s % SPW == 0) issue_window(s / SPW);
       const uint32_t st = (uint32_t)(s % NST) * STAGE;
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
       for (int j = 0; j < FN; ++j) acc[i][j] = floatx16{};
 
     i32x8 af[2][FM], bfr[2][FN];
-    int sca[FM], scb[FN];  // scales of the current slab pair, pre-shifted per lane
+    int sca[FM], scb[FN];  // scales of the current slab (E4M3: slab pair), shifted per lane
     auto read_frags = [&](int s, int slot) {
       const uint32_t so = (uint32_t)(s % NST) * STAGE;
 #pragma unroll
