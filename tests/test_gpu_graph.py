@@ -81,3 +81,58 @@ def test_capture_and_replay(g, M, N, K, bcol, dt):
         torch.cuda.synchronize()
         assert torch.equal(_bits(C), _bits(refs[i])), f"replay {rep} differs from the eager run"
         _ = (refs[i].float() * 2).sum().item()   # unrelated eager work between replays
+
+
+def test_capture_and_replay_epilogue_and_mx(g):
+    """The fused-epilogue and MX entry points are enqueue-only too: captured
+    once, replayed with rewritten inputs, each replay equal to an eager run."""
+    print("[graph epilogue + mx]", flush=True)
+    M, N, K = 300, 520, 256
+    A_np = [synth.draw(M, K, "normal", 700 + v) for v in range(2)]
+    B_np = [synth.draw(K, N, "normal", 710 + v, K ** -0.5) for v in range(2)]
+    mx_ops = [(synth.draw_mx(M, K, "normal", 720 + v), synth.draw_mx(N, K, "normal", 730 + v))
+              for v in range(2)]
+    bias = torch.from_numpy(synth.draw_bias(N, 740)).cuda()
+    A, B = _dev(A_np[0]), _dev(B_np[0])
+    (a8, sa), (b8, sb) = mx_ops[0]
+    Am, Bm = torch.from_numpy(a8).cuda(), torch.from_numpy(b8).cuda()
+    Sa, Sb = torch.from_numpy(sa).cuda(), torch.from_numpy(sb).cuda()
+    C1 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    C2 = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+
+    def work():
+        g(A, B, C1, bias=bias, act=tg.Act.SILU)
+        g.mx(Am, Bm, C2, Sa, Sb, bias=bias, act=tg.Act.RELU)
+
+    def load(v):
+        A.copy_(_dev(A_np[v])); B.copy_(_dev(B_np[v]))
+        (a8, sa), (b8, sb) = mx_ops[v]
+        Am.copy_(torch.from_numpy(a8)); Bm.copy_(torch.from_numpy(b8))
+        Sa.copy_(torch.from_numpy(sa)); Sb.copy_(torch.from_numpy(sb))
+
+    refs = []
+    for v in range(2):
+        load(v)
+        work()
+        torch.cuda.synchronize()
+        refs.append((C1.clone(), C2.clone()))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        v = rep % 2
+        load(v)
+        C1.fill_(float("nan")); C2.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(C1), _bits(refs[v][0])), f"epilogue replay {rep}"
+        assert torch.equal(_bits(C2), _bits(refs[v][1])), f"mx replay {rep}"
+        _ = (refs[v][1] * 2).sum().item()
