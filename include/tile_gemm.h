@@ -172,6 +172,8 @@ tile_gemm_status_t tile_gemm_run_epilogue(tile_gemm_t h, const void* A, const vo
  * E4M3 and of 128 for E2M1 (TILE_GEMM_ERR_BAD_SHAPE otherwise). C, dtype, bias and act (not
  * TILE_GEMM_ACT_SWIGLU) are as for tile_gemm_run_epilogue; accumulation is
  * fp32 in ascending K, one owner per output tile, each element written once.
+ * Outputs of up to 32 rows run a kernel that streams B in 256-byte pieces of
+ * K per row (plan bk = 256); larger ones the tile kernel (bk = 64).
  * A, B 16-byte aligned with 16-byte leading dimensions; scales 4-byte aligned.
  * All inputs are borrowed read-only until the stream reaches the work; C may
  * overlap none of them. Enqueue-only, allocates nothing.

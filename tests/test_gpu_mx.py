@@ -31,14 +31,24 @@ def g():
         yield gg
 
 
-def mx_config_table():
+def _mx_config_rows():
     import os
     import re
     src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                             "tile_partitioned_dense_amd", "csrc", "plan.hpp")).read()
     body = re.search(r"kMxConfigs\[kNumMxConfigs\]\s*=\s*\{(.*?)\n\};", src, re.S).group(1)
-    rows = re.findall(r"^\s*\{(\d+),\s*(\d+),", body, re.M)
-    return [tuple(int(v) for v in r) for r in rows]
+    return [[f.strip() for f in r.split(",")] for r in re.findall(r"^\s*\{([^}]*)\}", body, re.M)]
+
+
+def mx_config_table():
+    """(bm, bn) of every MX configuration, in index order."""
+    return [(int(r[0]), int(r[1])) for r in _mx_config_rows()]
+
+
+def mx_stream_configs():
+    """(index, bm, bn, stages) of the stream-kernel configurations."""
+    return [(i, int(r[0]), int(r[1]), int(r[4])) for i, r in enumerate(_mx_config_rows())
+            if len(r) > 6 and int(r[6]) > 0]
 
 
 FMTS = {"e4m3": tg.MX_E4M3, "e2m1": tg.MX_E2M1}
@@ -125,6 +135,20 @@ def test_mx_configs_integer_exact(g, fmt, cfg):
 
 
 @pytest.mark.parametrize("fmt", sorted(FMTS))
+@pytest.mark.parametrize("cfg,bm,bn,stages", mx_stream_configs())
+def test_mx_stream_ring(g, fmt, cfg, bm, bn, stages):
+    """Stream kernel over many stages: the stage ring and the scale-window
+    ring are each reused several times, the last stage is only partly inside
+    K, two tile rows (M > bm) and a ragged last tile column."""
+    slabs = 4 * (stages + 3) + 3
+    M, N = bm + 3, 3 * bn + 5
+    K = slabs * (128 if fmt == "e2m1" else 64)
+    print(f"[mx stream {fmt} cfg {cfg} {M}x{N}x{K}]", flush=True)
+    _run_and_check(g, MxCase(M, N, K, seed=70 + cfg, fmt=fmt), tg.DEBUG_FORCE_TILE(cfg),
+                   label=f"stream {fmt} cfg {cfg}")
+
+
+@pytest.mark.parametrize("fmt", sorted(FMTS))
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (17, 33, 128), (300, 520, 640), (16, 4096, 1024),
                                    (1000, 1000, 1024), (130, 130, 0)])
 def test_mx_planner_shapes(g, fmt, M, N, K):
@@ -136,13 +160,15 @@ def test_mx_planner_shapes(g, fmt, M, N, K):
 def test_mx_several_tiles_per_workgroup(g):
     case = MxCase(600, 700, 256, seed=61)
     print("[mx forced grid]", flush=True)
-    for cfg, grid in ((0, 3), (1, 5)):
+    for cfg, grid in ((0, 3), (1, 5), (3, 3)):
         _run_and_check(g, case, tg.DEBUG_FORCE_TILE(cfg) | tg.DEBUG_FORCE_GRID(grid),
                        label=f"cfg {cfg} grid {grid}")
 
 
-def test_mx_fused_epilogue(g):
-    case = MxCase(300, 264, 512, seed=62, b_scale=512 ** -0.5)
+@pytest.mark.parametrize("M", [300, 16])
+def test_mx_fused_epilogue(g, M):
+    """Tile kernel (300 rows) and stream kernel (16 rows, the planner's choice)."""
+    case = MxCase(M, 264, 512, seed=62, b_scale=512 ** -0.5)
     C, D = case.ref()
     b = synth.draw_bias(case.N, 900)
     bd = torch.from_numpy(b).cuda()

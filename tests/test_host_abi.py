@@ -221,3 +221,13 @@ def test_mx_plan():
     p = tg.tile_gemm_plan_mx(8192, 7168, 8192)
     assert p.variant == tg.VARIANT_MX and p.bm == 256 and p.bn == 256 and p.bk == 64
     assert p.tiles == 32 * 28 and p.grid == 224
+
+
+def test_mx_plan_few_rows_take_the_stream_kernel():
+    """Outputs of up to 32 rows stream B (one 32-row tile row of 128 columns,
+    256 bytes of K per stage); from 33 rows the tile kernel's configurations."""
+    for M in (1, 16, 17, 32):
+        p = tg.tile_gemm_plan_mx(M, 28672, 8192)
+        assert (p.variant, p.config, p.bm, p.bn, p.bk) == (tg.VARIANT_MX, 3, 32, 128, 256), M
+        assert p.tiles == 28672 // p.bn and p.grid == 224
+    assert tg.tile_gemm_plan_mx(33, 28672, 8192).bk == 64

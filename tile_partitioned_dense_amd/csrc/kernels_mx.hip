@@ -1,5 +1,6 @@
-// kernels_mx.hip -- instances of the MXFP8 tile kernel for one configuration,
-// selected at compile time with -DTG_MX_CONFIG=<index into kMxConfigs>.
+// kernels_mx.hip -- instances of the MX kernels (tile or stream) for one
+// configuration, selected at compile time with -DTG_MX_CONFIG=<index into
+// kMxConfigs>.
 #include "launch.hpp"
 
 #ifndef TG_MX_CONFIG
@@ -11,7 +12,10 @@ namespace tg {
 template <int CFG, int FMT, bool OB, bool DB>
 const void* mx_fn() {
   constexpr MxConfig c = kMxConfigs[CFG];
-  return reinterpret_cast<const void*>(&mx_gemm_kernel<c.bm, c.bn, c.wm, c.wn, c.stages, FMT, OB, DB>);
+  if constexpr (c.sb > 0)
+    return reinterpret_cast<const void*>(&mx_stream_kernel<c.bm, c.bn, c.sb, c.stages, FMT, OB, DB>);
+  else
+    return reinterpret_cast<const void*>(&mx_gemm_kernel<c.bm, c.bn, c.wm, c.wn, c.stages, FMT, OB, DB>);
 }
 
 template <int CFG, int FMT>

@@ -86,19 +86,24 @@ constexpr SkinnyConfig kSkinnyConfigs[kNumSkinnyConfigs] = {
     {4, 1}, {8, 1}, {4, 2}, {8, 2}, {4, 4}, {8, 4},
 };
 
-// MXFP8 tile-kernel configurations (mx_kernel.hpp); `eff` ranks them as in
-// the bf16 table.
+// MX configurations: the tile kernel (mx_kernel.hpp; `eff` ranks them as in
+// the bf16 table) and, with `sb` set, the few-row streaming kernel
+// (mx_stream_kernel.hpp: one 16- or 32-row block, sb bytes of K per row and
+// stage, one wave per 32 columns), which the planner takes for short outputs.
 struct MxConfig {
   int bm, bn, wm, wn, stages;
   float eff;
+  int sb = 0;  // stream kernel: bytes of K per row and stage; 0: tile kernel
 };
-constexpr int kNumMxConfigs = 3;
+constexpr int kNumMxConfigs = 4;
 constexpr MxConfig kMxConfigs[kNumMxConfigs] = {
     {256, 256, 2, 2, 4, 1.00f},  // 0: 4 waves of 128x128
     {128, 128, 2, 2, 4, 0.70f},  // 1: 4 waves of 64x64
     {64, 128, 2, 2, 12, 0.50f},  // 2: 4 waves of 32x64, 12 stages: few rows, weight streaming
+    {32, 128, 1, 4, 3, 0.0f, 256},  // 3: stream, 32 x 128, 3 stages of 256 bytes
 };
-constexpr int kMxBK = 64;  // K per slab of the MX kernel (a multiple of it is required)
+constexpr int kMxBK = 64;          // bytes of K per row in one slab of the MX tile kernel
+constexpr int kMxStreamMaxM = 32;  // M at or below this takes the stream kernel
 
 // Owned-tile map parameters (kernel argument; plain data).
 struct TileMap {
@@ -226,9 +231,9 @@ inline Plan plan_for_mx(int config, int64_t M, int64_t N, int cu_count) {
   p.config = config;
   p.bm = c.bm;
   p.bn = c.bn;
-  p.bk = kMxBK;
+  p.bk = c.sb ? c.sb : kMxBK;
   p.threads = c.wm * c.wn * 64;
-  p.lds_bytes = c.stages * (c.bm + c.bn) * kMxBK;
+  p.lds_bytes = c.stages * (c.bm + c.bn) * p.bk;
   p.k_split = 1;
   p.map.tiles_m = (int32_t)ceil_div(M, c.bm);
   p.map.tiles_n = (int32_t)ceil_div(N, c.bn);
@@ -239,15 +244,19 @@ inline Plan plan_for_mx(int config, int64_t M, int64_t N, int cu_count) {
   return p;
 }
 
-// MX plan: the configuration minimising (tiles on the busiest CU) x (tile
-// area) / rate, as for the bf16 tile kernel.
+// MX plan: outputs of at most kMxStreamMaxM rows stream B through the
+// stream kernel (one tile row); otherwise the tile-kernel configuration
+// minimising (tiles on the busiest CU) x (tile area) / rate, as for the bf16
+// tile kernel.
 inline Plan make_plan_mx(int64_t M, int64_t N, int64_t K, int cu_count) {
   (void)K;
   if (M <= 0 || N <= 0) return plan_for(0, 0, M, N, cu_count);
+  if (M <= kMxStreamMaxM) return plan_for_mx(3, M, N, cu_count);
   int best = 0;
   double best_cost = 0.0;
   for (int i = 0; i < kNumMxConfigs; ++i) {
     const MxConfig& c = kMxConfigs[i];
+    if (c.sb) continue;
     const int64_t per_cu = ceil_div(ceil_div(M, c.bm) * ceil_div(N, c.bn), cu_count);
     const double cost = (double)per_cu * c.bm * c.bn / c.eff;
     if (i == 0 || cost < best_cost * 0.999) {
