@@ -45,6 +45,18 @@ def tile_config_table():
     return [tuple(int(v) for v in r) for r in rows]
 
 
+def stream_tile_configs():
+    """Indices of the tile configurations that run the stream kernel (a field
+    sb > 0, the tenth of a row): column-major B only."""
+    import os
+    import re
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "tile_partitioned_dense_amd", "csrc", "plan.hpp")).read()
+    body = re.search(r"kTileConfigs\[kNumTileConfigs\]\s*=\s*\{(.*?)\n\};", src, re.S).group(1)
+    rows = [[f.strip() for f in r.split(",")] for r in re.findall(r"^\s*\{([^}]*)\}", body, re.M)]
+    return {i for i, r in enumerate(rows) if len(r) > 9 and int(r[9]) > 0}
+
+
 def round_up(x, m):
     return (x + m - 1) // m * m
 

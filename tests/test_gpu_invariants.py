@@ -20,7 +20,7 @@ import pytest
 import tile_partitioned_dense_amd as tg
 from tile_partitioned_dense_amd import synth
 
-from gpu_helpers import Case, check, host_out, workload_case
+from gpu_helpers import Case, check, host_out, stream_tile_configs, workload_case
 
 pytestmark = pytest.mark.gpu
 
@@ -82,19 +82,21 @@ def test_every_element_written_once(g, M, N, K, bcol):
 
 @pytest.mark.parametrize("cfg", range(tg.N_TILE_CONFIGS))
 def test_every_config_writes_once(g, cfg):
-    case = Case(300, 500, 70, False, seed=cfg)
+    case = Case(300, 500, 70, cfg in stream_tile_configs(), seed=cfg)
     store, C, counts = _counts_run(g, case, torch.float32,
                                    tg.DEBUG_COUNT_WRITES | tg.DEBUG_FORCE_TILE(cfg))
     assert int(counts.min()) == 1 and int(counts.max()) == 1
 
 
-@pytest.mark.parametrize("cfg,grid", [(1, 1), (1, 3), (7, 2), (9, 5), (6, 8), (10, 3), (11, 5), (12, 3)])
+@pytest.mark.parametrize("cfg,grid", [(1, 1), (1, 3), (7, 2), (9, 5), (6, 8), (10, 3), (11, 5), (12, 3),
+                                      (14, 3), (14, 7)])
 def test_workgroups_owning_several_tiles(g, cfg, grid):
     """A launch with fewer workgroups than tiles (workgroup w owns tile
     numbers w, w + grid, ...): every element still written once, and the
     result bit-identical to one workgroup per tile, since each tile keeps its
     own K loop and K order whichever workgroup runs it."""
-    case = Case(700, 900, 300, cfg in (1, 9), seed=40 + cfg, pad=8)  # steady loop + K tail
+    case = Case(700, 900, 300, cfg in (1, 9) or cfg in stream_tile_configs(), seed=40 + cfg,
+                pad=8)                                             # steady loop + K tail
     print(f"[several tiles per workgroup cfg {cfg} grid {grid}]", flush=True)
     for dt in (torch.float32, torch.bfloat16):
         store, C, counts = _counts_run(g, case, dt, tg.DEBUG_COUNT_WRITES | tg.DEBUG_FORCE_TILE(cfg)

@@ -13,7 +13,7 @@ import oracle
 import tile_partitioned_dense_amd as tg
 from tile_partitioned_dense_amd import synth
 
-from gpu_helpers import Case, check, host_out, tile_config_table, workload_case
+from gpu_helpers import Case, check, host_out, stream_tile_configs, tile_config_table, workload_case
 
 pytestmark = pytest.mark.gpu
 
@@ -64,6 +64,8 @@ def tile_shape(cfg):
 @pytest.mark.parametrize("cfg", range(tg.N_TILE_CONFIGS))
 @pytest.mark.parametrize("bcol", [False, True], ids=["Brow", "Bcol"])
 def test_tile_configs(g, cfg, bcol):
+    if cfg in stream_tile_configs() and not bcol:
+        pytest.skip("stream configurations take a column-major B (rejection: test_gpu_stream)")
     M, N = tile_shape(cfg)
     print(f"[tile cfg {cfg} bcol={bcol} {M}x{N}x200]", flush=True)
     case = Case(M, N, 200, bcol, seed=cfg, pad=8)     # K = 3 slabs + a partial one
@@ -73,11 +75,14 @@ def test_tile_configs(g, cfg, bcol):
 
 @pytest.mark.parametrize("cfg", range(tg.N_TILE_CONFIGS))
 def test_tile_configs_integer_k_tail(g, cfg):
-    """Integer data, K not a multiple of 8: exact, and the K tail is masked."""
+    """Integer data, K not a multiple of 8: exact, and the K tail is masked
+    (the stream configurations, column-major B only, take an even K: 130)."""
     M, N = tile_shape(cfg)
-    print(f"[tile int cfg {cfg} {M}x{N}x131]", flush=True)
-    for bcol in (False, True):
-        case = Case(M, N, 131, bcol, dist="int3", seed=10 + cfg)
+    stream = cfg in stream_tile_configs()
+    K = 130 if stream else 131
+    print(f"[tile int cfg {cfg} {M}x{N}x{K}]", flush=True)
+    for bcol in ((True,) if stream else (False, True)):
+        case = Case(M, N, K, bcol, dist="int3", seed=10 + cfg)
         for dt in (torch.float32, torch.bfloat16):
             _parity(g, case, dt, flags=tg.DEBUG_FORCE_TILE(cfg), integer=True)
 

@@ -62,7 +62,7 @@ def DEBUG_FORCE_GRID(g: int) -> int:
 DEBUG_ONE_TILE_PER_WG = 0x7F << 24
 
 
-N_TILE_CONFIGS = 14
+N_TILE_CONFIGS = 15
 N_MX_CONFIGS = 4
 MX_E4M3 = 0
 MX_E2M1 = 1

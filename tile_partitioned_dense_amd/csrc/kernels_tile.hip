@@ -8,12 +8,18 @@
 
 namespace tg {
 
-// The kernel instance of configuration CFG: the tile kernel, or the K-split
-// kernel for configurations whose waves share K.
+// The kernel instance of configuration CFG: the tile kernel, the K-split
+// kernel for configurations whose waves share K, or the stream kernel
+// (column-major B only; NULL for a row-major B).
 template <int CFG, bool BC, bool OB, bool DB>
 const void* tile_fn() {
   constexpr TileConfig c = kTileConfigs[CFG];
-  if constexpr (c.ks > 1)
+  if constexpr (c.sb > 0) {
+    if constexpr (BC)
+      return reinterpret_cast<const void*>(&stream_gemm_kernel<c.bm, c.bn, c.sb, c.stages, OB, DB>);
+    else
+      return nullptr;
+  } else if constexpr (c.ks > 1)
     return reinterpret_cast<const void*>(&ksplit_gemm_kernel<c.bm, c.bn, c.ks, c.stages, BC, OB, DB>);
   else
     return reinterpret_cast<const void*>(&tile_gemm_kernel<c.bm, c.bn, c.wm, c.wn, c.stages, BC, OB, DB>);
@@ -32,6 +38,7 @@ hipError_t launch_tile(const TileArgs& a, int64_t grid_wgs, const Variant& v, hi
     if (v.out_bf16) fn = v.debug ? tile_fn<CFG, false, true, true>() : tile_fn<CFG, false, true, false>();
     else fn = v.debug ? tile_fn<CFG, false, false, true>() : tile_fn<CFG, false, false, false>();
   }
+  if (!fn) return hipErrorInvalidValue;
   return launch_raw(fn, grid, block, a, stream);
 }
 

@@ -9,6 +9,7 @@
 #include "mx_kernel.hpp"
 #include "mx_stream_kernel.hpp"
 #include "skinny_kernel.hpp"
+#include "stream_kernel.hpp"
 #include "tile_kernel.hpp"
 
 namespace tg {

@@ -46,6 +46,8 @@ struct TileConfig {
                 // K and combine in a fixed tree (ksplit_kernel.hpp)
   float eff1 = 0.0f;  // rate of a workgroup alone on its compute unit (0: = eff)
   int occ = 1;        // workgroups that fit on one compute unit at once
+  int sb = 0;         // > 0: the stream kernel (stream_kernel.hpp, column-major B
+                      // only) with stages of sb bytes of K per row
 };
 
 // Rate of configuration c when each compute unit has `per_cu` of its tiles:
@@ -58,7 +60,7 @@ inline double tile_eff(const TileConfig& c, int64_t per_cu) {
   return e1 + (c.eff - e1) * (double)(n - 1) / (double)(c.occ - 1);
 }
 
-constexpr int kNumTileConfigs = 14;
+constexpr int kNumTileConfigs = 15;
 constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
     {256, 256, 2, 2, 4, 0.94f},  // 0: 4 waves of 128x128
     {256, 224, 4, 1, 5, 0.85f},  // 1: 4 waves of 64x224
@@ -74,7 +76,10 @@ constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
     {64, 64, 1, 1, 4, 0.28f, 4},    // 11: 4 waves, each 64x64 over a quarter of K
     {64, 128, 1, 1, 3, 0.42f, 4},   // 12: 4 waves, each 64x128 over a quarter of K
     {128, 64, 1, 1, 3, 0.39f, 4},   // 13: 4 waves, each 128x64 over a quarter of K
+    {32, 128, 1, 4, 3, 0.0f, 1, 0.0f, 1, 256},  // 14: stream, 32x128, 3 stages of 256 bytes
 };
+constexpr int kStreamConfig = 14;  // the planner's stream configuration
+constexpr int kStreamMaxM = 64;    // column-major B, even K and M at or below this: stream kernel
 
 // Skinny-kernel configurations: T output columns per lane (16*T per
 // workgroup) and MG groups of 16 rows.
@@ -153,6 +158,7 @@ struct Plan {
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 inline int tile_lds_bytes(const TileConfig& c) {
+  if (c.sb) return c.stages * (c.bm + c.bn) * c.sb;
   const int ring = c.ks * c.stages * (c.bm + c.bn) * 32 * 2;
   const int tree = (c.ks / 2) * c.bm * c.bn * 4;
   return ring > tree ? ring : tree;
@@ -212,6 +218,7 @@ inline Plan plan_for(int variant, int config, int64_t M, int64_t N, int cu_count
     p.bn = c.bn;
     p.threads = c.wm * c.wn * c.ks * 64;
     p.lds_bytes = tile_lds_bytes(c);
+    if (c.sb) p.bk = c.sb / 2;
     p.k_split = c.ks;
     p.map.tiles_m = (int32_t)ceil_div(M, c.bm);
     p.map.tiles_n = (int32_t)ceil_div(N, c.bn);
@@ -270,9 +277,11 @@ inline Plan make_plan_mx(int64_t M, int64_t N, int64_t K, int cu_count) {
 // Pure function of (M, N, K, B layout, CU count). The output type is not an
 // input, so fp32 and bf16 outputs of one shape share kernel, tile and K order.
 inline Plan make_plan(int64_t M, int64_t N, int64_t K, bool b_col_major, int cu_count) {
-  (void)K;
-  (void)b_col_major;
   if (M <= 0 || N <= 0) return plan_for(0, 0, M, N, cu_count);
+  // (odd K: the stream kernel's loads of whole dwords would drop the value
+  // K - 1 of each operand's last row, so those shapes stay on the others)
+  if (b_col_major && M <= kStreamMaxM && K % 2 == 0)
+    return plan_for(1, kStreamConfig, M, N, cu_count);
   if (M <= kSkinnyMaxM) {
     const int mg = (int)ceil_div(M, 16);
     const int mgp = mg <= 1 ? 1 : (mg <= 2 ? 2 : 4);
@@ -289,6 +298,7 @@ inline Plan make_plan(int64_t M, int64_t N, int64_t K, bool b_col_major, int cu_
   double best_cost = 0.0;
   for (int i = 0; i < kNumTileConfigs; ++i) {
     const TileConfig& c = kTileConfigs[i];
+    if (c.sb) continue;
     const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
     const int64_t per_cu = ceil_div(tiles, cu_count);
     const double cost = (double)per_cu * c.bm * c.bn / tile_eff(c, per_cu);

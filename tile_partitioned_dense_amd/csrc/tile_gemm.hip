@@ -191,10 +191,11 @@ hipError_t dispatch_tile(int cfg, const tg::TileArgs& a, int64_t grid, const tg:
     case 11: return tg::launch_tile<11>(a, grid, v, st);
     case 12: return tg::launch_tile<12>(a, grid, v, st);
     case 13: return tg::launch_tile<13>(a, grid, v, st);
+    case 14: return tg::launch_tile<14>(a, grid, v, st);
   }
   return hipErrorInvalidValue;
 }
-static_assert(tg::kNumTileConfigs == 14, "dispatch_tile covers every tile configuration");
+static_assert(tg::kNumTileConfigs == 15, "dispatch_tile covers every tile configuration");
 
 hipError_t dispatch_skinny(int cfg, const tg::SkinnyArgs& a, int64_t grid, const tg::Variant& v,
                            hipStream_t st) {
@@ -387,6 +388,11 @@ tile_gemm_status_t run_impl(tile_gemm_t h, const void* A, const void* B, void* C
                   (long long)M, force_skinny - 1);
     p = tg::plan_for(2, force_skinny - 1, M, N, h->cu_count);
   }
+  if (p.variant == 1 && tg::kTileConfigs[p.config].sb && (brow || K % 2))
+    return fail(TILE_GEMM_ERR_BAD_SHAPE,
+                "debug: tile configuration %d (stream kernel) takes a column-major B and an "
+                "even K only",
+                p.config);
   if (p.grid > 0x7fffffff)
     return fail(TILE_GEMM_ERR_BAD_SHAPE, "shape: %lld workgroups exceed the launch limit",
                 (long long)p.grid);
