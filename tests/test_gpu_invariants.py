@@ -89,7 +89,7 @@ def test_every_config_writes_once(g, cfg):
 
 
 @pytest.mark.parametrize("cfg,grid", [(1, 1), (1, 3), (7, 2), (9, 5), (6, 8), (10, 3), (11, 5), (12, 3),
-                                      (14, 3), (14, 7)])
+                                      (14, 3), (14, 7), (15, 5)])
 def test_workgroups_owning_several_tiles(g, cfg, grid):
     """A launch with fewer workgroups than tiles (workgroup w owns tile
     numbers w, w + grid, ...): every element still written once, and the

@@ -160,7 +160,7 @@ def test_mx_planner_shapes(g, fmt, M, N, K):
 def test_mx_several_tiles_per_workgroup(g):
     case = MxCase(600, 700, 256, seed=61)
     print("[mx forced grid]", flush=True)
-    for cfg, grid in ((0, 3), (1, 5), (3, 3)):
+    for cfg, grid in ((0, 3), (1, 5), (3, 3), (4, 2)):
         _run_and_check(g, case, tg.DEBUG_FORCE_TILE(cfg) | tg.DEBUG_FORCE_GRID(grid),
                        label=f"cfg {cfg} grid {grid}")
 

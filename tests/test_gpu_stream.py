@@ -59,6 +59,8 @@ def _run_check(g, case, flags, integer=False, label=""):
     (40, 520, 1030),      # two tile rows, K % 8 == 6 (values masked inside a chunk)
     (9, 200, 2),          # the smallest even K
     (3, 1100, 2304),      # ring reused (18 stages)
+    (64, 300, 520),       # the 64-row tile full
+    (77, 260, 264),       # a second tile row of 64 rows
 ])
 def test_stream_parity(g, cfg, M, N, K):
     print(f"[stream cfg {cfg} {M}x{N}x{K}]", flush=True)

@@ -224,10 +224,11 @@ def test_mx_plan():
 
 
 def test_mx_plan_few_rows_take_the_stream_kernel():
-    """Outputs of up to 32 rows stream B (one 32-row tile row of 128 columns,
-    256 bytes of K per stage); from 33 rows the tile kernel's configurations."""
-    for M in (1, 16, 17, 32):
+    """Outputs of up to 64 rows stream B (one tile row of 32 or 64 rows x 128
+    columns, 256 bytes of K per stage); from 65 rows the tile kernel's
+    configurations."""
+    for M, cfg, bm in ((1, 3, 32), (16, 3, 32), (17, 3, 32), (32, 3, 32), (33, 4, 64), (64, 4, 64)):
         p = tg.tile_gemm_plan_mx(M, 28672, 8192)
-        assert (p.variant, p.config, p.bm, p.bn, p.bk) == (tg.VARIANT_MX, 3, 32, 128, 256), M
+        assert (p.variant, p.config, p.bm, p.bn, p.bk) == (tg.VARIANT_MX, cfg, bm, 128, 256), M
         assert p.tiles == 28672 // p.bn and p.grid == 224
-    assert tg.tile_gemm_plan_mx(33, 28672, 8192).bk == 64
+    assert tg.tile_gemm_plan_mx(65, 28672, 8192).bk == 64

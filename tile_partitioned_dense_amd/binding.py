@@ -62,8 +62,8 @@ def DEBUG_FORCE_GRID(g: int) -> int:
 DEBUG_ONE_TILE_PER_WG = 0x7F << 24
 
 
-N_TILE_CONFIGS = 15
-N_MX_CONFIGS = 4
+N_TILE_CONFIGS = 16
+N_MX_CONFIGS = 5
 MX_E4M3 = 0
 MX_E2M1 = 1
 N_SKINNY_CONFIGS = 6

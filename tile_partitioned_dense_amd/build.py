@@ -25,9 +25,9 @@ LIB = os.path.join(PKG, "libtile_gemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-N_TILE_CONFIGS = 15
+N_TILE_CONFIGS = 16
 N_SKINNY_CONFIGS = 6
-N_MX_CONFIGS = 4
+N_MX_CONFIGS = 5
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

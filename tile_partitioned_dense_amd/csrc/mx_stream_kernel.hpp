@@ -4,7 +4,7 @@
 // Same operands, formats, ownership and store as mx_kernel.hpp (the OCP MX
 // reading of the TorchInductor page's MXFP8 and FP4 GEMMs: E4M3 or E2M1
 // elements, one E8M0 scale per 32 along K; B given as its N x K transpose).
-// Every BM x BN tile of C (BM = 16 or 32 rows, so one tile row covers a
+// Every BM x BN tile of C (BM = 16, 32 or 64 rows, so one tile row covers a
 // decode batch) is owned by one workgroup, which reads A and B as shared
 // immutable views and writes its tile once; a persistent grid walks tiles
 // wg, wg + grid, ...
@@ -22,8 +22,9 @@
 // row pieces.
 //
 // Wave w owns the tile's columns 32 w .. 32 w + 31 and all its rows, one
-// 32 x 32 accumulator block held transposed (as in the tile kernels: the B
-// fragment is the instruction's first operand). With BM = 16 the lanes of
+// 32 x 32 accumulator block per 32 rows held transposed (as in the tile
+// kernels: the B fragment is the instruction's first operand, read once for
+// all blocks). With BM = 16 the lanes of
 // rows 16..31 give zero A operands, so the block's upper half stays zero and
 // is never stored. The operand layout, the scale placement (lane r + 32 b
 // holds the scale of block b of row r) and the per-format instruction count
@@ -49,11 +50,13 @@ namespace tg {
 
 template <int BM, int BN, int SB, int NST, int FMT, bool OUT_BF16, bool DEBUG>
 __global__ __launch_bounds__(BN / 32 * 64, 1) void mx_stream_kernel(MxArgs p) {
-  static_assert(BM == 16 || BM == 32, "one 32-row block, half of it or all of it");
+  static_assert(BM == 16 || BM == 32 || BM == 64, "half a 32-row block, or one or two blocks");
   static_assert(BN % 64 == 0 && BN <= 256, "whole scale-window loads for B");
   static_assert(SB == 128 || SB == 256, "stage rows of whole 128-byte lines");
   static_assert(FMT == kMxE4M3 || FMT == kMxE2M1, "E4M3 or E2M1 elements");
   constexpr int NW = BN / 32;
+  constexpr int FM = BM < 32 ? 1 : BM / 32;   // 32-row accumulator blocks per wave
+  constexpr int BR = BM < 32 ? BM : 32;       // rows of one block that are stored
   constexpr bool FP4 = FMT == kMxE2M1;
   constexpr int HW = FP4 ? 4 : 0;
   constexpr int CPR = SB / 16;              // 16-byte chunks per stage row
@@ -113,9 +116,9 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void mx_stream_kernel(MxArgs p) {
   }
   const uint32_t ldsw = __builtin_amdgcn_readfirstlane(lds0 + 1024 * wave);
 
-  // Operand reads: A row lrow (rows >= BM give zeros), B row 32 wave + lrow;
-  // slab j of a stage is chunks 4 j + lgrp and 4 j + 2 + lgrp.
-  const int ar = lrow & (BM - 1);
+  // Operand reads: A row 32 i + lrow of block i (rows >= BM give zeros), B
+  // row 32 wave + lrow; slab j of a stage is chunks 4 j + lgrp and 4 j + 2 + lgrp.
+  const int ar = lrow & (BR - 1);
   const int br = 32 * wave + lrow;
   const bool a_live = lrow < BM;
   const uint32_t rA = lds0 + (uint32_t)(ar * SB), rB = lds0 + A_BYTES + (uint32_t)(br * SB);
@@ -178,7 +181,9 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void mx_stream_kernel(MxArgs p) {
       });
     };
 
-    floatx16 acc = floatx16{};
+    floatx16 acc[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) acc[i] = floatx16{};
     for (int s = 0; s < NST - 1 && s < nss; ++s) issue_stage(s);
     for (int s = 0; s < nss; ++s) {
       wait_after((nss - 1 < s + NST - 2 ? nss - 1 : s + NST - 2) - s);
@@ -191,29 +196,34 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void mx_stream_kernel(MxArgs p) {
         constexpr int j = decltype(j_c)::value;
         {
           const int c0 = 4 * j + lgrp, c1 = 4 * j + 2 + lgrp;
-          uint4 x = __builtin_bit_cast(uint4, lds_read16(rA + so + (uint32_t)(((c0 ^ swa)) << 4)));
-          uint4 y = __builtin_bit_cast(uint4, lds_read16(rA + so + (uint32_t)(((c1 ^ swa)) << 4)));
-          if (!a_live) x = y = make_uint4(0, 0, 0, 0);
-          const i32x8 af = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
-                                 (int)y.x, (int)y.y, (int)y.z, (int)y.w};
-          x = __builtin_bit_cast(uint4, lds_read16(rB + so + (uint32_t)(((c0 ^ swb)) << 4)));
-          y = __builtin_bit_cast(uint4, lds_read16(rB + so + (uint32_t)(((c1 ^ swb)) << 4)));
+          uint4 x = __builtin_bit_cast(uint4, lds_read16(rB + so + (uint32_t)(((c0 ^ swb)) << 4)));
+          uint4 y = __builtin_bit_cast(uint4, lds_read16(rB + so + (uint32_t)(((c1 ^ swb)) << 4)));
           const i32x8 bf = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
                                  (int)y.x, (int)y.y, (int)y.z, (int)y.w};
           // the scale dword of slab SPS s + j (slab SPS (s % SSW) + j of its
           // window): E4M3 holds two slabs per dword, E2M1 one
           const int sw = SPS * (s % SSW) + j;
           const int dw = FP4 ? sw : sw / 2;
-          const uint32_t va = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
-              wb + (uint32_t)(ar * 16 + 4 * dw));
           const uint32_t vb = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
               wb + (uint32_t)(SWA + br * 16 + 4 * dw));
-          const int sa = (int)(va >> sh), sb = (int)(vb >> sh);
-          if constexpr (FP4) {
-            acc = mma_mx<0, HW>(fp4_half<0>(af), fp4_half<0>(bf), sa, sb, acc);
-            acc = mma_mx<2, HW>(fp4_half<1>(af), fp4_half<1>(bf), sa, sb, acc);
-          } else {
-            acc = mma_mx<2 * (j % 2), HW>(af, bf, sa, sb, acc);
+          const int sb = (int)(vb >> sh);
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const uint32_t ra = rA + so + (uint32_t)(32 * i * SB);
+            x = __builtin_bit_cast(uint4, lds_read16(ra + (uint32_t)(((c0 ^ swa)) << 4)));
+            y = __builtin_bit_cast(uint4, lds_read16(ra + (uint32_t)(((c1 ^ swa)) << 4)));
+            if (!a_live) x = y = make_uint4(0, 0, 0, 0);
+            const i32x8 af = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
+                                   (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+            const uint32_t va = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
+                wb + (uint32_t)((32 * i + ar) * 16 + 4 * dw));
+            const int sa = (int)(va >> sh);
+            if constexpr (FP4) {
+              acc[i] = mma_mx<0, HW>(fp4_half<0>(af), fp4_half<0>(bf), sa, sb, acc[i]);
+              acc[i] = mma_mx<2, HW>(fp4_half<1>(af), fp4_half<1>(bf), sa, sb, acc[i]);
+            } else {
+              acc[i] = mma_mx<2 * (j % 2), HW>(af, bf, sa, sb, acc[i]);
+            }
           }
         }
       };
@@ -226,22 +236,27 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void mx_stream_kernel(MxArgs p) {
       }
     }
 
-    // Store: each wave stages its 32 columns (BM rows) as fp32 in the free
-    // ring and writes them once per element (with the fused epilogue when
-    // asked).
+    // Store: each wave stages its 32 columns (32 rows at a time) as fp32 in
+    // the free ring and writes them once per element (with the fused
+    // epilogue when asked).
     wait_lgkmcnt0();
     block_barrier();
     {
       constexpr int OPF = 32 * 4 + 16;
       static_assert(NW * 32 * OPF <= RING, "an fp32 strip of every wave fits the ring");
       const uint32_t stf = lds0 + (uint32_t)(wave * 32 * OPF);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        lds_store_f4(stf + (uint32_t)(lrow * OPF + (8 * q + 4 * lgrp) * 4),
-                     floatx4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]});
-      wait_lgkmcnt0();
       const EpiOut eo{p.C, p.ldc, M, N, p.bias, p.act, p.counts, p.flags};
-      store_staged_fused<OUT_BF16, DEBUG>(stf, OPF, BM, 32, m0, n0 + 32 * wave, lane, 64, eo);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          lds_store_f4(stf + (uint32_t)(lrow * OPF + (8 * q + 4 * lgrp) * 4),
+                       floatx4{acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]});
+        wait_lgkmcnt0();
+        store_staged_fused<OUT_BF16, DEBUG>(stf, OPF, BR, 32, m0 + 32 * i, n0 + 32 * wave, lane, 64,
+                                            eo);
+        wait_lgkmcnt0();
+      }
     }
     wait_lgkmcnt0();
     block_barrier();

@@ -60,7 +60,7 @@ inline double tile_eff(const TileConfig& c, int64_t per_cu) {
   return e1 + (c.eff - e1) * (double)(n - 1) / (double)(c.occ - 1);
 }
 
-constexpr int kNumTileConfigs = 15;
+constexpr int kNumTileConfigs = 16;
 constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
     {256, 256, 2, 2, 4, 0.94f},  // 0: 4 waves of 128x128
     {256, 224, 4, 1, 5, 0.85f},  // 1: 4 waves of 64x224
@@ -77,9 +77,11 @@ constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
     {64, 128, 1, 1, 3, 0.42f, 4},   // 12: 4 waves, each 64x128 over a quarter of K
     {128, 64, 1, 1, 3, 0.39f, 4},   // 13: 4 waves, each 128x64 over a quarter of K
     {32, 128, 1, 4, 3, 0.0f, 1, 0.0f, 1, 256},  // 14: stream, 32x128, 3 stages of 256 bytes
+    {64, 128, 1, 4, 3, 0.0f, 1, 0.0f, 1, 256},  // 15: stream, 64x128, 3 stages of 256 bytes
 };
-constexpr int kStreamConfig = 14;  // the planner's stream configuration
-constexpr int kStreamMaxM = 64;    // column-major B, even K and M at or below this: stream kernel
+constexpr int kStreamConfig = 14;    // the planner's stream configuration up to 32 rows,
+constexpr int kStreamConfig64 = 15;  // and from 33 to 64 rows
+constexpr int kStreamMaxM = 64;      // column-major B, even K and M at or below this: stream kernel
 
 // Skinny-kernel configurations: T output columns per lane (16*T per
 // workgroup) and MG groups of 16 rows.
@@ -100,15 +102,16 @@ struct MxConfig {
   float eff;
   int sb = 0;  // stream kernel: bytes of K per row and stage; 0: tile kernel
 };
-constexpr int kNumMxConfigs = 4;
+constexpr int kNumMxConfigs = 5;
 constexpr MxConfig kMxConfigs[kNumMxConfigs] = {
     {256, 256, 2, 2, 4, 1.00f},  // 0: 4 waves of 128x128
     {128, 128, 2, 2, 4, 0.70f},  // 1: 4 waves of 64x64
     {64, 128, 2, 2, 12, 0.50f},  // 2: 4 waves of 32x64, 12 stages: few rows, weight streaming
     {32, 128, 1, 4, 3, 0.0f, 256},  // 3: stream, 32 x 128, 3 stages of 256 bytes
+    {64, 128, 1, 4, 3, 0.0f, 256},  // 4: stream, 64 x 128, 3 stages of 256 bytes
 };
 constexpr int kMxBK = 64;          // bytes of K per row in one slab of the MX tile kernel
-constexpr int kMxStreamMaxM = 32;  // M at or below this takes the stream kernel
+constexpr int kMxStreamMaxM = 64;  // M at or below this takes the stream kernel
 
 // Owned-tile map parameters (kernel argument; plain data).
 struct TileMap {
@@ -252,13 +255,13 @@ inline Plan plan_for_mx(int config, int64_t M, int64_t N, int cu_count) {
 }
 
 // MX plan: outputs of at most kMxStreamMaxM rows stream B through the
-// stream kernel (one tile row); otherwise the tile-kernel configuration
+// stream kernel (one tile row of 32 or 64 rows); otherwise the tile-kernel configuration
 // minimising (tiles on the busiest CU) x (tile area) / rate, as for the bf16
 // tile kernel.
 inline Plan make_plan_mx(int64_t M, int64_t N, int64_t K, int cu_count) {
   (void)K;
   if (M <= 0 || N <= 0) return plan_for(0, 0, M, N, cu_count);
-  if (M <= kMxStreamMaxM) return plan_for_mx(3, M, N, cu_count);
+  if (M <= kMxStreamMaxM) return plan_for_mx(M <= 32 ? 3 : 4, M, N, cu_count);
   int best = 0;
   double best_cost = 0.0;
   for (int i = 0; i < kNumMxConfigs; ++i) {
@@ -281,7 +284,7 @@ inline Plan make_plan(int64_t M, int64_t N, int64_t K, bool b_col_major, int cu_
   // (odd K: the stream kernel's loads of whole dwords would drop the value
   // K - 1 of each operand's last row, so those shapes stay on the others)
   if (b_col_major && M <= kStreamMaxM && K % 2 == 0)
-    return plan_for(1, kStreamConfig, M, N, cu_count);
+    return plan_for(1, M <= 32 ? kStreamConfig : kStreamConfig64, M, N, cu_count);
   if (M <= kSkinnyMaxM) {
     const int mg = (int)ceil_div(M, 16);
     const int mgp = mg <= 1 ? 1 : (mg <= 2 ? 2 : 4);

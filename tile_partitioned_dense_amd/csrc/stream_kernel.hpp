@@ -2,8 +2,8 @@
 // (K-contiguous) B, the layout in which weights are usually stored: the
 // weight stream of a decode step, bound by HBM.
 //
-// Ownership is the tile kernel's: every BM x BN tile of C (BM = 16 or 32
-// rows, so one tile row covers a decode batch) is owned by one workgroup,
+// Ownership is the tile kernel's: every BM x BN tile of C (BM = 16, 32 or
+// 64 rows, so one tile row covers a decode batch) is owned by one workgroup,
 // which reads A and B as shared immutable views and writes its tile once; a
 // persistent grid walks tiles wg, wg + grid, ... (tile_of).
 //
@@ -19,10 +19,11 @@
 // consecutive rows) then sit in sixteen distinct bank groups.
 //
 // Wave w owns the tile's columns 32 w .. 32 w + 31 and all its rows: one
-// 32 x 32 accumulator block held transposed (the B fragment is the MFMA's
-// first operand, as in mma()), fed by v_mfma_f32_32x32x16_bf16 over chunk
-// pairs 2 t, 2 t + 1 of a stage. With BM = 16 the lanes of rows 16..31 give
-// zero A operands and are never stored.
+// 32 x 32 accumulator block per 32 rows, held transposed (the B fragment is
+// the MFMA's first operand, as in mma(), and is read once for all blocks),
+// fed by v_mfma_f32_32x32x16_bf16 over chunk pairs 2 t, 2 t + 1 of a stage.
+// With BM = 16 the lanes of rows 16..31 give zero A operands and are never
+// stored.
 //
 // Each step waits for stage s, passes one barrier (after which every wave is
 // done with stage s - 1), loads stage s + NST - 1 into stage s - 1's buffer
@@ -60,11 +61,13 @@ __device__ __forceinline__ bf16x8 keep_first(const bf16x8& v, int valid) {
 
 template <int BM, int BN, int SB, int NST, bool OUT_BF16, bool DEBUG>
 __global__ __launch_bounds__(BN / 32 * 64, 1) void stream_gemm_kernel(TileArgs p) {
-  static_assert(BM == 16 || BM == 32, "one 32-row block, half of it or all of it");
+  static_assert(BM == 16 || BM == 32 || BM == 64, "half a 32-row block, or one or two blocks");
   static_assert(BN % 64 == 0 && BN <= 256, "whole waves, even gate and up halves");
   static_assert(SB == 128 || SB == 256, "stage rows of whole 128-byte lines");
   constexpr int NW = BN / 32;
   constexpr int NT = NW * 64;
+  constexpr int FM = BM < 32 ? 1 : BM / 32;   // 32-row accumulator blocks per wave
+  constexpr int BR = BM < 32 ? BM : 32;       // rows of one block that are stored
   constexpr int CPR = SB / 16;              // 16-byte chunks per stage row
   constexpr int RPI = 1024 / SB;            // rows per load instruction
   constexpr int KST = SB / 2;               // K values per stage
@@ -116,9 +119,9 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void stream_gemm_kernel(TileArgs p
   }
   const uint32_t ldsw = __builtin_amdgcn_readfirstlane(lds0 + 1024 * wave);
 
-  // Operand reads: A row lrow (rows >= BM give zeros), B row 32 wave + lrow;
-  // MFMA step t of a stage takes chunk 2 t + lgrp.
-  const int ar = lrow & (BM - 1);
+  // Operand reads: A row 32 i + lrow of block i (rows >= BM give zeros), B
+  // row 32 wave + lrow; MFMA step t of a stage takes chunk 2 t + lgrp.
+  const int ar = lrow & (BR - 1);
   const int br = 32 * wave + lrow;
   const bool a_live = lrow < BM;
   const uint32_t rA = lds0 + (uint32_t)(ar * SB), rB = lds0 + A_BYTES + (uint32_t)(br * SB);
@@ -160,7 +163,9 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void stream_gemm_kernel(TileArgs p
       });
     };
 
-    floatx16 acc = floatx16{};
+    floatx16 acc[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) acc[i] = floatx16{};
     for (int s = 0; s < NST - 1 && s < nss; ++s) issue_stage(s);
     for (int s = 0; s < nss; ++s) {
       wait_after((nss - 1 < s + NST - 2 ? nss - 1 : s + NST - 2) - s);
@@ -171,15 +176,16 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void stream_gemm_kernel(TileArgs p
       auto step = [&](auto t_c, bool tail) {
         constexpr int t = decltype(t_c)::value;
         const int c = 2 * t + lgrp;
-        bf16x8 a = lds_read16(rA + so + (uint32_t)((c ^ swa) << 4));
+        const int valid = K - (s * KST + 8 * c);  // values of this chunk inside K
         bf16x8 b = lds_read16(rB + so + (uint32_t)((c ^ swb) << 4));
-        if (!a_live) a = bf16x8{};
-        if (tail) {
-          const int valid = K - (s * KST + 8 * c);  // values of this chunk inside K
-          a = keep_first(a, valid);
-          b = keep_first(b, valid);
+        if (tail) b = keep_first(b, valid);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          bf16x8 a = lds_read16(rA + so + (uint32_t)(32 * i * SB + ((c ^ swa) << 4)));
+          if (!a_live) a = bf16x8{};
+          if (tail) a = keep_first(a, valid);
+          acc[i] = mma(a, b, acc[i]);
         }
-        acc = mma(a, b, acc);
       };
       if (s < nfull) {
         static_for<0, NSTEP>([&](auto t_c) { step(t_c, false); });
@@ -195,23 +201,33 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void stream_gemm_kernel(TileArgs p
     wait_lgkmcnt0();
     block_barrier();
     if (glu) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        lds_store_f4(lds0 + (uint32_t)(lrow * OPG + (32 * wave + 8 * q + 4 * lgrp) * 4),
-                     floatx4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]});
-      wait_lgkmcnt0();
-      block_barrier();
       const EpiOut eo{p.C, p.ldc, M, glu, p.bias, p.act, p.counts, p.flags};
-      store_staged_glu<OUT_BF16, DEBUG>(lds0, OPG, BM, BN / 2, BM, 0, m0, n0, tid, NT, eo);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          lds_store_f4(lds0 + (uint32_t)(lrow * OPG + (32 * wave + 8 * q + 4 * lgrp) * 4),
+                       floatx4{acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]});
+        wait_lgkmcnt0();
+        block_barrier();
+        store_staged_glu<OUT_BF16, DEBUG>(lds0, OPG, BR, BN / 2, BR, 0, m0 + 32 * i, n0, tid, NT, eo);
+        wait_lgkmcnt0();
+        block_barrier();
+      }
     } else {
       const uint32_t stf = lds0 + (uint32_t)(wave * 32 * OPF);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        lds_store_f4(stf + (uint32_t)(lrow * OPF + (8 * q + 4 * lgrp) * 4),
-                     floatx4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]});
-      wait_lgkmcnt0();
       const EpiOut eo{p.C, p.ldc, M, N, p.bias, p.act, p.counts, p.flags};
-      store_staged_fused<OUT_BF16, DEBUG>(stf, OPF, BM, 32, m0, n0 + 32 * wave, lane, 64, eo);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          lds_store_f4(stf + (uint32_t)(lrow * OPF + (8 * q + 4 * lgrp) * 4),
+                       floatx4{acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]});
+        wait_lgkmcnt0();
+        store_staged_fused<OUT_BF16, DEBUG>(stf, OPF, BR, 32, m0 + 32 * i, n0 + 32 * wave, lane, 64,
+                                            eo);
+        wait_lgkmcnt0();
+      }
     }
     wait_lgkmcnt0();
     block_barrier();

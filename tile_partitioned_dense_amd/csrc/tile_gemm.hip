@@ -192,10 +192,11 @@ hipError_t dispatch_tile(int cfg, const tg::TileArgs& a, int64_t grid, const tg:
     case 12: return tg::launch_tile<12>(a, grid, v, st);
     case 13: return tg::launch_tile<13>(a, grid, v, st);
     case 14: return tg::launch_tile<14>(a, grid, v, st);
+    case 15: return tg::launch_tile<15>(a, grid, v, st);
   }
   return hipErrorInvalidValue;
 }
-static_assert(tg::kNumTileConfigs == 15, "dispatch_tile covers every tile configuration");
+static_assert(tg::kNumTileConfigs == 16, "dispatch_tile covers every tile configuration");
 
 hipError_t dispatch_skinny(int cfg, const tg::SkinnyArgs& a, int64_t grid, const tg::Variant& v,
                            hipStream_t st) {
@@ -218,10 +219,11 @@ hipError_t dispatch_mx(int cfg, const tg::MxArgs& a, int fmt, int64_t grid, cons
     case 1: return tg::launch_mx<1>(a, fmt, grid, v, st);
     case 2: return tg::launch_mx<2>(a, fmt, grid, v, st);
     case 3: return tg::launch_mx<3>(a, fmt, grid, v, st);
+    case 4: return tg::launch_mx<4>(a, fmt, grid, v, st);
   }
   return hipErrorInvalidValue;
 }
-static_assert(tg::kNumMxConfigs == 4, "dispatch_mx covers every MX configuration");
+static_assert(tg::kNumMxConfigs == 5, "dispatch_mx covers every MX configuration");
 
 // Checks of tile_gemm_run_mx's arguments (see the header).
 tile_gemm_status_t check_mx(const void* A, const void* B, const void* C, int64_t M, int64_t N,
