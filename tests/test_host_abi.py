@@ -232,3 +232,12 @@ def test_mx_plan_few_rows_take_the_stream_kernel():
         assert (p.variant, p.config, p.bm, p.bn, p.bk) == (tg.VARIANT_MX, cfg, bm, 128, 256), M
         assert p.tiles == 28672 // p.bn and p.grid == 224
     assert tg.tile_gemm_plan_mx(65, 28672, 8192).bk == 64
+
+
+def test_smoke_shape_passes_the_argument_checks():
+    """smoke() hands contiguous operands of SMOKE_SHAPE to the library, so that
+    shape must satisfy its alignment rules for both B layouts it could use."""
+    import __graft_entry__ as ge
+    M, N, K = ge.SMOKE_SHAPE
+    for dt in (Dtype.BF16_TO_F32, Dtype.BF16_TO_BF16):
+        assert chk(M=M, N=N, K=K, s=(K, 1, N, 1, N, 1), dtype=dt) == Status.OK, tg.last_error_detail()
