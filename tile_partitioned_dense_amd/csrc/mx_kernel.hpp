@@ -270,13 +270,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
       }
     };
 
-    // prologue: slabs 0 .. NST-2 in flight, slab 0 landed and read
-    if (nk > 0) {
-      for (int s = 0; s < NST - 1 && s < nk; ++s) issue_slab(s);
-      wait_after((nk - 1 < NST - 2 ? nk - 1 : NST - 2));
-      block_barrier();
-      read_frags(0, 0);
-    }
     // Slab s: its operands are in registers (slot s % 2); slab s + 1 must land
     // before its operands are read during slab s's MFMAs; the stage of slab
     // s - 1 (read before the last barrier) takes slab s + NST - 1.
@@ -314,20 +307,48 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
             i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
       }
     };
-    auto dma_slot = [](int t, int n) constexpr { return ((2 * t + 1) * NMFMA) / (2 * n); };
-    // Steady step s (slab s + NST - 1 exists): the first half of slab s's
-    // MFMAs needs nothing new, so they run while this wave issues slab s + NST
-    // - 1 (into the stage of slab s - 1, whose reads every wave completed
-    // before the previous step's barrier) and while slab s + 1 is still
-    // landing; then the wait and the barrier for slab s + 1, and the second
-    // half of the MFMAs each followed by its share of slab s + 1's reads.
+    // DMA unit t of a slab (t < A_PER: this wave's A load t, else its B load
+    // t - A_PER) into the stage at byte offset st.
+    auto dma_unit = [&](uint32_t st, const i32x4& rsA, const i32x4& rsB, auto t_c) {
+      constexpr int t = decltype(t_c)::value;
+      if constexpr (t < A_PER)
+        dma16(ldsw + st + 1024 * NW * t, rsA, voA[t], 0u);
+      else
+        dma16(ldsw + st + A_BYTES + 1024 * NW * (t - A_PER), rsB, voB[t - A_PER], 0u);
+    };
+    // Steady step s (slab s + NST - 1 exists). A slab's loads go out in two
+    // parts: its first H1 units (and the scale window it opens) right after
+    // the barrier of the step before, its other units during the first half of
+    // this step's MFMAs, so the loads of a slab are spread over a whole slab
+    // of MFMAs instead of arriving at the texture unit as one burst (a wave
+    // that finds the address queue full stalls, MFMAs included).
+    //   first half of slab s's MFMAs (they need nothing new), with the late
+    //     units of slab s + NST - 1 into the stage of slab s - 1;
+    //   wait for slab s + 1 and the barrier (every wave has then read slab s
+    //     into registers, so slab s's stage is free);
+    //   second half of the MFMAs, each followed by its share of slab s + 1's
+    //     operand reads and of the first units of slab s + NST into slab s's
+    //     stage. After the last steady step slab s + NST lies past K: those
+    //     loads read bytes inside the operand (or zeros past it) into a stage
+    //     nothing reads again, and the waits that follow count them as extra
+    //     loads, so they only wait longer.
     constexpr int HALF = NMFMA / 2;
     constexpr int UPH = (NUNIT + HALF - 1) / HALF;  // operand units read after each MFMA
+    constexpr int H1 = NDMA / 2;                     // units of a slab issued a step early
+    static_assert((NST - 2) * NDMA + H1 <= 63, "loads in flight fit the counter");
+    auto slot_late = [](int u) constexpr { return ((2 * u + 1) * HALF) / (2 * (NDMA - H1)); };
+    auto slot_early = [](int u) constexpr { return HALF + ((2 * u + 1) * (NMFMA - HALF)) / (2 * H1); };
+    auto issue_first = [&](int sl) {
+      if (sl % SPW == 0) issue_window(sl / SPW);
+      const uint32_t st = (uint32_t)(sl % NST) * STAGE;
+      const i32x4 rsA = make_rsrc(a_panel + (int64_t)sl * BKB, a_bytes - (int64_t)sl * BKB);
+      const i32x4 rsB = make_rsrc(b_panel + (int64_t)sl * BKB, b_bytes - (int64_t)sl * BKB);
+      static_for<0, H1>([&](auto t_c) { dma_unit(st, rsA, rsB, t_c); });
+    };
     auto step_full = [&](int s, auto par_c) {
       constexpr int PAR = decltype(par_c)::value;
       if (FP4 || PAR == 0) take_scales(s);
       const int sn = s + NST - 1;
-      if (sn % SPW == 0) issue_window(sn / SPW);
       const uint32_t stn = (uint32_t)(sn % NST) * STAGE;
       const i32x4 rsA = make_rsrc(a_panel + (int64_t)sn * BKB, a_bytes - (int64_t)sn * BKB);
       const i32x4 rsB = make_rsrc(b_panel + (int64_t)sn * BKB, b_bytes - (int64_t)sn * BKB);
@@ -336,30 +357,33 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
       static_for<0, HALF>([&](auto k_c) {
         constexpr int k = decltype(k_c)::value;
         mfma_k(k_c, par_c, PAR);
-        static_for<0, NDMA>([&](auto t_c) {
+        static_for<H1, NDMA>([&](auto t_c) {
           constexpr int t = decltype(t_c)::value;
-          if constexpr (dma_slot(t, NDMA) / 2 == k) {
-            if constexpr (t < A_PER)
-              dma16(ldsw + stn + 1024 * NW * t, rsA, voA[t], 0u);
-            else
-              dma16(ldsw + stn + A_BYTES + 1024 * NW * (t - A_PER), rsB, voB[t - A_PER], 0u);
-          }
+          if constexpr (slot_late(t - H1) == k) dma_unit(stn, rsA, rsB, t_c);
         });
       });
       __builtin_amdgcn_sched_barrier(0);
       // slab s + 1 has landed once at most the loads of slabs s + 2 .. s + NST - 1
       // remain (scale windows among them only make the wait longer); this
       // wave's LDS reads (of slab s, issued last step) are complete before the
-      // barrier, so the next step may load slab s + NST into slab s's stage
-      wait_vmcnt<((NST - 2) * NDMA < 63 ? (NST - 2) * NDMA : 63)>();
+      // barrier
+      wait_vmcnt<(NST - 2) * NDMA>();
       wait_lgkmcnt0();
       block_barrier();
+      const int se = sn + 1;
+      if (se % SPW == 0) issue_window(se / SPW);
+      const uint32_t ste = (uint32_t)(se % NST) * STAGE;
+      const i32x4 rsAe = make_rsrc(a_panel + (int64_t)se * BKB, a_bytes - (int64_t)se * BKB);
+      const i32x4 rsBe = make_rsrc(b_panel + (int64_t)se * BKB, b_bytes - (int64_t)se * BKB);
       static_for<HALF, NMFMA>([&](auto k_c) {
         constexpr int k = decltype(k_c)::value;
         mfma_k(k_c, par_c, PAR);
         static_for<0, UPH>([&](auto r_c) {
           constexpr int idx = (k - HALF) * UPH + decltype(r_c)::value;
           if constexpr (idx < NUNIT) read_unit(so, PAR ^ 1, std::integral_constant<int, idx>{});
+        });
+        static_for<0, H1>([&](auto t_c) {
+          if constexpr (slot_early(decltype(t_c)::value) == k) dma_unit(ste, rsAe, rsBe, t_c);
         });
       });
       static_for<HALF, NMFMA>([&](auto k_c) {
@@ -371,11 +395,35 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
       });
       __builtin_amdgcn_sched_barrier(0);
     };
+    // prologue: slabs 0 .. NST-2 in flight (and, when steady steps follow,
+    // the first units of slab NST - 1, as a step before step 0 would issue
+    // them), slab 0 landed and read
+    const int n_full = nk - (NST - 1);  // steady steps: slab s + NST - 1 exists
+    if (nk > 0) {
+      for (int sl = 0; sl < NST - 1 && sl < nk; ++sl) issue_slab(sl);
+      if (n_full > 0) {
+        issue_first(NST - 1);
+        wait_vmcnt<(NST - 2) * NDMA + H1>();
+      } else {
+        wait_after((nk - 1 < NST - 2 ? nk - 1 : NST - 2));
+      }
+      block_barrier();
+      read_frags(0, 0);
+    }
+    // Steps run in pairs (the register slot of slab s is s % 2). Every slab
+    // is issued by a steady step or the prologue, so the other steps issue
+    // nothing.
     int s = 0;
-    const int n_full = nk - (NST - 1);  // slabs whose slab + NST - 1 exists
+    const std::integral_constant<int, 0> p0{};
+    const std::integral_constant<int, 1> p1{};
     for (; s + 2 <= n_full; s += 2) {
-      step_full(s, std::integral_constant<int, 0>{});
-      step_full(s + 1, std::integral_constant<int, 1>{});
+      step_full(s, p0);
+      step_full(s + 1, p1);
+    }
+    if (s < n_full) {  // an odd number of steady steps: the last one, then realign
+      step_full(s, p0);
+      ++s;
+      if (s < nk) step(s++, p1);
     }
     for (; s + 2 <= nk; s += 2) {
       step(s, std::integral_constant<int, 0>{});
