@@ -354,6 +354,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
       const i32x4 rsB = make_rsrc(b_panel + (int64_t)sn * BKB, b_bytes - (int64_t)sn * BKB);
       const uint32_t so = (uint32_t)((s + 1) % NST) * STAGE;
       __builtin_amdgcn_sched_barrier(0);
+      // (a fence after each MFMA and its loads: the loads are inline assembly,
+      // which the scheduler would otherwise gather into one burst)
       static_for<0, HALF>([&](auto k_c) {
         constexpr int k = decltype(k_c)::value;
         mfma_k(k_c, par_c, PAR);
@@ -361,6 +363,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
           constexpr int t = decltype(t_c)::value;
           if constexpr (slot_late(t - H1) == k) dma_unit(stn, rsA, rsB, t_c);
         });
+        __builtin_amdgcn_sched_barrier(0);
       });
       __builtin_amdgcn_sched_barrier(0);
       // slab s + 1 has landed once at most the loads of slabs s + 2 .. s + NST - 1
