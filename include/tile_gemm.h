@@ -172,7 +172,7 @@ tile_gemm_status_t tile_gemm_run_epilogue(tile_gemm_t h, const void* A, const vo
  * E4M3 and of 128 for E2M1 (TILE_GEMM_ERR_BAD_SHAPE otherwise). C, dtype, bias and act (not
  * TILE_GEMM_ACT_SWIGLU) are as for tile_gemm_run_epilogue; accumulation is
  * fp32 in ascending K, one owner per output tile, each element written once.
- * Outputs of up to 32 rows run a kernel that streams B in 256-byte pieces of
+ * Outputs of up to 64 rows run a kernel that streams B in 256-byte pieces of
  * K per row (plan bk = 256); larger ones the tile kernel (bk = 64).
  * A, B 16-byte aligned with 16-byte leading dimensions; scales 4-byte aligned.
  * All inputs are borrowed read-only until the stream reaches the work; C may
@@ -254,6 +254,10 @@ typedef enum {
  *                  tiles / ceil(tiles / cu_count) (a multiple of 8) and
  *                  workgroup w owns tiles w, w + grid, w + 2 grid, ..., each
  *                  whole, with its own K loop and store.
+ *                  With a column-major B, an even K and M <= 64 the tile
+ *                  variant runs the stream configurations (32 or 64 rows x
+ *                  128 columns, bk = 128: K moves 256 bytes per row at a
+ *                  time, for a weight stream bound by HBM).
  *   skinny kernel: each workgroup owns rows [0, M) x bn columns; the waves of
  *                  one workgroup split K and combine their partial sums in a
  *                  fixed order; grid = tiles = tiles_n, tiles_m = 1.
@@ -300,7 +304,9 @@ enum {
 };
 /* Run a given compiled configuration instead of the planner's choice, so tests
  * can cover every configuration at small sizes. A forced skinny configuration
- * needs M <= its row capacity (16 * row groups). Forced configurations and
+ * needs M <= its row capacity (16 * row groups); a forced stream
+ * configuration a column-major B and an even K (else TILE_GEMM_ERR_BAD_SHAPE).
+ * Forced configurations and
  * grids run the production kernel instances; only TILE_GEMM_DEBUG_COUNT_WRITES
  * and TILE_GEMM_DEBUG_COLLIDE select the instrumented ones. */
 #define TILE_GEMM_DEBUG_FORCE_TILE(c) ((((c) + 1) & 0xff) << 8)
