@@ -13,7 +13,7 @@ template <int CFG, int FMT, bool OB, bool DB>
 const void* mx_fn() {
   constexpr MxConfig c = kMxConfigs[CFG];
   if constexpr (c.sb > 0)
-    return reinterpret_cast<const void*>(&mx_stream_kernel<c.bm, c.bn, c.sb, c.stages, FMT, OB, DB>);
+    return reinterpret_cast<const void*>(&mx_stream_kernel<c.bm, c.bn, c.sb, c.stages, c.ks, FMT, OB, DB>);
   else
     return reinterpret_cast<const void*>(&mx_gemm_kernel<c.bm, c.bn, c.wm, c.wn, c.stages, FMT, OB, DB>);
 }
@@ -29,7 +29,7 @@ hipError_t launch_mx(const MxArgs& a, int fmt, int64_t grid_wgs, const Variant& 
                      hipStream_t stream) {
   constexpr MxConfig c = kMxConfigs[CFG];
   const dim3 grid((unsigned)grid_wgs);
-  const dim3 block(c.wm * c.wn * 64);
+  const dim3 block(c.wm * c.wn * c.ks * 64);
   const void* fn = fmt == kMxE2M1 ? mx_fn_out<CFG, kMxE2M1>(v) : mx_fn_out<CFG, kMxE4M3>(v);
   return launch_raw(fn, grid, block, a, stream);
 }

@@ -16,7 +16,7 @@ const void* tile_fn() {
   constexpr TileConfig c = kTileConfigs[CFG];
   if constexpr (c.sb > 0) {
     if constexpr (BC)
-      return reinterpret_cast<const void*>(&stream_gemm_kernel<c.bm, c.bn, c.sb, c.stages, OB, DB>);
+      return reinterpret_cast<const void*>(&stream_gemm_kernel<c.bm, c.bn, c.sb, c.stages, c.ks, OB, DB>);
     else
       return nullptr;
   } else if constexpr (c.ks > 1)

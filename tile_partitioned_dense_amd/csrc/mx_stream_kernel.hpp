@@ -48,13 +48,15 @@
 
 namespace tg {
 
-template <int BM, int BN, int SB, int NST, int FMT, bool OUT_BF16, bool DEBUG>
-__global__ __launch_bounds__(BN / 32 * 64, 1) void mx_stream_kernel(MxArgs p) {
+template <int BM, int BN, int SB, int NST, int KS, int FMT, bool OUT_BF16, bool DEBUG>
+__global__ __launch_bounds__(BN / 32 * KS * 64, 1) void mx_stream_kernel(MxArgs p) {
   static_assert(BM == 16 || BM == 32 || BM == 64, "half a 32-row block, or one or two blocks");
   static_assert(BN % 64 == 0 && BN <= 256, "whole scale-window loads for B");
   static_assert(SB == 128 || SB == 256, "stage rows of whole 128-byte lines");
   static_assert(FMT == kMxE4M3 || FMT == kMxE2M1, "E4M3 or E2M1 elements");
-  constexpr int NW = BN / 32;
+  static_assert(KS == 1 || KS == 2, "one or two waves per 32-column block");
+  constexpr int NCB = BN / 32;               // 32-column blocks
+  constexpr int NW = NCB * KS;               // waves (all of them issue loads)
   constexpr int FM = BM < 32 ? 1 : BM / 32;   // 32-row accumulator blocks per wave
   constexpr int BR = BM < 32 ? BM : 32;       // rows of one block that are stored
   constexpr bool FP4 = FMT == kMxE2M1;
@@ -62,6 +64,8 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void mx_stream_kernel(MxArgs p) {
   constexpr int CPR = SB / 16;              // 16-byte chunks per stage row
   constexpr int RPI = 1024 / SB;            // rows per load instruction
   constexpr int SPS = SB / 64;              // 64-byte slabs per stage
+  constexpr int KSL = SPS / KS;             // of which each wave of a block takes
+  static_assert(KSL % 2 == 0 || KS == 1, "each wave's slabs start at an even slab");
   constexpr int KPS = FP4 ? 128 : 64;       // K values per slab
   constexpr int SPW = FP4 ? 4 : 8;          // slabs per 16-byte scale window
   constexpr int SSW = SPW / SPS;            // stages per scale window
@@ -116,10 +120,13 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void mx_stream_kernel(MxArgs p) {
   }
   const uint32_t ldsw = __builtin_amdgcn_readfirstlane(lds0 + 1024 * wave);
 
+  // Wave w works on column block cb = w % NCB and, with two waves per block,
+  // on slabs kh * KSL .. of every stage (kh = w / NCB).
+  const int cb = wave % NCB, kh = wave / NCB;
   // Operand reads: A row 32 i + lrow of block i (rows >= BM give zeros), B
-  // row 32 wave + lrow; slab j of a stage is chunks 4 j + lgrp and 4 j + 2 + lgrp.
+  // row 32 cb + lrow; slab j of a stage is chunks 4 j + lgrp and 4 j + 2 + lgrp.
   const int ar = lrow & (BR - 1);
-  const int br = 32 * wave + lrow;
+  const int br = 32 * cb + lrow;
   const bool a_live = lrow < BM;
   const uint32_t rA = lds0 + (uint32_t)(ar * SB), rB = lds0 + A_BYTES + (uint32_t)(br * SB);
   const int swa = swz(ar), swb = swz(br);
@@ -192,8 +199,10 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void mx_stream_kernel(MxArgs p) {
       if (s + NST - 1 < nss) issue_stage(s + NST - 1);
       const uint32_t so = (uint32_t)(s % NST) * STAGE;
       const uint32_t wb = swin0 + (uint32_t)(((s / SSW) % NWB) * SWIN);
-      auto slab = [&](auto j_c) {
-        constexpr int j = decltype(j_c)::value;
+      // slab j = kh KSL + jj of the stage; jj and j have the same parity
+      auto slab = [&](auto jj_c) {
+        constexpr int jj = decltype(jj_c)::value;
+        const int j = kh * KSL + jj;
         {
           const int c0 = 4 * j + lgrp, c1 = 4 * j + 2 + lgrp;
           uint4 x = __builtin_bit_cast(uint4, lds_read16(rB + so + (uint32_t)(((c0 ^ swb)) << 4)));
@@ -222,29 +231,55 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void mx_stream_kernel(MxArgs p) {
               acc[i] = mma_mx<0, HW>(fp4_half<0>(af), fp4_half<0>(bf), sa, sb, acc[i]);
               acc[i] = mma_mx<2, HW>(fp4_half<1>(af), fp4_half<1>(bf), sa, sb, acc[i]);
             } else {
-              acc[i] = mma_mx<2 * (j % 2), HW>(af, bf, sa, sb, acc[i]);
+              acc[i] = mma_mx<2 * (jj % 2), HW>(af, bf, sa, sb, acc[i]);
             }
           }
         }
       };
       if (SPS * (s + 1) <= nk) {
-        static_for<0, SPS>(slab);
+        static_for<0, KSL>(slab);
       } else {
-        static_for<0, SPS>([&](auto j_c) {
-          if (SPS * s + decltype(j_c)::value < nk) slab(j_c);
+        static_for<0, KSL>([&](auto jj_c) {
+          if (SPS * s + kh * KSL + decltype(jj_c)::value < nk) slab(jj_c);
         });
       }
     }
 
-    // Store: each wave stages its 32 columns (32 rows at a time) as fp32 in
-    // the free ring and writes them once per element (with the fused
-    // epilogue when asked).
+    // Store: the first wave of each block stages its 32 columns (32 rows at a
+    // time) as fp32 in the free ring and writes them once per element (with
+    // the fused epilogue when asked); with two waves per block the second
+    // passes its partial sums through the top of the ring first and the first
+    // adds them, always in that order.
     wait_lgkmcnt0();
     block_barrier();
-    {
+    constexpr int PART = KS > 1 ? NCB * FM * 4096 : 0;
+    if constexpr (KS > 1) {
+      const uint32_t pb = lds0 + (uint32_t)(RING - PART);
+      if (kh == 1) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            lds_store_f4(pb + (uint32_t)((cb * FM + i) * 4096 + q * 1024 + lane * 16),
+                         floatx4{acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]});
+      }
+      wait_lgkmcnt0();
+      block_barrier();
+      if (kh == 0) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const floatx4 v = lds_load_f4(pb + (uint32_t)((cb * FM + i) * 4096 + q * 1024 + lane * 16));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][4 * q + e] += v[e];
+          }
+      }
+    }
+    if (kh == 0) {
       constexpr int OPF = 32 * 4 + 16;
-      static_assert(NW * 32 * OPF <= RING, "an fp32 strip of every wave fits the ring");
-      const uint32_t stf = lds0 + (uint32_t)(wave * 32 * OPF);
+      static_assert(NCB * 32 * OPF + PART <= RING, "fp32 strips and partial sums fit the ring");
+      const uint32_t stf = lds0 + (uint32_t)(cb * 32 * OPF);
       const EpiOut eo{p.C, p.ldc, M, N, p.bias, p.act, p.counts, p.flags};
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -253,7 +288,7 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void mx_stream_kernel(MxArgs p) {
           lds_store_f4(stf + (uint32_t)(lrow * OPF + (8 * q + 4 * lgrp) * 4),
                        floatx4{acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]});
         wait_lgkmcnt0();
-        store_staged_fused<OUT_BF16, DEBUG>(stf, OPF, BR, 32, m0 + 32 * i, n0 + 32 * wave, lane, 64,
+        store_staged_fused<OUT_BF16, DEBUG>(stf, OPF, BR, 32, m0 + 32 * i, n0 + 32 * cb, lane, 64,
                                             eo);
         wait_lgkmcnt0();
       }

@@ -76,8 +76,10 @@ constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
     {64, 64, 1, 1, 4, 0.28f, 4},    // 11: 4 waves, each 64x64 over a quarter of K
     {64, 128, 1, 1, 3, 0.42f, 4},   // 12: 4 waves, each 64x128 over a quarter of K
     {128, 64, 1, 1, 3, 0.39f, 4},   // 13: 4 waves, each 128x64 over a quarter of K
-    {32, 128, 1, 4, 3, 0.0f, 1, 0.0f, 1, 256},  // 14: stream, 32x128, 3 stages of 256 bytes
-    {64, 128, 1, 4, 3, 0.0f, 1, 0.0f, 1, 256},  // 15: stream, 64x128, 3 stages of 256 bytes
+    // 14, 15: stream, 32 or 64 rows x 128 columns, 3 stages of 256 bytes, two
+    // waves per 32-column block, each taking half of every stage's K
+    {32, 128, 1, 4, 3, 0.0f, 2, 0.0f, 1, 256},
+    {64, 128, 1, 4, 3, 0.0f, 2, 0.0f, 1, 256},
 };
 constexpr int kStreamConfig = 14;    // the planner's stream configuration up to 32 rows,
 constexpr int kStreamConfig64 = 15;  // and from 33 to 64 rows
@@ -101,14 +103,17 @@ struct MxConfig {
   int bm, bn, wm, wn, stages;
   float eff;
   int sb = 0;  // stream kernel: bytes of K per row and stage; 0: tile kernel
+  int ks = 1;  // stream kernel: waves per 32-column block (each a share of every stage's K)
 };
 constexpr int kNumMxConfigs = 5;
 constexpr MxConfig kMxConfigs[kNumMxConfigs] = {
     {256, 256, 2, 2, 4, 1.00f},  // 0: 4 waves of 128x128
     {128, 128, 2, 2, 4, 0.70f},  // 1: 4 waves of 64x64
     {64, 128, 2, 2, 12, 0.50f},  // 2: 4 waves of 32x64, 12 stages: few rows, weight streaming
-    {32, 128, 1, 4, 3, 0.0f, 256},  // 3: stream, 32 x 128, 3 stages of 256 bytes
-    {64, 128, 1, 4, 3, 0.0f, 256},  // 4: stream, 64 x 128, 3 stages of 256 bytes
+    // 3, 4: stream, 32 or 64 rows x 128 columns, 3 stages of 256 bytes, two
+    // waves per 32-column block, each taking half of every stage's slabs
+    {32, 128, 1, 4, 3, 0.0f, 256, 2},
+    {64, 128, 1, 4, 3, 0.0f, 256, 2},
 };
 constexpr int kMxBK = 64;          // bytes of K per row in one slab of the MX tile kernel
 constexpr int kMxStreamMaxM = 64;  // M at or below this takes the stream kernel
@@ -242,7 +247,7 @@ inline Plan plan_for_mx(int config, int64_t M, int64_t N, int cu_count) {
   p.bm = c.bm;
   p.bn = c.bn;
   p.bk = c.sb ? c.sb : kMxBK;
-  p.threads = c.wm * c.wn * 64;
+  p.threads = c.wm * c.wn * c.ks * 64;
   p.lds_bytes = c.stages * (c.bm + c.bn) * p.bk;
   p.k_split = 1;
   p.map.tiles_m = (int32_t)ceil_div(M, c.bm);

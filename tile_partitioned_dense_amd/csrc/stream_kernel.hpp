@@ -59,12 +59,14 @@ __device__ __forceinline__ bf16x8 keep_first(const bf16x8& v, int valid) {
   return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
-template <int BM, int BN, int SB, int NST, bool OUT_BF16, bool DEBUG>
-__global__ __launch_bounds__(BN / 32 * 64, 1) void stream_gemm_kernel(TileArgs p) {
+template <int BM, int BN, int SB, int NST, int KS, bool OUT_BF16, bool DEBUG>
+__global__ __launch_bounds__(BN / 32 * KS * 64, 1) void stream_gemm_kernel(TileArgs p) {
   static_assert(BM == 16 || BM == 32 || BM == 64, "half a 32-row block, or one or two blocks");
   static_assert(BN % 64 == 0 && BN <= 256, "whole waves, even gate and up halves");
   static_assert(SB == 128 || SB == 256, "stage rows of whole 128-byte lines");
-  constexpr int NW = BN / 32;
+  static_assert(KS == 1 || KS == 2, "one or two waves per 32-column block");
+  constexpr int NCB = BN / 32;               // 32-column blocks
+  constexpr int NW = NCB * KS;               // waves (all of them issue loads)
   constexpr int NT = NW * 64;
   constexpr int FM = BM < 32 ? 1 : BM / 32;   // 32-row accumulator blocks per wave
   constexpr int BR = BM < 32 ? BM : 32;       // rows of one block that are stored
@@ -72,6 +74,7 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void stream_gemm_kernel(TileArgs p
   constexpr int RPI = 1024 / SB;            // rows per load instruction
   constexpr int KST = SB / 2;               // K values per stage
   constexpr int NSTEP = SB / 32;            // 16-K MFMA steps per stage
+  constexpr int KSTEP = NSTEP / KS;         // of which each wave of a block takes
   constexpr int A_BYTES = BM * SB, B_BYTES = BN * SB;
   constexpr int STAGE = A_BYTES + B_BYTES;
   constexpr int A_DMA = A_BYTES / 1024, B_DMA = B_BYTES / 1024;
@@ -85,7 +88,9 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void stream_gemm_kernel(TileArgs p
   static_assert(RING <= 160 * 1024, "LDS");
   constexpr int OPF = 32 * 4 + 16;          // per-wave fp32 strip pitch
   constexpr int OPG = BN * 4 + 16;          // block-wide fp32 strip pitch (SiLU(gate) * up)
-  static_assert(NW * 32 * OPF <= RING && 32 * OPG <= RING, "staged strips fit the ring");
+  constexpr int PART = KS > 1 ? NCB * FM * 4096 : 0;  // second waves' partial sums
+  static_assert(NCB * 32 * OPF + PART <= RING && 32 * OPG + PART <= RING,
+                "staged strips and partial sums fit the ring side by side");
 
   __shared__ __attribute__((aligned(1024))) uint4 smem[RING / 16];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
@@ -119,10 +124,13 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void stream_gemm_kernel(TileArgs p
   }
   const uint32_t ldsw = __builtin_amdgcn_readfirstlane(lds0 + 1024 * wave);
 
+  // Wave w works on column block cb = w % NCB and, with two waves per block,
+  // on MFMA steps kh * KSTEP .. of every stage (kh = w / NCB).
+  const int cb = wave % NCB, kh = wave / NCB;
   // Operand reads: A row 32 i + lrow of block i (rows >= BM give zeros), B
-  // row 32 wave + lrow; MFMA step t of a stage takes chunk 2 t + lgrp.
+  // row 32 cb + lrow; MFMA step t of a stage takes chunk 2 t + lgrp.
   const int ar = lrow & (BR - 1);
-  const int br = 32 * wave + lrow;
+  const int br = 32 * cb + lrow;
   const bool a_live = lrow < BM;
   const uint32_t rA = lds0 + (uint32_t)(ar * SB), rB = lds0 + A_BYTES + (uint32_t)(br * SB);
   const int swa = swz(ar), swb = swz(br);
@@ -174,7 +182,7 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void stream_gemm_kernel(TileArgs p
       if (s + NST - 1 < nss) issue_stage(s + NST - 1);
       const uint32_t so = (uint32_t)(s % NST) * STAGE;
       auto step = [&](auto t_c, bool tail) {
-        constexpr int t = decltype(t_c)::value;
+        const int t = kh * KSTEP + decltype(t_c)::value;
         const int c = 2 * t + lgrp;
         const int valid = K - (s * KST + 8 * c);  // values of this chunk inside K
         bf16x8 b = lds_read16(rB + so + (uint32_t)((c ^ swb) << 4));
@@ -188,34 +196,61 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void stream_gemm_kernel(TileArgs p
         }
       };
       if (s < nfull) {
-        static_for<0, NSTEP>([&](auto t_c) { step(t_c, false); });
+        static_for<0, KSTEP>([&](auto t_c) { step(t_c, false); });
       } else {
-        static_for<0, NSTEP>([&](auto t_c) {
-          if (s * KST + 16 * decltype(t_c)::value < K) step(t_c, true);
+        static_for<0, KSTEP>([&](auto t_c) {
+          if (s * KST + 16 * (kh * KSTEP + decltype(t_c)::value) < K) step(t_c, true);
         });
       }
     }
 
     // Store: the finished accumulators are staged as fp32 in the free ring
-    // and written once per element (bias and activation applied there).
+    // and written once per element (bias and activation applied there). With
+    // two waves per block the second passes its partial sums through LDS
+    // (the top of the ring) and the first adds them, always in that order.
     wait_lgkmcnt0();
     block_barrier();
+    if constexpr (KS > 1) {
+      const uint32_t pb = lds0 + (uint32_t)(RING - PART);
+      if (kh == 1) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            lds_store_f4(pb + (uint32_t)((cb * FM + i) * 4096 + q * 1024 + lane * 16),
+                         floatx4{acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]});
+      }
+      wait_lgkmcnt0();
+      block_barrier();
+      if (kh == 0) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const floatx4 v = lds_load_f4(pb + (uint32_t)((cb * FM + i) * 4096 + q * 1024 + lane * 16));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][4 * q + e] += v[e];
+          }
+      }
+    }
     if (glu) {
       const EpiOut eo{p.C, p.ldc, M, glu, p.bias, p.act, p.counts, p.flags};
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
+        if (kh == 0) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          lds_store_f4(lds0 + (uint32_t)(lrow * OPG + (32 * wave + 8 * q + 4 * lgrp) * 4),
-                       floatx4{acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]});
+          for (int q = 0; q < 4; ++q)
+            lds_store_f4(lds0 + (uint32_t)(lrow * OPG + (32 * cb + 8 * q + 4 * lgrp) * 4),
+                         floatx4{acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]});
+        }
         wait_lgkmcnt0();
         block_barrier();
         store_staged_glu<OUT_BF16, DEBUG>(lds0, OPG, BR, BN / 2, BR, 0, m0 + 32 * i, n0, tid, NT, eo);
         wait_lgkmcnt0();
         block_barrier();
       }
-    } else {
-      const uint32_t stf = lds0 + (uint32_t)(wave * 32 * OPF);
+    } else if (kh == 0) {
+      const uint32_t stf = lds0 + (uint32_t)(cb * 32 * OPF);
       const EpiOut eo{p.C, p.ldc, M, N, p.bias, p.act, p.counts, p.flags};
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -224,7 +259,7 @@ __global__ __launch_bounds__(BN / 32 * 64, 1) void stream_gemm_kernel(TileArgs p
           lds_store_f4(stf + (uint32_t)(lrow * OPF + (8 * q + 4 * lgrp) * 4),
                        floatx4{acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]});
         wait_lgkmcnt0();
-        store_staged_fused<OUT_BF16, DEBUG>(stf, OPF, BR, 32, m0 + 32 * i, n0 + 32 * wave, lane, 64,
+        store_staged_fused<OUT_BF16, DEBUG>(stf, OPF, BR, 32, m0 + 32 * i, n0 + 32 * cb, lane, 64,
                                             eo);
         wait_lgkmcnt0();
       }
