@@ -21,10 +21,14 @@
 // chunk each lane fetches; every instruction still reads one KiB of whole
 // row pieces.
 //
-// Wave w owns the tile's columns 32 w .. 32 w + 31 and all its rows, one
-// 32 x 32 accumulator block per 32 rows held transposed (as in the tile
-// kernels: the B fragment is the instruction's first operand, read once for
-// all blocks). With BM = 16 the lanes of
+// KS waves (one or two) work on each 32-column block of the tile, all its
+// rows: wave w takes block w % (BN / 32) and, of every stage's slabs, the
+// share (w / (BN / 32)) * SPS / KS ..; every wave issues a share of the
+// loads. A wave holds one 32 x 32 accumulator block per 32 rows, transposed
+// (as in the tile kernels: the B fragment is the instruction's first operand,
+// read once for all blocks); with KS = 2 the second wave of a block adds its
+// partial sums into the first's after the K loop, always in that order, and
+// the first stores. With BM = 16 the lanes of
 // rows 16..31 give zero A operands, so the block's upper half stays zero and
 // is never stored. The operand layout, the scale placement (lane r + 32 b
 // holds the scale of block b of row r) and the per-format instruction count
@@ -36,9 +40,10 @@
 //
 // Each step waits for stage s, passes one barrier (after which every wave is
 // done with stage s - 1), loads stage s + NST - 1 into stage s - 1's buffer
-// and then runs stage s's MFMAs; NST - 1 stages stay in flight. K advances in
-// ascending order with fp32 accumulation, so results are bit-identical run
-// to run. K must be a multiple of the slab (64 E4M3 or 128 E2M1 values); a
+// and then runs stage s's MFMAs; NST - 1 stages stay in flight. Each wave
+// accumulates its share of K in ascending order in fp32 and the two shares
+// of a block meet in a fixed order, so results are bit-identical run to run.
+// K must be a multiple of the slab (64 E4M3 or 128 E2M1 values); a
 // last stage that is only partly inside K runs only its valid slabs (the
 // bytes loaded past a row's end belong to the next row or read as zero and
 // are never used).

@@ -18,17 +18,23 @@
 // fetches; the sixteen rows one MFMA operand read touches (same chunk,
 // consecutive rows) then sit in sixteen distinct bank groups.
 //
-// Wave w owns the tile's columns 32 w .. 32 w + 31 and all its rows: one
-// 32 x 32 accumulator block per 32 rows, held transposed (the B fragment is
+// KS waves (one or two) work on each 32-column block of the tile, all its
+// rows: wave w takes block w % (BN / 32) and, of every stage's MFMA steps,
+// the share (w / (BN / 32)) * NSTEP / KS ..; every wave issues a share of
+// the loads (two waves per SIMD hide each other's issue stalls). A wave holds
+// one 32 x 32 accumulator block per 32 rows, transposed (the B fragment is
 // the MFMA's first operand, as in mma(), and is read once for all blocks),
 // fed by v_mfma_f32_32x32x16_bf16 over chunk pairs 2 t, 2 t + 1 of a stage.
-// With BM = 16 the lanes of rows 16..31 give zero A operands and are never
+// With KS = 2 the second wave of a block adds its partial sums into the
+// first's after the K loop, always in that order, and the first stores. With
+// BM = 16 the lanes of rows 16..31 give zero A operands and are never
 // stored.
 //
 // Each step waits for stage s, passes one barrier (after which every wave is
 // done with stage s - 1), loads stage s + NST - 1 into stage s - 1's buffer
-// and then runs stage s's MFMAs. K advances in ascending order with fp32
-// accumulation: results are bit-identical run to run. A last stage that ends
+// and then runs stage s's MFMAs. Each wave accumulates its share of K in
+// ascending order in fp32, and the two shares of a block meet in a fixed
+// order: results are bit-identical run to run. A last stage that ends
 // inside K zeroes, in both operands, every value at or past K (the bytes
 // loaded there belong to the next row, or read as zero past the operand).
 // K must be even: the range check of a buffer load works on whole dwords, so
