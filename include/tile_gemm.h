@@ -255,9 +255,10 @@ typedef enum {
  *                  workgroup w owns tiles w, w + grid, w + 2 grid, ..., each
  *                  whole, with its own K loop and store.
  *                  With a column-major B, an even K and M <= 64 the tile
- *                  variant runs the stream configurations (32 or 64 rows x
- *                  128 columns, bk = 128: K moves 256 bytes per row at a
- *                  time, for a weight stream bound by HBM).
+ *                  variant runs the stream configurations (32 x 64 tiles
+ *                  with bk = 256 up to 32 rows, 64 x 128 with bk = 128
+ *                  above: K moves 512 or 256 bytes per row at a time, for a
+ *                  weight stream bound by HBM).
  *   skinny kernel: each workgroup owns rows [0, M) x bn columns; the waves of
  *                  one workgroup split K and combine their partial sums in a
  *                  fixed order; grid = tiles = tiles_n, tiles_m = 1.

@@ -2,7 +2,7 @@
 planner's choice for column-major B, even K and M <= 64) against the fp64
 oracle, through the C ABI.
 
-The stream kernel moves K in stages of 128 values per row and zeroes, in
+The stream kernel moves K in stages of 128 or 256 values per row and zeroes, in
 its last stage, every value at or past K; these cases put K on both sides of
 stage and 8-value chunk boundaries, rows on both sides of the 32-row tile,
 columns on both sides of the 128-column tile, and the owned tiles on one or

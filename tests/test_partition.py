@@ -86,12 +86,12 @@ def test_expected_plans_for_workloads():
 
 def test_few_rows_of_column_major_b_take_the_stream_kernel():
     """Column-major B, even K and M <= 64: the stream configurations (one
-    tile row of 32 or 64 rows x 128 columns, 128 K values per stage);
-    row-major B keeps the skinny kernel, 65 rows the tile kernel's other
-    configurations."""
+    tile row: 32 x 64 tiles with 256 K values per stage up to 32 rows, 64 x
+    128 with 128 above); row-major B keeps the skinny kernel, 65 rows the
+    tile kernel's other configurations."""
     for M in (1, 16, 17, 32):
         p = tg.tile_gemm_plan(M, 28672, 8192, True, CU)
-        assert (p.variant, p.bm, p.bn, p.bk, p.tiles, p.grid) == (tg.VARIANT_TILE, 32, 128, 128, 224, 224)
+        assert (p.variant, p.bm, p.bn, p.bk, p.tiles, p.grid) == (tg.VARIANT_TILE, 32, 64, 256, 448, 224)
     p = tg.tile_gemm_plan(64, 28672, 8192, True, CU)
     assert (p.bm, p.bn, p.bk, p.tiles, p.grid) == (64, 128, 128, 224, 224)
     assert tg.tile_gemm_plan(16, 28672, 8192, False, CU).variant == tg.VARIANT_SKINNY

@@ -76,9 +76,10 @@ constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
     {64, 64, 1, 1, 4, 0.28f, 4},    // 11: 4 waves, each 64x64 over a quarter of K
     {64, 128, 1, 1, 3, 0.42f, 4},   // 12: 4 waves, each 64x128 over a quarter of K
     {128, 64, 1, 1, 3, 0.39f, 4},   // 13: 4 waves, each 128x64 over a quarter of K
-    // 14, 15: stream, 32 or 64 rows x 128 columns, 3 stages of 256 bytes, two
-    // waves per 32-column block, each taking half of every stage's K
-    {32, 128, 1, 4, 3, 0.0f, 2, 0.0f, 1, 256},
+    // 14, 15: stream, 3 stages, two waves per 32-column block, each taking
+    // half of every stage's K: 32 rows x 64 columns with stages of 512 bytes
+    // per row (up to 32 rows), 64 x 128 with 256 bytes (33 to 64 rows)
+    {32, 64, 1, 2, 3, 0.0f, 2, 0.0f, 1, 512},
     {64, 128, 1, 4, 3, 0.0f, 2, 0.0f, 1, 256},
 };
 constexpr int kStreamConfig = 14;    // the planner's stream configuration up to 32 rows,

@@ -13,8 +13,8 @@
 // covers 1024 / SB B columns with whole 128-byte lines; the tile kernel's
 // 64-byte slab would cover sixteen columns with half a line each. In LDS a
 // stage row is SB / 16 chunks of 16 bytes (8 values), chunk c of row r at
-// position c ^ swz(r) (swz(r) = r & 15 for 256-byte rows, (r >> 1) & 7 for
-// 128-byte rows), which the loads produce by permuting which chunk each lane
+// position c ^ swz(r) (swz(r) = r & 15 for rows of 256 bytes or more,
+// (r >> 1) & 7 for 128-byte rows), which the loads produce by permuting which chunk each lane
 // fetches; the sixteen rows one MFMA operand read touches (same chunk,
 // consecutive rows) then sit in sixteen distinct bank groups.
 //
@@ -69,7 +69,7 @@ template <int BM, int BN, int SB, int NST, int KS, bool OUT_BF16, bool DEBUG>
 __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void stream_gemm_kernel(TileArgs p) {
   static_assert(BM == 16 || BM == 32 || BM == 64, "half a 32-row block, or one or two blocks");
   static_assert(BN % 64 == 0 && BN <= 256, "whole waves, even gate and up halves");
-  static_assert(SB == 128 || SB == 256, "stage rows of whole 128-byte lines");
+  static_assert(SB == 128 || SB == 256 || SB == 512, "stage rows of whole 128-byte lines");
   static_assert(KS == 1 || KS == 2, "one or two waves per 32-column block");
   constexpr int NCB = BN / 32;               // 32-column blocks
   constexpr int NW = NCB * KS;               // waves (all of them issue loads)
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void stream_gemm_kernel(TileA
   const int glu = p.glu_half;
   const int gshift = glu ? glu - BN / 2 : 0;
 
-  auto swz = [](int r) { return SB == 256 ? (r & 15) : ((r >> 1) & 7); };
+  auto swz = [](int r) { return SB >= 256 ? (r & 15) : ((r >> 1) & 7); };
   // Load sources (bytes): instruction ins of a stage covers rows RPI ins ..;
   // lane l fills position l % CPR of row RPI ins + l / CPR, i.e. fetches chunk
   // (l % CPR) ^ swz(row) of that row's SB bytes.
