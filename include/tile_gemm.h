@@ -173,7 +173,8 @@ tile_gemm_status_t tile_gemm_run_epilogue(tile_gemm_t h, const void* A, const vo
  * TILE_GEMM_ACT_SWIGLU) are as for tile_gemm_run_epilogue; accumulation is
  * fp32 in ascending K, one owner per output tile, each element written once.
  * Outputs of up to 64 rows run a kernel that streams B in 256-byte pieces of
- * K per row (plan bk = 256); larger ones the tile kernel (bk = 64).
+ * K per row (plan bk = 256; 512 for few-column outputs of up to 32 rows);
+ * larger ones the tile kernel (bk = 64).
  * A, B 16-byte aligned with 16-byte leading dimensions; scales 4-byte aligned.
  * All inputs are borrowed read-only until the stream reaches the work; C may
  * overlap none of them. Enqueue-only, allocates nothing.

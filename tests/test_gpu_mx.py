@@ -46,8 +46,9 @@ def mx_config_table():
 
 
 def mx_stream_configs():
-    """(index, bm, bn, stages) of the stream-kernel configurations."""
-    return [(i, int(r[0]), int(r[1]), int(r[4])) for i, r in enumerate(_mx_config_rows())
+    """(index, bm, bn, stages, bytes of K per row and stage) of the stream-kernel
+    configurations."""
+    return [(i, int(r[0]), int(r[1]), int(r[4]), int(r[6])) for i, r in enumerate(_mx_config_rows())
             if len(r) > 6 and int(r[6]) > 0]
 
 
@@ -135,12 +136,12 @@ def test_mx_configs_integer_exact(g, fmt, cfg):
 
 
 @pytest.mark.parametrize("fmt", sorted(FMTS))
-@pytest.mark.parametrize("cfg,bm,bn,stages", mx_stream_configs())
-def test_mx_stream_ring(g, fmt, cfg, bm, bn, stages):
+@pytest.mark.parametrize("cfg,bm,bn,stages,sb", mx_stream_configs())
+def test_mx_stream_ring(g, fmt, cfg, bm, bn, stages, sb):
     """Stream kernel over many stages: the stage ring and the scale-window
     ring are each reused several times, the last stage is only partly inside
     K, two tile rows (M > bm) and a ragged last tile column."""
-    slabs = 4 * (stages + 3) + 3
+    slabs = (sb // 64) * (stages + 3) + 3
     M, N = bm + 3, 3 * bn + 5
     K = slabs * (128 if fmt == "e2m1" else 64)
     print(f"[mx stream {fmt} cfg {cfg} {M}x{N}x{K}]", flush=True)

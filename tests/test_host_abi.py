@@ -232,6 +232,9 @@ def test_mx_plan_few_rows_take_the_stream_kernel():
         assert (p.variant, p.config, p.bm, p.bn, p.bk) == (tg.VARIANT_MX, cfg, bm, 128, 256), M
         assert p.tiles == 28672 // p.bn and p.grid == 224
     assert tg.tile_gemm_plan_mx(65, 28672, 8192).bk == 64
+    # few columns: 64-column tiles with 512-byte stages keep more compute units busy
+    p = tg.tile_gemm_plan_mx(16, 7168, 8192)
+    assert (p.config, p.bm, p.bn, p.bk, p.tiles) == (5, 32, 64, 512, 112)
 
 
 def test_smoke_shape_passes_the_argument_checks():

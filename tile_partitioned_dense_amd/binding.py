@@ -63,7 +63,7 @@ DEBUG_ONE_TILE_PER_WG = 0x7F << 24
 
 
 N_TILE_CONFIGS = 16
-N_MX_CONFIGS = 5
+N_MX_CONFIGS = 6
 MX_E4M3 = 0
 MX_E2M1 = 1
 N_SKINNY_CONFIGS = 6

@@ -27,7 +27,7 @@ ARCH = "gfx950"
 
 N_TILE_CONFIGS = 16
 N_SKINNY_CONFIGS = 6
-N_MX_CONFIGS = 5
+N_MX_CONFIGS = 6
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -15,7 +15,7 @@
 // or four B rows with whole 128-byte lines, instead of sixteen rows with half
 // a line each: HBM sees long runs of each weight row. In LDS a stage row is
 // SB / 16 16-byte chunks, chunk c of row r at position c ^ swz(r) (swz(r) =
-// r & 15 for 256-byte rows, (r >> 1) & 7 for 128-byte rows), so the sixteen
+// r & 15 for rows of 256 bytes or more, (r >> 1) & 7 for 128-byte rows), so the sixteen
 // rows one MFMA operand read touches (same chunk, consecutive rows) land in
 // sixteen distinct bank groups. The loads place the chunks by permuting which
 // chunk each lane fetches; every instruction still reads one KiB of whole
@@ -35,8 +35,9 @@
 // per 64-byte slab are those of mx_kernel.hpp.
 //
 // Scales: 16 bytes of each row's scale row (eight E4M3 slabs or four E2M1
-// slabs, SSW stages) are loaded into a ring of LDS windows just before the
-// first stage they cover, so the wait that covers that stage covers them.
+// slabs: one or more stages, or part of one) are loaded into a ring of LDS
+// windows just before the first stage they cover, so the wait that covers
+// that stage covers them.
 //
 // Each step waits for stage s, passes one barrier (after which every wave is
 // done with stage s - 1), loads stage s + NST - 1 into stage s - 1's buffer
@@ -57,7 +58,7 @@ template <int BM, int BN, int SB, int NST, int KS, int FMT, bool OUT_BF16, bool 
 __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void mx_stream_kernel(MxArgs p) {
   static_assert(BM == 16 || BM == 32 || BM == 64, "half a 32-row block, or one or two blocks");
   static_assert(BN % 64 == 0 && BN <= 256, "whole scale-window loads for B");
-  static_assert(SB == 128 || SB == 256, "stage rows of whole 128-byte lines");
+  static_assert(SB == 128 || SB == 256 || SB == 512, "stage rows of whole 128-byte lines");
   static_assert(FMT == kMxE4M3 || FMT == kMxE2M1, "E4M3 or E2M1 elements");
   static_assert(KS == 1 || KS == 2, "one or two waves per 32-column block");
   constexpr int NCB = BN / 32;               // 32-column blocks
@@ -73,7 +74,8 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void mx_stream_kernel(MxArgs 
   static_assert(KSL % 2 == 0 || KS == 1, "each wave's slabs start at an even slab");
   constexpr int KPS = FP4 ? 128 : 64;       // K values per slab
   constexpr int SPW = FP4 ? 4 : 8;          // slabs per 16-byte scale window
-  constexpr int SSW = SPW / SPS;            // stages per scale window
+  constexpr int SSW = SPS < SPW ? SPW / SPS : 1;  // stages per scale window
+  constexpr int WPS = SPS > SPW ? SPS / SPW : 1;  // scale windows per stage
   constexpr int A_BYTES = BM * SB, B_BYTES = BN * SB;
   constexpr int STAGE = A_BYTES + B_BYTES;
   constexpr int A_DMA = A_BYTES / 1024, B_DMA = B_BYTES / 1024;
@@ -86,11 +88,16 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void mx_stream_kernel(MxArgs 
   constexpr int RING = NST * STAGE;
   constexpr int SWA = 64 * 16;              // window: 64 A-row slots, then the BN B rows
   constexpr int SWIN = SWA + BN * 16;
-  // Window v is loaded with stage SSW v, issued in step SSW v - (NST - 1);
-  // its buffer takes window v + NWB, issued in step SSW (v + NWB) - (NST - 1),
-  // which must come after step SSW (v + 1) - 1, the last to read window v.
-  constexpr int NWB = 1 + (NST - 1 + SSW - 1) / SSW;
-  static_assert(SSW * (NWB - 1) >= NST - 1, "a scale window is reloaded only after its last use");
+  // Window v is loaded with the first stage that reads it. With SSW stages
+  // per window: stage SSW v, issued in step SSW v - (NST - 1); its buffer
+  // takes window v + NWB, issued in step SSW (v + NWB) - (NST - 1), which
+  // must come after step SSW (v + 1) - 1, the last to read window v. With WPS
+  // windows per stage: windows WPS s .. WPS s + WPS - 1 go with stage s, and
+  // window v + WPS NST is issued in step v / WPS + 1, after the only step
+  // that reads window v.
+  constexpr int NWB = WPS > 1 ? WPS * NST : 1 + (NST - 1 + SSW - 1) / SSW;
+  static_assert(WPS > 1 || SSW * (NWB - 1) >= NST - 1,
+                "a scale window is reloaded only after its last use");
   constexpr int NWIN = 1 + BN / 64;         // window load instructions (one KiB each)
   static_assert(RING + NWB * SWIN <= 160 * 1024, "LDS");
 
@@ -107,7 +114,7 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void mx_stream_kernel(MxArgs 
   const int nss = (nk + SPS - 1) / SPS;     // stages
   const int kbytes = FP4 ? K / 2 : K;
 
-  auto swz = [](int r) { return SB == 256 ? (r & 15) : ((r >> 1) & 7); };
+  auto swz = [](int r) { return SB >= 256 ? (r & 15) : ((r >> 1) & 7); };
   // Load sources: instruction ins of a stage covers rows RPI ins ..; lane l
   // fills position l % CPR of row RPI ins + l / CPR, i.e. fetches chunk
   // (l % CPR) ^ swz(row) of that row's SB bytes.
@@ -170,7 +177,11 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void mx_stream_kernel(MxArgs 
       }
     };
     auto issue_stage = [&](int s) {
-      if (s % SSW == 0) issue_window(s / SSW);
+      if constexpr (WPS > 1) {
+        for (int w = 0; w < WPS; ++w) issue_window(s * WPS + w);
+      } else {
+        if (s % SSW == 0) issue_window(s / SSW);
+      }
       const uint32_t st = (uint32_t)(s % NST) * STAGE;
       const i32x4 rsA = make_rsrc(a_panel + (int64_t)s * SB, a_bytes - (int64_t)s * SB);
       const i32x4 rsB = make_rsrc(b_panel + (int64_t)s * SB, b_bytes - (int64_t)s * SB);
@@ -203,7 +214,6 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void mx_stream_kernel(MxArgs 
       block_barrier();
       if (s + NST - 1 < nss) issue_stage(s + NST - 1);
       const uint32_t so = (uint32_t)(s % NST) * STAGE;
-      const uint32_t wb = swin0 + (uint32_t)(((s / SSW) % NWB) * SWIN);
       // slab j = kh KSL + jj of the stage; jj and j have the same parity
       auto slab = [&](auto jj_c) {
         constexpr int jj = decltype(jj_c)::value;
@@ -214,9 +224,11 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void mx_stream_kernel(MxArgs 
           uint4 y = __builtin_bit_cast(uint4, lds_read16(rB + so + (uint32_t)(((c1 ^ swb)) << 4)));
           const i32x8 bf = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
                                  (int)y.x, (int)y.y, (int)y.z, (int)y.w};
-          // the scale dword of slab SPS s + j (slab SPS (s % SSW) + j of its
-          // window): E4M3 holds two slabs per dword, E2M1 one
-          const int sw = SPS * (s % SSW) + j;
+          // the scale dword of slab g = SPS s + j: window g / SPW, slab g % SPW
+          // of it; E4M3 holds two slabs per dword, E2M1 one
+          const int g = SPS * s + j;
+          const uint32_t wb = swin0 + (uint32_t)(((g / SPW) % NWB) * SWIN);
+          const int sw = g % SPW;
           const int dw = FP4 ? sw : sw / 2;
           const uint32_t vb = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
               wb + (uint32_t)(SWA + br * 16 + 4 * dw));

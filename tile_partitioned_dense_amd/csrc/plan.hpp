@@ -106,7 +106,7 @@ struct MxConfig {
   int sb = 0;  // stream kernel: bytes of K per row and stage; 0: tile kernel
   int ks = 1;  // stream kernel: waves per 32-column block (each a share of every stage's K)
 };
-constexpr int kNumMxConfigs = 5;
+constexpr int kNumMxConfigs = 6;
 constexpr MxConfig kMxConfigs[kNumMxConfigs] = {
     {256, 256, 2, 2, 4, 1.00f},  // 0: 4 waves of 128x128
     {128, 128, 2, 2, 4, 0.70f},  // 1: 4 waves of 64x64
@@ -115,6 +115,9 @@ constexpr MxConfig kMxConfigs[kNumMxConfigs] = {
     // waves per 32-column block, each taking half of every stage's slabs
     {32, 128, 1, 4, 3, 0.0f, 256, 2},
     {64, 128, 1, 4, 3, 0.0f, 256, 2},
+    // 5: stream, 32 x 64 with stages of 512 bytes: twice the workgroups of
+    // configuration 3, for outputs with few columns
+    {32, 64, 1, 2, 3, 0.0f, 512, 2},
 };
 constexpr int kMxBK = 64;          // bytes of K per row in one slab of the MX tile kernel
 constexpr int kMxStreamMaxM = 64;  // M at or below this takes the stream kernel
@@ -267,7 +270,12 @@ inline Plan plan_for_mx(int config, int64_t M, int64_t N, int cu_count) {
 inline Plan make_plan_mx(int64_t M, int64_t N, int64_t K, int cu_count) {
   (void)K;
   if (M <= 0 || N <= 0) return plan_for(0, 0, M, N, cu_count);
-  if (M <= kMxStreamMaxM) return plan_for_mx(M <= 32 ? 3 : 4, M, N, cu_count);
+  if (M <= kMxStreamMaxM) {
+    // up to 32 rows: 128-column tiles, or 64-column ones when those would
+    // leave more than half of the compute units without a tile
+    const int c = M > 32 ? 4 : (2 * ceil_div(N, 128) < cu_count ? 5 : 3);
+    return plan_for_mx(c, M, N, cu_count);
+  }
   int best = 0;
   double best_cost = 0.0;
   for (int i = 0; i < kNumMxConfigs; ++i) {

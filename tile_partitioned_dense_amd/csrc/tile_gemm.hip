@@ -220,10 +220,11 @@ hipError_t dispatch_mx(int cfg, const tg::MxArgs& a, int fmt, int64_t grid, cons
     case 2: return tg::launch_mx<2>(a, fmt, grid, v, st);
     case 3: return tg::launch_mx<3>(a, fmt, grid, v, st);
     case 4: return tg::launch_mx<4>(a, fmt, grid, v, st);
+    case 5: return tg::launch_mx<5>(a, fmt, grid, v, st);
   }
   return hipErrorInvalidValue;
 }
-static_assert(tg::kNumMxConfigs == 5, "dispatch_mx covers every MX configuration");
+static_assert(tg::kNumMxConfigs == 6, "dispatch_mx covers every MX configuration");
 
 // Checks of tile_gemm_run_mx's arguments (see the header).
 tile_gemm_status_t check_mx(const void* A, const void* B, const void* C, int64_t M, int64_t N,
