@@ -258,8 +258,8 @@ typedef enum {
  *                  With a column-major B, an even K and M <= 64 the tile
  *                  variant runs the stream configurations (32 x 64 tiles
  *                  with bk = 256 up to 32 rows, 64 x 128 with bk = 128
- *                  above: K moves 512 or 256 bytes per row at a time, for a
- *                  weight stream bound by HBM).
+ *                  above, 64 x 64 when N is small: K moves 512 or 256 bytes
+ *                  per row at a time, for a weight stream bound by HBM).
  *   skinny kernel: each workgroup owns rows [0, M) x bn columns; the waves of
  *                  one workgroup split K and combine their partial sums in a
  *                  fixed order; grid = tiles = tiles_n, tiles_m = 1.

@@ -92,6 +92,8 @@ def test_few_rows_of_column_major_b_take_the_stream_kernel():
     for M in (1, 16, 17, 32):
         p = tg.tile_gemm_plan(M, 28672, 8192, True, CU)
         assert (p.variant, p.bm, p.bn, p.bk, p.tiles, p.grid) == (tg.VARIANT_TILE, 32, 64, 256, 448, 224)
+    p = tg.tile_gemm_plan(64, 7168, 8192, True, CU)                 # few columns: 64 x 64
+    assert (p.bm, p.bn, p.bk, p.tiles) == (64, 64, 128, 112)
     p = tg.tile_gemm_plan(64, 28672, 8192, True, CU)
     assert (p.bm, p.bn, p.bk, p.tiles, p.grid) == (64, 128, 128, 224, 224)
     assert tg.tile_gemm_plan(16, 28672, 8192, False, CU).variant == tg.VARIANT_SKINNY

@@ -62,7 +62,7 @@ def DEBUG_FORCE_GRID(g: int) -> int:
 DEBUG_ONE_TILE_PER_WG = 0x7F << 24
 
 
-N_TILE_CONFIGS = 16
+N_TILE_CONFIGS = 17
 N_MX_CONFIGS = 6
 MX_E4M3 = 0
 MX_E2M1 = 1

@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libtile_gemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-N_TILE_CONFIGS = 16
+N_TILE_CONFIGS = 17
 N_SKINNY_CONFIGS = 6
 N_MX_CONFIGS = 6
 

@@ -60,7 +60,7 @@ inline double tile_eff(const TileConfig& c, int64_t per_cu) {
   return e1 + (c.eff - e1) * (double)(n - 1) / (double)(c.occ - 1);
 }
 
-constexpr int kNumTileConfigs = 16;
+constexpr int kNumTileConfigs = 17;
 constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
     {256, 256, 2, 2, 4, 0.94f},  // 0: 4 waves of 128x128
     {256, 224, 4, 1, 5, 0.85f},  // 1: 4 waves of 64x224
@@ -76,14 +76,17 @@ constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
     {64, 64, 1, 1, 4, 0.28f, 4},    // 11: 4 waves, each 64x64 over a quarter of K
     {64, 128, 1, 1, 3, 0.42f, 4},   // 12: 4 waves, each 64x128 over a quarter of K
     {128, 64, 1, 1, 3, 0.39f, 4},   // 13: 4 waves, each 128x64 over a quarter of K
-    // 14, 15: stream, 3 stages, two waves per 32-column block, each taking
+    // 14-16: stream, 3 stages, two waves per 32-column block, each taking
     // half of every stage's K: 32 rows x 64 columns with stages of 512 bytes
-    // per row (up to 32 rows), 64 x 128 with 256 bytes (33 to 64 rows)
+    // per row (up to 32 rows), 64 x 128 with 256 bytes (33 to 64 rows), and
+    // 64 x 64 with 256 bytes (33 to 64 rows with few columns)
     {32, 64, 1, 2, 3, 0.0f, 2, 0.0f, 1, 512},
     {64, 128, 1, 4, 3, 0.0f, 2, 0.0f, 1, 256},
+    {64, 64, 1, 2, 3, 0.0f, 2, 0.0f, 1, 256},
 };
-constexpr int kStreamConfig = 14;    // the planner's stream configuration up to 32 rows,
-constexpr int kStreamConfig64 = 15;  // and from 33 to 64 rows
+constexpr int kStreamConfig = 14;      // the planner's stream configuration up to 32 rows,
+constexpr int kStreamConfig64 = 15;    // from 33 to 64 rows,
+constexpr int kStreamConfig64n = 16;   // and from 33 to 64 rows with few columns
 constexpr int kStreamMaxM = 64;      // column-major B, even K and M at or below this: stream kernel
 
 // Skinny-kernel configurations: T output columns per lane (16*T per
@@ -298,7 +301,9 @@ inline Plan make_plan(int64_t M, int64_t N, int64_t K, bool b_col_major, int cu_
   // (odd K: the stream kernel's loads of whole dwords would drop the value
   // K - 1 of each operand's last row, so those shapes stay on the others)
   if (b_col_major && M <= kStreamMaxM && K % 2 == 0)
-    return plan_for(1, M <= 32 ? kStreamConfig : kStreamConfig64, M, N, cu_count);
+    return plan_for(1, M <= 32 ? kStreamConfig
+                               : (2 * ceil_div(N, 128) < cu_count ? kStreamConfig64n : kStreamConfig64),
+                    M, N, cu_count);
   if (M <= kSkinnyMaxM) {
     const int mg = (int)ceil_div(M, 16);
     const int mgp = mg <= 1 ? 1 : (mg <= 2 ? 2 : 4);

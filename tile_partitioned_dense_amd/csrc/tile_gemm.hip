@@ -193,10 +193,11 @@ hipError_t dispatch_tile(int cfg, const tg::TileArgs& a, int64_t grid, const tg:
     case 13: return tg::launch_tile<13>(a, grid, v, st);
     case 14: return tg::launch_tile<14>(a, grid, v, st);
     case 15: return tg::launch_tile<15>(a, grid, v, st);
+    case 16: return tg::launch_tile<16>(a, grid, v, st);
   }
   return hipErrorInvalidValue;
 }
-static_assert(tg::kNumTileConfigs == 16, "dispatch_tile covers every tile configuration");
+static_assert(tg::kNumTileConfigs == 17, "dispatch_tile covers every tile configuration");
 
 hipError_t dispatch_skinny(int cfg, const tg::SkinnyArgs& a, int64_t grid, const tg::Variant& v,
                            hipStream_t st) {
