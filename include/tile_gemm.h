@@ -76,10 +76,25 @@ typedef struct {
  * no device memory. On success *out holds a new handle; on failure *out is
  * set to NULL (when out is not NULL).
  * Errors: TILE_GEMM_ERR_NULL_ARG (out == NULL), TILE_GEMM_ERR_DEVICE.
+ *
+ * Source: the split between a once-only preparation and cheap recording of
+ * work ("Rust Compute Kernels", section "Quick example": prepare compiles or
+ * hits the cache once, record only appends), and an operation built once and
+ * then driven synchronously, chained or replayed from a graph ("GPU speed,
+ * without leaving Rust's safety model", section "Build once, choose how to
+ * execute"). The handle is what is prepared once; every run reuses it.
  */
 tile_gemm_status_t tile_gemm_create(tile_gemm_t* out, int device);
 
 /*
+ * Source: the output partitioned into disjoint owned tiles with the inputs as
+ * shared read-only views, and a launcher that holds its operands while the
+ * work is in flight ("GPU speed, without leaving Rust's safety model", section
+ * "Ownership crosses the launch boundary"); capture into a graph limited to
+ * operations that allocate nothing (same page, section "Why scoped graph
+ * capture helps borrowing"). The signature is C = A . B with shape, strides,
+ * output type and stream.
+ *
  * Enqueue C := A . B on `stream` (a hipStream_t; NULL means the default
  * stream) and return without waiting. A and B are device pointers to bf16
  * data, C a device pointer to fp32 or bf16 data per `dtype`; all three must be
@@ -95,7 +110,11 @@ tile_gemm_status_t tile_gemm_create(tile_gemm_t* out, int device);
  * Shapes: M = 0 or N = 0 is a successful no-op (pointers are not checked);
  * K = 0 writes zeros to C (A and B are not read: they may be NULL and their
  * strides are not checked). M, N and K must be below 2^31, and A and B must
- * each span less than 4 GiB (TILE_GEMM_ERR_BAD_SHAPE otherwise).
+ * each span less than 4 GiB (TILE_GEMM_ERR_BAD_SHAPE otherwise); the leading
+ * dimensions a_m, the non-unit B stride and c_m must be below 2^31 elements
+ * (TILE_GEMM_ERR_BAD_STRIDE otherwise), and every byte span is computed with
+ * overflow checks, so no stride can wrap an extent past the 4 GiB and overlap
+ * checks.
  *
  * Errors are returned before anything is enqueued and leave C untouched:
  * NULL_ARG, BAD_SHAPE, BAD_STRIDE, MISALIGNED, ALIAS, DTYPE, DEVICE (the
@@ -176,6 +195,9 @@ tile_gemm_status_t tile_gemm_run_epilogue(tile_gemm_t h, const void* A, const vo
  * K per row (plan bk = 256; 512 for few-column outputs of up to 32 rows);
  * larger ones the tile kernel (bk = 64).
  * A, B 16-byte aligned with 16-byte leading dimensions; scales 4-byte aligned.
+ * Leading dimensions and scale_stride below 2^31 bytes, and the scale rows
+ * (up to 256 past the last row of A or B) times scale_stride below 2 GiB
+ * (TILE_GEMM_ERR_BAD_STRIDE or TILE_GEMM_ERR_BAD_SHAPE otherwise).
  * All inputs are borrowed read-only until the stream reaches the work; C may
  * overlap none of them. Enqueue-only, allocates nothing.
  */
@@ -193,10 +215,23 @@ tile_gemm_status_t tile_gemm_run_mx(tile_gemm_t h, const void* A, const void* B,
                                     tile_gemm_mx_format_t fmt, tile_gemm_dtype_t dtype,
                                     const float* bias, tile_gemm_act_t act, void* stream);
 
-/* Release a handle (host memory only). NULL is accepted and returns OK. */
+/*
+ * Release a handle (host memory only). NULL is accepted and returns OK.
+ * Source: the counterpart of the one-time preparation ("Rust Compute
+ * Kernels", section "Quick example"); it touches no device memory, since the
+ * handle owns none, and caller buffers are never freed by the library (the
+ * launcher returns borrowed operands in their ownership form: "GPU speed,
+ * without leaving Rust's safety model", section "Ownership crosses the launch
+ * boundary").
+ */
 tile_gemm_status_t tile_gemm_destroy(tile_gemm_t h);
 
-/* Static text for a status code; never NULL. */
+/*
+ * Static text for a status code; never NULL. Source: argument errors are
+ * reported when work is recorded, before anything is bound or launched, and
+ * name what was wrong ("Rust Compute Kernels", section "Shape contracts").
+ * Unknown codes map to a fixed "unknown status" text.
+ */
 const char* tile_gemm_status_str(tile_gemm_status_t s);
 
 /*

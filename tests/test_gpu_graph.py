@@ -3,17 +3,21 @@ be captured into a HIP graph and replayed: the split between preparing work
 once and replaying it that "Rust Compute Kernels" describes (section "Why
 scoped graph capture helps borrowing").
 
-Each replay is checked against an eager run of the same operands, with eager
-work and synchronisation between replays, and with the captured inputs
-rewritten in place between replays (a graph keeps its pointers, not their
-contents).
+Each replay is checked against the fp64 CPU oracle (the 1e-5 * |A|.|B| rule,
+exact for integer inputs) and bitwise against an eager run of the same
+operands, with eager work and synchronisation between replays, and with the
+captured inputs rewritten in place between replays (a graph keeps its
+pointers, not their contents).
 """
 
 import numpy as np
 import pytest
 
+import oracle
 import tile_partitioned_dense_amd as tg
 from tile_partitioned_dense_amd import synth
+
+from gpu_helpers import host_out
 
 pytestmark = pytest.mark.gpu
 
@@ -36,18 +40,30 @@ def _bits(C):
     return C.view(torch.int32) if C.dtype == torch.float32 else C.view(torch.int16)
 
 
+def _oracle_check(out, A, Bs, bcol, dt, integer):
+    C64, D64 = oracle.gemm(A, Bs.T if bcol else Bs)
+    bf16 = dt == torch.bfloat16
+    if integer:
+        return oracle.check_exact(out, C64, bf16)
+    return oracle.check_bf16(out, C64, D64) if bf16 else oracle.check_f32(out, C64, D64)
+
+
 @pytest.mark.parametrize("M,N,K,bcol,dt", [
     (700, 904, 296, False, torch.float32),    # tile kernel, several tiles, K tail
     (700, 904, 296, True, torch.bfloat16),
     (16, 2048, 512, False, torch.bfloat16),   # skinny kernel
+    (16, 2048, 512, True, torch.float32),     # stream kernel
+    (256, 256, 256, False, torch.float32),    # the launch-bound 256^3 shape (K-split)
 ])
 def test_capture_and_replay(g, M, N, K, bcol, dt):
     print(f"[graph {M}x{N}x{K} bcol={bcol} {dt}]", flush=True)
-    versions = []
+    versions, host = [], []
     for v in range(3):
-        A = synth.draw(M, K, "normal", 500 + v)
-        Bs = synth.draw(N, K, "normal", 600 + v) if bcol else synth.draw(K, N, "normal", 600 + v)
+        dist = "int3" if v == 2 else "normal"     # the third version is integer-valued
+        A = synth.draw(M, K, dist, 500 + v)
+        Bs = synth.draw(N, K, dist, 600 + v) if bcol else synth.draw(K, N, dist, 600 + v)
         versions.append((_dev(A), _dev(Bs)))
+        host.append((A, Bs))
     A = versions[0][0].clone()
     Bs = versions[0][1].clone()
     B = Bs.t() if bcol else Bs
@@ -79,6 +95,8 @@ def test_capture_and_replay(g, M, N, K, bcol, dt):
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
+        rep_ok = _oracle_check(host_out(C), *host[i], bcol, dt, integer=(i == 2))
+        assert rep_ok.ok, f"replay {rep} (version {i}) against the oracle: {rep_ok}"
         assert torch.equal(_bits(C), _bits(refs[i])), f"replay {rep} differs from the eager run"
         _ = (refs[i].float() * 2).sum().item()   # unrelated eager work between replays
 

@@ -1,12 +1,16 @@
 """GPU parity of the MXFP8 product (tile_gemm_run_mx) against the oracle's
 microscaled product (oracle/mx.py), through the C ABI.
 
-Acceptance: fp32 output within the oracle's per-element MX bound T of the
-fp64 sum (T follows the instruction's grouped fixed-point summation, see
-oracle/mx.py), bf16 output inside the RNE bracket of that interval,
-integer-valued inputs exactly equal. Outputs start as NaN
-(padding columns included) and a write counter checks that every element is
-written exactly once.
+Acceptance, first and device-independent: integer-valued elements, with unit
+scales or with every block's E8M0 scale drawn from a range (the product
+exponents then span 6, so every partial sum is exact in fp32 in any order and
+the result is the exact sum), must equal the oracle exactly, on every
+configuration, both formats and the full-size workloads. Then, for random
+operands: fp32 output within the oracle's per-element MX bound T of the fp64
+sum (a model of the instruction's grouped fixed-point summation, see
+oracle/mx.py), bf16 output inside the RNE bracket of that interval. Outputs
+start as NaN (padding columns included) and a write counter checks that
+every element is written exactly once.
 """
 
 import numpy as np
@@ -56,13 +60,16 @@ FMTS = {"e4m3": tg.MX_E4M3, "e2m1": tg.MX_E2M1}
 
 
 class MxCase:
-    def __init__(self, M, N, K, dist="normal", seed=0, pad=16, b_scale=1.0, fmt="e4m3"):
+    def __init__(self, M, N, K, dist="normal", seed=0, pad=16, b_scale=1.0, fmt="e4m3",
+                 varied_scales=False):
         self.M, self.N, self.K, self.fmt = M, N, K, fmt
         fp4 = fmt == "e2m1"
         kb = K // 2 if fp4 else K                      # bytes of K in a row
         lk = K + (2 * pad if fp4 else pad)             # padded rows (16 more bytes)
-        A, sA = synth.draw_mx(M, lk, dist, 2 * seed + 1, fmt=fmt)
-        Bt, sB = synth.draw_mx(N, lk, dist, 2 * seed + 2, b_scale, fmt=fmt)
+        sca = synth.MX_INT_SCALES_A if varied_scales else None
+        scb = synth.MX_INT_SCALES_B if varied_scales else None
+        A, sA = synth.draw_mx(M, lk, dist, 2 * seed + 1, fmt=fmt, scale_codes=sca)
+        Bt, sB = synth.draw_mx(N, lk, dist, 2 * seed + 2, b_scale, fmt=fmt, scale_codes=scb)
         ls = synth.mx_scale_stride(K)
         self.A, self.Bt = A[:, :kb], Bt[:, :kb]
         K = kb
@@ -133,6 +140,51 @@ def test_mx_configs_integer_exact(g, fmt, cfg):
     print(f"[mx int {fmt} cfg {cfg} {M}x{N}x{K}]", flush=True)
     _run_and_check(g, MxCase(M, N, K, dist="int3", seed=50 + cfg, fmt=fmt),
                    tg.DEBUG_FORCE_TILE(cfg), integer=True, label=f"int {fmt} cfg {cfg}")
+
+
+@pytest.mark.parametrize("fmt", sorted(FMTS))
+@pytest.mark.parametrize("cfg", range(tg.N_MX_CONFIGS))
+def test_mx_configs_scaled_integer_exact(g, fmt, cfg):
+    """Integer elements with per-block scales that vary along K and across
+    rows (A's bytes 120..123, B's 131..134): exact, so every scale is applied
+    to exactly its own block, whatever the arithmetic inside the instruction.
+    19 slabs run the steady loop and reuse the LDS scale windows; two tile rows
+    and columns plus ragged edges."""
+    bm, bn = mx_config_table()[cfg]
+    M, N = 2 * bm + 37, 2 * bn + 19
+    K = 19 * (128 if fmt == "e2m1" else 64)
+    print(f"[mx scaled int {fmt} cfg {cfg} {M}x{N}x{K}]", flush=True)
+    case = MxCase(M, N, K, dist="int3", seed=80 + cfg, fmt=fmt, varied_scales=True)
+    _run_and_check(g, case, tg.DEBUG_FORCE_TILE(cfg), integer=True,
+                   label=f"scaled int {fmt} cfg {cfg}")
+
+
+@pytest.mark.parametrize("fmt", sorted(FMTS))
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (16, 4096, 1024), (64, 1000, 2048),
+                                   (1000, 1000, 1024)])
+def test_mx_planner_scaled_integer_exact(g, fmt, M, N, K):
+    print(f"[mx planner scaled int {fmt} {M}x{N}x{K}]", flush=True)
+    case = MxCase(M, N, K, dist="int3", seed=M + N, fmt=fmt, varied_scales=True)
+    _run_and_check(g, case, integer=True, label=f"planner scaled int {fmt} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("name", sorted(synth.MX_WORKLOADS))
+def test_mx_workload_scaled_integer_exact(g, name):
+    """Full size, in the launch configuration the benchmark times, every
+    element: integer codes with varied per-block scales, exact."""
+    w = synth.MX_WORKLOADS[name]
+    ops = synth.mx_operands(w, integer=True, varied_scales=True)
+    print(f"[mx workload scaled int {name} {w.M}x{w.N}x{w.K}]", flush=True)
+    A, Bt = torch.from_numpy(ops.A).cuda(), torch.from_numpy(ops.Bt).cuda()
+    sA, sB = torch.from_numpy(ops.sA).cuda(), torch.from_numpy(ops.sB).cuda()
+    C64, _ = oracle.mx.mx_gemm(ops.A, ops.sA, ops.Bt, ops.sB, w.K, w.fmt, want_d=False)
+    for dt in (torch.float32, torch.bfloat16):
+        C = torch.full((w.M, w.N), float("nan"), dtype=dt, device="cuda")
+        g.mx(A, Bt, C, sA, sB, fmt=FMTS[w.fmt])
+        torch.cuda.synchronize()
+        rep = oracle.check_exact(host_out(C), C64, dt == torch.bfloat16)
+        assert rep.ok, f"{name} {dt}: {rep}"
+        del C
 
 
 @pytest.mark.parametrize("fmt", sorted(FMTS))

@@ -87,6 +87,32 @@ def test_tile_configs_integer_k_tail(g, cfg):
             _parity(g, case, dt, flags=tg.DEBUG_FORCE_TILE(cfg), integer=True)
 
 
+@pytest.mark.parametrize("cfg", [c for c in range(tg.N_TILE_CONFIGS) if c not in stream_tile_configs()])
+def test_tile_configs_odd_n_whole_slabs(g, cfg):
+    """Row-major B, odd N and K a multiple of 32, integer data, exact. B's last
+    value (K - 1, N - 1) then shares a dword with the first padding element;
+    a buffer load zeroes a dword that straddles the end of its resource, so
+    that slab must not go through the DMA path (every term of column N - 1
+    would lose A[:, K - 1] * B[K - 1, N - 1])."""
+    M, N = tile_shape(cfg)          # N = 2 bn + 19: odd
+    assert N % 2 == 1
+    for K in (256, 64):
+        print(f"[tile odd-N cfg {cfg} {M}x{N}x{K}]", flush=True)
+        case = Case(M, N, K, False, dist="int3", seed=40 + cfg)
+        for dt in (torch.float32, torch.bfloat16):
+            _parity(g, case, dt, flags=tg.DEBUG_FORCE_TILE(cfg), integer=True)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 257, 256), (40, 33, 64), (2000, 1001, 512)])
+def test_planner_odd_n_whole_slabs(g, M, N, K):
+    print(f"[planner odd-N {M}x{N}x{K}]", flush=True)
+    case = Case(M, N, K, False, dist="int3", seed=M + N)
+    for dt in (torch.float32, torch.bfloat16):
+        _parity(g, case, dt, integer=True)
+    ncase = Case(M, N, K, False, seed=M + N + 1)
+    _parity(g, ncase, torch.float32)
+
+
 SKINNY_MG = {0: 1, 1: 1, 2: 2, 3: 2, 4: 4, 5: 4}
 
 
@@ -144,18 +170,12 @@ def test_workload_parity(g, name):
     print(f"[workload {name} {w.M}x{w.N}x{w.K}]", flush=True)
     outs = {dt: host_out(_run_workload(g, A, B, w, dt))
             for dt in (torch.float32, torch.bfloat16)}
-    Cr, Dr = oracle.gemm_blas(ops.A, ops.B)
+    # every element against the plain fp64 triple loop (ascending k per element)
+    Cr, Dr = oracle.gemm(ops.A, ops.B)
     for dt, out in outs.items():
         rep = check(out, Cr, Dr, dt == torch.bfloat16)
         assert rep.ok, f"{name} {dt}: {rep}"
         print(f"  {dt}: max |g-C|/D = {rep.max_ratio:.3e}", flush=True)
-    # sampled elements against the plain triple loop (one element at a time)
-    rng = np.random.default_rng(9)
-    ii = np.concatenate([rng.integers(0, w.M, 400), [0, w.M - 1, 0, w.M - 1]])
-    jj = np.concatenate([rng.integers(0, w.N, 400), [0, 0, w.N - 1, w.N - 1]])
-    c, d = oracle.gemm_at(ops.A, ops.B, ii, jj)
-    rep = oracle.check_f32(outs[torch.float32][ii, jj], c, d)
-    assert rep.ok, rep
 
 
 @pytest.mark.parametrize("name", WORKLOADS)
@@ -167,6 +187,58 @@ def test_workload_integer_exact(g, name):
         out = host_out(_run_workload(g, A, B, w, dt))
         rep = oracle.check_exact(out, Cr, dt == torch.bfloat16)
         assert rep.ok, f"{name} {dt}: {rep}"
+
+
+# The decode / tall-skinny sweep: decode batches of 1-64 rows against the
+# widest weight of the gate+up projection, in both B layouts, and the
+# tall-skinny (4096, 256, 4096) shape; every element against the plain loop.
+SWEEP = [(M, 28672, 8192, bcol) for M in (1, 8, 32, 64) for bcol in (False, True)] + \
+        [(4096, 256, 4096, False), (4096, 256, 4096, True)]
+
+
+class _Rows:
+    """The first M rows of a larger case's A against its B (the decode shapes of
+    one width share their weight matrix, which takes seconds to draw)."""
+
+    def __init__(self, base, M):
+        self.base, self.M, self.N, self.K, self.bcol = base, M, base.N, base.K, base.bcol
+        self.A, self.B = base.A[:M], base.B
+        self.A_dev, self.B_dev = base.A_dev[:M], base.B_dev
+        self.pad, self.device, self._ref = base.pad, base.device, None
+
+    def out(self, dtype, fill=float("nan")):
+        return Case.out(self, dtype, fill)
+
+    def ref(self):
+        if self._ref is None:
+            self._ref = oracle.gemm(self.A, self.B)
+        return self._ref
+
+
+@pytest.fixture(scope="module")
+def sweep_bases():
+    cache = {}
+
+    def get(M, N, K, bcol, dist):
+        rows = 64 if M <= 64 else M
+        key = (rows, N, K, bcol, dist)
+        if key not in cache:
+            cache[key] = Case(rows, N, K, bcol, dist=dist, seed=3 * N + K + (7 if dist == "int3" else 0),
+                              b_scale=1.0 if dist == "int3" else K ** -0.5, pad=8)
+        return _Rows(cache[key], M)
+    yield get
+    cache.clear()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("M,N,K,bcol", SWEEP)
+def test_sweep_shapes_parity(g, sweep_bases, M, N, K, bcol):
+    print(f"[sweep {M}x{N}x{K} bcol={bcol}]", flush=True)
+    case = sweep_bases(M, N, K, bcol, "normal")
+    for dt in (torch.float32, torch.bfloat16):
+        _parity(g, case, dt)
+    icase = sweep_bases(M, N, K, bcol, "int3")
+    _parity(g, icase, torch.bfloat16, integer=True)
 
 
 def test_bf16_output_is_rne_of_fp32_output(g):

@@ -244,3 +244,82 @@ def test_smoke_shape_passes_the_argument_checks():
     M, N, K = ge.SMOKE_SHAPE
     for dt in (Dtype.BF16_TO_F32, Dtype.BF16_TO_BF16):
         assert chk(M=M, N=N, K=K, s=(K, 1, N, 1, N, 1), dtype=dt) == Status.OK, tg.last_error_detail()
+
+
+# --- strides that would overflow the span arithmetic (each was accepted before
+# the leading dimensions were bounded and the spans computed with checks)
+@pytest.mark.parametrize("kw", [
+    dict(M=5, s=(1 << 62, 1, 64, 1, 64, 1)),                 # a_m = 2^62
+    dict(M=5, s=(1 << 31, 1, 64, 1, 64, 1)),                 # a_m = 2^31
+    dict(s=(64, 1, 1 << 62, 1, 64, 1)),                      # row-major b_k = 2^62
+    dict(s=(64, 1, 1, 1 << 62, 64, 1)),                      # column-major b_n = 2^62
+    dict(s=(64, 1, 64, 1, 1 << 61, 1)),                      # c_m = 2^61
+    dict(s=(64, 1, 64, 1, 1 << 62, 1), C=A0 - 0x1000),       # c_m = 2^62, C just below A
+    dict(K=0, s=(0, 1, 64, 1, 1 << 62, 1)),                  # K = 0 still checks C
+])
+def test_check_args_refuses_huge_strides(kw):
+    st = chk(**kw)
+    assert st in (Status.ERR_BAD_STRIDE, Status.ERR_BAD_SHAPE), (kw, st)
+    assert tg.last_error_detail()
+
+
+@pytest.mark.parametrize("kw", [
+    dict(s=(1 << 62, 1, 1, 128, 64, 1)),                     # a_m
+    dict(s=(128, 1, 1, 1 << 62, 64, 1)),                     # b_n
+    dict(s=(128, 1, 1, 128, 1 << 61, 1)),                    # c_m
+    dict(ls=1 << 40),                                        # scale_stride
+    dict(ls=(1 << 31) // 64 // 4 * 4 * 4),                   # (M + 256) * ls >= 2^31
+])
+def test_check_mx_refuses_huge_strides(kw):
+    st = chk_mx(**kw)
+    assert st in (Status.ERR_BAD_STRIDE, Status.ERR_BAD_SHAPE), (kw, st)
+
+
+# --- the binding's own checks of torch tensors (the C ABI sees raw pointers
+# only, so a host tensor, a wrong dtype or a short bias must stop here)
+def _bf16(*shape):
+    import torch
+    return torch.zeros(*shape, dtype=torch.bfloat16)
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    A, B = _bf16(64, 64), _bf16(64, 64)
+    C = torch.zeros(64, 64, dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU"):
+        tg.tile_gemm_run(None, A, B, C)
+    with pytest.raises(ValueError, match="GPU"):
+        tg.tile_gemm_run_epilogue(None, A, B, C)
+
+
+def test_binding_refuses_dtype_mismatch():
+    import torch
+    A, B = _bf16(64, 64), _bf16(64, 64)
+    C = _bf16(64, 64)
+    with pytest.raises(TypeError, match="does not match"):
+        tg.tile_gemm_run(None, A, B, C, dtype=Dtype.BF16_TO_F32)
+    with pytest.raises(TypeError, match="bfloat16"):
+        tg.tile_gemm_run(None, A.float(), B, C)
+    with pytest.raises(TypeError, match="float32 or bfloat16"):
+        tg.tile_gemm_run(None, A, B, C.to(torch.float16))
+
+
+@pytest.mark.parametrize("bias_kw,err", [
+    (dict(n=64, dtype="bfloat16"), TypeError),
+    (dict(n=63, dtype="float32"), ValueError),
+    (dict(n=128, dtype="float32", step=2), ValueError),
+])
+def test_binding_refuses_bad_bias(bias_kw, err):
+    import torch
+    A, B = _bf16(64, 64), _bf16(64, 64)
+    C = torch.zeros(64, 64, dtype=torch.float32)
+    bias = torch.zeros(bias_kw["n"], dtype=getattr(torch, bias_kw["dtype"]))
+    if bias_kw.get("step"):
+        bias = bias[::bias_kw["step"]]
+    with pytest.raises(err):
+        tg.tile_gemm_run_epilogue(None, A, B, C, bias=bias)
+
+
+def test_binding_refuses_mixed_pointer_kinds():
+    with pytest.raises(TypeError, match="all torch tensors or all raw pointers"):
+        tg.tile_gemm_run(None, _bf16(8, 8), 0x1000, 0x2000, 8, 8, 8, (8, 1, 8, 1, 8, 1), 0)

@@ -249,3 +249,117 @@ def test_planted_swiglu_mistakes_are_caught(kind):
         except AssertionError:
             caught += 1
     assert caught >= 1, kind
+
+
+# ------------------------------------------------- the acceptance bounds' values
+#
+# epilogue_bound's value, worked out by hand for single elements (the rule in
+# oracle/fused_epilogue.py: L (tau + 2^-22 |x|) + 2^-20 |y| + 2^-126 with
+# tau = 1e-5 D, x = C + bias, y = act(x), L = 1, 1/4, 1, 1.1 for none/relu/tanh,
+# sigmoid, silu). Each expected value below is a number, not a call of the
+# bound: a bound ten times too loose (or tight), a wrong Lipschitz constant or
+# a missing term fails here.
+
+EPS22, EPS20, TINY = 2.0 ** -22, 2.0 ** -20, 2.0 ** -126
+
+BOUND_CASES = [
+    # act, C, D, bias, expected t
+    ("none", 2.0, 100.0, None, 1e-3 + 2 * EPS22 + 2 * EPS20 + TINY),
+    ("sigmoid", 0.0, 8.0, None, 0.25 * 8e-5 + 0.5 * EPS20 + TINY),
+    ("relu", -3.0, 1000.0, 0.5, 1e-2 + 2.5 * EPS22 + TINY),
+    ("relu", 3.0, 1000.0, 0.5, 1e-2 + 3.5 * EPS22 + 3.5 * EPS20 + TINY),
+    ("tanh", LN2, 50.0, None, 5e-4 + LN2 * EPS22 + 0.6 * EPS20 + TINY),
+    ("silu", LN3, 0.0, None, 1.1 * LN3 * EPS22 + 0.75 * LN3 * EPS20 + TINY),
+    ("silu", 0.0, 0.0, None, TINY),
+]
+
+
+def pin_epilogue_bound(bound):
+    for act, c, d, b, want in BOUND_CASES:
+        bias = None if b is None else np.array([b], np.float32)
+        t = float(bound(np.array([[c]]), np.array([[d]]), bias, act)[0, 0])
+        assert abs(t - want) <= 1e-12 * want, (act, c, d, b, t, want)
+
+
+# swiglu_bound, by hand: gate g, up u, e_g = 1e-5 D_g + 2^-22 |g|, e_u likewise,
+# t = 1.1 |u| e_g + |silu g| e_u + 1.1 e_g e_u + 2^-20 |silu(g) u| + 2^-126.
+def _sw_want(g, u, dg, du):
+    eg, eu = 1e-5 * dg + EPS22 * abs(g), 1e-5 * du + EPS22 * abs(u)
+    sg = g / (1.0 + math.exp(-g))
+    return 1.1 * abs(u) * eg + abs(sg) * eu + 1.1 * eg * eu + EPS20 * abs(sg * u) + TINY
+
+
+SW_CASES = [(LN3, 2.0, 100.0, 10.0), (0.0, 5.0, 1000.0, 1.0), (-LN3, -4.0, 0.0, 0.0)]
+
+
+def pin_swiglu_bound(bound):
+    for g, u, dg, du in SW_CASES:
+        t = float(bound(np.array([[g, u]]), np.array([[dg, du]]))[0, 0])
+        # closed form of the first case, fully by hand: silu(ln 3) = 0.75 ln 3
+        want = _sw_want(g, u, dg, du)
+        assert abs(t - want) <= 1e-12 * want, (g, u, dg, du, t, want)
+    e = 1e-3 + EPS22 * LN3
+    f = 1e-4 + 2 * EPS22
+    hand = 1.1 * 2 * e + 0.75 * LN3 * f + 1.1 * e * f + EPS20 * 1.5 * LN3 + TINY
+    t0 = float(bound(np.array([[LN3, 2.0]]), np.array([[100.0, 10.0]]))[0, 0])
+    assert abs(t0 - hand) <= 1e-12 * hand
+
+
+def test_epilogue_bound_values():
+    pin_epilogue_bound(oracle.epilogue_bound)
+
+
+def test_swiglu_bound_values():
+    pin_swiglu_bound(oracle.swiglu_bound)
+
+
+def test_epilogue_bound_is_what_fp32_arithmetic_needs():
+    """Not too tight: the product accumulated in fp32 (error well inside
+    1e-5 D), the bias added in fp32 and the activation evaluated in fp32 land
+    inside the bound; and with the accumulation error set to its full
+    allowance 1e-5 D the result still lands inside."""
+    rng = np.random.default_rng(11)
+    K = 512
+    A = rng.normal(size=(8, K))
+    B = rng.normal(size=(K, 12)) / np.sqrt(K)
+    C = A @ B
+    D = np.abs(A) @ np.abs(B)
+    b = rng.normal(size=12).astype(np.float32)
+    acc = np.zeros((8, 12), np.float32)
+    for k in range(K):
+        acc = (acc + (A[:, k:k + 1].astype(np.float32) * B[k:k + 1].astype(np.float32))).astype(np.float32)
+    for act in oracle.ACTS:
+        x32 = (acc + b[None, :]).astype(np.float32)
+        x64 = x32.astype(np.float64)
+        y32 = oracle.act_f64(x64, act).astype(np.float32)     # fp32 rounding of the activation
+        Ce = C + 1e-5 * D * 0.999                              # worst allowed accumulation error
+        y_worst = oracle.act_f64(Ce + b.astype(np.float64)[None, :], act)
+        for g in (y32, y_worst):
+            rep = oracle.check_epilogue(np.asarray(g, np.float64), C, D, b, act)
+            assert rep.ok, (act, rep)
+
+
+BOUND_MUTANTS = {
+    "ten times looser": lambda C, D, bias=None, act="none", rel=1e-5, tau=None:
+        10.0 * ep.epilogue_bound(C, D, bias, act, rel, tau),
+    "ten times tighter": lambda C, D, bias=None, act="none", rel=1e-5, tau=None:
+        0.1 * ep.epilogue_bound(C, D, bias, act, rel, tau),
+    "sigmoid slope 1": lambda C, D, bias=None, act="none", rel=1e-5, tau=None:
+        ep.epilogue_bound(C, D, bias, "none" if act == "sigmoid" else act, rel, tau),
+    "no bias-add rounding": lambda C, D, bias=None, act="none", rel=1e-5, tau=None:
+        ep.epilogue_bound(C, D, bias, act, rel, tau)
+        - ep.LIPSCHITZ[act] * 2.0 ** -22 * np.abs(np.asarray(C, float)
+                                                  + (0 if bias is None else np.asarray(bias, float))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BOUND_MUTANTS))
+def test_planted_bound_mistakes_are_caught(name):
+    with pytest.raises(AssertionError):
+        pin_epilogue_bound(BOUND_MUTANTS[name])
+
+
+@pytest.mark.parametrize("scale", [10.0, 0.1])
+def test_planted_swiglu_bound_mistakes_are_caught(scale):
+    with pytest.raises(AssertionError):
+        pin_swiglu_bound(lambda C, D, bias=None, rel=1e-5: scale * ep.swiglu_bound(C, D, bias, rel))

@@ -70,3 +70,46 @@ def test_draw_mx_fp4_packing_and_scales():
     Ai, si = synth.draw_mx(3, 64, "int3", 5, fmt="e2m1")
     vi = mx.mx_decode(Ai, si, 64, "e2m1")
     assert set(np.unique(vi)).issubset({-3.0, -2.0, -1.0, 0.0, 1.0, 2.0, 3.0})
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_draw_mx_scaled_integer_variant(fmt):
+    """Integer codes with per-block scales drawn from the stated ranges: the
+    scales vary from block to block and row to row, stay inside the range,
+    and the exactness condition 9 K 2^S < 2^24 holds for the ranges the tests
+    use at K = 8192 (S: spread of the product exponents)."""
+    k = 1024
+    A, sA = synth.draw_mx(40, k, "int3", 11, fmt=fmt, scale_codes=synth.MX_INT_SCALES_A)
+    B, sB = synth.draw_mx(40, k, "int3", 12, fmt=fmt, scale_codes=synth.MX_INT_SCALES_B)
+    nb = k // 32
+    for s, (lo, hi) in ((sA, synth.MX_INT_SCALES_A), (sB, synth.MX_INT_SCALES_B)):
+        blocks = s[:, :nb]
+        assert blocks.min() == lo and blocks.max() == hi
+        assert len(np.unique(blocks[0])) == hi - lo + 1        # varies along K
+        assert len(np.unique(blocks[:, 0])) > 1                # and across rows
+        assert (s[:, nb:] == 127).all()                        # padding untouched
+    dec = mx.e2m1_to_f64(mx.unpack_fp4(A, k)) if fmt == "e2m1" else mx.e4m3_to_f64(A)
+    assert set(np.unique(dec)).issubset({-3.0, -2.0, -1.0, 0.0, 1.0, 2.0, 3.0})
+    lo = synth.MX_INT_SCALES_A[0] + synth.MX_INT_SCALES_B[0]
+    hi = synth.MX_INT_SCALES_A[1] + synth.MX_INT_SCALES_B[1]
+    assert 9 * 8192 * 2 ** (hi - lo) < 2 ** 24
+
+
+def test_scaled_integer_product_is_exact_in_fp32_any_order():
+    """The reason the exact GPU test may demand equality: with these scales,
+    summing the K scaled products in fp32 in ascending, descending or a random
+    order gives the fp64 sum exactly (a check of the claim on the CPU)."""
+    k = 4096
+    A, sA = synth.draw_mx(3, k, "int3", 21, scale_codes=synth.MX_INT_SCALES_A)
+    B, sB = synth.draw_mx(3, k, "int3", 22, scale_codes=synth.MX_INT_SCALES_B)
+    a = mx.mx_decode(A, sA, k)
+    b = mx.mx_decode(B, sB, k)
+    rng = np.random.default_rng(0)
+    for i in range(3):
+        p = (a[i] * b[i]).astype(np.float64)
+        exact = float(p.sum())
+        for order in (np.arange(k), np.arange(k)[::-1], rng.permutation(k)):
+            acc = np.float32(0.0)
+            for v in p[order].astype(np.float32):
+                acc = np.float32(acc + v)
+            assert float(acc) == exact

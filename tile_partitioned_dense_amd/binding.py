@@ -189,6 +189,55 @@ def _is_tensor(x):
     return hasattr(x, "data_ptr") and hasattr(x, "stride")
 
 
+def _check_devices(named):
+    """The library sees raw pointers only, so the binding checks what it cannot:
+    every tensor argument lives on the GPU that is current (the device the
+    library launches on), all on the same one. A host tensor's pointer handed
+    to a kernel would fault the GPU."""
+    import torch
+    cur = torch.cuda.current_device() if torch.cuda.is_available() else None
+    for name, t in named:
+        if t is None or not _is_tensor(t):
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} is on {t.device}; every tensor argument must be on the GPU")
+        if t.device.index != cur:
+            raise ValueError(f"{name} is on {t.device}, but the current device is cuda:{cur}")
+
+
+def _check_bias(bias, n):
+    """A bias tensor must be a contiguous vector of n float32 values (the
+    kernels read exactly that many)."""
+    import torch
+    if bias is None or not _is_tensor(bias):
+        return
+    if bias.dtype != torch.float32:
+        raise TypeError(f"bias must be float32, got {bias.dtype}")
+    if bias.dim() != 1 or bias.numel() != n or not bias.is_contiguous():
+        raise ValueError(f"bias must be a contiguous vector of {n} values, got shape "
+                         f"{tuple(bias.shape)} strides {tuple(bias.stride())}")
+
+
+def _check_counts(counts, m, n):
+    """Write counts: a contiguous 32-bit integer array of at least m*n elements."""
+    import torch
+    if counts is None or not _is_tensor(counts):
+        return
+    if counts.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32)):
+        raise TypeError(f"counts must be a 32-bit integer tensor, got {counts.dtype}")
+    if counts.numel() < m * n or not counts.is_contiguous():
+        raise ValueError(f"counts must be contiguous with at least {m * n} elements")
+
+
+def _c_dtype(C):
+    import torch
+    if C.dtype == torch.float32:
+        return Dtype.BF16_TO_F32
+    if C.dtype == torch.bfloat16:
+        return Dtype.BF16_TO_BF16
+    raise TypeError("C must be float32 or bfloat16")
+
+
 def _operands(A, B, C, M, N, K, strides, dtype, c_cols_div=1):
     """Pointers, shape, strides and dtype from torch tensors or raw values.
     C has N / c_cols_div columns (2 for SiLU(gate) * up)."""
@@ -203,15 +252,15 @@ def _operands(A, B, C, M, N, K, strides, dtype, c_cols_div=1):
         if K2 != K_ or N_ % c_cols_div or tuple(C.shape) != (M_, N_ // c_cols_div):
             raise ValueError(f"shapes do not chain: A{tuple(A.shape)} B{tuple(B.shape)} "
                              f"C{tuple(C.shape)}")
+        cdt = _c_dtype(C)
         if dtype is None:
-            if C.dtype == torch.float32:
-                dtype = Dtype.BF16_TO_F32
-            elif C.dtype == torch.bfloat16:
-                dtype = Dtype.BF16_TO_BF16
-            else:
-                raise TypeError("C must be float32 or bfloat16")
+            dtype = cdt
+        elif int(dtype) != cdt:
+            raise TypeError(f"dtype {Dtype(int(dtype)).name} does not match C's {C.dtype}")
         s = Strides(A.stride(0), A.stride(1), B.stride(0), B.stride(1), C.stride(0), C.stride(1))
         return (A.data_ptr(), B.data_ptr(), C.data_ptr(), M_, N_, K_, s, int(dtype))
+    if any(_is_tensor(x) for x in (A, B, C)):
+        raise TypeError("A, B and C must be all torch tensors or all raw pointers")
     if None in (M, N, K, strides, dtype):
         raise ValueError("raw pointers need M, N, K, strides and dtype")
     s = strides if isinstance(strides, Strides) else Strides(*strides)
@@ -235,6 +284,7 @@ def tile_gemm_run(h, A, B, C, M=None, N=None, K=None, strides=None, dtype=None, 
     (unless given) the current stream are taken from them. Returns the status;
     raises TileGemmError on a non-OK status when `check` is true."""
     a, b, c, M_, N_, K_, s, dt = _operands(A, B, C, M, N, K, strides, dtype)
+    _check_devices((("A", A), ("B", B), ("C", C)))
     st = load_library().tile_gemm_run(h, a, b, c, M_, N_, K_, ctypes.byref(s), dt,
                                       _stream_ptr(stream, C))
     if check:
@@ -249,6 +299,8 @@ def tile_gemm_run_epilogue(h, A, B, C, bias=None, act=Act.NONE, M=None, N=None, 
     times its last N/2."""
     div = 2 if int(act) == Act.SWIGLU else 1
     a, b, c, M_, N_, K_, s, dt = _operands(A, B, C, M, N, K, strides, dtype, div)
+    _check_bias(bias, N_)
+    _check_devices((("A", A), ("B", B), ("C", C), ("bias", bias)))
     bp = bias.data_ptr() if _is_tensor(bias) else bias
     st = load_library().tile_gemm_run_epilogue(h, a, b, c, M_, N_, K_, ctypes.byref(s), dt, bp,
                                                int(act), _stream_ptr(stream, C))
@@ -263,6 +315,9 @@ def tile_gemm_run_debug(h, A, B, C, counts=None, flags=0, M=None, N=None, K=None
     instrumentation (write counts, collision, forced configuration or grid)."""
     div = 2 if int(act) == Act.SWIGLU else 1
     a, b, c, M_, N_, K_, s, dt = _operands(A, B, C, M, N, K, strides, dtype, div)
+    _check_bias(bias, N_)
+    _check_counts(counts, M_, N_ // div)
+    _check_devices((("A", A), ("B", B), ("C", C), ("bias", bias), ("counts", counts)))
     cnt = counts.data_ptr() if _is_tensor(counts) else counts
     bp = bias.data_ptr() if _is_tensor(bias) else bias
     st = load_library().tile_gemm_run_debug(h, a, b, c, M_, N_, K_, ctypes.byref(s), dt,
@@ -290,12 +345,7 @@ def _mx_operands(A, Bt, C, a_scale, b_scale, fmt=MX_E4M3):
     if a_scale.shape[0] != M or b_scale.shape[0] != N or a_scale.stride(1) != 1 \
             or b_scale.stride(1) != 1 or a_scale.stride(0) != b_scale.stride(0):
         raise ValueError("scales: M and N rows with one common row stride and unit column stride")
-    if C.dtype == torch.float32:
-        dtype = Dtype.BF16_TO_F32
-    elif C.dtype == torch.bfloat16:
-        dtype = Dtype.BF16_TO_BF16
-    else:
-        raise TypeError("C must be float32 or bfloat16")
+    dtype = _c_dtype(C)
     s = Strides(A.stride(0), A.stride(1), Bt.stride(1), Bt.stride(0), C.stride(0), C.stride(1))
     return M, N, K, s, a_scale.stride(0), int(dtype)
 
@@ -304,6 +354,10 @@ def tile_gemm_run_mx(h, A, Bt, C, a_scale, b_scale, bias=None, act=Act.NONE, str
                      counts=None, flags=0, check: bool = True, fmt=MX_E4M3):
     """Enqueue the MX product C := act((sa * A) . (sb * Bt)^T + bias) (torch tensors)."""
     M, N, K, s, ls, dt = _mx_operands(A, Bt, C, a_scale, b_scale, fmt)
+    _check_bias(bias, N)
+    _check_counts(counts, M, N)
+    _check_devices((("A", A), ("Bt", Bt), ("C", C), ("a_scale", a_scale), ("b_scale", b_scale),
+                    ("bias", bias), ("counts", counts)))
     bp = bias.data_ptr() if _is_tensor(bias) else bias
     lib = load_library()
     args = (h, A.data_ptr(), Bt.data_ptr(), C.data_ptr(), M, N, K, ctypes.byref(s),

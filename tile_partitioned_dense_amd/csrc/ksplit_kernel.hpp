@@ -60,7 +60,10 @@ __global__ __launch_bounds__(KS * 64, 1) void ksplit_gemm_kernel(TileArgs p) {
 
   // this wave's K range, in slabs
   const int nk = (K + BK - 1) / BK;
-  const int nk_full = K / BK;
+  // DMA slabs; with a row-major B and an odd N the slab holding row K - 1
+  // goes through the register path, as in the tile kernel (a buffer load
+  // zeroes the dword that straddles the end of B, which holds its last value)
+  const int nk_full = (!BCOL && (N & 1)) ? (K - 1) / BK : K / BK;
   const int kb0 = (wave * nk) / KS, kb1 = ((wave + 1) * nk) / KS;
 
   // per-lane DMA source offsets within a slab (bytes), as in the tile kernel

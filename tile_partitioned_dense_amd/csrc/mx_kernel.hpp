@@ -169,11 +169,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
 #pragma unroll
       for (int q = 0; q < SA_DMA; ++q)
         if (q % NW == wave)
-          dma16(dst + 1024 * q, rsSA, (uint32_t)((m0 + 64 * q + lane) * p.ls + 16 * w), 0u);
+          dma16(dst + 1024 * q, rsSA, (uint32_t)(m0 + 64 * q + lane) * (uint32_t)p.ls + 16u * w, 0u);
 #pragma unroll
       for (int q = 0; q < SB_DMA; ++q)
         if (q % NW == wave)
-          dma16(dst + BM * 16 + 1024 * q, rsSB, (uint32_t)((n0 + 64 * q + lane) * p.ls + 16 * w), 0u);
+          dma16(dst + BM * 16 + 1024 * q, rsSB, (uint32_t)(n0 + 64 * q + lane) * (uint32_t)p.ls + 16u * w, 0u);
     };
 
     // The window of slabs SPW w .. goes out just before slab SPW w's own loads,

@@ -169,9 +169,9 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void mx_stream_kernel(MxArgs 
       for (int q = 0; q < NWIN; ++q) {
         if (q % NW == wave) {
           if (q == 0)
-            dma16(dst, rsSA, (uint32_t)((m0 + lane) * p.ls + 16 * v), 0u);
+            dma16(dst, rsSA, (uint32_t)(m0 + lane) * (uint32_t)p.ls + 16u * v, 0u);
           else
-            dma16(dst + SWA + 1024 * (q - 1), rsSB, (uint32_t)((n0 + 64 * (q - 1) + lane) * p.ls + 16 * v),
+            dma16(dst + SWA + 1024 * (q - 1), rsSB, (uint32_t)(n0 + 64 * (q - 1) + lane) * (uint32_t)p.ls + 16u * v,
                   0u);
         }
       }

@@ -63,6 +63,17 @@ bool overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
   return a0 < a1 && b0 < b1 && a0 < b1 && b0 < a1;
 }
 
+// Bytes from the first to one past the last element touched by `rows` rows of
+// `extent` elements, `stride` elements apart: esz * ((rows - 1) * stride +
+// extent). -1 when that overflows int64 (the caller then refuses the call).
+int64_t span_bytes(int64_t rows, int64_t stride, int64_t extent, int64_t esz) {
+  int64_t t, u, v;
+  if (__builtin_mul_overflow(rows - 1, stride, &t) || __builtin_add_overflow(t, extent, &u) ||
+      __builtin_mul_overflow(u, esz, &v))
+    return -1;
+  return v;
+}
+
 // n_out: C's width (N, or N/2 for SiLU(gate) * up); -1 means N.
 tile_gemm_status_t check_args(const void* A, const void* B, const void* C, int64_t M, int64_t N,
                               int64_t K, const tile_gemm_strides_t* s, int dtype,
@@ -101,12 +112,28 @@ tile_gemm_status_t check_args(const void* A, const void* B, const void* C, int64
     return fail(TILE_GEMM_ERR_BAD_STRIDE,
                 "C strides (c_m=%lld, c_n=%lld): need c_n == 1 and c_m >= %lld (C's width)",
                 (long long)s->c_m, (long long)s->c_n, (long long)n_out);
+  // Leading dimensions below 2^31 elements: every span below is then a small
+  // multiple of 2^62 at most, and the checked arithmetic of span_bytes
+  // refuses the rest instead of letting a product wrap.
+  if (s->c_m >= kMaxDim)
+    return fail(TILE_GEMM_ERR_BAD_STRIDE, "C: c_m=%lld, must be < 2^31", (long long)s->c_m);
+  if (K > 0) {
+    if (s->a_m >= kMaxDim)
+      return fail(TILE_GEMM_ERR_BAD_STRIDE, "A: a_m=%lld, must be < 2^31", (long long)s->a_m);
+    if ((brow ? s->b_k : s->b_n) >= kMaxDim)
+      return fail(TILE_GEMM_ERR_BAD_STRIDE, "B: %s=%lld, must be < 2^31", brow ? "b_k" : "b_n",
+                  (long long)(brow ? s->b_k : s->b_n));
+  }
 
   const int64_t esz = (dtype == TILE_GEMM_BF16_TO_F32) ? 4 : 2;
   if ((uintptr_t)C % 16) return fail(TILE_GEMM_ERR_MISALIGNED, "C: base pointer not 16-byte aligned");
   if ((s->c_m * esz) % 16)
     return fail(TILE_GEMM_ERR_MISALIGNED, "C: c_m=%lld elements is not a multiple of 16 bytes",
                 (long long)s->c_m);
+  const int64_t c_span = span_bytes(M, s->c_m, n_out, esz);
+  const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)c_span;
+  if (c_span < 0 || c1 < c0)
+    return fail(TILE_GEMM_ERR_BAD_SHAPE, "C: its byte range overflows the address space");
   if (K == 0) return TILE_GEMM_OK;
   if ((uintptr_t)A % 16) return fail(TILE_GEMM_ERR_MISALIGNED, "A: base pointer not 16-byte aligned");
   if ((uintptr_t)B % 16) return fail(TILE_GEMM_ERR_MISALIGNED, "B: base pointer not 16-byte aligned");
@@ -119,18 +146,17 @@ tile_gemm_status_t check_args(const void* A, const void* B, const void* C, int64
                 brow ? "b_k" : "b_n", (long long)ldb);
 
   // Byte extents actually touched.
-  const int64_t a_span = 2 * ((M - 1) * s->a_m + K);
-  const int64_t b_span = 2 * (brow ? (K - 1) * s->b_k + N : (N - 1) * s->b_n + K);
+  const int64_t a_span = span_bytes(M, s->a_m, K, 2);
+  const int64_t b_span = brow ? span_bytes(K, s->b_k, N, 2) : span_bytes(N, s->b_n, K, 2);
   // the kernels address each operand with 32-bit byte offsets
-  if (a_span >= ((int64_t)1 << 32))
+  if (a_span < 0 || a_span >= ((int64_t)1 << 32))
     return fail(TILE_GEMM_ERR_BAD_SHAPE, "A: spans %lld bytes, must be below 4 GiB", (long long)a_span);
-  if (b_span >= ((int64_t)1 << 32))
+  if (b_span < 0 || b_span >= ((int64_t)1 << 32))
     return fail(TILE_GEMM_ERR_BAD_SHAPE, "B: spans %lld bytes, must be below 4 GiB", (long long)b_span);
 
-  const uintptr_t a0 = (uintptr_t)A, b0 = (uintptr_t)B, c0 = (uintptr_t)C;
+  const uintptr_t a0 = (uintptr_t)A, b0 = (uintptr_t)B;
   const uintptr_t a1 = a0 + (uintptr_t)a_span;
   const uintptr_t b1 = b0 + (uintptr_t)b_span;
-  const uintptr_t c1 = c0 + (uintptr_t)(esz * ((M - 1) * s->c_m + n_out));
   if (overlap(c0, c1, a0, a1)) return fail(TILE_GEMM_ERR_ALIAS, "C overlaps A (C is written)");
   if (overlap(c0, c1, b0, b1)) return fail(TILE_GEMM_ERR_ALIAS, "C overlaps B (C is written)");
   return TILE_GEMM_OK;
@@ -265,24 +291,31 @@ tile_gemm_status_t check_mx(const void* A, const void* B, const void* C, int64_t
                   "B strides (b_k=%lld, b_n=%lld): the MX product takes B as N x K, b_k == 1, "
                   "b_n >= %lld bytes",
                   (long long)s->b_k, (long long)s->b_n, (long long)kb);
-    if (ls < K / 32 || ls % 4)
+    if (ls < K / 32 || ls % 4 || ls >= kMaxDim)
       return fail(TILE_GEMM_ERR_BAD_STRIDE,
-                  "scale_stride=%lld: need a multiple of 4 bytes and >= K/32=%lld", (long long)ls,
-                  (long long)(K / 32));
-    // the kernel addresses scale rows (up to one tile past the edge) with
-    // 32-bit byte offsets
-    if ((M + 256) * ls >= ((int64_t)1 << 32) || (N + 256) * ls >= ((int64_t)1 << 32))
-      return fail(TILE_GEMM_ERR_BAD_SHAPE, "scales: rows x scale_stride must stay below 4 GiB");
+                  "scale_stride=%lld: need a multiple of 4 bytes, >= K/32=%lld and < 2^31",
+                  (long long)ls, (long long)(K / 32));
+    if (s->a_m >= kMaxDim || s->b_n >= kMaxDim)
+      return fail(TILE_GEMM_ERR_BAD_STRIDE, "A or B: a_m=%lld, b_n=%lld, each must be < 2^31",
+                  (long long)s->a_m, (long long)s->b_n);
+    // the kernels address scale rows (up to one tile past the edge) with
+    // 32-bit byte offsets, formed as signed 32-bit products
+    if ((M + 256) * ls >= kMaxDim || (N + 256) * ls >= kMaxDim)
+      return fail(TILE_GEMM_ERR_BAD_SHAPE, "scales: rows x scale_stride must stay below 2 GiB");
   }
-  if (s->c_n != 1 || s->c_m < N)
-    return fail(TILE_GEMM_ERR_BAD_STRIDE, "C strides (c_m=%lld, c_n=%lld): need c_n == 1, c_m >= N",
+  if (s->c_n != 1 || s->c_m < N || s->c_m >= kMaxDim)
+    return fail(TILE_GEMM_ERR_BAD_STRIDE,
+                "C strides (c_m=%lld, c_n=%lld): need c_n == 1, N <= c_m < 2^31",
                 (long long)s->c_m, (long long)s->c_n);
   const int64_t esz = dtype == TILE_GEMM_BF16_TO_F32 ? 4 : 2;
   if ((uintptr_t)C % 16) return fail(TILE_GEMM_ERR_MISALIGNED, "C: base pointer not 16-byte aligned");
   if ((s->c_m * esz) % 16)
     return fail(TILE_GEMM_ERR_MISALIGNED, "C: c_m=%lld elements is not a multiple of 16 bytes",
                 (long long)s->c_m);
-  const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)(esz * ((M - 1) * s->c_m + N));
+  const int64_t c_span = span_bytes(M, s->c_m, N, esz);
+  const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)c_span;
+  if (c_span < 0 || c1 < c0)
+    return fail(TILE_GEMM_ERR_BAD_SHAPE, "C: its byte range overflows the address space");
   if (K > 0) {
     if ((uintptr_t)A % 16 || s->a_m % 16)
       return fail(TILE_GEMM_ERR_MISALIGNED, "A: base or a_m not a multiple of 16 bytes");
@@ -290,8 +323,8 @@ tile_gemm_status_t check_mx(const void* A, const void* B, const void* C, int64_t
       return fail(TILE_GEMM_ERR_MISALIGNED, "B: base or b_n not a multiple of 16 bytes");
     if ((uintptr_t)sa % 4 || (uintptr_t)sb % 4)
       return fail(TILE_GEMM_ERR_MISALIGNED, "scales: base pointers must be 4-byte aligned");
-    const int64_t a_span = (M - 1) * s->a_m + kb, b_span = (N - 1) * s->b_n + kb;
-    if (a_span >= ((int64_t)1 << 32) || b_span >= ((int64_t)1 << 32))
+    const int64_t a_span = span_bytes(M, s->a_m, kb, 1), b_span = span_bytes(N, s->b_n, kb, 1);
+    if (a_span < 0 || b_span < 0 || a_span >= ((int64_t)1 << 32) || b_span >= ((int64_t)1 << 32))
       return fail(TILE_GEMM_ERR_BAD_SHAPE, "A or B spans 4 GiB or more");
     const uintptr_t a0 = (uintptr_t)A, b0 = (uintptr_t)B, s0 = (uintptr_t)sa, t0 = (uintptr_t)sb;
     if (overlap(c0, c1, a0, a0 + a_span)) return fail(TILE_GEMM_ERR_ALIAS, "C overlaps A");

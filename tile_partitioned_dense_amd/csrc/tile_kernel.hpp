@@ -46,9 +46,14 @@
 // Bounds: each slab's buffer resources start at the slab and end at the last
 // valid element of the operand, so rows (or, for a row-major B, columns) past
 // the edge read as zero and no load can leave the operand. Values read for
-// rows >= M or columns >= N only reach accumulators that are never stored. A K tail (K % 32 != 0) must be
-// exact zeros in both operands; that one slab is fetched through registers
-// with element masks and written to LDS with ds_write.
+// rows >= M or columns >= N only reach accumulators that are never stored. A
+// K tail (K % 32 != 0) must be exact zeros in both operands; that one slab is
+// fetched through registers with element masks and written to LDS with
+// ds_write. The range check zeroes whole dwords: a dword that straddles the
+// end of a resource reads as zero, including its valid half. Only the
+// operand's very last value can sit in such a dword; for A and a column-major
+// B it lies in the K tail whenever K is odd, and for a row-major B with an
+// odd N the last slab (row K - 1) is sent through the register path as well.
 #pragma once
 
 #include <type_traits>
@@ -274,7 +279,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile_gemm_kernel(TileArgs p) 
     }
 
     const int nk = (K + BK - 1) / BK;
-    const int nk_full = K / BK;  // slabs with no K tail
+    // Slabs loaded by DMA; the rest (a K tail) go through registers. A buffer
+    // load's range check works on whole dwords, so with a row-major B and an
+    // odd N the dword holding B's last value (K - 1, N - 1) reaches past the
+    // resource and would read as zero: the slab holding row K - 1 then takes
+    // the masked register path too.
+    const int nk_full = (!BCOL && (N & 1)) ? (K - 1) / BK : K / BK;
 
     // Issue the loads of slab s into its stage.
     auto issue_slab = [&](int s) {

@@ -171,6 +171,14 @@ def operands(w: Workload, integer: bool = False, M: int | None = None,
 # (8 being E4M3's largest exponent), and each x / 2^e is rounded to the
 # nearest E4M3 value (ties to even), saturating at +-448. The integer variant
 # uses the E4M3 codes of -3..3 with unit scales, so products are exact.
+# The scaled-integer variant keeps those codes and draws every block's scale
+# uniformly from a given range of E8M0 bytes: products are then integers
+# times 2^(ea + eb), and when the exponents ea + eb of one product span at
+# most S across all blocks, every partial sum of the K products is a multiple
+# of 2^(min ea + eb) below 9 K 2^S of that unit. With 9 K 2^S < 2^24 each
+# partial sum is exact in fp32 whatever the order of summation, so the GPU's
+# result is the exact sum: the ranges used below (A in [120, 123], B in
+# [131, 134], S = 6) allow K up to 29127.
 
 MX_BLOCK = 32
 _E4M3_INT_CODES = {-3: 0xC4, -2: 0xC0, -1: 0xB8, 0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44}
@@ -221,11 +229,19 @@ def mx_scale_stride(k: int) -> int:
     return (((k + MX_BLOCK - 1) // MX_BLOCK) + 3) // 4 * 4
 
 
-def draw_mx(rows: int, k: int, dist: str, seed: int, scale: float = 1.0, fmt: str = "e4m3"):
+MX_INT_SCALES_A = (120, 123)   # E8M0 bytes of A's blocks in the scaled-integer variant
+MX_INT_SCALES_B = (131, 134)   # and of B's: product exponents span -3 .. 3
+
+
+def draw_mx(rows: int, k: int, dist: str, seed: int, scale: float = 1.0, fmt: str = "e4m3",
+            scale_codes: tuple | None = None):
     """(codes, scales): rows x k E4M3 codes (E2M1: rows x k/2 packed bytes) and
     rows x mx_scale_stride(k) E8M0 bytes (padding bytes 127). Values are drawn
     like draw() (row-major, in chunks of rows), then quantised per block of 32
-    as described above (E2M1: largest exponent 2, so e = floor(log2 max) - 2)."""
+    as described above (E2M1: largest exponent 2, so e = floor(log2 max) - 2).
+    With dist "int3" the codes are those of -3..3; `scale_codes` = (lo, hi)
+    then draws each block's scale byte uniformly from lo..hi (after all the
+    codes, from the same generator), else every scale is 127 (unit)."""
     if dist not in ("normal", "uniform", "int3"):
         raise ValueError(f"unknown distribution {dist!r}")
     if fmt not in ("e4m3", "e2m1"):
@@ -258,6 +274,11 @@ def draw_mx(rows: int, k: int, dist: str, seed: int, scale: float = 1.0, fmt: st
         scales[r0:r1, :nb] = (e + 127.0).astype(np.uint8)
         q = blocks / np.exp2(e)[:, :, None]
         codes[r0:r1] = encode(q).reshape(r1 - r0, nb * MX_BLOCK)[:, :k]
+    if dist == "int3" and scale_codes is not None:
+        lo, hi = scale_codes
+        if not (0 <= lo <= hi <= 254):
+            raise ValueError(f"scale bytes {scale_codes} outside 0..254")
+        scales[:, :nb] = rng.integers(lo, hi + 1, (rows, nb)).astype(np.uint8)
     return (pack_fp4(codes) if fp4 else codes), scales
 
 
@@ -313,11 +334,21 @@ class MxOperands:
 
 
 def mx_operands(w: MxWorkload, integer: bool = False, M: int | None = None,
-                N: int | None = None, K: int | None = None) -> MxOperands:
+                N: int | None = None, K: int | None = None,
+                varied_scales: bool = False) -> MxOperands:
+    """Operands of an MX workload (optionally at another shape). integer: the
+    codes of -3..3, with unit scales, or with varied_scales each block's scale
+    drawn from MX_INT_SCALES_A / MX_INT_SCALES_B (seeds op 5 and 6)."""
     M = w.M if M is None else M
     N = w.N if N is None else N
     K = w.K if K is None else K
-    da, db = ("int3", "int3") if integer else ("normal", "normal")
-    A, sA = draw_mx(M, K, da, 1000 * w.case + (3 if integer else 1), fmt=w.fmt)
-    Bt, sB = draw_mx(N, K, db, 1000 * w.case + (4 if integer else 2), w.b_scale, fmt=w.fmt)
+    if integer:
+        opa, opb = (5, 6) if varied_scales else (3, 4)
+        A, sA = draw_mx(M, K, "int3", 1000 * w.case + opa, fmt=w.fmt,
+                        scale_codes=MX_INT_SCALES_A if varied_scales else None)
+        Bt, sB = draw_mx(N, K, "int3", 1000 * w.case + opb, fmt=w.fmt,
+                         scale_codes=MX_INT_SCALES_B if varied_scales else None)
+        return MxOperands(A, sA, Bt, sB)
+    A, sA = draw_mx(M, K, "normal", 1000 * w.case + 1, fmt=w.fmt)
+    Bt, sB = draw_mx(N, K, "normal", 1000 * w.case + 2, w.b_scale, fmt=w.fmt)
     return MxOperands(A, sA, Bt, sB)
