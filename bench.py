@@ -33,6 +33,18 @@ PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA (twice the bf16 rate)
 PEAK_FP4_TFLOPS = 10066.3      # MI355X dense fp4 / fp6 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 MIN_ROTATION_BYTES = 600 << 20  # > 2x the 256 MB last-level cache
+RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # below: HBM-bound
+
+# Secondary legs of the default run: the other bf16 workloads (4096^3 in both
+# output types), the decode / tall-skinny sweep in both B layouts, the
+# per-call cost on a ~1 us kernel, and the MX products in both formats.
+DEFAULT_SECONDARY = ",".join([
+    "qkv_shard", "square4096", "square4096@f32",
+    "decode_m64", "decode_m32", "decode", "decode_m8", "decode_m1",
+    "decode_colB_m64", "decode_colB_m32", "decode_colB", "decode_colB_m8", "decode_colB_m1",
+    "tall_skinny", "tall_skinny_colB", "gemm256", "launch64",
+    "mx_mlp_gate_up_shard", "mx_decode", "mxfp4_mlp_gate_up_shard", "mxfp4_decode",
+])
 
 
 def log(*a):
@@ -48,10 +60,12 @@ def parse():
     # Each default leg runs its own kernel instance, so a profiler's per-kernel
     # averages match the legs; epilogue legs (NAME:EPI, same instances as the
     # plain product) and mx_square4096 are available on request.
-    ap.add_argument("--secondary", default="qkv_shard,square4096,decode,decode_colB,gemm256,"
-                    "mx_mlp_gate_up_shard,mx_decode",
+    ap.add_argument("--secondary", default=DEFAULT_SECONDARY,
                     help="comma-separated extra workloads reported on the same line; NAME:EPI adds a "
-                    "fused epilogue, e.g. decode:bias+silu ('' for none)")
+                    "fused epilogue, e.g. decode:bias+silu; NAME@f32 or NAME@bf16 picks the output "
+                    "type ('' for none)")
+    ap.add_argument("--probes", action="store_true",
+                    help="also run the MFMA-rate and HBM streaming-read probes (libtile_probes.so)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time for the oracle baseline sample")
@@ -60,15 +74,99 @@ def parse():
     return ap.parse_args()
 
 
+class ClockSampler:
+    """Samples the GPU's clocks and power through amdsmi's GPU metrics from a
+    side thread while a leg's timed launches run. Context for the roofline
+    fractions: the published peaks assume 2.4 GHz."""
+
+    def __init__(self, period_s=0.005):
+        self.period, self.err, self.samples = period_s, None, []
+        self.amdsmi = self.h = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.amdsmi = amdsmi
+            self.h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception as e:  # no amdsmi, no permission: report why
+            self.err = f"{type(e).__name__}: {e}"
+
+    @staticmethod
+    def _num(v):
+        if isinstance(v, (list, tuple)):
+            vals = [x for x in v if isinstance(x, (int, float)) and 0 < x < 65535]
+            return sum(vals) / len(vals) if vals else None
+        return v if isinstance(v, (int, float)) and 0 < v < 65535 else None
+
+    def _one(self):
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
+        gfx = self._num(m.get("current_gfxclk")) or self._num(m.get("current_gfxclks"))
+        avg_gfx = self._num(m.get("average_gfxclk_frequency"))
+        mem = self._num(m.get("current_uclk"))
+        pwr = self._num(m.get("current_socket_power")) or self._num(m.get("average_socket_power"))
+        return gfx, avg_gfx, mem, pwr
+
+    def __enter__(self):
+        import threading
+        self.samples, self._stop = [], False
+        if self.h is None:
+            return self
+
+        def loop():
+            while not self._stop:
+                try:
+                    self.samples.append(self._one())
+                except Exception as e:
+                    self.err = f"{type(e).__name__}: {e}"
+                    return
+                time.sleep(self.period)
+        self._t = threading.Thread(target=loop, daemon=True)
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop = True
+        if self.h is not None:
+            self._t.join()
+
+    def report(self):
+        def stats(i):
+            v = [x[i] for x in self.samples if x[i] is not None]
+            if not v:
+                return None
+            return {"mean": round(sum(v) / len(v), 1), "min": round(min(v), 1), "max": round(max(v), 1)}
+        if not self.samples:
+            return {"source": "amdsmi GPU metrics", "samples": 0, "error": self.err}
+        return {"source": "amdsmi GPU metrics, sampled every 5 ms during the timed launches",
+                "samples": len(self.samples), "gfx_clock_mhz": stats(0),
+                "gfx_clock_avg_mhz": stats(1), "mem_clock_mhz": stats(2),
+                "socket_power_w": stats(3), "error": self.err}
+
+
 class Bench:
     def __init__(self, torch, tg, synth):
         self.torch, self.tg, self.synth = torch, tg, synth
         self.g = tg.TileGemm(0)
+        self.clock = ClockSampler()
+        self._host = {}
+
+    def operands(self, w):
+        """Host operands of a workload. The decode sweep's legs share the seeds
+        of their layout, so B is the same draw and A's rows are the first rows
+        of one stream: drawn once for the largest M (the default legs run that
+        one first), sliced for the others."""
+        key = (w.case, w.b_col_major, w.N, w.K)
+        ops = self._host.get(key)
+        if ops is None or ops.A.shape[0] < w.M:
+            ops = self.synth.operands(w)
+            self._host[key] = ops
+        if ops.A.shape[0] != w.M:
+            ops = self.synth.Operands(ops.A[:w.M], ops.B, ops.B_storage)
+        return ops
 
     def make(self, w, out):
         torch, synth = self.torch, self.synth
         t0 = time.time()
-        ops = synth.operands(w)
+        ops = self.operands(w)
         A = torch.from_numpy(ops.A.view(np.int16)).cuda().view(torch.bfloat16)
         Bs = torch.from_numpy(ops.B_storage.view(np.int16)).cuda().view(torch.bfloat16)
         odt = torch.float32 if out == "f32" else torch.bfloat16
@@ -158,14 +256,16 @@ class Bench:
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            A, B, C = sets[i % len(sets)]
-            starts[i].record()
-            g(A, B, C, **kw)
-            ends[i].record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+        with self.clock:
+            t0 = time.perf_counter()
+            for i in range(steps):
+                A, B, C = sets[i % len(sets)]
+                starts[i].record()
+                g(A, B, C, **kw)
+                ends[i].record()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        clock = self.clock.report()
         per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms per launch
         unfused = None
         if epi:
@@ -198,6 +298,7 @@ class Bench:
             "plan": {"variant": "tile" if plan.variant == 1 else "skinny", "bm": plan.bm,
                      "bn": plan.bn, "grid": int(plan.grid), "k_split": plan.k_split},
         }
+        res["clock"] = clock
         if unfused is not None:
             res["unfused_torch_ms_mean"] = unfused
         mean_s = res["kernel_ms_mean"] * 1e-3
@@ -205,7 +306,7 @@ class Bench:
         res["gbs"] = w.algorithmic_bytes(out) / mean_s / 1e9
         res["frac_mfma"] = res["tflops"] / PEAK_BF16_TFLOPS
         res["frac_hbm"] = res["gbs"] / PEAK_HBM_GBS
-        if w.flops < 1e9:
+        if w.flops < 1e8:
             res["launch_us"] = self.launch_overhead(sets[0])
         log(f"[bench] {w.name}: mean {res['kernel_ms_mean'] * 1e3:.1f} us "
             f"(median {res['kernel_ms_median'] * 1e3:.1f}, min {res['kernel_ms_min'] * 1e3:.1f}) "
@@ -243,14 +344,15 @@ def time_mx_workload(b, w, steps, warmup):
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        a, bt, sa, sb = sets[i % copies]
-        ev[i][0].record()
-        g.mx(a, bt, Cs[i % copies], sa, sb, fmt=fmt)
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with b.clock:
+        t0 = time.perf_counter()
+        for i in range(steps):
+            a, bt, sa, sb = sets[i % copies]
+            ev[i][0].record()
+            g.mx(a, bt, Cs[i % copies], sa, sb, fmt=fmt)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     per = np.array([x.elapsed_time(y) for x, y in ev])
     plan = b.tg.tile_gemm_plan_mx(w.M, w.N, w.K, 256)
     res = {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
@@ -259,7 +361,8 @@ def time_mx_workload(b, w, steps, warmup):
            "kernel_ms_mean": float(per.mean()), "kernel_ms_median": float(np.median(per)),
            "kernel_ms_min": float(per.min()), "kernel_ms_max": float(per.max()),
            "flop": w.flops, "bytes": w.algorithmic_bytes(out),
-           "plan": {"variant": "mx", "bm": plan.bm, "bn": plan.bn, "grid": int(plan.grid)}}
+           "plan": {"variant": "mx", "bm": plan.bm, "bn": plan.bn, "grid": int(plan.grid)},
+           "clock": b.clock.report()}
     mean_s = res["kernel_ms_mean"] * 1e-3
     res["tflops"] = w.flops / mean_s / 1e12
     res["gbs"] = w.algorithmic_bytes(out) / mean_s / 1e9
@@ -295,6 +398,69 @@ def measured_traffic(workload):
         return int(round(1024 * (w["fetch_kib"] * rec["fetch_scale"] + w["write_kib"] * rec["write_scale"])))
     except (OSError, KeyError, ValueError):
         return None
+
+
+def run_probes(torch, clock):
+    """The MFMA-rate and HBM streaming-read probes (csrc/probes.hip): the
+    ceilings the GEMM kernels meet on this machine, beside the published peaks."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "tile_partitioned_dense_amd", "libtile_probes.so"))
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.tg_probe_mfma.argtypes = [vp, vp, i32, i32, i32, i32, vp]
+    lib.tg_probe_read.argtypes = [vp, vp, i64, i32, i32, vp]
+    stream = torch.cuda.current_stream().cuda_stream
+    grid = 256
+    out = torch.empty(grid * 512, dtype=torch.float32, device="cuda")
+    rnd = torch.randn(grid * 8 * 16 * 1024 // 2, device="cuda").to(torch.bfloat16)
+    const = torch.full_like(rnd, 1.0)
+
+    def timed(fn, n=20, warm=3):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        with clock:
+            for a, b in ev:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3, clock.report()
+
+    mfma = []
+    for shape, sname in ((0, "v_mfma_f32_32x32x16_bf16"), (1, "v_mfma_f32_16x16x32_bf16")):
+        for wps in (1, 2):
+            for data, src in (("random N(0,1)", rnd), ("constant 1.0", const)):
+                iters = 2400 // wps
+                fn = lambda: lib.tg_probe_mfma(src.data_ptr(), out.data_ptr(), grid, wps, shape,
+                                               iters, stream)
+                t, clk = timed(fn)
+                flop = grid * 4 * wps * iters * 64 * 32768
+                tf = flop / t / 1e12
+                mfma.append({"instruction": sname, "waves_per_simd": wps, "operands": data,
+                             "launch_ms": round(t * 1e3, 3), "tflops": round(tf, 1),
+                             "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                             "gfx_clock_mhz": (clk.get("gfx_clock_mhz") or {}).get("mean"),
+                             "socket_power_w": (clk.get("socket_power_w") or {}).get("mean")})
+                log(f"[probe] {sname} {wps} wave(s)/SIMD {data}: {tf:.0f} TFLOP/s")
+    del rnd, const
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(7)
+    rout = torch.empty(8192 * 256, dtype=torch.int32, device="cuda")
+    read = []
+    for chunk, g in ((1, 256), (1, 512), (1, 1024), (1, 2048), (0, 2048), (0, 8192)):
+        fn = lambda: lib.tg_probe_read(buf.data_ptr(), rout.data_ptr(), nbytes, g, chunk, stream)
+        t, clk = timed(fn, n=10)
+        gbs = nbytes / t / 1e9
+        read.append({"pattern": "one contiguous chunk per workgroup" if chunk else "grid-strided",
+                     "workgroups": g, "bytes": nbytes, "launch_ms": round(t * 1e3, 3),
+                     "gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)})
+        log(f"[probe] read {read[-1]['pattern']} x{g}: {gbs:.0f} GB/s")
+    del buf
+    torch.cuda.empty_cache()
+    return {"mfma": mfma, "hbm_read": read}
 
 
 def roofline(res, hbm_bound):
@@ -383,10 +549,14 @@ def main():
             secondary.append(time_mx_workload(b, synth.MX_WORKLOADS[name], args.steps, args.warmup))
             continue
         base, _, epi = name.partition(":")
+        base, _, out = base.partition("@")
         w = synth.WORKLOADS[base]
-        _, r = b.time_workload(w, w.outs[0], args.steps, args.warmup, epi or None)
-        r["roofline"] = roofline(r, hbm_bound=name.startswith("decode"))
+        _, r = b.time_workload(w, out or w.outs[0], args.steps, args.warmup, epi or None)
+        if out:
+            r["workload"] = f"{base}@{out}" + (f":{epi}" if epi else "")
+        r["roofline"] = roofline(r, hbm_bound=w.flops / r["bytes"] < RIDGE_FLOP_PER_BYTE)
         secondary.append(r)
+    probes = run_probes(torch, b.clock) if args.probes else None
     if args.copy_calibration_mib:
         copy_calibration(torch, args.copy_calibration_mib)
 
@@ -408,11 +578,14 @@ def main():
                    "b_layout": res["b_layout"], "out": head_out, "parallelism": "none (1 GPU)",
                    "plan": res["plan"]},
         "roofline": roofline(res, hbm_head),
+        "clock": res["clock"],
         "kernel_ms": {k: round(res[k], 5) for k in
                       ("kernel_ms_mean", "kernel_ms_median", "kernel_ms_min", "kernel_ms_max")},
         "secondary": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                       for r in secondary],
     }
+    if probes is not None:
+        line["probes"] = probes
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample of the headline workload")
         line["cpu_baseline"] = cpu_baseline(head, ops, args.cpu_seconds)

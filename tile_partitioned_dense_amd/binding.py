@@ -343,11 +343,17 @@ def _mx_operands(A, Bt, C, a_scale, b_scale, fmt=MX_E4M3):
     if K2 != K or tuple(C.shape) != (M, N):
         raise ValueError(f"shapes do not chain: A{tuple(A.shape)} Bt{tuple(Bt.shape)} C{tuple(C.shape)}")
     if a_scale.shape[0] != M or b_scale.shape[0] != N or a_scale.stride(1) != 1 \
-            or b_scale.stride(1) != 1 or a_scale.stride(0) != b_scale.stride(0):
-        raise ValueError("scales: M and N rows with one common row stride and unit column stride")
+            or b_scale.stride(1) != 1:
+        raise ValueError("scales: M and N rows with unit column stride")
+    # One row stride serves both scale arrays. The stride of a single-row
+    # array is never used (and torch may report any value for it), so it takes
+    # the other array's; two single rows use their row length.
+    if M > 1 and N > 1 and a_scale.stride(0) != b_scale.stride(0):
+        raise ValueError("scales: A's and B's scale rows must have one common stride")
+    ls = a_scale.stride(0) if M > 1 else (b_scale.stride(0) if N > 1 else a_scale.shape[1])
     dtype = _c_dtype(C)
     s = Strides(A.stride(0), A.stride(1), Bt.stride(1), Bt.stride(0), C.stride(0), C.stride(1))
-    return M, N, K, s, a_scale.stride(0), int(dtype)
+    return M, N, K, s, ls, int(dtype)
 
 
 def tile_gemm_run_mx(h, A, Bt, C, a_scale, b_scale, bias=None, act=Act.NONE, stream=None,

@@ -22,6 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtile_gemm.so")
+PROBES_LIB = os.path.join(PKG, "libtile_probes.so")   # measurement probes, not the GEMM ABI
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -73,6 +74,15 @@ def _compile(unit, save_temps):
     return obj, "\n".join(msgs)
 
 
+def _link(objs, out):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
+
+
 def build(jobs: int | None = None, save_temps: bool = False, verbose: bool = False) -> str:
     """Compile every kernel unit and link the shared library. Always rebuilds."""
     if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
@@ -84,11 +94,14 @@ def build(jobs: int | None = None, save_temps: bool = False, verbose: bool = Fal
     objs = []
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         futs = [ex.submit(_compile, u, save_temps) for u in units]
+        probe = ex.submit(_compile, ("probes", os.path.join(CSRC, "probes.hip"), []), False)
         for f in futs:
             obj, msg = f.result()
             objs.append(obj)
             if verbose and msg.strip():
                 print(msg, file=sys.stderr)
+        probe_obj, _ = probe.result()
+    _link([probe_obj], PROBES_LIB)
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,0 +1,146 @@
+// probes.hip -- measurement probes for the roofline figures (not part of the
+// GEMM library's ABI; built as its own small library, libtile_probes.so).
+//
+// Two ceilings the GEMM kernels are compared against on the same box:
+//  * the rate at which the chip sustains bf16 MFMA instructions when nothing
+//    else runs (no memory traffic, no LDS), with random or constant operands
+//    and one or two waves per SIMD, for the 32x32x16 and 16x16x32 shapes;
+//  * the rate at which HBM delivers a plain streaming read.
+// Under sustained MFMA load the clock settles below the 2.4 GHz that the
+// published peak assumes; the MFMA probe measures where it settles.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int kOps = 8;  // distinct operand registers per side
+
+// Every wave loads kOps A and kOps B fragments (16 bytes per lane each) from
+// `src` and then issues iters * 64 independent-chain MFMAs, rotating through
+// the fragments so consecutive instructions see different data. 8 (or 16)
+// accumulator chains keep every MFMA independent of the previous several.
+template <int SHAPE>
+__global__ __launch_bounds__(512) void mfma_probe(const u32x4* __restrict__ src, float* __restrict__ out, int iters) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  bf16x8 a[kOps], b[kOps];
+#pragma unroll
+  for (int i = 0; i < kOps; ++i) {
+    a[i] = __builtin_bit_cast(bf16x8, src[(wave * 2 * kOps + i) * 64 + lane]);
+    b[i] = __builtin_bit_cast(bf16x8, src[(wave * 2 * kOps + kOps + i) * 64 + lane]);
+  }
+  float total = 0.0f;
+  if constexpr (SHAPE == 0) {
+    floatx16 acc[kOps];
+#pragma unroll
+    for (int i = 0; i < kOps; ++i) acc[i] = floatx16{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < kOps; ++j)
+#pragma unroll
+        for (int i = 0; i < kOps; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(i + j) % kOps], b[(5 * i + j) % kOps],
+                                                            acc[i], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kOps; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) total += acc[i][e];
+  } else {
+    floatx4 acc[2 * kOps];
+#pragma unroll
+    for (int i = 0; i < 2 * kOps; ++i) acc[i] = floatx4{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < kOps; ++j)
+#pragma unroll
+        for (int i = 0; i < 2 * kOps; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[(i + j) % kOps], b[(5 * i + j) % kOps],
+                                                            acc[i], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * kOps; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) total += acc[i][e];
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = total;
+}
+
+// Streaming read of n16 16-byte units: workgroup g reads its own contiguous
+// chunk (chunk = 1) or the whole grid strides through the buffer (chunk = 0),
+// each lane 16 bytes per load, several loads in flight. The XOR of everything
+// read is stored per thread so no load can be dropped.
+__global__ __launch_bounds__(256) void read_probe(const u32x4* __restrict__ src, uint32_t* __restrict__ out, int64_t n16,
+                           int chunk) {
+  const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+  u32x4 x = {0u, 0u, 0u, 0u};
+  if (chunk) {
+    const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const int64_t lo = (int64_t)blockIdx.x * per;
+    const int64_t hi = lo + per < n16 ? lo + per : n16;
+    int64_t i = lo + threadIdx.x;
+    for (; i + 3 * (int64_t)blockDim.x < hi; i += 4 * (int64_t)blockDim.x) {
+      const u32x4 v0 = __builtin_nontemporal_load(src + i);
+      const u32x4 v1 = __builtin_nontemporal_load(src + i + blockDim.x);
+      const u32x4 v2 = __builtin_nontemporal_load(src + i + 2 * blockDim.x);
+      const u32x4 v3 = __builtin_nontemporal_load(src + i + 3 * blockDim.x);
+      x ^= v0 ^ v1 ^ v2 ^ v3;
+    }
+    for (; i < hi; i += blockDim.x) x ^= __builtin_nontemporal_load(src + i);
+  } else {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * nthreads < n16; i += 4 * nthreads) {
+      const u32x4 v0 = __builtin_nontemporal_load(src + i);
+      const u32x4 v1 = __builtin_nontemporal_load(src + i + nthreads);
+      const u32x4 v2 = __builtin_nontemporal_load(src + i + 2 * nthreads);
+      const u32x4 v3 = __builtin_nontemporal_load(src + i + 3 * nthreads);
+      x ^= v0 ^ v1 ^ v2 ^ v3;
+    }
+    for (; i < n16; i += nthreads) x ^= __builtin_nontemporal_load(src + i);
+  }
+  out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = x.x ^ x.y ^ x.z ^ x.w;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Launch the MFMA probe: `grid` workgroups of 4 * waves_per_simd waves (one
+// workgroup per compute unit when grid = CU count), shape 0 = 32x32x16 bf16,
+// 1 = 16x16x32 bf16. `src` holds at least grid * 4 * waves_per_simd * 16 KiB of
+// operand bytes, `out` grid * 256 * waves_per_simd floats. Returns a hipError_t.
+// FLOP per launch: waves * iters * 64 * 32768 (both shapes: 16x16x32 issues
+// twice the instructions of half the size).
+int tg_probe_mfma(const void* src, float* out, int grid, int waves_per_simd, int shape, int iters,
+                  void* stream) {
+  if (grid <= 0 || (waves_per_simd != 1 && waves_per_simd != 2) || (shape != 0 && shape != 1) ||
+      iters <= 0)
+    return (int)hipErrorInvalidValue;
+  const dim3 block(256 * waves_per_simd);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (shape == 0)
+    hipLaunchKernelGGL(mfma_probe<0>, dim3(grid), block, 0, st, static_cast<const u32x4*>(src), out,
+                       iters);
+  else
+    hipLaunchKernelGGL(mfma_probe<1>, dim3(grid), block, 0, st, static_cast<const u32x4*>(src), out,
+                       iters);
+  return (int)hipGetLastError();
+}
+
+// Launch the read probe over `bytes` (a multiple of 16) of `src`; `out` holds
+// grid * 256 uint32. chunk: 1 = one contiguous chunk per workgroup, 0 =
+// grid-strided. Returns a hipError_t.
+int tg_probe_read(const void* src, uint32_t* out, int64_t bytes, int grid, int chunk,
+                  void* stream) {
+  if (grid <= 0 || bytes <= 0 || bytes % 16) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(read_probe, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), out, bytes / 16, chunk);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

@@ -137,6 +137,27 @@ WORKLOADS = {
              "contiguous, the usual layout of a projection's weight matrix)"),
 }
 
+# The decode / tall-skinny sweep: decode batches of 1, 8, 32 and 64 rows against
+# the same weight matrix as the decode workload (same seeds, so B is the same
+# draw and A's rows are the first rows of one stream), in both B layouts, and
+# the tall-skinny (4096, 256, 4096) shape.
+for _m in (1, 8, 32, 64):
+    WORKLOADS[f"decode_m{_m}"] = Workload(
+        f"decode_m{_m}", 5, _m, 28672, 8192, False, ("bf16",), "normal", "normal", b_scale=_S,
+        note=f"decode sweep: {_m} rows, B row-major")
+    WORKLOADS[f"decode_colB_m{_m}"] = Workload(
+        f"decode_colB_m{_m}", 6, _m, 28672, 8192, True, ("bf16",), "normal", "normal", b_scale=_S,
+        note=f"decode sweep: {_m} rows, B column-major")
+WORKLOADS["tall_skinny"] = Workload(
+    "tall_skinny", 7, 4096, 256, 4096, False, ("bf16",), "normal", "normal", b_scale=1.0 / 64.0,
+    note="tall-skinny (4096, 256, 4096), B row-major")
+WORKLOADS["tall_skinny_colB"] = Workload(
+    "tall_skinny_colB", 8, 4096, 256, 4096, True, ("bf16",), "normal", "normal", b_scale=1.0 / 64.0,
+    note="tall-skinny (4096, 256, 4096), B column-major")
+WORKLOADS["launch64"] = Workload(
+    "launch64", 9, 64, 64, 64, False, ("bf16",), "uniform", "uniform",
+    note="64^3: a kernel of about a microsecond, for the per-call cost")
+
 
 @dataclass
 class Operands:
