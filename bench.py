@@ -33,6 +33,7 @@ PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA (twice the bf16 rate)
 PEAK_FP4_TFLOPS = 10066.3      # MI355X dense fp4 / fp6 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 MIN_ROTATION_BYTES = 600 << 20  # > 2x the 256 MB last-level cache
+CU_COUNT = 256                  # MI355X compute units
 RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # below: HBM-bound
 
 # Secondary legs of the default run: the other bf16 workloads (4096^3 in both
@@ -74,79 +75,78 @@ def parse():
     return ap.parse_args()
 
 
-class ClockSampler:
-    """Samples the GPU's clocks and power through amdsmi's GPU metrics from a
-    side thread while a leg's timed launches run. Context for the roofline
-    fractions: the published peaks assume 2.4 GHz."""
+class ClockProbe:
+    """The average shader clock while a leg's timed launches run: a one-wave
+    kernel (csrc/probes.hip, clock_probe) on a second stream reads the
+    shader-cycle and real-time counters over a window that the timed launches
+    cover. The real-time counter's rate is calibrated once against HIP events.
+    Context for the roofline fractions: the published peaks assume 2.4 GHz."""
 
-    def __init__(self, period_s=0.005):
-        self.period, self.err, self.samples = period_s, None, []
-        self.amdsmi = self.h = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            self.amdsmi = amdsmi
-            self.h = amdsmi.amdsmi_get_processor_handles()[0]
-        except Exception as e:  # no amdsmi, no permission: report why
-            self.err = f"{type(e).__name__}: {e}"
+    def __init__(self, torch):
+        import ctypes
+        self.torch = torch
+        self.lib = ctypes.CDLL(os.path.join(ROOT, "tile_partitioned_dense_amd", "libtile_probes.so"))
+        self.lib.tg_probe_clock.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p]
+        self.out = torch.zeros(2, dtype=torch.int64, device="cuda")
+        self.side = torch.cuda.Stream()
+        self.window_s = 0.0
+        self.last = None
+        # real-time ticks per second: a 2 ms-scale window timed with events
+        ticks = 200000
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(2):
+            e0.record()
+            self._launch(ticks, torch.cuda.current_stream())
+            e1.record()
+            torch.cuda.synchronize()
+        secs = e0.elapsed_time(e1) * 1e-3
+        self.rt_hz = int(self.out[1].item()) / secs
 
-    @staticmethod
-    def _num(v):
-        if isinstance(v, (list, tuple)):
-            vals = [x for x in v if isinstance(x, (int, float)) and 0 < x < 65535]
-            return sum(vals) / len(vals) if vals else None
-        return v if isinstance(v, (int, float)) and 0 < v < 65535 else None
+    def _launch(self, ticks, stream):
+        st = self.lib.tg_probe_clock(self.out.data_ptr(), int(ticks), stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"clock probe launch failed ({st})")
 
-    def _one(self):
-        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
-        gfx = self._num(m.get("current_gfxclk")) or self._num(m.get("current_gfxclks"))
-        avg_gfx = self._num(m.get("average_gfxclk_frequency"))
-        mem = self._num(m.get("current_uclk"))
-        pwr = self._num(m.get("current_socket_power")) or self._num(m.get("average_socket_power"))
-        return gfx, avg_gfx, mem, pwr
+    def __call__(self, window_s, grid=0):
+        """A window of about `window_s` seconds beside a kernel of `grid`
+        workgroups. A kernel with a workgroup on every compute unit leaves no
+        room for the probe's wave (each workgroup holds its unit's whole
+        register file), so a probe would push one workgroup into a second
+        round: then none is launched and the clock is not reported."""
+        self.window_s = window_s
+        self.active = grid < CU_COUNT
+        return self
 
     def __enter__(self):
-        import threading
-        self.samples, self._stop = [], False
-        if self.h is None:
+        torch = self.torch
+        if not self.active:
             return self
-
-        def loop():
-            while not self._stop:
-                try:
-                    self.samples.append(self._one())
-                except Exception as e:
-                    self.err = f"{type(e).__name__}: {e}"
-                    return
-                time.sleep(self.period)
-        self._t = threading.Thread(target=loop, daemon=True)
-        self._t.start()
+        self.side.wait_stream(torch.cuda.current_stream())
+        ticks = max(1000, min(int(self.window_s * self.rt_hz), 10 ** 9))
+        self._launch(ticks, self.side)
         return self
 
     def __exit__(self, *exc):
-        self._stop = True
-        if self.h is not None:
-            self._t.join()
+        self.torch.cuda.synchronize()
+        if not self.active:
+            self.last = {"shader_clock_mhz": None,
+                         "source": "not measured: the kernel's workgroups occupy every compute unit"}
+            return
+        cycles, ticks = (int(v) for v in self.out.tolist())
+        self.last = {"shader_clock_mhz": round(cycles / (ticks / self.rt_hz) / 1e6, 1),
+                     "window_ms": round(ticks / self.rt_hz * 1e3, 3),
+                     "source": "s_memtime over s_memrealtime in a one-wave kernel beside the "
+                               "timed launches"}
 
     def report(self):
-        def stats(i):
-            v = [x[i] for x in self.samples if x[i] is not None]
-            if not v:
-                return None
-            return {"mean": round(sum(v) / len(v), 1), "min": round(min(v), 1), "max": round(max(v), 1)}
-        if not self.samples:
-            return {"source": "amdsmi GPU metrics", "samples": 0, "error": self.err}
-        return {"source": "amdsmi GPU metrics, sampled every 5 ms during the timed launches",
-                "samples": len(self.samples), "gfx_clock_mhz": stats(0),
-                "gfx_clock_avg_mhz": stats(1), "mem_clock_mhz": stats(2),
-                "socket_power_w": stats(3), "error": self.err}
+        return self.last
 
 
 class Bench:
     def __init__(self, torch, tg, synth):
         self.torch, self.tg, self.synth = torch, tg, synth
         self.g = tg.TileGemm(0)
-        self.clock = ClockSampler()
+        self.clock = ClockProbe(torch)
         self._host = {}
 
     def operands(self, w):
@@ -249,21 +249,26 @@ class Bench:
                         for A, B, C in sets]
         full_c = {i: (s[3] if len(s) > 3 else s[2]) for i, s in enumerate(sets)}
         sets = [s[:3] for s in sets]
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0.record()
         for i in range(warmup):
             A, B, C = sets[i % len(sets)]
             g(A, B, C, **kw)
+        w1.record()
         torch.cuda.synchronize()
+        est = w0.elapsed_time(w1) * 1e-3 / max(warmup, 1)
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         torch.cuda.synchronize()
-        with self.clock:
+        plan = self.tg.tile_gemm_plan(w.M, w.N, w.K, w.b_col_major, CU_COUNT)
+        with self.clock(0.7 * est * steps, plan.grid):
             t0 = time.perf_counter()
             for i in range(steps):
                 A, B, C = sets[i % len(sets)]
                 starts[i].record()
                 g(A, B, C, **kw)
                 ends[i].record()
-            torch.cuda.synchronize()
+            torch.cuda.current_stream().synchronize()   # the launching stream, not the probe's
             wall = time.perf_counter() - t0
         clock = self.clock.report()
         per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms per launch
@@ -287,7 +292,6 @@ class Bench:
             torch.cuda.synchronize()
             unfused = float(np.mean([a.elapsed_time(b) for a, b in t[warmup:]]))
             del y
-        plan = self.tg.tile_gemm_plan(w.M, w.N, w.K, w.b_col_major, 256)
         res = {
             "workload": w.name + (f":{epi}" if epi else ""), "M": w.M, "N": w.N, "K": w.K,
             "b_layout": "column-major" if w.b_col_major else "row-major", "out": out,
@@ -310,6 +314,7 @@ class Bench:
             res["launch_us"] = self.launch_overhead(sets[0])
         log(f"[bench] {w.name}: mean {res['kernel_ms_mean'] * 1e3:.1f} us "
             f"(median {res['kernel_ms_median'] * 1e3:.1f}, min {res['kernel_ms_min'] * 1e3:.1f}) "
+            f"at {clock['shader_clock_mhz'] or 0:.0f} MHz "
             f"-> {res['tflops']:.1f} TFLOP/s ({100 * res['frac_mfma']:.1f}% MFMA), "
             f"{res['gbs']:.0f} GB/s ({100 * res['frac_hbm']:.1f}% HBM)")
         del sets
@@ -338,23 +343,27 @@ def time_mx_workload(b, w, steps, warmup):
         f"(operands ready in {time.time() - t0:.1f}s)")
     fmt = b.tg.MX_E2M1 if w.fmt == "e2m1" else b.tg.MX_E4M3
     peak = PEAK_FP4_TFLOPS if w.fmt == "e2m1" else PEAK_FP8_TFLOPS
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record()
     for i in range(warmup):
         a, bt, sa, sb = sets[i % copies]
         g.mx(a, bt, Cs[i % copies], sa, sb, fmt=fmt)
+    w1.record()
     torch.cuda.synchronize()
+    est = w0.elapsed_time(w1) * 1e-3 / max(warmup, 1)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
-    with b.clock:
+    plan = b.tg.tile_gemm_plan_mx(w.M, w.N, w.K, CU_COUNT)
+    with b.clock(0.7 * est * steps, plan.grid):
         t0 = time.perf_counter()
         for i in range(steps):
             a, bt, sa, sb = sets[i % copies]
             ev[i][0].record()
             g.mx(a, bt, Cs[i % copies], sa, sb, fmt=fmt)
             ev[i][1].record()
-        torch.cuda.synchronize()
+        torch.cuda.current_stream().synchronize()
         wall = time.perf_counter() - t0
     per = np.array([x.elapsed_time(y) for x, y in ev])
-    plan = b.tg.tile_gemm_plan_mx(w.M, w.N, w.K, 256)
     res = {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
            "format": "MXFP4 (E2M1, E8M0 / 32)" if w.fmt == "e2m1" else "MXFP8 (E4M3, E8M0 / 32)",
            "out": out, "wall_ms_per_step": 1e3 * wall / steps,
@@ -414,13 +423,17 @@ def run_probes(torch, clock):
     rnd = torch.randn(grid * 8 * 16 * 1024 // 2, device="cuda").to(torch.bfloat16)
     const = torch.full_like(rnd, 1.0)
 
-    def timed(fn, n=20, warm=3):
+    def timed(fn, n=20, warm=3, grid_of_fn=0):
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0.record()
         for _ in range(warm):
             fn()
+        w1.record()
         torch.cuda.synchronize()
+        est = w0.elapsed_time(w1) * 1e-3 / warm
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(n)]
-        with clock:
+        with clock(0.7 * est * n, grid_of_fn):
             for a, b in ev:
                 a.record()
                 fn()
@@ -438,12 +451,13 @@ def run_probes(torch, clock):
                 t, clk = timed(fn)
                 flop = grid * 4 * wps * iters * 64 * 32768
                 tf = flop / t / 1e12
+                mhz = clk["shader_clock_mhz"]
                 mfma.append({"instruction": sname, "waves_per_simd": wps, "operands": data,
                              "launch_ms": round(t * 1e3, 3), "tflops": round(tf, 1),
                              "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                             "gfx_clock_mhz": (clk.get("gfx_clock_mhz") or {}).get("mean"),
-                             "socket_power_w": (clk.get("socket_power_w") or {}).get("mean")})
-                log(f"[probe] {sname} {wps} wave(s)/SIMD {data}: {tf:.0f} TFLOP/s")
+                             "shader_clock_mhz": mhz,
+                             "mfma_busy_at_that_clock": round(tf / (PEAK_BF16_TFLOPS * mhz / 2400.0), 4)})
+                log(f"[probe] {sname} {wps} wave(s)/SIMD {data}: {tf:.0f} TFLOP/s at {mhz:.0f} MHz")
     del rnd, const
     nbytes = 4 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -456,7 +470,8 @@ def run_probes(torch, clock):
         gbs = nbytes / t / 1e9
         read.append({"pattern": "one contiguous chunk per workgroup" if chunk else "grid-strided",
                      "workgroups": g, "bytes": nbytes, "launch_ms": round(t * 1e3, 3),
-                     "gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)})
+                     "gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+                     "shader_clock_mhz": clk["shader_clock_mhz"]})
         log(f"[probe] read {read[-1]['pattern']} x{g}: {gbs:.0f} GB/s")
     del buf
     torch.cuda.empty_cache()

@@ -352,6 +352,11 @@ enum {
  * kernel instead of the planner's grid, so each takes several tiles; or, with
  * TILE_GEMM_DEBUG_ONE_TILE_PER_WG, one workgroup per tile. */
 #define TILE_GEMM_DEBUG_FORCE_GRID(g) (((g) & 0x7f) << 24)
+/* Raster group height g (1 <= g <= 63 tile rows; clipped to the tile rows)
+ * for the tile kernel's owned-tile map instead of the planner's, so the
+ * effect of the tile order on cache traffic can be measured. Any height keeps
+ * the map a bijection. */
+#define TILE_GEMM_DEBUG_GROUP_M(g) (((g) & 0x3f) << 2)
 #define TILE_GEMM_DEBUG_ONE_TILE_PER_WG (0x7f << 24)
 
 /*

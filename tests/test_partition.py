@@ -179,3 +179,17 @@ def test_negative_control_map_is_caught_by_cover_check():
         dup |= t in seen
         seen.add(t)
     assert dup and len(seen) == plan.tiles - 1
+
+
+@pytest.mark.parametrize("M,N", [(8192, 7168), (8192, 1280), (1000, 3000), (300, 257)])
+@pytest.mark.parametrize("group_m", [1, 2, 3, 5, 8, 13, 63])
+def test_tile_of_is_a_bijection_for_any_raster_group(M, N, group_m):
+    """The debug raster-group override (TILE_GEMM_DEBUG_GROUP_M) only changes
+    the order of tiles: for every height the map stays a bijection."""
+    plan = tg.tile_gemm_plan(M, N, 4096, False, CU)
+    plan.group_m = min(group_m, plan.tiles_m)
+    seen = set()
+    for wg in range(plan.tiles):
+        m0, n0, rows, cols = tg.tile_gemm_tile_of(plan, M, N, wg)
+        seen.add((m0, n0))
+    assert len(seen) == plan.tiles

@@ -21,7 +21,7 @@ __all__ = ["tile_gemm_create", "tile_gemm_run", "tile_gemm_run_debug", "tile_gem
            "tile_gemm_tile_of", "TileGemm", "TileGemmError", "Status", "Dtype",
            "Strides", "Plan", "library_path", "load_library", "last_error_detail",
            "DEBUG_COUNT_WRITES", "DEBUG_COLLIDE", "DEBUG_FORCE_TILE",
-           "DEBUG_FORCE_SKINNY", "DEBUG_FORCE_GRID", "DEBUG_ONE_TILE_PER_WG", "N_TILE_CONFIGS", "N_SKINNY_CONFIGS", "VARIANT_NONE", "VARIANT_TILE",
+           "DEBUG_FORCE_SKINNY", "DEBUG_FORCE_GRID", "DEBUG_ONE_TILE_PER_WG", "DEBUG_GROUP_M", "N_TILE_CONFIGS", "N_SKINNY_CONFIGS", "VARIANT_NONE", "VARIANT_TILE",
            "VARIANT_SKINNY"]
 
 

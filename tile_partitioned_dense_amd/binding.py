@@ -62,7 +62,11 @@ def DEBUG_FORCE_GRID(g: int) -> int:
 DEBUG_ONE_TILE_PER_WG = 0x7F << 24
 
 
-N_TILE_CONFIGS = 17
+def DEBUG_GROUP_M(g: int) -> int:
+    return (g & 0x3F) << 2
+
+
+N_TILE_CONFIGS = 24
 N_MX_CONFIGS = 6
 MX_E4M3 = 0
 MX_E2M1 = 1

@@ -8,9 +8,9 @@
 
 namespace tg {
 
-// The kernel instance of configuration CFG: the tile kernel, the K-split
-// kernel for configurations whose waves share K, or the stream kernel
-// (column-major B only; NULL for a row-major B).
+// The kernel instance of configuration CFG: the tile kernel (on 32x32x16 or
+// 16x16x32 MFMA blocks), the K-split kernel for configurations whose waves
+// share K, or the stream kernel (column-major B only; NULL for a row-major B).
 template <int CFG, bool BC, bool OB, bool DB>
 const void* tile_fn() {
   constexpr TileConfig c = kTileConfigs[CFG];
@@ -21,6 +21,8 @@ const void* tile_fn() {
       return nullptr;
   } else if constexpr (c.ks > 1)
     return reinterpret_cast<const void*>(&ksplit_gemm_kernel<c.bm, c.bn, c.ks, c.stages, BC, OB, DB>);
+  else if constexpr (c.mi == 16)
+    return reinterpret_cast<const void*>(&tile16_gemm_kernel<c.bm, c.bn, c.wm, c.wn, c.stages, BC, OB, DB>);
   else
     return reinterpret_cast<const void*>(&tile_gemm_kernel<c.bm, c.bn, c.wm, c.wn, c.stages, BC, OB, DB>);
 }

@@ -10,6 +10,7 @@
 #include "mx_stream_kernel.hpp"
 #include "skinny_kernel.hpp"
 #include "stream_kernel.hpp"
+#include "tile16_kernel.hpp"
 #include "tile_kernel.hpp"
 
 namespace tg {

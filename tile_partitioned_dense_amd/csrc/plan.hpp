@@ -48,6 +48,8 @@ struct TileConfig {
   int occ = 1;        // workgroups that fit on one compute unit at once
   int sb = 0;         // > 0: the stream kernel (stream_kernel.hpp, column-major B
                       // only) with stages of sb bytes of K per row
+  int mi = 32;        // MFMA block: 32 (32x32x16, tile_kernel.hpp) or 16
+                      // (16x16x32, tile16_kernel.hpp)
 };
 
 // Rate of configuration c when each compute unit has `per_cu` of its tiles:
@@ -60,7 +62,7 @@ inline double tile_eff(const TileConfig& c, int64_t per_cu) {
   return e1 + (c.eff - e1) * (double)(n - 1) / (double)(c.occ - 1);
 }
 
-constexpr int kNumTileConfigs = 17;
+constexpr int kNumTileConfigs = 24;
 constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
     {256, 256, 2, 2, 4, 0.94f},  // 0: 4 waves of 128x128
     {256, 224, 4, 1, 5, 0.85f},  // 1: 4 waves of 64x224
@@ -83,6 +85,18 @@ constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
     {32, 64, 1, 2, 3, 0.0f, 2, 0.0f, 1, 512},
     {64, 128, 1, 4, 3, 0.0f, 2, 0.0f, 1, 256},
     {64, 64, 1, 2, 3, 0.0f, 2, 0.0f, 1, 256},
+    // 17-23: the tile kernel on 16x16x32 blocks (two waves per SIMD issue it
+    // at close to the full MFMA rate, the 32x32x16 form at about 60%)
+    {256, 256, 2, 4, 4, 1.09f, 1, 0.0f, 1, 0, 16},  // 17: 8 waves of 128x64
+    {256, 256, 2, 4, 5, 1.08f, 1, 0.0f, 1, 0, 16},  // 18: the same with 5 stages
+    {256, 160, 4, 2, 4, 0.83f, 1, 0.0f, 1, 0, 16},  // 19: 8 waves of 64x80
+    {128, 256, 2, 4, 5, 0.80f, 1, 0.0f, 1, 0, 16},  // 20: 8 waves of 64x64
+    {256, 128, 4, 2, 5, 0.77f, 1, 0.0f, 1, 0, 16},  // 21: 8 waves of 64x64
+    // 22-23: one wave per SIMD on 16x16 blocks: the 128-wide wave tiles read a
+    // third less from LDS, but their accumulators do not stay put in the
+    // accumulation registers (the compiler shuffles them every few MFMAs)
+    {256, 256, 2, 2, 4, 0.50f, 1, 0.0f, 1, 0, 16},  // 22: 4 waves of 128x128
+    {256, 160, 2, 2, 4, 0.80f, 1, 0.0f, 1, 0, 16},  // 23: 4 waves of 128x80
 };
 constexpr int kStreamConfig = 14;      // the planner's stream configuration up to 32 rows,
 constexpr int kStreamConfig64 = 15;    // from 33 to 64 rows,
@@ -185,8 +199,10 @@ inline int skinny_lds_bytes(const SkinnyConfig& c) {
 // Raster group height: enough tile rows that the tiles co-running on one XCD
 // (32 compute units) form a roughly square block of the tile grid.
 inline int32_t pick_group_m(int32_t tiles_m, int32_t tiles_n) {
+  // 8 rows for narrow grids; 8 also for wide ones (at 32 x 28 tiles of
+  // 256 x 256, 8 rows measured 2-3% faster than 4 and 16 rows 10% slower)
   int32_t g = 4;
-  if (tiles_n < 8) g = 8;
+  if (tiles_n < 8 || tiles_n >= 16) g = 8;
   if (g > tiles_m) g = tiles_m;
   return g < 1 ? 1 : g;
 }

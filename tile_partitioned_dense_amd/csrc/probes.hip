@@ -1,11 +1,14 @@
 // probes.hip -- measurement probes for the roofline figures (not part of the
 // GEMM library's ABI; built as its own small library, libtile_probes.so).
 //
-// Two ceilings the GEMM kernels are compared against on the same box:
+// Two ceilings the GEMM kernels are compared against on the same box, and the
+// shader clock while a kernel runs:
 //  * the rate at which the chip sustains bf16 MFMA instructions when nothing
 //    else runs (no memory traffic, no LDS), with random or constant operands
 //    and one or two waves per SIMD, for the 32x32x16 and 16x16x32 shapes;
-//  * the rate at which HBM delivers a plain streaming read.
+//  * the rate at which HBM delivers a plain streaming read;
+//  * the average shader clock over a window (a one-wave kernel beside the
+//    measured work).
 // Under sustained MFMA load the clock settles below the 2.4 GHz that the
 // published peak assumes; the MFMA probe measures where it settles.
 #include <hip/hip_runtime.h>
@@ -106,9 +109,39 @@ __global__ __launch_bounds__(256) void read_probe(const u32x4* __restrict__ src,
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = x.x ^ x.y ^ x.z ^ x.w;
 }
 
+// One wave on one compute unit reads the shader-clock counter (s_memtime)
+// and the constant-rate real-time counter (s_memrealtime) at its start, sleeps
+// in short steps until `ticks` real-time ticks have passed, and reads both
+// again: launched beside other work on a second stream it gives the average
+// shader clock while that work runs. The wait is bounded by `ticks`.
+__global__ __launch_bounds__(64) void clock_probe(unsigned long long* __restrict__ out,
+                                                  long long ticks) {
+  if (threadIdx.x != 0) return;
+  const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  unsigned long long r1 = r0;
+  while ((long long)(r1 - r0) < ticks) {
+    __builtin_amdgcn_s_sleep(8);
+    r1 = __builtin_amdgcn_s_memrealtime();
+  }
+  const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+  out[0] = c1 - c0;
+  out[1] = r1 - r0;
+}
+
 }  // namespace
 
 extern "C" {
+
+// Launch the clock probe for `ticks` real-time ticks (at most 10^9; the
+// real-time counter runs at hipDeviceAttributeWallClockRate kHz). out[0]
+// receives the shader cycles elapsed, out[1] the real-time ticks.
+int tg_probe_clock(unsigned long long* out, long long ticks, void* stream) {
+  if (ticks <= 0 || ticks > 1000000000ll) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(clock_probe, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), out,
+                     ticks);
+  return (int)hipGetLastError();
+}
 
 // Launch the MFMA probe: `grid` workgroups of 4 * waves_per_simd waves (one
 // workgroup per compute unit when grid = CU count), shape 0 = 32x32x16 bf16,

@@ -220,10 +220,17 @@ hipError_t dispatch_tile(int cfg, const tg::TileArgs& a, int64_t grid, const tg:
     case 14: return tg::launch_tile<14>(a, grid, v, st);
     case 15: return tg::launch_tile<15>(a, grid, v, st);
     case 16: return tg::launch_tile<16>(a, grid, v, st);
+    case 17: return tg::launch_tile<17>(a, grid, v, st);
+    case 18: return tg::launch_tile<18>(a, grid, v, st);
+    case 19: return tg::launch_tile<19>(a, grid, v, st);
+    case 20: return tg::launch_tile<20>(a, grid, v, st);
+    case 21: return tg::launch_tile<21>(a, grid, v, st);
+    case 22: return tg::launch_tile<22>(a, grid, v, st);
+    case 23: return tg::launch_tile<23>(a, grid, v, st);
   }
   return hipErrorInvalidValue;
 }
-static_assert(tg::kNumTileConfigs == 17, "dispatch_tile covers every tile configuration");
+static_assert(tg::kNumTileConfigs == 24, "dispatch_tile covers every tile configuration");
 
 hipError_t dispatch_skinny(int cfg, const tg::SkinnyArgs& a, int64_t grid, const tg::Variant& v,
                            hipStream_t st) {
@@ -433,6 +440,13 @@ tile_gemm_status_t run_impl(tile_gemm_t h, const void* A, const void* B, void* C
   if (p.grid > 0x7fffffff)
     return fail(TILE_GEMM_ERR_BAD_SHAPE, "shape: %lld workgroups exceed the launch limit",
                 (long long)p.grid);
+  const int force_group = (flags >> 2) & 0x3f;
+  if (force_group) {
+    if (p.variant != 1)
+      return fail(TILE_GEMM_ERR_BAD_SHAPE, "debug: a raster group applies to the tile kernel only");
+    // any height >= 1 keeps tile_of a bijection (the last group may be short)
+    p.map.group_m = force_group < p.map.tiles_m ? force_group : p.map.tiles_m;
+  }
   const int force_grid = (flags >> 24) & 0x7f;
   if (force_grid) {
     if (p.variant != 1)
@@ -552,7 +566,7 @@ tile_gemm_status_t tile_gemm_run_debug(tile_gemm_t h, const void* A, const void*
                                        const tile_gemm_strides_t* strides, tile_gemm_dtype_t dtype,
                                        void* stream, uint32_t* counts, int flags,
                                        const float* bias, tile_gemm_act_t act) {
-  if (flags & ~(TILE_GEMM_DEBUG_COUNT_WRITES | TILE_GEMM_DEBUG_COLLIDE | 0x7fffff00))
+  if (flags & ~(TILE_GEMM_DEBUG_COUNT_WRITES | TILE_GEMM_DEBUG_COLLIDE | 0x7fffff00 | 0xfc))
     return fail(TILE_GEMM_ERR_BAD_SHAPE, "flags: unknown bits 0x%x", flags);
   return run_impl(h, A, B, C, M, N, K, strides, dtype, stream, counts, flags, bias, (int)act);
 }
