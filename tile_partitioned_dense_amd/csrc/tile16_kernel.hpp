@@ -4,7 +4,8 @@
 // BM x BN tile has one owning workgroup, its only writer; 32-wide K slabs
 // reach LDS by direct buffer-to-LDS loads through a ring of NST stages; A and
 // a column-major B are stored K-contiguous in 64-byte rows with chunk
-// swizzling, a row-major B N-contiguous and read transposed). What differs is
+// swizzling -- by other row bits, see swz16 -- a row-major B N-contiguous and
+// read transposed). What differs is
 // the matrix instruction: v_mfma_f32_16x16x32_bf16 instead of the 32x32x16
 // form. Measured on gfx950 with random operands, two waves per SIMD issue the
 // 32x32x16 instruction at about 61% of the MFMA pipe's rate while the
@@ -41,6 +42,15 @@
 #include "tile_kernel.hpp"
 
 namespace tg {
+
+// Chunk swizzle of the K-contiguous layout (A, column-major B): 16-byte
+// chunk c of slab row r sits at position c ^ swz16(r) of its 64-byte row.
+// A fragment read covers 16 consecutive rows and all four chunks; measured
+// with the kernel's own read sequences on gfx950 (bank-conflict and LDS-busy
+// counters), XOR with bits 1-2 of the row makes those reads conflict-free,
+// while bits 2-3 (the 32x32x16 kernel's choice, whose reads cover 32 rows of
+// one chunk) or bits 0-1 double the LDS cycles per read.
+__device__ __forceinline__ int swz16(int r) { return (r >> 1) & 3; }
 
 // 16 x 16 x 32 step of a C block held transposed (see above).
 __device__ __forceinline__ floatx4 mma16(const bf16x8& a_frag, const bf16x8& b_frag, const floatx4& acc) {
@@ -119,7 +129,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile16_gemm_kernel(TileArgs p
     for (int t = 0; t < A_PER; ++t) {
       const int ins = wave + NW * t;
       const int r = 16 * ins + (lane >> 2);
-      const int c = (lane & 3) ^ swzA(r);
+      const int c = (lane & 3) ^ swz16(r);
       voA[t] = (uint32_t)(r * lda * 2) + c * 16;
     }
     const int b_cnt = (wave < B_DMA % NW) ? B_MAX : B_MIN;
@@ -129,7 +139,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile16_gemm_kernel(TileArgs p
       const int ins = wave + NW * t;
       if constexpr (BCOL) {
         const int r = 16 * ins + (lane >> 2);
-        const int c = (lane & 3) ^ swzA(r);
+        const int c = (lane & 3) ^ swz16(r);
         voB[t] = (uint32_t)((r + (r >= BN / 2 ? gshift : 0)) * ldb * 2) + c * 16;
       } else {
         const int q = 64 * ins + lane;
@@ -166,7 +176,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile16_gemm_kernel(TileArgs p
           const int r = q >> 2, c = q & 3;
           const uint4 v = (m0 + r < M) ? load8_masked(p.A + (int64_t)(m0 + r) * lda, k0 + 8 * c, K)
                                        : make_uint4(0, 0, 0, 0);
-          dA[r * 4 + (c ^ swzA(r))] = v;
+          dA[r * 4 + (c ^ swz16(r))] = v;
         }
         if constexpr (BCOL) {
           for (int q = tid; q < BN * 4; q += NT) {
@@ -174,7 +184,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile16_gemm_kernel(TileArgs p
             const int col = n0 + r + (r >= BN / 2 ? gshift : 0);
             const uint4 v = (col < N) ? load8_masked(p.B + (int64_t)col * ldb, k0 + 8 * c, K)
                                       : make_uint4(0, 0, 0, 0);
-            dB[r * 4 + (c ^ swzA(r))] = v;
+            dB[r * 4 + (c ^ swz16(r))] = v;
           }
         } else {
           for (int q = tid; q < BK * CPR; q += NT) {
@@ -225,10 +235,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile16_gemm_kernel(TileArgs p
       for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{};
 
     // ---- LDS read addresses. Lane bases per stage pair (a ds_read immediate
-    // reaches 64 KiB, two stages plus the block offsets); swzA of a block row
+    // reaches 64 KiB, two stages plus the block offsets); swz16 of a block row
     // depends only on the row within its 16-row block.
     constexpr int NPAIR = (kStages + 1) / 2;
-    const uint32_t chunk = (uint32_t)((lg ^ swzA(l16)) << 4);
+    const uint32_t chunk = (uint32_t)((lg ^ swz16(l16)) << 4);
     uint32_t rA[NPAIR], rB[NPAIR];
 #pragma unroll
     for (int h = 0; h < NPAIR; ++h) {
