@@ -21,6 +21,8 @@ const void* tile_fn() {
       return nullptr;
   } else if constexpr (c.ks > 1)
     return reinterpret_cast<const void*>(&ksplit_gemm_kernel<c.bm, c.bn, c.ks, c.stages, BC, OB, DB>);
+  else if constexpr (c.mi == 16 && c.bk == 64)
+    return reinterpret_cast<const void*>(&tile64_gemm_kernel<c.bm, c.bn, c.wm, c.wn, BC, OB, DB>);
   else if constexpr (c.mi == 16)
     return reinterpret_cast<const void*>(&tile16_gemm_kernel<c.bm, c.bn, c.wm, c.wn, c.stages, BC, OB, DB>);
   else

@@ -11,6 +11,7 @@
 #include "skinny_kernel.hpp"
 #include "stream_kernel.hpp"
 #include "tile16_kernel.hpp"
+#include "tile64_kernel.hpp"
 #include "tile_kernel.hpp"
 
 namespace tg {

@@ -50,6 +50,8 @@ struct TileConfig {
                       // only) with stages of sb bytes of K per row
   int mi = 32;        // MFMA block: 32 (32x32x16, tile_kernel.hpp) or 16
                       // (16x16x32, tile16_kernel.hpp)
+  int bk = 32;        // K per slab: 32, or 64 (tile64_kernel.hpp: 16x16x32
+                      // blocks, two stages of 128-byte rows)
 };
 
 // Rate of configuration c when each compute unit has `per_cu` of its tiles:
@@ -62,7 +64,7 @@ inline double tile_eff(const TileConfig& c, int64_t per_cu) {
   return e1 + (c.eff - e1) * (double)(n - 1) / (double)(c.occ - 1);
 }
 
-constexpr int kNumTileConfigs = 24;
+constexpr int kNumTileConfigs = 26;
 constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
     {256, 256, 2, 2, 4, 0.94f},  // 0: 4 waves of 128x128
     {256, 224, 4, 1, 5, 0.85f},  // 1: 4 waves of 64x224
@@ -97,6 +99,10 @@ constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
     // accumulation registers (the compiler shuffles them every few MFMAs)
     {256, 256, 2, 2, 4, 0.50f, 1, 0.0f, 1, 0, 16},  // 22: 4 waves of 128x128
     {256, 160, 2, 2, 4, 0.80f, 1, 0.0f, 1, 0, 16},  // 23: 4 waves of 128x80
+    // 24-25: 16x16x32 blocks with 64-deep slabs (two stages of 128-byte rows;
+    // each load instruction moves whole 128-byte lines)
+    {256, 256, 2, 4, 2, 0.01f, 1, 0.0f, 1, 0, 16, 64},  // 24: 8 waves of 128x64
+    {256, 160, 4, 2, 2, 0.01f, 1, 0.0f, 1, 0, 16, 64},  // 25: 8 waves of 64x80
 };
 constexpr int kStreamConfig = 14;      // the planner's stream configuration up to 32 rows,
 constexpr int kStreamConfig64 = 15;    // from 33 to 64 rows,
@@ -188,7 +194,7 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 inline int tile_lds_bytes(const TileConfig& c) {
   if (c.sb) return c.stages * (c.bm + c.bn) * c.sb;
-  const int ring = c.ks * c.stages * (c.bm + c.bn) * 32 * 2;
+  const int ring = c.ks * c.stages * (c.bm + c.bn) * c.bk * 2;
   const int tree = (c.ks / 2) * c.bm * c.bn * 4;
   return ring > tree ? ring : tree;
 }
@@ -249,7 +255,7 @@ inline Plan plan_for(int variant, int config, int64_t M, int64_t N, int cu_count
     p.bn = c.bn;
     p.threads = c.wm * c.wn * c.ks * 64;
     p.lds_bytes = tile_lds_bytes(c);
-    if (c.sb) p.bk = c.sb / 2;
+    p.bk = c.sb ? c.sb / 2 : c.bk;
     p.k_split = c.ks;
     p.map.tiles_m = (int32_t)ceil_div(M, c.bm);
     p.map.tiles_n = (int32_t)ceil_div(N, c.bn);
