@@ -420,7 +420,10 @@ def run_probes(torch, clock):
     stream = torch.cuda.current_stream().cuda_stream
     grid = 256
     out = torch.empty(grid * 512, dtype=torch.float32, device="cuda")
-    rnd = torch.randn(grid * 8 * 16 * 1024 // 2, device="cuda").to(torch.bfloat16)
+    # 32 KiB of operands per wave (two waves per SIMD): bf16 N(0,1) values,
+    # read by the E4M3 shapes as bytes (random codes) or, for constant
+    # operands, bf16 1.0 = bytes 0x80 0x3f (E4M3 -0 and 1.875)
+    rnd = torch.randn(grid * 8 * 32 * 1024 // 2, device="cuda").to(torch.bfloat16)
     const = torch.full_like(rnd, 1.0)
 
     def timed(fn, n=20, warm=3, grid_of_fn=0):
@@ -442,21 +445,25 @@ def run_probes(torch, clock):
         return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3, clock.report()
 
     mfma = []
-    for shape, sname in ((0, "v_mfma_f32_32x32x16_bf16"), (1, "v_mfma_f32_16x16x32_bf16")):
+    for shape, sname in ((0, "v_mfma_f32_32x32x16_bf16"), (1, "v_mfma_f32_16x16x32_bf16"),
+                         (2, "v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3)"),
+                         (3, "v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3)")):
+        f8 = shape >= 2
+        peak = PEAK_FP8_TFLOPS if f8 else PEAK_BF16_TFLOPS
         for wps in (1, 2):
             for data, src in (("random N(0,1)", rnd), ("constant 1.0", const)):
-                iters = 2400 // wps
+                iters = (1200 if f8 else 2400) // wps
                 fn = lambda: lib.tg_probe_mfma(src.data_ptr(), out.data_ptr(), grid, wps, shape,
                                                iters, stream)
                 t, clk = timed(fn)
-                flop = grid * 4 * wps * iters * 64 * 32768
+                flop = grid * 4 * wps * iters * 64 * 32768 * (4 if f8 else 1)
                 tf = flop / t / 1e12
                 mhz = clk["shader_clock_mhz"]
                 mfma.append({"instruction": sname, "waves_per_simd": wps, "operands": data,
                              "launch_ms": round(t * 1e3, 3), "tflops": round(tf, 1),
-                             "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                             "frac_of_peak": round(tf / peak, 4),
                              "shader_clock_mhz": mhz,
-                             "mfma_busy_at_that_clock": round(tf / (PEAK_BF16_TFLOPS * mhz / 2400.0), 4)})
+                             "mfma_busy_at_that_clock": round(tf / (peak * mhz / 2400.0), 4)})
                 log(f"[probe] {sname} {wps} wave(s)/SIMD {data}: {tf:.0f} TFLOP/s at {mhz:.0f} MHz")
     del rnd, const
     nbytes = 4 << 30

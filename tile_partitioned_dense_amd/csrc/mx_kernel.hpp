@@ -24,7 +24,12 @@
 // like the operands: 16 bytes of every row of the tile (the scales of 8
 // slabs) are loaded straight into a ring of LDS windows together with the
 // first slab they cover, so their loads are ordered with the slabs' and need
-// no wait of their own.
+// no wait of their own. Row r of a window starts g = (r / 8) % 4 dwords
+// later in its scale row (window w holds its dwords 4 w + g .. 4 w + g + 3,
+// and a window -1 the first g), so one 4-byte read of dword d of 32 rows, 16
+// bytes apart, takes it from position (d - g) % 4 of window w or w - 1: rows
+// that share a bank group (r, r + 8, r + 16, r + 24) read four different
+// positions, and the 32 reads fall in 32 banks instead of 8 banks four times.
 //
 // MXFP4 (E2M1, two elements per byte, the lower K index in the low nibble)
 // uses the same 64-byte rows, now 128 K values per slab: each 16-byte LDS
@@ -101,11 +106,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
   constexpr int NDMA = A_PER + B_PER;     // DMA instructions per wave and slab
   constexpr int RING = NST * STAGE;
   constexpr int SWIN = (BM + BN) * 16;    // one scale window: 16 bytes per row
-  // Window w + NWB reuses window w's buffer. It is loaded with slab SPW (w +
-  // NWB), issued at step SPW (w + NWB) - (NST - 1), which must come after the
-  // step that last reads window w (SPW (w + 1) - 1 at the latest).
-  constexpr int NWB = 1 + (NST - 1 + SPW - 1) / SPW;
-  static_assert(SPW * (NWB - 1) >= NST - 1, "a scale window is reloaded only after its last use");
+  // Window w lives in buffer (w + 1) % NWB (window -1 in buffer 0). Window w
+  // + NWB - 1 reuses window w - 1's buffer. It goes out with slab SPW (w + NWB
+  // - 1), at step SPW (w + NWB - 1) - NST at the earliest, after that step's
+  // barrier; the last read of window w - 1's buffer is the take of window w's
+  // third dword (rows with g = 3), at the start of step SPW w + T1.
+  constexpr int T1 = FP4 ? 2 : 4;
+  constexpr int NWB = 1 + (NST + T1 + SPW - 1) / SPW;
+  static_assert(SPW * (NWB - 1) - NST >= T1, "a scale window is reloaded only after its last use");
   static_assert(BM % 64 == 0 && BN % 64 == 0, "scale windows are whole KiB per wave instruction");
   constexpr int SA_DMA = BM / 64, SB_DMA = BN / 64;   // window loads (1 KiB each)
 
@@ -161,19 +169,26 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
     const i32x4 rsSA = make_rsrc(p.sA, (int64_t)M * p.ls);
     const i32x4 rsSB = make_rsrc(p.sB, (int64_t)N * p.ls);
     const uint32_t swin0 = lds0 + RING;
-    // Load window w (16 bytes of each of the tile's rows, the scales of slabs
-    // SPW w .. SPW w + SPW - 1) into buffer w % NWB: instruction q covers rows
-    // 64 q ..
+    // Load window w (16 bytes of each of the tile's rows: the scales of slabs
+    // SPW w .. SPW w + SPW - 1, from 4 g bytes later for row r, g = (r / 8) %
+    // 4) into buffer (w + 1) % NWB: instruction q covers rows 64 q ..; of
+    // window -1 only the first g dwords of each row are ever read (rows with
+    // g = 0 load their row's first bytes instead of reaching before it).
     auto issue_window = [&](int w) {
-      const uint32_t dst = swin0 + (uint32_t)((w % NWB) * SWIN);
+      const uint32_t dst = swin0 + (uint32_t)(((w + 1) % NWB) * SWIN);
+      // the byte of its scale row this lane starts at (window -1, g > 0:
+      // 4 g - 16, inside the row before, as such a row is never the first)
+      const int g = (lane >> 3) & 3;
+      const int kofs = (w < 0 && g == 0) ? 0 : 16 * w + 4 * g;
+      const uint32_t k8 = (uint32_t)kofs;
 #pragma unroll
       for (int q = 0; q < SA_DMA; ++q)
         if (q % NW == wave)
-          dma16(dst + 1024 * q, rsSA, (uint32_t)(m0 + 64 * q + lane) * (uint32_t)p.ls + 16u * w, 0u);
+          dma16(dst + 1024 * q, rsSA, (uint32_t)(m0 + 64 * q + lane) * (uint32_t)p.ls + k8, 0u);
 #pragma unroll
       for (int q = 0; q < SB_DMA; ++q)
         if (q % NW == wave)
-          dma16(dst + BM * 16 + 1024 * q, rsSB, (uint32_t)(n0 + 64 * q + lane) * (uint32_t)p.ls + 16u * w, 0u);
+          dma16(dst + BM * 16 + 1024 * q, rsSB, (uint32_t)(n0 + 64 * q + lane) * (uint32_t)p.ls + k8, 0u);
     };
 
     // The window of slabs SPW w .. goes out just before slab SPW w's own loads,
@@ -228,8 +243,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
     // (s even), byte 2 (s % 2) + l / 32 after the shift; E2M1: the dword of
     // slab s (its four blocks), byte 2 m + l / 32 for the slab's MFMA m.
     auto take_scales = [&](int s) {
+      const int w = s / SPW;
       const int dw = FP4 ? (s % SPW) : ((s % SPW) >> 1);
-      const uint32_t wb = swin0 + (uint32_t)(((s / SPW) % NWB) * SWIN) + (uint32_t)(4 * dw);
+      // dword dw of a row with g = (row / 8) % 4 (row = 32 k + lrow): position
+      // (dw - g) % 4 of window w, or of window w - 1 when dw < g
+      const int g = (lrow >> 3) & 3;
+      const int buf = dw < g ? w : w + 1;
+      const uint32_t wb = swin0 + (uint32_t)((buf % NWB) * SWIN) + (uint32_t)(4 * ((dw - g) & 3));
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const uint32_t v = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
@@ -403,6 +423,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
     // them), slab 0 landed and read
     const int n_full = nk - (NST - 1);  // steady steps: slab s + NST - 1 exists
     if (nk > 0) {
+      issue_window(-1);
       for (int sl = 0; sl < NST - 1 && sl < nk; ++sl) issue_slab(sl);
       if (n_full > 0) {
         issue_first(NST - 1);

@@ -37,7 +37,9 @@
 // Scales: 16 bytes of each row's scale row (eight E4M3 slabs or four E2M1
 // slabs: one or more stages, or part of one) are loaded into a ring of LDS
 // windows just before the first stage they cover, so the wait that covers
-// that stage covers them.
+// that stage covers them. A window is stored dword-major (dword d of row r
+// at 4 (d R + r), R rows per part), by 4-byte direct loads, so the 32 rows
+// one scale read covers sit in 32 consecutive banks.
 //
 // Each step waits for stage s, passes one barrier (after which every wave is
 // done with stage s - 1), loads stage s + NST - 1 into stage s - 1's buffer
@@ -86,8 +88,8 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void mx_stream_kernel(MxArgs 
   constexpr int NDMA_MAX = A_MAX + B_PER, NDMA_MIN = A_MIN + B_PER;
   static_assert(NST >= 2 && (NST - 2) * NDMA_MAX <= 63, "stage loads in flight fit the counter");
   constexpr int RING = NST * STAGE;
-  constexpr int SWA = 64 * 16;              // window: 64 A-row slots, then the BN B rows
-  constexpr int SWIN = SWA + BN * 16;
+  constexpr int SWA = 64 * 16;              // window: 64 A-row slots, then the BN B rows,
+  constexpr int SWIN = SWA + BN * 16;       // each part dword-major
   // Window v is loaded with the first stage that reads it. With SSW stages
   // per window: stage SSW v, issued in step SSW v - (NST - 1); its buffer
   // takes window v + NWB, issued in step SSW (v + NWB) - (NST - 1), which
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void mx_stream_kernel(MxArgs 
   constexpr int NWB = WPS > 1 ? WPS * NST : 1 + (NST - 1 + SSW - 1) / SSW;
   static_assert(WPS > 1 || SSW * (NWB - 1) >= NST - 1,
                 "a scale window is reloaded only after its last use");
-  constexpr int NWIN = 1 + BN / 64;         // window load instructions (one KiB each)
+  constexpr int NWIN = 4 * (1 + BN / 64);   // window load instructions (256 bytes each)
   static_assert(RING + NWB * SWIN <= 160 * 1024, "LDS");
 
   __shared__ __attribute__((aligned(1024))) uint4 smem[(RING + NWB * SWIN) / 16];
@@ -160,19 +162,22 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void mx_stream_kernel(MxArgs 
     const i32x4 rsSA = make_rsrc(p.sA, (int64_t)M * p.ls);
     const i32x4 rsSB = make_rsrc(p.sB, (int64_t)N * p.ls);
 
-    // Window v into buffer v % NWB: instruction 0 takes A scale rows m0 ..
-    // m0 + 63 (rows past M read as zero; only the first BM are used),
-    // instruction q > 0 takes B scale rows n0 + 64 (q - 1) ...
+    // Window v into buffer v % NWB: instruction u < 4 takes dword u of A
+    // scale rows m0 .. m0 + 63 (rows past M read as zero; only the first BM
+    // are used), instruction 4 + d (BN / 64) + q dword d of B scale rows
+    // n0 + 64 q ..; lane l fetches row (first row) + l.
     auto issue_window = [&](int v) {
       const uint32_t dst = swin0 + (uint32_t)((v % NWB) * SWIN);
 #pragma unroll
-      for (int q = 0; q < NWIN; ++q) {
-        if (q % NW == wave) {
-          if (q == 0)
-            dma16(dst, rsSA, (uint32_t)(m0 + lane) * (uint32_t)p.ls + 16u * v, 0u);
-          else
-            dma16(dst + SWA + 1024 * (q - 1), rsSB, (uint32_t)(n0 + 64 * (q - 1) + lane) * (uint32_t)p.ls + 16u * v,
-                  0u);
+      for (int u = 0; u < NWIN; ++u) {
+        if (u % NW == wave) {
+          if (u < 4) {
+            dma4(dst + 256 * u, rsSA, (uint32_t)(m0 + lane) * (uint32_t)p.ls + 16u * v + 4u * u, 0u);
+          } else {
+            const int d = (u - 4) / (BN / 64), q = (u - 4) % (BN / 64);
+            dma4(dst + SWA + d * (BN * 4) + 256 * q, rsSB,
+                 (uint32_t)(n0 + 64 * q + lane) * (uint32_t)p.ls + 16u * v + 4u * d, 0u);
+          }
         }
       }
     };
@@ -231,7 +236,7 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void mx_stream_kernel(MxArgs 
           const int sw = g % SPW;
           const int dw = FP4 ? sw : sw / 2;
           const uint32_t vb = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
-              wb + (uint32_t)(SWA + br * 16 + 4 * dw));
+              wb + (uint32_t)(SWA + dw * (BN * 4) + br * 4));
           const int sb = (int)(vb >> sh);
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
@@ -242,7 +247,7 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void mx_stream_kernel(MxArgs 
             const i32x8 af = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
                                    (int)y.x, (int)y.y, (int)y.z, (int)y.w};
             const uint32_t va = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
-                wb + (uint32_t)((32 * i + ar) * 16 + 4 * dw));
+                wb + (uint32_t)(dw * 256 + (32 * i + ar) * 4));
             const int sa = (int)(va >> sh);
             if constexpr (FP4) {
               acc[i] = mma_mx<0, HW>(fp4_half<0>(af), fp4_half<0>(bf), sa, sb, acc[i]);

@@ -5,7 +5,8 @@
 // shader clock while a kernel runs:
 //  * the rate at which the chip sustains bf16 MFMA instructions when nothing
 //    else runs (no memory traffic, no LDS), with random or constant operands
-//    and one or two waves per SIMD, for the 32x32x16 and 16x16x32 shapes;
+//    and one or two waves per SIMD, for the 32x32x16 and 16x16x32 shapes,
+//    and of the block-scaled FP8 (E4M3) forms 32x32x64 and 16x16x128;
 //  * the rate at which HBM delivers a plain streaming read;
 //  * the average shader clock over a window (a one-wave kernel beside the
 //    measured work).
@@ -18,6 +19,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 namespace {
 
@@ -65,6 +67,61 @@ __global__ __launch_bounds__(512) void mfma_probe(const u32x4* __restrict__ src,
         for (int i = 0; i < 2 * kOps; ++i)
           acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[(i + j) % kOps], b[(5 * i + j) % kOps],
                                                             acc[i], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * kOps; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) total += acc[i][e];
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = total;
+}
+
+// As mfma_probe for the block-scaled E4M3 forms (SHAPE 0: 32x32x64, 1:
+// 16x16x128): 32-byte fragments, every scale byte 127 (a factor of 1).
+template <int SHAPE>
+__global__ __launch_bounds__(512) void mfma_probe_f8(const u32x4* __restrict__ src, float* __restrict__ out,
+                                                    int iters) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  i32x8 a[kOps], b[kOps];
+#pragma unroll
+  for (int i = 0; i < kOps; ++i) {
+    const u32x4 a0 = src[(wave * 4 * kOps + 2 * i) * 64 + lane];
+    const u32x4 a1 = src[(wave * 4 * kOps + 2 * i + 1) * 64 + lane];
+    const u32x4 b0 = src[(wave * 4 * kOps + 2 * kOps + 2 * i) * 64 + lane];
+    const u32x4 b1 = src[(wave * 4 * kOps + 2 * kOps + 2 * i + 1) * 64 + lane];
+    a[i] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    b[i] = i32x8{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  }
+  constexpr int kScale = 127;
+  float total = 0.0f;
+  if constexpr (SHAPE == 0) {
+    floatx16 acc[kOps];
+#pragma unroll
+    for (int i = 0; i < kOps; ++i) acc[i] = floatx16{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < kOps; ++j)
+#pragma unroll
+        for (int i = 0; i < kOps; ++i)
+          acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[(i + j) % kOps], b[(5 * i + j) % kOps],
+                                                                   acc[i], 0, 0, 0, kScale, 0, kScale);
+    }
+#pragma unroll
+    for (int i = 0; i < kOps; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) total += acc[i][e];
+  } else {
+    floatx4 acc[2 * kOps];
+#pragma unroll
+    for (int i = 0; i < 2 * kOps; ++i) acc[i] = floatx4{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < kOps; ++j)
+#pragma unroll
+        for (int i = 0; i < 2 * kOps; ++i)
+          acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[(i + j) % kOps], b[(5 * i + j) % kOps],
+                                                                    acc[i], 0, 0, 0, kScale, 0, kScale);
     }
 #pragma unroll
     for (int i = 0; i < 2 * kOps; ++i)
@@ -145,13 +202,15 @@ int tg_probe_clock(unsigned long long* out, long long ticks, void* stream) {
 
 // Launch the MFMA probe: `grid` workgroups of 4 * waves_per_simd waves (one
 // workgroup per compute unit when grid = CU count), shape 0 = 32x32x16 bf16,
-// 1 = 16x16x32 bf16. `src` holds at least grid * 4 * waves_per_simd * 16 KiB of
-// operand bytes, `out` grid * 256 * waves_per_simd floats. Returns a hipError_t.
-// FLOP per launch: waves * iters * 64 * 32768 (both shapes: 16x16x32 issues
-// twice the instructions of half the size).
+// 1 = 16x16x32 bf16, 2 = 32x32x64 scaled E4M3, 3 = 16x16x128 scaled E4M3.
+// `src` holds at least grid * 4 * waves_per_simd * 16 KiB of operand bytes
+// (32 KiB for shapes 2 and 3), `out` grid * 256 * waves_per_simd floats.
+// Returns a hipError_t. FLOP per launch: waves * iters * 64 * 32768 for the
+// bf16 shapes, four times that for the E4M3 ones (the 16x16 forms issue twice
+// the instructions of half the size).
 int tg_probe_mfma(const void* src, float* out, int grid, int waves_per_simd, int shape, int iters,
                   void* stream) {
-  if (grid <= 0 || (waves_per_simd != 1 && waves_per_simd != 2) || (shape != 0 && shape != 1) ||
+  if (grid <= 0 || (waves_per_simd != 1 && waves_per_simd != 2) || shape < 0 || shape > 3 ||
       iters <= 0)
     return (int)hipErrorInvalidValue;
   const dim3 block(256 * waves_per_simd);
@@ -159,8 +218,14 @@ int tg_probe_mfma(const void* src, float* out, int grid, int waves_per_simd, int
   if (shape == 0)
     hipLaunchKernelGGL(mfma_probe<0>, dim3(grid), block, 0, st, static_cast<const u32x4*>(src), out,
                        iters);
-  else
+  else if (shape == 1)
     hipLaunchKernelGGL(mfma_probe<1>, dim3(grid), block, 0, st, static_cast<const u32x4*>(src), out,
+                       iters);
+  else if (shape == 2)
+    hipLaunchKernelGGL(mfma_probe_f8<0>, dim3(grid), block, 0, st, static_cast<const u32x4*>(src), out,
+                       iters);
+  else
+    hipLaunchKernelGGL(mfma_probe_f8<1>, dim3(grid), block, 0, st, static_cast<const u32x4*>(src), out,
                        iters);
   return (int)hipGetLastError();
 }

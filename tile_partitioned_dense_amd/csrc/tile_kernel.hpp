@@ -124,6 +124,20 @@ __device__ __forceinline__ void dma16(uint32_t lds, const i32x4& rsrc_in, uint32
       : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
       : "memory", "m0");
 }
+// 4 bytes per lane from rsrc + voff + soff straight into LDS at lds + 4 *
+// lane (256 contiguous bytes per wave). Tracked by vmcnt only.
+__device__ __forceinline__ void dma4(uint32_t lds, const i32x4& rsrc_in, uint32_t voff,
+                                     uint32_t soff) {
+  const i32x4 rsrc = uniform_rsrc(rsrc_in);
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  soff = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dword %1, %2, %3 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // As dma16, with the LDS address formed as an SGPR base plus a constant.
