@@ -420,10 +420,10 @@ def run_probes(torch, clock):
     stream = torch.cuda.current_stream().cuda_stream
     grid = 256
     out = torch.empty(grid * 512, dtype=torch.float32, device="cuda")
-    # 32 KiB of operands per wave (two waves per SIMD): bf16 N(0,1) values,
+    # 16 KiB of operands per wave (two waves per SIMD): bf16 N(0,1) values,
     # read by the E4M3 shapes as bytes (random codes) or, for constant
     # operands, bf16 1.0 = bytes 0x80 0x3f (E4M3 -0 and 1.875)
-    rnd = torch.randn(grid * 8 * 32 * 1024 // 2, device="cuda").to(torch.bfloat16)
+    rnd = torch.randn(grid * 8 * 16 * 1024 // 2, device="cuda").to(torch.bfloat16)
     const = torch.full_like(rnd, 1.0)
 
     def timed(fn, n=20, warm=3, grid_of_fn=0):

@@ -204,15 +204,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
       for (int t = 0; t < B_PER; ++t) dma16(ldsw + st + A_BYTES + 1024 * NW * t, rsB, voB[t], 0u);
     };
     // wait until this wave's loads of slab s have landed, given the slabs
-    // issued after it (whole slabs only: scale loads make the real count
-    // larger, so this waits at least as long as needed)
+    // issued after it (0 .. NST - 1 of them; whole slabs only: scale loads
+    // make the real count larger, so this waits at least as long as needed)
     auto wait_after = [&](int after) {
-      switch (after) {
-        case 0: wait_vmcnt<0>(); break;
-        case 1: wait_vmcnt<1 * NDMA>(); break;
-        case 2: wait_vmcnt<(2 * NDMA < 63 ? 2 * NDMA : 63)>(); break;
-        default: wait_vmcnt<(3 * NDMA < 63 ? 3 * NDMA : 63)>(); break;
-      }
+      static_for<0, NST>([&](auto a_c) {
+        constexpr int a = decltype(a_c)::value;
+        if (after == a) wait_vmcnt<a * NDMA>();
+      });
     };
 
     floatx16 acc[FM][FN];
@@ -222,7 +220,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
       for (int j = 0; j < FN; ++j) acc[i][j] = floatx16{};
 
     i32x8 af[2][FM], bfr[2][FN];
-    int sca[FM], scb[FN];  // scales of the current slab (E4M3: slab pair), shifted per lane
+    // scales of slab s in set s % 2, shifted per lane: the set a take writes
+    // is never the one the MFMAs still in flight read
+    int sca[2][FM], scb[2][FN];
+    uint32_t rsa[FM], rsb[FN];  // their scale dwords, read a step ahead
+    // this lane's first A and B rows in a scale window (bytes)
+    const uint32_t sra = (uint32_t)((wm * WTM + lrow) * 16);
+    const uint32_t srb = (uint32_t)(BM * 16 + (wn * WTN + lrow) * 16);
     auto read_frags = [&](int s, int slot) {
       const uint32_t so = (uint32_t)(s % NST) * STAGE;
 #pragma unroll
@@ -239,10 +243,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
       }
     };
     // Scales from window s / SPW, landed with its first slab before the
-    // barrier that made that slab readable. E4M3: the dword of slabs s, s + 1
-    // (s even), byte 2 (s % 2) + l / 32 after the shift; E2M1: the dword of
-    // slab s (its four blocks), byte 2 m + l / 32 for the slab's MFMA m.
-    auto take_scales = [&](int s) {
+    // barrier that made that slab readable. A scale dword is read one step
+    // before the first step that takes it (after that step's barrier), so the
+    // read latency never stands before an MFMA; every step takes (shifts) its
+    // slab's scales into the register set of its parity. E4M3: the dword of
+    // slabs s, s + 1 (s even), read once for both, byte 2 (s % 2) + l / 32
+    // after the shift; E2M1: the dword of slab s (its four blocks), byte
+    // 2 m + l / 32 for the slab's MFMA m.
+    auto fetch_scales = [&](int s) {
       const int w = s / SPW;
       const int dw = FP4 ? (s % SPW) : ((s % SPW) >> 1);
       // dword dw of a row with g = (row / 8) % 4 (row = 32 k + lrow): position
@@ -250,18 +258,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
       const int g = (lrow >> 3) & 3;
       const int buf = dw < g ? w : w + 1;
       const uint32_t wb = swin0 + (uint32_t)((buf % NWB) * SWIN) + (uint32_t)(4 * ((dw - g) & 3));
+      // one address per operand; the fragments' rows are constant offsets
+      const uint32_t wa = wb + sra, wbb = wb + srb;
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const uint32_t v = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
-            wb + (uint32_t)((wm * WTM + 32 * i + lrow) * 16));
-        sca[i] = (int)(v >> sh);
-      }
+      for (int i = 0; i < FM; ++i)
+        rsa[i] = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(wa + 512u * i);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const uint32_t v = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
-            wb + (uint32_t)(BM * 16 + (wn * WTN + 32 * j + lrow) * 16));
-        scb[j] = (int)(v >> sh);
-      }
+      for (int j = 0; j < FN; ++j)
+        rsb[j] = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(wbb + 512u * j);
+    };
+    auto take_scales = [&](int set) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sca[set][i] = (int)(rsa[i] >> sh);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) scb[set][j] = (int)(rsb[j] >> sh);
     };
     // MFMA k of a slab (k < NMFMA): block (i, j) and, for E2M1, half m
     constexpr int NBLK = FM * FN;
@@ -271,49 +281,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
       constexpr int b = k % NBLK, i = b / FN, j = b % FN;
       if constexpr (FP4) {
         constexpr int m = k / NBLK;
-        acc[i][j] = mma_mx<2 * m, HW>(fp4_half<m>(af[slot][i]), fp4_half<m>(bfr[slot][j]), sca[i],
-                                      scb[j], acc[i][j]);
+        acc[i][j] = mma_mx<2 * m, HW>(fp4_half<m>(af[slot][i]), fp4_half<m>(bfr[slot][j]), sca[PAR][i],
+                                      scb[PAR][j], acc[i][j]);
       } else {
-        acc[i][j] = mma_mx<2 * PAR, HW>(af[slot][i], bfr[slot][j], sca[i], scb[j], acc[i][j]);
+        acc[i][j] = mma_mx<2 * PAR, HW>(af[slot][i], bfr[slot][j], sca[PAR][i], scb[PAR][j], acc[i][j]);
       }
     };
-    auto mfmas = [&](auto par_c, int slot) {
-      static_for<0, NMFMA>([&](auto k_c) { mfma_k(k_c, par_c, slot); });
-    };
-    constexpr int NREAD = 2 * (FM + FN);
-    constexpr int RPM = (NREAD + NMFMA - 1) / NMFMA;
-    auto interleave = [&]() {
-#pragma unroll
-      for (int k = 0; k < NMFMA; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (k * RPM < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
-      }
-    };
-
-    // Slab s: its operands are in registers (slot s % 2); slab s + 1 must land
-    // before its operands are read during slab s's MFMAs; the stage of slab
-    // s - 1 (read before the last barrier) takes slab s + NST - 1.
-    auto step = [&](int s, auto par_c) {
-      constexpr int PAR = decltype(par_c)::value;  // s % 2
-      if (FP4 || PAR == 0) take_scales(s);
-      if (s + 1 < nk) {
-        const int issued_after = (nk - 1 < s + NST - 2 ? nk - 1 : s + NST - 2) - (s + 1);
-        wait_after(issued_after);
-        block_barrier();
-        if (s + NST - 1 < nk) issue_slab(s + NST - 1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(par_c, PAR);
-      // unconditional so it interleaves with the MFMAs; after the last slab
-      // it reads a stale stage (in bounds) whose values are never used
-      read_frags(s + 1, PAR ^ 1);
-      interleave();
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // Operand units of the steady step: A fragment IDX < FM, else B fragment
-    // IDX - FM, each two 16-byte LDS reads. The DMA loads of a slab are spread
-    // evenly among the MFMAs so they never reach the texture unit as one burst.
-    constexpr int NUNIT = FM + FN;
+    // Step s: slab s's operands are in registers (slot s % 2). At its start
+    // the wave waits for slab s + 1's loads and for its own reads of slab s
+    // (issued last step), then one barrier: every wave has slab s in
+    // registers, so slab s's stage takes slab s + NST, and slab s + 1 may be
+    // read. Slab s's MFMAs then run with slab s + 1's operand reads and slab
+    // s + NST's loads spread evenly among them, so neither the LDS nor the
+    // texture unit sees a burst.
+    constexpr int NUNIT = FM + FN;  // operand units: A fragment u < FM, else B fragment u - FM
     auto read_unit = [&](uint32_t so, int slot, auto idx_c) {
       constexpr int IDX = decltype(idx_c)::value;
       if constexpr (IDX < FM) {
@@ -336,107 +317,75 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
       else
         dma16(ldsw + st + A_BYTES + 1024 * NW * (t - A_PER), rsB, voB[t - A_PER], 0u);
     };
-    // Steady step s (slab s + NST - 1 exists). A slab's loads go out in two
-    // parts: its first H1 units (and the scale window it opens) right after
-    // the barrier of the step before, its other units during the first half of
-    // this step's MFMAs, so the loads of a slab are spread over a whole slab
-    // of MFMAs instead of arriving at the texture unit as one burst (a wave
-    // that finds the address queue full stalls, MFMAs included).
-    //   first half of slab s's MFMAs (they need nothing new), with the late
-    //     units of slab s + NST - 1 into the stage of slab s - 1;
-    //   wait for slab s + 1 and the barrier (every wave has then read slab s
-    //     into registers, so slab s's stage is free);
-    //   second half of the MFMAs, each followed by its share of slab s + 1's
-    //     operand reads and of the first units of slab s + NST into slab s's
-    //     stage. After the last steady step slab s + NST lies past K: those
-    //     loads read bytes inside the operand (or zeros past it) into a stage
-    //     nothing reads again, and the waits that follow count them as extra
-    //     loads, so they only wait longer.
-    constexpr int HALF = NMFMA / 2;
-    constexpr int UPH = (NUNIT + HALF - 1) / HALF;  // operand units read after each MFMA
-    constexpr int H1 = NDMA / 2;                     // units of a slab issued a step early
-    static_assert((NST - 2) * NDMA + H1 <= 63, "loads in flight fit the counter");
-    auto slot_late = [](int u) constexpr { return ((2 * u + 1) * HALF) / (2 * (NDMA - H1)); };
-    auto slot_early = [](int u) constexpr { return HALF + ((2 * u + 1) * (NMFMA - HALF)) / (2 * H1); };
-    auto issue_first = [&](int sl) {
-      if (sl % SPW == 0) issue_window(sl / SPW);
-      const uint32_t st = (uint32_t)(sl % NST) * STAGE;
-      const i32x4 rsA = make_rsrc(a_panel + (int64_t)sl * BKB, a_bytes - (int64_t)sl * BKB);
-      const i32x4 rsB = make_rsrc(b_panel + (int64_t)sl * BKB, b_bytes - (int64_t)sl * BKB);
-      static_for<0, H1>([&](auto t_c) { dma_unit(st, rsA, rsB, t_c); });
-    };
+    // the MFMA after which operand unit u, and DMA unit t, are issued
+    auto read_slot = [](int u) constexpr { return ((2 * u + 1) * NMFMA) / (2 * NUNIT); };
+    auto dma_slot = [](int t) constexpr { return ((2 * t + 1) * NMFMA) / (2 * NDMA); };
+    static_assert(NST >= 2 && (NST - 1) * NDMA <= 63, "loads in flight fit the counter");
+    // Steady step (slab s + NST exists, so NST - 2 whole slabs follow s + 1)
     auto step_full = [&](int s, auto par_c) {
-      constexpr int PAR = decltype(par_c)::value;
-      if (FP4 || PAR == 0) take_scales(s);
-      const int sn = s + NST - 1;
+      constexpr int PAR = decltype(par_c)::value;  // s % 2
+      take_scales(PAR);
+      wait_vmcnt<(NST - 2) * NDMA>();
+      wait_lgkmcnt0();
+      block_barrier();
+      if (FP4 || PAR == 1) fetch_scales(s + 1);
+      const int sn = s + NST;
+      if (sn % SPW == 0) issue_window(sn / SPW);
       const uint32_t stn = (uint32_t)(sn % NST) * STAGE;
       const i32x4 rsA = make_rsrc(a_panel + (int64_t)sn * BKB, a_bytes - (int64_t)sn * BKB);
       const i32x4 rsB = make_rsrc(b_panel + (int64_t)sn * BKB, b_bytes - (int64_t)sn * BKB);
       const uint32_t so = (uint32_t)((s + 1) % NST) * STAGE;
       __builtin_amdgcn_sched_barrier(0);
-      // (a fence after each MFMA and its loads: the loads are inline assembly,
-      // which the scheduler would otherwise gather into one burst)
-      static_for<0, HALF>([&](auto k_c) {
+      // (a fence after each MFMA and what goes with it: the loads are inline
+      // assembly, which the scheduler would otherwise gather into one burst)
+      static_for<0, NMFMA>([&](auto k_c) {
         constexpr int k = decltype(k_c)::value;
         mfma_k(k_c, par_c, PAR);
-        static_for<H1, NDMA>([&](auto t_c) {
-          constexpr int t = decltype(t_c)::value;
-          if constexpr (slot_late(t - H1) == k) dma_unit(stn, rsA, rsB, t_c);
+        static_for<0, NUNIT>([&](auto u_c) {
+          if constexpr (read_slot(decltype(u_c)::value) == k) read_unit(so, PAR ^ 1, u_c);
+        });
+        static_for<0, NDMA>([&](auto t_c) {
+          if constexpr (dma_slot(decltype(t_c)::value) == k) dma_unit(stn, rsA, rsB, t_c);
         });
         __builtin_amdgcn_sched_barrier(0);
       });
-      __builtin_amdgcn_sched_barrier(0);
-      // slab s + 1 has landed once at most the loads of slabs s + 2 .. s + NST - 1
-      // remain (scale windows among them only make the wait longer); this
-      // wave's LDS reads (of slab s, issued last step) are complete before the
-      // barrier
-      wait_vmcnt<(NST - 2) * NDMA>();
+    };
+    // Any step, near the end of K: the same order, with the waits counted
+    // from the slabs that exist and slab s + NST's loads (if it exists) in
+    // one burst after the barrier.
+    auto step = [&](int s, auto par_c) {
+      constexpr int PAR = decltype(par_c)::value;
+      take_scales(PAR);
+      if (s + 1 < nk) wait_after((nk - 1 < s + NST - 1 ? nk - 1 : s + NST - 1) - (s + 1));
       wait_lgkmcnt0();
       block_barrier();
-      const int se = sn + 1;
-      if (se % SPW == 0) issue_window(se / SPW);
-      const uint32_t ste = (uint32_t)(se % NST) * STAGE;
-      const i32x4 rsAe = make_rsrc(a_panel + (int64_t)se * BKB, a_bytes - (int64_t)se * BKB);
-      const i32x4 rsBe = make_rsrc(b_panel + (int64_t)se * BKB, b_bytes - (int64_t)se * BKB);
-      static_for<HALF, NMFMA>([&](auto k_c) {
+      // (after the last slab: dwords of a buffer in bounds, never used)
+      if (FP4 || PAR == 1) fetch_scales(s + 1);
+      if (s + NST < nk) issue_slab(s + NST);
+      const uint32_t so = (uint32_t)((s + 1) % NST) * STAGE;
+      __builtin_amdgcn_sched_barrier(0);
+      // unconditional, after the last slab too: it then reads a stale stage
+      // (in bounds) whose values are never used
+      static_for<0, NMFMA>([&](auto k_c) {
         constexpr int k = decltype(k_c)::value;
         mfma_k(k_c, par_c, PAR);
-        static_for<0, UPH>([&](auto r_c) {
-          constexpr int idx = (k - HALF) * UPH + decltype(r_c)::value;
-          if constexpr (idx < NUNIT) read_unit(so, PAR ^ 1, std::integral_constant<int, idx>{});
+        static_for<0, NUNIT>([&](auto u_c) {
+          if constexpr (read_slot(decltype(u_c)::value) == k) read_unit(so, PAR ^ 1, u_c);
         });
-        static_for<0, H1>([&](auto t_c) {
-          if constexpr (slot_early(decltype(t_c)::value) == k) dma_unit(ste, rsAe, rsBe, t_c);
-        });
+        __builtin_amdgcn_sched_barrier(0);
       });
-      static_for<HALF, NMFMA>([&](auto k_c) {
-        constexpr int k = decltype(k_c)::value;
-        constexpr int lo = (k - HALF) * UPH, hi = (k - HALF + 1) * UPH < NUNIT ? (k - HALF + 1) * UPH : NUNIT;
-        constexpr int n_rd = lo < NUNIT ? 2 * (hi - lo) : 0;
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if constexpr (n_rd > 0) __builtin_amdgcn_sched_group_barrier(0x100, n_rd, 0);
-      });
-      __builtin_amdgcn_sched_barrier(0);
     };
-    // prologue: slabs 0 .. NST-2 in flight (and, when steady steps follow,
-    // the first units of slab NST - 1, as a step before step 0 would issue
-    // them), slab 0 landed and read
-    const int n_full = nk - (NST - 1);  // steady steps: slab s + NST - 1 exists
+    // prologue: slabs 0 .. NST - 1 in flight, slab 0 landed and read
+    const int n_full = nk - NST;  // steady steps: slab s + NST exists
     if (nk > 0) {
       issue_window(-1);
-      for (int sl = 0; sl < NST - 1 && sl < nk; ++sl) issue_slab(sl);
-      if (n_full > 0) {
-        issue_first(NST - 1);
-        wait_vmcnt<(NST - 2) * NDMA + H1>();
-      } else {
-        wait_after((nk - 1 < NST - 2 ? nk - 1 : NST - 2));
-      }
+      for (int sl = 0; sl < NST && sl < nk; ++sl) issue_slab(sl);
+      wait_after((nk - 1 < NST - 1 ? nk - 1 : NST - 1));
       block_barrier();
       read_frags(0, 0);
+      fetch_scales(0);
     }
-    // Steps run in pairs (the register slot of slab s is s % 2). Every slab
-    // is issued by a steady step or the prologue, so the other steps issue
-    // nothing.
+    // Steps run in pairs (the register slot of slab s is s % 2).
     int s = 0;
     const std::integral_constant<int, 0> p0{};
     const std::integral_constant<int, 1> p1{};
@@ -450,10 +399,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx_gemm_kernel(MxArgs p) {
       if (s < nk) step(s++, p1);
     }
     for (; s + 2 <= nk; s += 2) {
-      step(s, std::integral_constant<int, 0>{});
-      step(s + 1, std::integral_constant<int, 1>{});
+      step(s, p0);
+      step(s + 1, p1);
     }
-    if (s < nk) step(s, std::integral_constant<int, 0>{});
+    if (s < nk) step(s, p0);
 
     // Store: the summed tile is staged in the free ring as fp32 strips and
     // written once per element (with the fused epilogue when asked).

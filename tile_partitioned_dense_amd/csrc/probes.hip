@@ -77,19 +77,22 @@ __global__ __launch_bounds__(512) void mfma_probe(const u32x4* __restrict__ src,
 }
 
 // As mfma_probe for the block-scaled E4M3 forms (SHAPE 0: 32x32x64, 1:
-// 16x16x128): 32-byte fragments, every scale byte 127 (a factor of 1).
+// 16x16x128): 32-byte fragments (kF8Ops per side, so that fragments and
+// accumulators fit the registers of two waves per SIMD without spilling),
+// every scale byte 127 (a factor of 1).
+constexpr int kF8Ops = 4;
 template <int SHAPE>
 __global__ __launch_bounds__(512) void mfma_probe_f8(const u32x4* __restrict__ src, float* __restrict__ out,
                                                     int iters) {
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  i32x8 a[kOps], b[kOps];
+  i32x8 a[kF8Ops], b[kF8Ops];
 #pragma unroll
-  for (int i = 0; i < kOps; ++i) {
-    const u32x4 a0 = src[(wave * 4 * kOps + 2 * i) * 64 + lane];
-    const u32x4 a1 = src[(wave * 4 * kOps + 2 * i + 1) * 64 + lane];
-    const u32x4 b0 = src[(wave * 4 * kOps + 2 * kOps + 2 * i) * 64 + lane];
-    const u32x4 b1 = src[(wave * 4 * kOps + 2 * kOps + 2 * i + 1) * 64 + lane];
+  for (int i = 0; i < kF8Ops; ++i) {
+    const u32x4 a0 = src[(wave * 4 * kF8Ops + 2 * i) * 64 + lane];
+    const u32x4 a1 = src[(wave * 4 * kF8Ops + 2 * i + 1) * 64 + lane];
+    const u32x4 b0 = src[(wave * 4 * kF8Ops + 2 * kF8Ops + 2 * i) * 64 + lane];
+    const u32x4 b1 = src[(wave * 4 * kF8Ops + 2 * kF8Ops + 2 * i + 1) * 64 + lane];
     a[i] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
     b[i] = i32x8{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
   }
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(512) void mfma_probe_f8(const u32x4* __restrict__ s
       for (int j = 0; j < kOps; ++j)
 #pragma unroll
         for (int i = 0; i < kOps; ++i)
-          acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[(i + j) % kOps], b[(5 * i + j) % kOps],
+          acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[(i + j) % kF8Ops], b[(3 * i + j) % kF8Ops],
                                                                    acc[i], 0, 0, 0, kScale, 0, kScale);
     }
 #pragma unroll
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(512) void mfma_probe_f8(const u32x4* __restrict__ s
       for (int j = 0; j < kOps; ++j)
 #pragma unroll
         for (int i = 0; i < 2 * kOps; ++i)
-          acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[(i + j) % kOps], b[(5 * i + j) % kOps],
+          acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[(i + j) % kF8Ops], b[(3 * i + j) % kF8Ops],
                                                                     acc[i], 0, 0, 0, kScale, 0, kScale);
     }
 #pragma unroll
@@ -203,8 +206,8 @@ int tg_probe_clock(unsigned long long* out, long long ticks, void* stream) {
 // Launch the MFMA probe: `grid` workgroups of 4 * waves_per_simd waves (one
 // workgroup per compute unit when grid = CU count), shape 0 = 32x32x16 bf16,
 // 1 = 16x16x32 bf16, 2 = 32x32x64 scaled E4M3, 3 = 16x16x128 scaled E4M3.
-// `src` holds at least grid * 4 * waves_per_simd * 16 KiB of operand bytes
-// (32 KiB for shapes 2 and 3), `out` grid * 256 * waves_per_simd floats.
+// `src` holds at least grid * 4 * waves_per_simd * 16 KiB of operand bytes,
+// `out` grid * 256 * waves_per_simd floats.
 // Returns a hipError_t. FLOP per launch: waves * iters * 64 * 32768 for the
 // bf16 shapes, four times that for the E4M3 ones (the 16x16 forms issue twice
 // the instructions of half the size).
