@@ -65,6 +65,9 @@ def parse():
                     help="comma-separated extra workloads reported on the same line; NAME:EPI adds a "
                     "fused epilogue, e.g. decode:bias+silu; NAME@f32 or NAME@bf16 picks the output "
                     "type ('' for none)")
+    ap.add_argument("--k", type=int, default=0,
+                    help="run the headline workload with this K instead (counter runs at two K "
+                         "separate what a K step costs from what a tile's prologue and epilogue cost)")
     ap.add_argument("--probes", action="store_true",
                     help="also run the MFMA-rate and HBM streaming-read probes (libtile_probes.so)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -312,10 +315,11 @@ class Bench:
         res["frac_hbm"] = res["gbs"] / PEAK_HBM_GBS
         if w.flops < 1e8:
             res["launch_us"] = self.launch_overhead(sets[0])
+        mhz = clock.get("shader_clock_mhz")
         log(f"[bench] {w.name}: mean {res['kernel_ms_mean'] * 1e3:.1f} us "
             f"(median {res['kernel_ms_median'] * 1e3:.1f}, min {res['kernel_ms_min'] * 1e3:.1f}) "
-            f"at {clock['shader_clock_mhz'] or 0:.0f} MHz "
-            f"-> {res['tflops']:.1f} TFLOP/s ({100 * res['frac_mfma']:.1f}% MFMA), "
+            + (f"at {mhz:.0f} MHz " if mhz else "(clock not sampled: the grid fills every CU) ")
+            + f"-> {res['tflops']:.1f} TFLOP/s ({100 * res['frac_mfma']:.1f}% MFMA), "
             f"{res['gbs']:.0f} GB/s ({100 * res['frac_hbm']:.1f}% HBM)")
         del sets
         torch.cuda.empty_cache()
@@ -563,6 +567,9 @@ def main():
 
     b = Bench(torch, tg, synth)
     head = synth.WORKLOADS[args.workload]
+    if args.k:
+        import dataclasses
+        head = dataclasses.replace(head, name=f"{head.name}@K{args.k}", K=args.k)
     head_out = head.outs[0]
     ops, res = b.time_workload(head, head_out, args.steps, args.warmup)
     secondary = []

@@ -52,6 +52,25 @@ namespace tg {
 // one chunk) or bits 0-1 double the LDS cycles per read.
 __device__ __forceinline__ int swz16(int r) { return (r >> 1) & 3; }
 
+// Chunk placement of a row-major B slab (k rows of CPR 16-byte chunks):
+// chunk c of k row r sits at position swzB<CPR>(c, r) of its row. A B
+// fragment is two transposing 8-byte reads; each 16 lanes of one read take
+// 32 bytes (two chunks) from each of four consecutive k rows, which must land
+// in four different 32-byte bank groups. The rows' chunks are XORed in
+// aligned groups (so each group stays in place and the map is its own
+// inverse): the first CPR & ~15 chunks with (r % 4) in bits 1-2 and bit 3 of
+// r in bit 3, the next aligned 8 with (r % 4) in bits 1-2, and an aligned 4
+// that follows (rows then start 64 bytes apart mod 128) with bit 1 of r in
+// bit 1. Any chunks after those stay in place.
+template <int CPR>
+__device__ __forceinline__ int swzB(int c, int r) {
+  constexpr int GA = CPR >= 16 ? (CPR & ~15) : 0, GB = CPR & ~7, GC = CPR & ~3;
+  if (c < GA) return c ^ (((r & 3) << 1) | (((r >> 3) & 1) << 3));
+  if (c < GB) return c ^ ((r & 3) << 1);
+  if (c < GC) return c ^ (((r >> 1) & 1) << 1);
+  return c;
+}
+
 // 16 x 16 x 32 step of a C block held transposed (see above).
 __device__ __forceinline__ floatx4 mma16(const bf16x8& a_frag, const bf16x8& b_frag, const floatx4& acc) {
   return mfma16(b_frag, a_frag, acc);
@@ -85,7 +104,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile16_gemm_kernel(TileArgs p
   constexpr int B_MAX = (B_DMA + NW - 1) / NW;
   constexpr int B_MIN = B_DMA / NW;
   constexpr int PITCH = BN * 2;  // row-major B: bytes per k row
-  constexpr bool SWB = !BCOL && (PITCH % 256 == 0);
   constexpr int CPR = BN / 8;  // row-major B: 16-byte chunks per k row
 
   __shared__ __attribute__((aligned(1024))) uint4 smem[kStages * STAGE / 16];
@@ -144,7 +162,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile16_gemm_kernel(TileArgs p
       } else {
         const int q = 64 * ins + lane;
         const int row = q / CPR, pc = q - (q / CPR) * CPR;
-        const int lc = SWB ? ((((pc >> 2) ^ (row & 3)) << 2) | (pc & 3)) : pc;
+        const int lc = swzB<CPR>(pc, row);  // the chunk that belongs at position pc
         voB[t] = (uint32_t)(row * ldb * 2) + lc * 16 + (lc >= CPR / 2 ? 2 * gshift : 0);
       }
     }
@@ -189,7 +207,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile16_gemm_kernel(TileArgs p
         } else {
           for (int q = tid; q < BK * CPR; q += NT) {
             const int row = q / CPR, pc = q - (q / CPR) * CPR;
-            const int lc = SWB ? ((((pc >> 2) ^ (row & 3)) << 2) | (pc & 3)) : pc;
+            const int lc = swzB<CPR>(pc, row);
             const int gk = k0 + row;
             const int col = n0 + 8 * lc + (lc >= CPR / 2 ? gshift : 0);
             const uint4 v = (gk < K) ? load8_masked(p.B + (int64_t)gk * ldb, col, N)
@@ -248,8 +266,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile16_gemm_kernel(TileArgs p
     uint32_t rT[BCOL ? 1 : FN][NPAIR];  // row-major B: per block and stage pair
 #pragma unroll
     for (int j = 0; j < (BCOL ? 1 : FN); ++j) {
+      // rows 8 G + j and 8 G + 4 + j share their chunk placement
       const int n = wn * WTN + 16 * j + 4 * tq;
-      const int col = SWB ? ((((n >> 5) ^ tj) << 5) | (n & 31)) : n;
+      const int col = (swzB<CPR>(n >> 3, 8 * tG + tj) << 3) | (n & 7);
       const uint32_t b = lds0 + A_BYTES + (uint32_t)((8 * tG + tj) * PITCH + col * 2);
 #pragma unroll
       for (int h = 0; h < NPAIR; ++h) rT[j][h] = b + 2 * h * STAGE;

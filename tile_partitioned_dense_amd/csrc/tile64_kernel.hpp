@@ -56,7 +56,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
   constexpr int B_MAX = (B_DMA + NW - 1) / NW;
   constexpr int B_MIN = B_DMA / NW;
   constexpr int PITCH = BN * 2;  // row-major B: bytes per k row
-  constexpr bool SWB = !BCOL && (PITCH % 256 == 0);
   constexpr int CPR = BN / 8;  // row-major B: 16-byte chunks per k row
   static_assert(A_BYTES <= 65536 - 16 * 1024 && B_BYTES <= 65536, "ds_read immediates within a stage");
 
@@ -114,7 +113,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
       } else {
         const int q = 64 * ins + lane;
         const int row = q / CPR, pc = q - (q / CPR) * CPR;
-        const int lc = SWB ? ((((pc >> 2) ^ (row & 3)) << 2) | (pc & 3)) : pc;
+        const int lc = swzB<CPR>(pc, row);
         voB[t] = (uint32_t)(row * ldb * 2) + lc * 16 + (lc >= CPR / 2 ? 2 * gshift : 0);
       }
     }
@@ -159,7 +158,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
         } else {
           for (int q = tid; q < BK * CPR; q += NT) {
             const int row = q / CPR, pc = q - (q / CPR) * CPR;
-            const int lc = SWB ? ((((pc >> 2) ^ (row & 3)) << 2) | (pc & 3)) : pc;
+            const int lc = swzB<CPR>(pc, row);
             const int gk = k0 + row;
             const int col = n0 + 8 * lc + (lc >= CPR / 2 ? gshift : 0);
             const uint4 v = (gk < K) ? load8_masked(p.B + (int64_t)gk * ldb, col, N)
@@ -207,7 +206,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
 #pragma unroll
     for (int j = 0; j < (BCOL ? 1 : FN); ++j) {
       const int n = wn * WTN + 16 * j + 4 * tq;
-      const int col = SWB ? ((((n >> 5) ^ tj) << 5) | (n & 31)) : n;
+      const int col = (swzB<CPR>(n >> 3, 8 * tG + tj) << 3) | (n & 7);
 #pragma unroll
       for (int st = 0; st < 2; ++st)
         rT[j][st] = lds0 + st * STAGE + A_BYTES + (uint32_t)((8 * tG + tj) * PITCH + col * 2);
