@@ -193,3 +193,18 @@ def test_tile_of_is_a_bijection_for_any_raster_group(M, N, group_m):
         m0, n0, rows, cols = tg.tile_gemm_tile_of(plan, M, N, wg)
         seen.add((m0, n0))
     assert len(seen) == plan.tiles
+
+
+def test_rate_tool_reads_the_configuration_table():
+    """The configuration-rate tool (tile_partitioned_dense_amd/rate_configs.py)
+    reads the planner's table from plan.hpp: it must see every entry with the
+    struct's defaults applied."""
+    from tile_partitioned_dense_amd import build, rate_configs
+    t = rate_configs.config_table()
+    assert len(t) == build.N_TILE_CONFIGS
+    assert t[0] == dict(bm=256, bn=256, wm=2, wn=2, stages=4, eff=0.94, ks=1, eff1=0.0, occ=1, sb=0,
+                        mi=32, bk=32)
+    assert t[5]["eff1"] == 0.59 and t[5]["occ"] == 2
+    assert t[14]["sb"] == 512 and t[14]["ks"] == 2
+    assert t[17]["mi"] == 16 and t[17]["bk"] == 32
+    assert t[24]["mi"] == 16 and t[24]["bk"] == 64
