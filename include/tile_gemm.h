@@ -18,8 +18,9 @@
  * a bf16 output is the round-to-nearest-even of the fp32 result of the same
  * shape.
  *
- * Threading: a handle is read-only after tile_gemm_create, so concurrent
- * tile_gemm_run calls on different streams may share it.
+ * Threading: a handle's plan state is read-only after tile_gemm_create, so
+ * concurrent tile_gemm_run calls on different streams may share it (the
+ * optional plan log below is guarded by a lock inside the handle).
  */
 #ifndef TILE_GEMM_H
 #define TILE_GEMM_H
@@ -76,6 +77,11 @@ typedef struct {
  * no device memory. On success *out holds a new handle; on failure *out is
  * set to NULL (when out is not NULL).
  * Errors: TILE_GEMM_ERR_NULL_ARG (out == NULL), TILE_GEMM_ERR_DEVICE.
+ *
+ * Environment, read here once: TILE_GEMM_LOG set to anything but "" or "0"
+ * makes every run entry point print the plan it launches (variant,
+ * configuration, tile, K step, threads, tiles, grid) to stderr, once per
+ * distinct call shape (the first 64 shapes; every call after that).
  *
  * Source: the split between a once-only preparation and cheap recording of
  * work ("Rust Compute Kernels", section "Quick example": prepare compiles or

@@ -182,3 +182,36 @@ def test_handle_checks_current_device(g):
     assert lib.tile_gemm_create(ctypes.byref(h), 10_000) == tg.Status.ERR_DEVICE
     assert lib.tile_gemm_create(ctypes.byref(h), 0) == tg.Status.OK
     assert lib.tile_gemm_destroy(h) == tg.Status.OK
+
+
+def test_plan_log_prints_each_shape_once(capfd, monkeypatch):
+    """TILE_GEMM_LOG=1 (read at create) prints the launched plan to stderr once
+    per call shape, and the printed plan is the planner's."""
+    monkeypatch.setenv("TILE_GEMM_LOG", "1")
+    with tg.TileGemm(0) as lg:
+        cases = [(300, 264, 200), (16, 512, 256)]
+        for M, N, K in cases + cases[:1]:
+            A = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
+            B = torch.zeros((K, N), dtype=torch.bfloat16, device="cuda")
+            C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            lg(A, B, C)
+        torch.cuda.synchronize()
+    err = capfd.readouterr().err
+    lines = [ln for ln in err.splitlines() if ln.startswith("tile_gemm: run ")]
+    assert len(lines) == 2, err
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    for (M, N, K), ln in zip(cases, lines):
+        p = tg.tile_gemm_plan(M, N, K, False, cu)
+        assert f" M={M} N={N} K={K} B=row-major" in ln, ln
+        assert f" config {p.config}, tile {p.bm}x{p.bn}," in ln and f" grid {p.grid}," in ln, ln
+
+
+def test_plan_log_off_by_default(capfd, monkeypatch):
+    monkeypatch.delenv("TILE_GEMM_LOG", raising=False)
+    with tg.TileGemm(0) as lg:
+        A = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+        B = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+        C = torch.empty((64, 64), dtype=torch.float32, device="cuda")
+        lg(A, B, C)
+        torch.cuda.synchronize()
+    assert "tile_gemm: run" not in capfd.readouterr().err

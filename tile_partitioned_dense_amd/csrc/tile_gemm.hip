@@ -14,8 +14,11 @@
 //    argument and axis ("Rust Compute Kernels", section "Shape contracts");
 //  * a written argument may not overlap another argument ("Rust Compute
 //    Kernels", section "Fusing invocations", which rejects exactly that).
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "launch.hpp"  // first: the HIP runtime headers plan.hpp relies on under hipcc
@@ -24,9 +27,39 @@
 struct tile_gemm_handle {
   int device;
   int cu_count;
+  // TILE_GEMM_LOG=1 at create: the chosen plan is printed to stderr once per
+  // shape (the first kLogShapes shapes; every call after that). A fixed table,
+  // so run still allocates nothing.
+  bool log;
+  std::mutex log_mu;
+  int n_logged;
+  uint64_t logged[64];
 };
 
 namespace {
+
+constexpr int kLogShapes = 64;
+
+void log_plan(tile_gemm_handle* h, const char* kind, int64_t M, int64_t N, int64_t K, int layout,
+              int dtype, int act, const tg::Plan& p) {
+  if (!h->log) return;
+  uint64_t key = 1469598103934665603ull;  // FNV-1a over the call's kind and shape
+  for (const char* c = kind; *c; ++c) key = (key ^ (uint64_t)(unsigned char)*c) * 1099511628211ull;
+  const int64_t parts[6] = {M, N, K, layout, dtype, act};
+  for (int64_t v : parts)
+    for (int b = 0; b < 8; ++b) key = (key ^ (uint64_t)((v >> (8 * b)) & 0xff)) * 1099511628211ull;
+  std::lock_guard<std::mutex> lock(h->log_mu);
+  for (int i = 0; i < h->n_logged; ++i)
+    if (h->logged[i] == key) return;
+  if (h->n_logged < kLogShapes) h->logged[h->n_logged++] = key;
+  static const char* const kVariant[] = {"none", "tile", "skinny", "mx"};
+  fprintf(stderr,
+          "tile_gemm: %s M=%lld N=%lld K=%lld B=%s dtype=%d act=%d -> %s config %d, tile %dx%d, "
+          "K step %d, %d threads, %lld tiles, grid %lld, k_split %d, group_m %d\n",
+          kind, (long long)M, (long long)N, (long long)K, layout ? "column-major" : "row-major", dtype,
+          act, kVariant[p.variant & 3], p.config, p.bm, p.bn, p.bk, p.threads, (long long)p.tiles,
+          (long long)p.grid, p.k_split, p.map.group_m);
+}
 
 hipError_t dispatch_tile(int cfg, const tg::TileArgs& a, int64_t grid, const tg::Variant& v,
                          hipStream_t st) {
@@ -136,6 +169,7 @@ tile_gemm_status_t run_mx_impl(tile_gemm_t h, const void* A, const void* B, void
   a.flags = flags;
   a.bias = bias;
   a.act = act;
+  log_plan(h, fmt == TILE_GEMM_MX_E2M1 ? "run_mx e2m1" : "run_mx e4m3", M, N, K, 1, (int)dtype, act, p);
   const tg::Variant v{true, dtype == TILE_GEMM_BF16_TO_BF16, instrumented(flags)};
   const hipError_t e =
       dispatch_mx(p.config, a, fmt, p.grid, v, static_cast<hipStream_t>(stream));
@@ -202,6 +236,7 @@ tile_gemm_status_t run_impl(tile_gemm_t h, const void* A, const void* B, void* C
   if ((flags & TILE_GEMM_DEBUG_COLLIDE) && (p.variant != 1 || p.tiles < 2))
     return fail(TILE_GEMM_ERR_BAD_SHAPE, "debug collide: needs the tile kernel and >= 2 tiles");
 
+  log_plan(h, "run", M, N, K, !brow, (int)dtype, act, p);
   const tg::Variant v{!brow, dtype == TILE_GEMM_BF16_TO_BF16, instrumented(flags)};
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
@@ -264,8 +299,12 @@ tile_gemm_status_t tile_gemm_create(tile_gemm_t* out, int device) {
     return fail(TILE_GEMM_ERR_DEVICE, "cannot query device %d", device);
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(TILE_GEMM_ERR_DEVICE, "device %d is %s, not gfx950", device, prop.gcnArchName);
-  tile_gemm_handle* hnd = new (std::nothrow) tile_gemm_handle{device, prop.multiProcessorCount};
+  tile_gemm_handle* hnd = new (std::nothrow) tile_gemm_handle{};
   if (!hnd) return fail(TILE_GEMM_ERR_HIP, "out of host memory");
+  hnd->device = device;
+  hnd->cu_count = prop.multiProcessorCount;
+  const char* lg = getenv("TILE_GEMM_LOG");
+  hnd->log = lg && lg[0] && strcmp(lg, "0") != 0;
   *out = hnd;
   return TILE_GEMM_OK;
 }
