@@ -32,7 +32,12 @@
 //
 // Each step waits for stage s, passes one barrier (after which every wave is
 // done with stage s - 1), loads stage s + NST - 1 into stage s - 1's buffer
-// and then runs stage s's MFMAs. Each wave accumulates its share of K in
+// and then runs stage s's MFMAs. Stages are numbered on across a workgroup's
+// tiles (buffer (g + s) % NST, g the stages of its earlier tiles), so the
+// last steps of a tile load the first stages of the workgroup's next tile
+// and the next tile starts with its ring already filling; the store stages
+// the tile in the buffer of its last stage, the one buffer no load is
+// filling then. Each wave accumulates its share of K in
 // ascending order in fp32, and the two shares of a block meet in a fixed
 // order: results are bit-identical run to run. A last stage that ends
 // inside K zeroes, in both operands, every value at or past K (the bytes
@@ -95,8 +100,8 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void stream_gemm_kernel(TileA
   constexpr int OPF = 32 * 4 + 16;          // per-wave fp32 strip pitch
   constexpr int OPG = BN * 4 + 16;          // block-wide fp32 strip pitch (SiLU(gate) * up)
   constexpr int PART = KS > 1 ? NCB * FM * 4096 : 0;  // second waves' partial sums
-  static_assert(NCB * 32 * OPF + PART <= RING && 32 * OPG + PART <= RING,
-                "staged strips and partial sums fit the ring side by side");
+  static_assert(NCB * 32 * OPF <= STAGE && 32 * OPG <= STAGE && PART <= STAGE,
+                "staged strips, and before them the partial sums, fit one stage buffer");
 
   __shared__ __attribute__((aligned(1024))) uint4 smem[RING / 16];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
@@ -141,8 +146,15 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void stream_gemm_kernel(TileA
   const uint32_t rA = lds0 + (uint32_t)(ar * SB), rB = lds0 + A_BYTES + (uint32_t)(br * SB);
   const int swa = swz(ar), swb = swz(br);
 
-  const int n_tiles = p.map.tiles_m * p.map.tiles_n;
-  for (int wg_it = blockIdx.x; wg_it < n_tiles; wg_it += gridDim.x) {
+  // A tile's panels (the rows of A and the columns of B it reads) and their
+  // valid extents in bytes, to the operand's last element.
+  struct Panels {
+    const char* a;
+    int64_t a_bytes;
+    const char* b;
+    int64_t b_bytes;
+  };
+  auto panels_of = [&](int wg_it) -> Panels {
     int wg = wg_it;
     if constexpr (DEBUG) {
       if ((p.flags & kDbgCollide) && wg == 1) wg = 0;  // negative control only
@@ -150,21 +162,42 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void stream_gemm_kernel(TileA
     int32_t tm, tn;
     tile_of(p.map, wg, tm, tn);
     const int m0 = tm * BM, n0 = tn * (glu ? BN / 2 : BN);
-    const char* a_panel = reinterpret_cast<const char*>(p.A + (int64_t)m0 * lda);
-    const int64_t a_bytes = K > 0 ? (((int64_t)(M - 1) * lda + K) - (int64_t)m0 * lda) * 2 : 0;
-    const char* b_panel = reinterpret_cast<const char*>(p.B + (int64_t)n0 * ldb);
-    const int64_t b_bytes = K > 0 ? (((int64_t)(N - 1) * ldb + K) - (int64_t)n0 * ldb) * 2 : 0;
+    return Panels{reinterpret_cast<const char*>(p.A + (int64_t)m0 * lda),
+                  K > 0 ? (((int64_t)(M - 1) * lda + K) - (int64_t)m0 * lda) * 2 : 0,
+                  reinterpret_cast<const char*>(p.B + (int64_t)n0 * ldb),
+                  K > 0 ? (((int64_t)(N - 1) * ldb + K) - (int64_t)n0 * ldb) * 2 : 0};
+  };
+  // Stage s of the tile with panels pn into buffer `buf`.
+  auto issue_stage = [&](const Panels& pn, int s, int buf) {
+    const uint32_t st = (uint32_t)buf * STAGE;
+    const i32x4 rsA = make_rsrc(pn.a + (int64_t)s * SB, pn.a_bytes - (int64_t)s * SB);
+    const i32x4 rsB = make_rsrc(pn.b + (int64_t)s * SB, pn.b_bytes - (int64_t)s * SB);
+#pragma unroll
+    for (int t = 0; t < A_MAX; ++t)
+      if (t < A_MIN || t < a_cnt) dma16(ldsw + st + 1024 * NW * t, rsA, voA[t], 0u);
+#pragma unroll
+    for (int t = 0; t < B_PER; ++t) dma16(ldsw + st + A_BYTES + 1024 * NW * t, rsB, voB[t], 0u);
+  };
 
-    auto issue_stage = [&](int s) {
-      const uint32_t st = (uint32_t)(s % NST) * STAGE;
-      const i32x4 rsA = make_rsrc(a_panel + (int64_t)s * SB, a_bytes - (int64_t)s * SB);
-      const i32x4 rsB = make_rsrc(b_panel + (int64_t)s * SB, b_bytes - (int64_t)s * SB);
-#pragma unroll
-      for (int t = 0; t < A_MAX; ++t)
-        if (t < A_MIN || t < a_cnt) dma16(ldsw + st + 1024 * NW * t, rsA, voA[t], 0u);
-#pragma unroll
-      for (int t = 0; t < B_PER; ++t) dma16(ldsw + st + A_BYTES + 1024 * NW * t, rsB, voB[t], 0u);
-    };
+  const int n_tiles = p.map.tiles_m * p.map.tiles_n;
+  int gbase = 0;  // buffer of this tile's stage 0
+  int pre = 0;    // this tile's leading stages already issued by the previous tile
+  for (int wg_it = blockIdx.x; wg_it < n_tiles; wg_it += gridDim.x) {
+    int32_t tm, tn;
+    {
+      int wg = wg_it;
+      if constexpr (DEBUG) {
+        if ((p.flags & kDbgCollide) && wg == 1) wg = 0;
+      }
+      tile_of(p.map, wg, tm, tn);
+    }
+    const int m0 = tm * BM, n0 = tn * (glu ? BN / 2 : BN);
+    const Panels cur = panels_of(wg_it);
+    // the workgroup's next tile takes its first NST - 1 stages from this
+    // tile's last steps (when this tile has that many)
+    const bool cross = wg_it + (int)gridDim.x < n_tiles && nss >= NST - 1;
+    const Panels nxt = cross ? panels_of(wg_it + gridDim.x) : cur;
+
     // Wait until this wave's loads of stage s have landed, `after` stages
     // having been issued after it.
     auto wait_after = [&](int after) {
@@ -180,13 +213,16 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void stream_gemm_kernel(TileA
     floatx16 acc[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) acc[i] = floatx16{};
-    for (int s = 0; s < NST - 1 && s < nss; ++s) issue_stage(s);
+    for (int s = pre; s < NST - 1 && s < nss; ++s) issue_stage(cur, s, (gbase + s) % NST);
     for (int s = 0; s < nss; ++s) {
-      wait_after((nss - 1 < s + NST - 2 ? nss - 1 : s + NST - 2) - s);
+      // stages issued after s: this tile's, then (cross) the next tile's
+      wait_after(cross ? NST - 2 : (nss - 1 < s + NST - 2 ? nss - 1 : s + NST - 2) - s);
       wait_lgkmcnt0();
       block_barrier();
-      if (s + NST - 1 < nss) issue_stage(s + NST - 1);
-      const uint32_t so = (uint32_t)(s % NST) * STAGE;
+      const int sn = s + NST - 1;
+      if (sn < nss) issue_stage(cur, sn, (gbase + sn) % NST);
+      else if (cross) issue_stage(nxt, sn - nss, (gbase + sn) % NST);
+      const uint32_t so = (uint32_t)((gbase + s) % NST) * STAGE;
       auto step = [&](auto t_c, bool tail) {
         const int t = kh * KSTEP + decltype(t_c)::value;
         const int c = 2 * t + lgrp;
@@ -216,8 +252,11 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void stream_gemm_kernel(TileA
     // (the top of the ring) and the first adds them, always in that order.
     wait_lgkmcnt0();
     block_barrier();
+    // the buffer of this tile's last stage: read by now, and the one buffer no
+    // load of the next tile is filling
+    const uint32_t ebuf = lds0 + (uint32_t)(((gbase + nss + NST - 1) % NST) * STAGE);
     if constexpr (KS > 1) {
-      const uint32_t pb = lds0 + (uint32_t)(RING - PART);
+      const uint32_t pb = ebuf;
       if (kh == 1) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -238,6 +277,9 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void stream_gemm_kernel(TileA
             for (int e = 0; e < 4; ++e) acc[i][4 * q + e] += v[e];
           }
       }
+      // the strips below reuse the partial sums' bytes
+      wait_lgkmcnt0();
+      block_barrier();
     }
     if (glu) {
       const EpiOut eo{p.C, p.ldc, M, glu, p.bias, p.act, p.counts, p.flags};
@@ -246,17 +288,17 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void stream_gemm_kernel(TileA
         if (kh == 0) {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            lds_store_f4(lds0 + (uint32_t)(lrow * OPG + (32 * cb + 8 * q + 4 * lgrp) * 4),
+            lds_store_f4(ebuf + (uint32_t)(lrow * OPG + (32 * cb + 8 * q + 4 * lgrp) * 4),
                          floatx4{acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]});
         }
         wait_lgkmcnt0();
         block_barrier();
-        store_staged_glu<OUT_BF16, DEBUG>(lds0, OPG, BR, BN / 2, BR, 0, m0 + 32 * i, n0, tid, NT, eo);
+        store_staged_glu<OUT_BF16, DEBUG>(ebuf, OPG, BR, BN / 2, BR, 0, m0 + 32 * i, n0, tid, NT, eo);
         wait_lgkmcnt0();
         block_barrier();
       }
     } else if (kh == 0) {
-      const uint32_t stf = lds0 + (uint32_t)(cb * 32 * OPF);
+      const uint32_t stf = ebuf + (uint32_t)(cb * 32 * OPF);
       const EpiOut eo{p.C, p.ldc, M, N, p.bias, p.act, p.counts, p.flags};
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -272,6 +314,8 @@ __global__ __launch_bounds__(BN / 32 * KS * 64, 1) void stream_gemm_kernel(TileA
     }
     wait_lgkmcnt0();
     block_barrier();
+    gbase = (gbase + nss) % NST;
+    pre = cross ? NST - 1 : 0;
   }
 }
 
