@@ -71,9 +71,39 @@ __device__ __forceinline__ int swzB(int c, int r) {
   return c;
 }
 
-// 16 x 16 x 32 step of a C block held transposed (see above).
-__device__ __forceinline__ floatx4 mma16(const bf16x8& a_frag, const bf16x8& b_frag, const floatx4& acc) {
-  return mfma16(b_frag, a_frag, acc);
+// 16 x 16 x 32 step of a C block held transposed (see above), accumulated in
+// place. With one wave per SIMD the 128 x 128 wave tiles hold 256
+// accumulator values, the whole accumulation-register file: there the
+// compiler's own form of the instruction (destination distinct from the
+// accumulator input) makes it move every accumulator every few MFMAs, so the
+// instruction is written out with its accumulator tied in place. The compiler
+// does not see an MFMA in it, so the kernel keeps the instruction's hazards
+// itself: a vector ALU write of an operand (the accumulators' zeroing, a
+// register copy) needs two wait states before the MFMA reads it, issued by
+// tied_entry() at the head of every K loop iteration (the fragments inside an
+// iteration come straight from LDS reads; a check of the built code's MFMAs
+// against the vector ALU writes before them guards this), and settle_tied()
+// waits out the result latency before the accumulators are read.
+template <bool TIED>
+__device__ __forceinline__ void mma16(floatx4& acc, const bf16x8& a_frag, const bf16x8& b_frag) {
+  if constexpr (TIED)
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(b_frag), "v"(a_frag));
+  else
+    acc = mfma16(b_frag, a_frag, acc);
+}
+__device__ __forceinline__ void tied_entry() { asm volatile("s_nop 1"); }
+
+// Before the accumulators of written-out MFMAs (mma16<true>) are read: wait
+// out the last MFMA's result latency (32 wait states, more than any MFMA form
+// needs before another instruction reads its result), and tie every
+// accumulator to a point after the wait so that no read moves above it.
+template <int FM, int FN>
+__device__ __forceinline__ void settle_tied(floatx4 (&acc)[FM][FN]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) asm volatile("" : "+a"(acc[i][j]));
 }
 
 template <int BM, int BN, int WM, int WN, int NST, bool BCOL, bool OUT_BF16, bool DEBUG>
@@ -91,6 +121,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile16_gemm_kernel(TileArgs p
   static_assert(WTM % (32 * FQ) == 0 && WTN % 16 == 0,
                 "wave tile: an even number of steps of FQ 16-row blocks, whole 16-column blocks");
   static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
+  constexpr bool TIED = NW == 4;  // accumulators tied in place (see mma16)
   constexpr int BK = kTileBK;
   constexpr int A_BYTES = BM * BK * 2;  // per stage
   constexpr int B_BYTES = BN * BK * 2;
@@ -125,6 +156,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile16_gemm_kernel(TileArgs p
     }
     int32_t tm, tn;
     tile_of(p.map, wg, tm, tn);
+    // With the accumulators tied, the compiler's count of outstanding vector
+    // memory operations carries the last tile's epilogue into the K loop and
+    // it drains every load at the loop's head; settled here, once per tile,
+    // the loop keeps only its own waits.
+    if constexpr (TIED) wait_vmcnt<0>();
     const int M = p.M, N = p.N, K = p.K;
     const int64_t lda = p.lda, ldb = p.ldb;
     const int glu = p.glu_half;
@@ -389,6 +425,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile16_gemm_kernel(TileArgs p
       i32x4 rsAn = make_rsrc(a_panel + (kStages - 2) * a_step, a_bytes - (kStages - 2) * a_step);
       i32x4 rsBn = make_rsrc(b_panel + (kStages - 2) * b_step, b_bytes - (kStages - 2) * b_step);
       for (; s + kStages <= n_steady; s += kStages) {
+        if constexpr (TIED) tied_entry();
         static_for<0, kStages>([&](auto st_c) {
           constexpr int ST = decltype(st_c)::value;         // stage of slab s + ST
           constexpr int STN = (ST + 1) % kStages;            // stage of slab s + ST + 1
@@ -408,7 +445,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile16_gemm_kernel(TileArgs p
             static_for<0, NM>([&](auto k_c) {
               constexpr int k = decltype(k_c)::value;
               constexpr int b = blk(Q, k), i = b / FN, j = b % FN;
-              acc[Q * FQ + i][j] = mma16(aS[Q & 1][i], bq[j], acc[Q * FQ + i][j]);
+              mma16<TIED>(acc[Q * FQ + i][j], aS[Q & 1][i], bq[j]);
               if constexpr (!LAST) {
                 if constexpr ((k * FQ) % NM == 0)
                   aS[(Q + 1) & 1][k * FQ / NM] =
@@ -430,12 +467,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile16_gemm_kernel(TileArgs p
                 });
               }
             });
-            static_for<0, NM>([&](auto k_c) {
-              constexpr int k = decltype(k_c)::value;
-              constexpr int nr = nreads(Q, k);
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
-            });
+            // (the written-out MFMAs keep their place among the memory
+            // instructions by themselves)
+            if constexpr (!TIED) {
+              static_for<0, NM>([&](auto k_c) {
+                constexpr int k = decltype(k_c)::value;
+                constexpr int nr = nreads(Q, k);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
+              });
+            }
           });
         });
       }
@@ -457,6 +498,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile16_gemm_kernel(TileArgs p
     // ---- remaining slabs (and a K tail): the general loop, same steps with
     // run-time stage indices and whole-slab loads
     for (int s = s0; s < nk; ++s) {
+      if constexpr (TIED) tied_entry();
       const int st = s % kStages, stn = (s + 1) % kStages;
       static_for<0, NSTEP>([&](auto q_c) {
         constexpr int Q = decltype(q_c)::value;
@@ -479,7 +521,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile16_gemm_kernel(TileArgs p
         static_for<0, NM>([&](auto k_c) {
           constexpr int k = decltype(k_c)::value;
           constexpr int b = blk(Q, k), i = b / FN, j = b % FN;
-          acc[Q * FQ + i][j] = mma16(aS[Q & 1][i], bq[j], acc[Q * FQ + i][j]);
+          mma16<TIED>(acc[Q * FQ + i][j], aS[Q & 1][i], bq[j]);
           if constexpr (!LAST) {
             if constexpr ((k * FQ) % NM == 0)
               aS[(Q + 1) & 1][k * FQ / NM] = readA_rt(st, (Q + 1) * FQ + k * FQ / NM);
@@ -499,6 +541,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile16_gemm_kernel(TileArgs p
     // strips of its sub-tile (one A block row at a time) and stores them as
     // 16-byte row chunks. Lane l holds row l16 of block row i, columns
     // 16 j + 4 lg .. + 3.
+    if constexpr (TIED) settle_tied(acc);
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
     constexpr int RING = kStages * STAGE;
     constexpr int SH = 16;

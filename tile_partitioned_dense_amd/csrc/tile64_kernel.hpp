@@ -44,6 +44,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
   constexpr int RB = BCOL ? 1 : 2;  // LDS instructions per B fragment
   static_assert(WTM % (16 * FQ) == 0 && WTN % 16 == 0, "wave tile: whole phases of 16-row blocks");
   static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
+  constexpr bool TIED = NW == 4;  // accumulators tied in place (see mma16)
+  // one wave per SIMD (no other wave fills the MFMA pipe while this one waits):
+  // the steady loop takes its barrier TL phases before a slab's end and reads
+  // every fragment TL phases ahead; T1 quarters of a slab's loads go out in
+  // the TL phases after the barrier two slabs ahead, the rest spread over the
+  // next slab's first DW phases
+  constexpr int TL = 1, DW = 3, T1 = 2;
+  static_assert(!TIED || (TL >= 1 && TL <= NSTEP && TL <= 3 && DW <= NSTEP && T1 >= 1 && T1 <= 4),
+                "tied schedule");
   constexpr int BK = 64;
   constexpr int A_BYTES = BM * BK * 2;  // per stage
   constexpr int B_BYTES = BN * BK * 2;
@@ -77,6 +86,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
     }
     int32_t tm, tn;
     tile_of(p.map, wg, tm, tn);
+    // (see tile16_kernel.hpp: the K loop keeps only its own waits)
+    if constexpr (TIED) wait_vmcnt<0>();
     const int M = p.M, N = p.N, K = p.K;
     const int64_t lda = p.lda, ldb = p.ldb;
     const int glu = p.glu_half;
@@ -247,17 +258,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
     const bool steady_on = nk_full >= 3;
     constexpr int NDMA_MAX = A_PER + B_MAX;
     const int ndma = A_PER + b_cnt;
-    const int nh1 = (ndma + 1) / 2;  // units issued in a slab's last phase for slab + 2
+    // units issued after a slab's barrier for slab + 2
+    const int nh1 = TIED ? (ndma * T1 + 3) / 4 : (ndma + 1) / 2;
 
     // ---- prologue
     if (nk > 0) {
       issue_slab(0);
       if (steady_on) {
         issue_units(1, 0, nh1);
+        // slab 0 has landed once at most slab 1's nh1 loads remain
+        constexpr int NMAX = A_PER + B_MAX, NMIN = A_PER + B_MIN;
         if (B_MAX != B_MIN && b_cnt == B_MAX)
-          wait_vmcnt<(A_PER + B_MAX + 1) / 2>();
+          wait_vmcnt<TIED ? (NMAX * T1 + 3) / 4 : (NMAX + 1) / 2>();
         else
-          wait_vmcnt<(A_PER + B_MIN + 1) / 2>();
+          wait_vmcnt<TIED ? (NMIN * T1 + 3) / 4 : (NMIN + 1) / 2>();
       } else {
         wait_vmcnt<0>();
       }
@@ -309,7 +323,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
             static_for<0, NM>([&](auto k_c) {
               constexpr int k = decltype(k_c)::value;
               constexpr int b = blk(Q, k), i = b / FN, j = b % FN;
-              acc[Q * FQ + i][j] = mma16(aS[P & 1][i], bq[j], acc[Q * FQ + i][j]);
+              mma16<false>(acc[Q * FQ + i][j], aS[P & 1][i], bq[j]);
               if constexpr (Q != NSTEP - 1) {
                 // next phase's A fragments, same k half
                 if constexpr ((k * FQ) % NM == 0)
@@ -354,8 +368,124 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
       }
       return s;
     };
+    // The steady loop of the one-wave-per-SIMD tiles (the same slabs, stages
+    // and loads, the same ownership; a different order):
+    //   phase P of slab s (P = 0 .. NPH-1): its FQ x FN blocks column by
+    //     column, reading the A fragments of the phase TL later (a ring of four
+    //     phase sets), in phases NSTEP-TL .. NSTEP-1 the second k half's B
+    //     fragments (B has one register set per k half), and from the barrier
+    //     on the next slab's first-half B fragments;
+    //   before phase NPH-TL: wait for every load of slab s + 1, barrier (no
+    //     wave reads slab s's stage any more: its last fragments were read
+    //     TL phases ahead);
+    //   loads of slab s + 2 into slab s's stage: the first NH1 in the TL
+    //     phases after the barrier, the rest in slab s + 1's first DW phases.
+    auto steady_tied = [&](auto bc_c) -> int {
+      constexpr int BC = decltype(bc_c)::value;
+      constexpr int NDMA = A_PER + BC;
+      constexpr int NH1 = (NDMA * T1 + 3) / 4;  // of slab s + 2, after slab s's barrier
+      constexpr int NH2 = NDMA - NH1;           // of slab s + 1, in slab s's first DW phases
+      constexpr int PB = NPH - TL;              // the barrier comes before phase PB
+      constexpr int NBR = FN / TL;              // B reads per phase (the last phase takes the rest)
+      if (!steady_on) return 0;
+      auto unit = [&](auto stg_c, auto u_c, const i32x4& rA_, const i32x4& rB_) {
+        constexpr int STG = decltype(stg_c)::value, U = decltype(u_c)::value;
+        if constexpr (U < A_PER)
+          dma16_off<STG * STAGE + 1024 * NW * U>(ldsw, rA_, voA[U]);
+        else
+          dma16_off<STG * STAGE + A_BYTES + 1024 * NW * (U - A_PER)>(ldsw, rB_, voB[U - A_PER]);
+      };
+      bf16x8 aR[4][FQ];  // A fragments of phase g in set g % 4
+      bf16x8 bR[2][FN];  // B fragments of k half h
+      // slab 0: the A fragments of its first TL phases, its first-half B
+      static_for<0, TL>([&](auto p_c) {
+        constexpr int P = decltype(p_c)::value;
+        static_for<0, FQ>([&](auto f_c) {
+          constexpr int F = decltype(f_c)::value;
+          aR[P][F] = readA(0, P / NSTEP, (P % NSTEP) * FQ + F);
+        });
+      });
+      static_for<0, FN>([&](auto j_c) {
+        constexpr int J = decltype(j_c)::value;
+        bR[0][J] = readB(0, 0, J);
+      });
+      i32x4 rsA1 = make_rsrc(a_panel + 1 * a_step, a_bytes - 1 * a_step);  // slab s + 1
+      i32x4 rsB1 = make_rsrc(b_panel + 1 * b_step, b_bytes - 1 * b_step);
+      i32x4 rsA2 = make_rsrc(a_panel + 2 * a_step, a_bytes - 2 * a_step);  // slab s + 2
+      i32x4 rsB2 = make_rsrc(b_panel + 2 * b_step, b_bytes - 2 * b_step);
+      int s = 0;
+      for (; s + 4 <= nk_full; s += 2) {
+        tied_entry();
+        static_for<0, 2>([&](auto st_c) {
+          constexpr int ST = decltype(st_c)::value;  // stage of this slab
+          static_for<0, NPH>([&](auto p_c) {
+            constexpr int P = decltype(p_c)::value;
+            constexpr int G = ST * NPH + P;  // phase within the two slabs
+            constexpr int H = P / NSTEP, Q = P % NSTEP;
+            if constexpr (P == PB) {
+              wait_vmcnt<0>();
+              wait_lgkmcnt0();
+              block_barrier();
+            }
+            // this phase's reads, in order: A of phase P + TL, then its B share
+            constexpr int PA = P + TL;  // phase whose A fragments are read
+            constexpr bool B1 = P >= NSTEP - TL && P < NSTEP;  // second half's B
+            constexpr bool B0 = P >= PB;                       // next slab's first-half B
+            constexpr int BI = B1 ? P - (NSTEP - TL) : B0 ? P - PB : 0;
+            constexpr int BLO = BI * NBR, BHI = (BI == TL - 1) ? FN : BLO + NBR;
+            constexpr int NRD = FQ + ((B1 || B0) ? BHI - BLO : 0);
+            static_for<0, NM>([&](auto k_c) {
+              constexpr int k = decltype(k_c)::value;
+              constexpr int i = k % FQ, j = k / FQ;
+              mma16<true>(acc[Q * FQ + i][j], aR[G % 4][i], bR[H][j]);
+              static_for<0, NRD>([&](auto r_c) {
+                constexpr int r = decltype(r_c)::value;
+                if constexpr (((2 * r + 1) * NM) / (2 * NRD) == k) {
+                  if constexpr (r < FQ) {
+                    if constexpr (PA < NPH)
+                      aR[(G + TL) % 4][r] = readA(ST, PA / NSTEP, (PA % NSTEP) * FQ + r);
+                    else
+                      aR[(G + TL) % 4][r] = readA(ST ^ 1, (PA - NPH) / NSTEP, ((PA - NPH) % NSTEP) * FQ + r);
+                  } else if constexpr (B1) {
+                    bR[1][BLO + r - FQ] = readB(ST, 1, BLO + r - FQ);
+                  } else {
+                    bR[0][BLO + r - FQ] = readB(ST ^ 1, 0, BLO + r - FQ);
+                  }
+                }
+              });
+              if constexpr (P < DW) {
+                static_for<0, NH2>([&](auto t_c) {
+                  constexpr int t = decltype(t_c)::value;
+                  if constexpr (((2 * t + 1) * DW * NM) / (2 * NH2) == P * NM + k)
+                    unit(std::integral_constant<int, ST ^ 1>{}, std::integral_constant<int, NH1 + t>{}, rsA1, rsB1);
+                });
+              }
+              if constexpr (P >= PB) {
+                static_for<0, NH1>([&](auto t_c) {
+                  constexpr int t = decltype(t_c)::value;
+                  if constexpr (((2 * t + 1) * TL * NM) / (2 * NH1) == (P - PB) * NM + k)
+                    unit(std::integral_constant<int, ST>{}, std::integral_constant<int, t>{}, rsA2, rsB2);
+                });
+              }
+            });
+          });
+          advance_rsrc(rsA1, (uint32_t)a_step);
+          advance_rsrc(rsB1, (uint32_t)b_step);
+          advance_rsrc(rsA2, (uint32_t)a_step);
+          advance_rsrc(rsB2, (uint32_t)b_step);
+        });
+      }
+      return s;
+    };
     int s0 = 0;
-    if constexpr (B_MAX != B_MIN) {
+    if constexpr (TIED) {
+      if constexpr (B_MAX != B_MIN) {
+        if (b_cnt == B_MAX) s0 = steady_tied(std::integral_constant<int, B_MAX>{});
+        else s0 = steady_tied(std::integral_constant<int, B_MIN>{});
+      } else {
+        s0 = steady_tied(std::integral_constant<int, B_MIN>{});
+      }
+    } else if constexpr (B_MAX != B_MIN) {
       if (b_cnt == B_MAX) s0 = steady(std::integral_constant<int, B_MAX>{});
       else s0 = steady(std::integral_constant<int, B_MIN>{});
     } else {
@@ -372,6 +502,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
       else issue_slab(s0 + 1);
     }
     for (int s = s0; s < nk; ++s) {
+      if constexpr (TIED) tied_entry();
       const int st = s & 1;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -387,7 +518,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
 #pragma unroll
           for (int i = 0; i < FQ; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) acc[q * FQ + i][j] = mma16(aS[0][i], bq[j], acc[q * FQ + i][j]);
+            for (int j = 0; j < FN; ++j) mma16<TIED>(acc[q * FQ + i][j], aS[0][i], bq[j]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -399,6 +530,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
 
     // ---- epilogue (as in tile16_kernel.hpp): 16-row strips staged in the
     // now idle stages, stored as 16-byte row chunks, each element once
+    if constexpr (TIED) settle_tied(acc);
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
     constexpr int RING = 2 * STAGE;
     constexpr int SH = 16;
