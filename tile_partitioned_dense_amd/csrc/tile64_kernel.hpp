@@ -46,12 +46,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
   static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
   constexpr bool TIED = NW == 4;  // accumulators tied in place (see mma16)
   // one wave per SIMD (no other wave fills the MFMA pipe while this one waits):
-  // the steady loop takes its barrier TL phases before a slab's end and reads
-  // every fragment TL phases ahead; T1 quarters of a slab's loads go out in
-  // the TL phases after the barrier two slabs ahead, the rest spread over the
-  // next slab's first DW phases
+  // the steady loop takes its end barrier TL phases before a slab's end and
+  // reads every fragment TL phases ahead; a slab's B loads go out in the
+  // second k half two slabs ahead, T1 quarters of its A loads after that
+  // slab's end barrier and the rest spread over the next slab's first DW
+  // phases
   constexpr int TL = 1, DW = 3, T1 = 2;
-  static_assert(!TIED || (TL >= 1 && TL <= NSTEP && TL <= 3 && DW <= NSTEP && T1 >= 1 && T1 <= 4),
+  static_assert(!TIED || (TL >= 1 && TL <= NSTEP && TL <= 3 && DW < NPH - TL && T1 >= 1 && T1 <= 4),
                 "tied schedule");
   constexpr int BK = 64;
   constexpr int A_BYTES = BM * BK * 2;  // per stage
@@ -182,18 +183,28 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
     };
     // DMA units [lo, hi) of full slab s (units 0 .. A_PER-1: this wave's A
     // loads, then its b_cnt B loads).
+    // (one wave per SIMD: its b_cnt B loads first, then its A loads)
     auto issue_units = [&](int s, int lo, int hi) {
       const uint32_t la = lds0 + (s & 1) * STAGE;
       const uint32_t lb = la + A_BYTES;
       const i32x4 rsA = make_rsrc(a_panel + s * a_step, a_bytes - s * a_step);
       const i32x4 rsB = make_rsrc(b_panel + s * b_step, b_bytes - s * b_step);
+      if constexpr (TIED) {
 #pragma unroll
-      for (int t = 0; t < A_PER; ++t)
-        if (t >= lo && t < hi) dma16(la + 1024 * (wave + NW * t), rsA, voA[t], 0u);
+        for (int t = 0; t < B_MAX; ++t)
+          if (t < b_cnt && t >= lo && t < hi) dma16(lb + 1024 * (wave + NW * t), rsB, voB[t], 0u);
 #pragma unroll
-      for (int t = 0; t < B_MAX; ++t)
-        if (t < b_cnt && A_PER + t >= lo && A_PER + t < hi)
-          dma16(lb + 1024 * (wave + NW * t), rsB, voB[t], 0u);
+        for (int t = 0; t < A_PER; ++t)
+          if (b_cnt + t >= lo && b_cnt + t < hi) dma16(la + 1024 * (wave + NW * t), rsA, voA[t], 0u);
+      } else {
+#pragma unroll
+        for (int t = 0; t < A_PER; ++t)
+          if (t >= lo && t < hi) dma16(la + 1024 * (wave + NW * t), rsA, voA[t], 0u);
+#pragma unroll
+        for (int t = 0; t < B_MAX; ++t)
+          if (t < b_cnt && A_PER + t >= lo && A_PER + t < hi)
+            dma16(lb + 1024 * (wave + NW * t), rsB, voB[t], 0u);
+      }
     };
 
     floatx4 acc[FM][FN];
@@ -259,7 +270,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
     constexpr int NDMA_MAX = A_PER + B_MAX;
     const int ndma = A_PER + b_cnt;
     // units issued after a slab's barrier for slab + 2
-    const int nh1 = TIED ? (ndma * T1 + 3) / 4 : (ndma + 1) / 2;
+    constexpr int NA1 = (A_PER * T1 + 3) / 4;  // one wave per SIMD: A loads after the end barrier
+    const int nh1 = TIED ? b_cnt + NA1 : (ndma + 1) / 2;
 
     // ---- prologue
     if (nk > 0) {
@@ -269,9 +281,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
         // slab 0 has landed once at most slab 1's nh1 loads remain
         constexpr int NMAX = A_PER + B_MAX, NMIN = A_PER + B_MIN;
         if (B_MAX != B_MIN && b_cnt == B_MAX)
-          wait_vmcnt<TIED ? (NMAX * T1 + 3) / 4 : (NMAX + 1) / 2>();
+          wait_vmcnt<TIED ? B_MAX + NA1 : (NMAX + 1) / 2>();
         else
-          wait_vmcnt<TIED ? (NMIN * T1 + 3) / 4 : (NMIN + 1) / 2>();
+          wait_vmcnt<TIED ? B_MIN + NA1 : (NMIN + 1) / 2>();
       } else {
         wait_vmcnt<0>();
       }
@@ -375,17 +387,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
     //     phase sets), in phases NSTEP-TL .. NSTEP-1 the second k half's B
     //     fragments (B has one register set per k half), and from the barrier
     //     on the next slab's first-half B fragments;
+    //   before phase NSTEP (the second k half): barrier, after which no wave
+    //     reads slab s's B any more (its second-half fragments were read in
+    //     the phases before), so slab s + 2's B loads go out, spread over
+    //     phases NSTEP .. NPH-TL-1;
     //   before phase NPH-TL: wait for every load of slab s + 1, barrier (no
     //     wave reads slab s's stage any more: its last fragments were read
-    //     TL phases ahead);
-    //   loads of slab s + 2 into slab s's stage: the first NH1 in the TL
-    //     phases after the barrier, the rest in slab s + 1's first DW phases.
+    //     TL phases ahead); then slab s + 2's first NA1 A loads, the rest
+    //     spread over slab s + 1's first DW phases.
     auto steady_tied = [&](auto bc_c) -> int {
       constexpr int BC = decltype(bc_c)::value;
-      constexpr int NDMA = A_PER + BC;
-      constexpr int NH1 = (NDMA * T1 + 3) / 4;  // of slab s + 2, after slab s's barrier
-      constexpr int NH2 = NDMA - NH1;           // of slab s + 1, in slab s's first DW phases
-      constexpr int PB = NPH - TL;              // the barrier comes before phase PB
+      constexpr int NA2 = A_PER - NA1;          // A loads of slab s + 1 in slab s's first DW phases
+      constexpr int PB = NPH - TL;              // the end barrier comes before phase PB
+      constexpr int BW = PB - NSTEP;            // phases the B loads spread over
+      static_assert(BW >= 1 && DW <= NSTEP, "tied load windows");
       constexpr int NBR = FN / TL;              // B reads per phase (the last phase takes the rest)
       if (!steady_on) return 0;
       auto unit = [&](auto stg_c, auto u_c, const i32x4& rA_, const i32x4& rB_) {
@@ -422,8 +437,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
             constexpr int P = decltype(p_c)::value;
             constexpr int G = ST * NPH + P;  // phase within the two slabs
             constexpr int H = P / NSTEP, Q = P % NSTEP;
+            if constexpr (P == NSTEP) {
+              wait_lgkmcnt0();
+              block_barrier();
+            }
             if constexpr (P == PB) {
-              wait_vmcnt<0>();
+              wait_vmcnt<BC>();  // all but slab s + 2's B loads
               wait_lgkmcnt0();
               block_barrier();
             }
@@ -453,17 +472,24 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
                   }
                 }
               });
-              if constexpr (P < DW) {
-                static_for<0, NH2>([&](auto t_c) {
+              if constexpr (P < DW) {  // A of slab s + 1, the rest
+                static_for<0, NA2>([&](auto t_c) {
                   constexpr int t = decltype(t_c)::value;
-                  if constexpr (((2 * t + 1) * DW * NM) / (2 * NH2) == P * NM + k)
-                    unit(std::integral_constant<int, ST ^ 1>{}, std::integral_constant<int, NH1 + t>{}, rsA1, rsB1);
+                  if constexpr (((2 * t + 1) * DW * NM) / (2 * NA2) == P * NM + k)
+                    unit(std::integral_constant<int, ST ^ 1>{}, std::integral_constant<int, NA1 + t>{}, rsA1, rsB1);
                 });
               }
-              if constexpr (P >= PB) {
-                static_for<0, NH1>([&](auto t_c) {
+              if constexpr (P >= NSTEP && P < PB) {  // B of slab s + 2
+                static_for<0, BC>([&](auto t_c) {
                   constexpr int t = decltype(t_c)::value;
-                  if constexpr (((2 * t + 1) * TL * NM) / (2 * NH1) == (P - PB) * NM + k)
+                  if constexpr (((2 * t + 1) * BW * NM) / (2 * BC) == (P - NSTEP) * NM + k)
+                    unit(std::integral_constant<int, ST>{}, std::integral_constant<int, A_PER + t>{}, rsA2, rsB2);
+                });
+              }
+              if constexpr (P >= PB) {  // A of slab s + 2, the first NA1
+                static_for<0, NA1>([&](auto t_c) {
+                  constexpr int t = decltype(t_c)::value;
+                  if constexpr (((2 * t + 1) * TL * NM) / (2 * NA1) == (P - PB) * NM + k)
                     unit(std::integral_constant<int, ST>{}, std::integral_constant<int, t>{}, rsA2, rsB2);
                 });
               }
