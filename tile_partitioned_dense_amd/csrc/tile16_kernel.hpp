@@ -95,15 +95,28 @@ __device__ __forceinline__ void tied_entry() { asm volatile("s_nop 1"); }
 
 // Before the accumulators of written-out MFMAs (mma16<true>) are read: wait
 // out the last MFMA's result latency (32 wait states, more than any MFMA form
-// needs before another instruction reads its result), and tie every
-// accumulator to a point after the wait so that no read moves above it.
+// needs before another instruction reads its result), then tie accumulators
+// to a point after the wait so that no read moves above it: all of them at
+// once (settle_tied(acc)), or a block row right before the epilogue takes it
+// (pin_row), which also keeps the reads of later rows from moving ahead --
+// reading all 256 values at once needs more registers than a wave has, and
+// the compiler then spills. Which of the two a kernel uses is fixed by what
+// its build passes in the hazard check: given the freedom of row pins, the
+// 32-deep 256 x 256 kernel's allocator moved accumulators through vector
+// registers inside its K loop.
+__device__ __forceinline__ void settle_tied() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"); }
 template <int FM, int FN>
 __device__ __forceinline__ void settle_tied(floatx4 (&acc)[FM][FN]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+  settle_tied();
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
+template <int FN>
+__device__ __forceinline__ void pin_row(floatx4 (&row)[FN]) {
+#pragma unroll
+  for (int j = 0; j < FN; ++j) asm volatile("" : "+a"(row[j]));
 }
 
 template <int BM, int BN, int WM, int WN, int NST, bool BCOL, bool OUT_BF16, bool DEBUG>

@@ -556,7 +556,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
 
     // ---- epilogue (as in tile16_kernel.hpp): 16-row strips staged in the
     // now idle stages, stored as 16-byte row chunks, each element once
-    if constexpr (TIED) settle_tied(acc);
+    if constexpr (TIED) settle_tied();
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
     constexpr int RING = 2 * STAGE;
     constexpr int SH = 16;
@@ -572,6 +572,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
       const EpiOut eo{p.C, p.ldc, M, glu, p.bias, p.act, p.counts, p.flags};
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
+        if constexpr (TIED) pin_row(acc[i]);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           lds_store_f4(lds0 + (uint32_t)((wm * SH + l16) * OPG + (wn * WTN + 16 * j + 4 * lg) * 4),
@@ -591,6 +592,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
       const EpiOut eo{p.C, p.ldc, M, N, p.bias, p.act, p.counts, p.flags};
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
+        if constexpr (TIED) pin_row(acc[i]);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           lds_store_f4(stf + (uint32_t)(l16 * OPF + (16 * j + 4 * lg) * 4), acc[i][j]);
@@ -607,6 +609,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void tile64_gemm_kernel(TileArgs p
     const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      if constexpr (TIED) pin_row(acc[i]);
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const uint32_t a = stg + (uint32_t)(l16 * OPITCH + (16 * j + 4 * lg) * ESZ);
