@@ -98,17 +98,17 @@ constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
     // third less from LDS; their 256 accumulators fill the accumulation
     // registers, where the MFMAs are written out with the accumulator tied in
     // place (tile16_kernel.hpp, mma16)
-    {256, 256, 2, 2, 4, 1.00f, 1, 0.92f, 1, 0, 16},  // 22: 4 waves of 128x128
+    {256, 256, 2, 2, 4, 1.05f, 1, 0.94f, 1, 0, 16},  // 22: 4 waves of 128x128
     {256, 160, 2, 2, 4, 0.84f, 1, 0.0f, 1, 0, 16},   // 23: 4 waves of 128x80
     // 24-25: 16x16x32 blocks with 64-deep slabs (two stages of 128-byte rows;
     // each load instruction moves whole 128-byte lines)
     {256, 256, 2, 4, 2, 0.01f, 1, 0.0f, 1, 0, 16, 64},  // 24: 8 waves of 128x64
     {256, 160, 4, 2, 2, 0.01f, 1, 0.0f, 1, 0, 16, 64},  // 25: 8 waves of 64x80
     // 26-27: one wave per SIMD, 64-deep slabs, accumulators tied in place
-    // (its own K-loop order, tile64_kernel.hpp); with a single tile per CU
-    // the eight-wave kernel hides the K loop's start and end better
-    {256, 256, 2, 2, 2, 1.12f, 1, 0.99f, 1, 0, 16, 64},  // 26: 4 waves of 128x128
-    {256, 160, 2, 2, 2, 0.86f, 1, 0.0f, 1, 0, 16, 64},   // 27: 4 waves of 128x80
+    // (its own K-loop order, tile64_kernel.hpp); with a single 256 x 256 tile
+    // per CU level with configuration 17, which keeps those shapes
+    {256, 256, 2, 2, 2, 1.19f, 1, 1.08f, 1, 0, 16, 64},  // 26: 4 waves of 128x128
+    {256, 160, 2, 2, 2, 1.04f, 1, 1.05f, 1, 0, 16, 64},  // 27: 4 waves of 128x80
 };
 constexpr int kStreamConfig = 14;      // the planner's stream configuration up to 32 rows,
 constexpr int kStreamConfig64 = 15;    // from 33 to 64 rows,
