@@ -218,8 +218,10 @@ def test_check_mx(kw, want):
 
 
 def test_mx_plan():
+    """The MX MLP shard: 256 x 256 tiles of the 128-byte-row kernel
+    (configuration 6, two slabs of 64 bytes per stage row)."""
     p = tg.tile_gemm_plan_mx(8192, 7168, 8192)
-    assert p.variant == tg.VARIANT_MX and p.bm == 256 and p.bn == 256 and p.bk == 64
+    assert p.variant == tg.VARIANT_MX and p.config == 6 and p.bm == 256 and p.bn == 256 and p.bk == 128
     assert p.tiles == 32 * 28 and p.grid == 224
 
 

@@ -1,12 +1,14 @@
 """Hazard check of the built kernels whose MFMAs are written out with tied
-accumulators (the one-wave-per-SIMD tile kernels, mma16<true>).
+accumulators (the one-wave-per-SIMD tile kernels, mma16<true>, and the
+128-byte-row MX kernel, mma_mx_tied).
 
 The compiler inserts the wait states an MFMA needs only around MFMAs it
 generated itself; around a written-out one the kernel keeps them: a vector
 ALU write of any MFMA operand needs two wait states before the MFMA issues,
 and an MFMA's result must not be read or overwritten by another kind of
 instruction for the instruction's result latency (checked against 19 wait
-states, more than any 16x16 form needs). This test disassembles the device
+states for the 16x16 forms and 24 for the 16-pass 32x32 ones, more than
+either needs). This test disassembles the device
 code of the in-tree libtile_gemm.so (ROCm's own llvm tools on code built here)
 and walks back from every MFMA of those kernels, across branches, counting
 wait states (one per instruction, N + 1 for s_nop N).
@@ -22,10 +24,10 @@ import pytest
 from tile_partitioned_dense_amd import binding
 
 LLVM = "/opt/rocm/llvm/bin"
-TIED_KERNEL = re.compile(r"^_ZN2tg1[68]tile(16|64)_gemm_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E")
+TIED_KERNEL = re.compile(r"^_ZN2tg(?:1[68]tile(16|64)|17mx128)_gemm_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E")
 REG = re.compile(r"\b([va])(?:\[(\d+):(\d+)\]|(\d+)(?!\d))")
 VALU_WRITE_BEFORE_MFMA = 2
-MFMA_RESULT_LATENCY = 19
+MFMA_RESULT_LATENCY = {"16x16": 19, "32x32": 24}
 
 
 def _tool(name):
@@ -172,13 +174,13 @@ def _check_function(name, items):
             continue
 
         def res_check(p, dist, regs=regs, i=i):
-            if p.is_mfma:
+            if p.is_mfma and dist < MFMA_RESULT_LATENCY["32x32" if "32x32" in p.op else "16x16"]:
                 hit = _regs(p.operands()[0]) & regs
                 if hit:
                     problems.append(f"{name}: '{ins.op} {ins.ops}' touches the result of "
                                     f"'{p.op} {p.ops}' {dist} wait states after it")
 
-        walk_back(i, MFMA_RESULT_LATENCY, res_check, set())
+        walk_back(i, max(MFMA_RESULT_LATENCY.values()), res_check, set())
     return problems
 
 
@@ -201,9 +203,10 @@ def tied_functions(tmp_path_factory):
 
 
 def test_tied_kernels_are_present(tied_functions):
-    # the one-wave-per-SIMD configurations of both tile kernels, every variant
+    # the one-wave-per-SIMD configurations of both tile kernels and the
+    # 128-byte-row MX kernel, every variant
     bits = {n.split("kernel")[0] for n in tied_functions}
-    assert any("tile16" in b for b in bits) and any("tile64" in b for b in bits), sorted(tied_functions)
+    assert all(any(k in b for b in bits) for k in ("tile16", "tile64", "mx128")), sorted(tied_functions)
 
 
 def test_tied_kernels_keep_mfma_hazards(tied_functions):

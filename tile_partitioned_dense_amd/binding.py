@@ -67,7 +67,7 @@ def DEBUG_GROUP_M(g: int) -> int:
 
 
 N_TILE_CONFIGS = 28
-N_MX_CONFIGS = 6
+N_MX_CONFIGS = 7
 MX_E4M3 = 0
 MX_E2M1 = 1
 N_SKINNY_CONFIGS = 6

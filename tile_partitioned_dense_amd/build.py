@@ -28,7 +28,7 @@ ARCH = "gfx950"
 
 N_TILE_CONFIGS = 28
 N_SKINNY_CONFIGS = 6
-N_MX_CONFIGS = 6
+N_MX_CONFIGS = 7
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

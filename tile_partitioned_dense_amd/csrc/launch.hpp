@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include "ksplit_kernel.hpp"
+#include "mx128_kernel.hpp"
 #include "mx_kernel.hpp"
 #include "mx_stream_kernel.hpp"
 #include "skinny_kernel.hpp"

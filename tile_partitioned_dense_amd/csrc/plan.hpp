@@ -134,8 +134,9 @@ struct MxConfig {
   float eff;
   int sb = 0;  // stream kernel: bytes of K per row and stage; 0: tile kernel
   int ks = 1;  // stream kernel: waves per 32-column block (each a share of every stage's K)
+  int rb = 64;  // tile kernel: bytes per row and stage (128: two slabs, mx128_kernel.hpp)
 };
-constexpr int kNumMxConfigs = 6;
+constexpr int kNumMxConfigs = 7;
 constexpr MxConfig kMxConfigs[kNumMxConfigs] = {
     {256, 256, 2, 2, 4, 1.00f},  // 0: 4 waves of 128x128
     {128, 128, 2, 2, 4, 0.70f},  // 1: 4 waves of 64x64
@@ -147,6 +148,10 @@ constexpr MxConfig kMxConfigs[kNumMxConfigs] = {
     // 5: stream, 32 x 64 with stages of 512 bytes: twice the workgroups of
     // configuration 3, for outputs with few columns
     {32, 64, 1, 2, 3, 0.0f, 512, 2},
+    // 6: 4 waves of 128x128, 128-byte rows (two slabs per stage, two stages;
+    // 1.09 times configuration 0 on the MXFP8 MLP shard, 1.06 on MXFP4,
+    // interleaved in one process)
+    {256, 256, 2, 2, 2, 1.09f, 0, 1, 128},
 };
 constexpr int kMxBK = 64;          // bytes of K per row in one slab of the MX tile kernel
 constexpr int kMxStreamMaxM = 64;  // M at or below this takes the stream kernel
@@ -281,7 +286,7 @@ inline Plan plan_for_mx(int config, int64_t M, int64_t N, int cu_count) {
   p.config = config;
   p.bm = c.bm;
   p.bn = c.bn;
-  p.bk = c.sb ? c.sb : kMxBK;
+  p.bk = c.sb ? c.sb : c.rb;
   p.threads = c.wm * c.wn * c.ks * 64;
   p.lds_bytes = c.stages * (c.bm + c.bn) * p.bk;
   p.k_split = 1;

@@ -120,10 +120,11 @@ hipError_t dispatch_mx(int cfg, const tg::MxArgs& a, int fmt, int64_t grid, cons
     case 3: return tg::launch_mx<3>(a, fmt, grid, v, st);
     case 4: return tg::launch_mx<4>(a, fmt, grid, v, st);
     case 5: return tg::launch_mx<5>(a, fmt, grid, v, st);
+    case 6: return tg::launch_mx<6>(a, fmt, grid, v, st);
   }
   return hipErrorInvalidValue;
 }
-static_assert(tg::kNumMxConfigs == 6, "dispatch_mx covers every MX configuration");
+static_assert(tg::kNumMxConfigs == 7, "dispatch_mx covers every MX configuration");
 
 tile_gemm_status_t run_mx_impl(tile_gemm_t h, const void* A, const void* B, void* C, int64_t M,
                                int64_t N, int64_t K, const tile_gemm_strides_t* s, const void* sa,
