@@ -75,8 +75,10 @@ def test_expected_plans_for_workloads():
     W = synth.WORKLOADS
     p = tg.tile_gemm_plan(W["qkv_shard"].M, W["qkv_shard"].N, W["qkv_shard"].K, False, CU)
     assert (p.variant, p.bm, p.bn, p.tiles, p.grid) == (tg.VARIANT_TILE, 256, 160, 256, 256)
-    p = tg.tile_gemm_plan(8192, 7168, 8192, True, CU)     # 32 x 28 tiles, 4 rounds of 224
-    assert (p.variant, p.bm, p.bn, p.tiles, p.grid) == (tg.VARIANT_TILE, 256, 256, 896, 224)
+    # 256 x 224 tiles: 32 x 32 = 1024 tiles, 4 rounds of all 256 compute units
+    # (256 x 256 tiles would be 4 rounds of 224)
+    p = tg.tile_gemm_plan(8192, 7168, 8192, True, CU)
+    assert (p.variant, p.bm, p.bn, p.tiles, p.grid) == (tg.VARIANT_TILE, 256, 224, 1024, 256)
     p = tg.tile_gemm_plan(4096, 4096, 4096, False, CU)
     assert (p.variant, p.bm, p.bn, p.tiles, p.grid) == (tg.VARIANT_TILE, 256, 256, 256, 256)
     p = tg.tile_gemm_plan(16, 28672, 8192, False, CU)

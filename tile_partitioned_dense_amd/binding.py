@@ -66,7 +66,7 @@ def DEBUG_GROUP_M(g: int) -> int:
     return (g & 0x3F) << 2
 
 
-N_TILE_CONFIGS = 28
+N_TILE_CONFIGS = 29
 N_MX_CONFIGS = 7
 MX_E4M3 = 0
 MX_E2M1 = 1

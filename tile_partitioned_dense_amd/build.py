@@ -26,7 +26,7 @@ PROBES_LIB = os.path.join(PKG, "libtile_probes.so")   # measurement probes, not 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-N_TILE_CONFIGS = 28
+N_TILE_CONFIGS = 29
 N_SKINNY_CONFIGS = 6
 N_MX_CONFIGS = 7
 

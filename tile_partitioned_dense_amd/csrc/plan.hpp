@@ -64,7 +64,7 @@ inline double tile_eff(const TileConfig& c, int64_t per_cu) {
   return e1 + (c.eff - e1) * (double)(n - 1) / (double)(c.occ - 1);
 }
 
-constexpr int kNumTileConfigs = 28;
+constexpr int kNumTileConfigs = 29;
 constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
     {256, 256, 2, 2, 4, 0.94f},  // 0: 4 waves of 128x128
     {256, 224, 4, 1, 5, 0.85f},  // 1: 4 waves of 64x224
@@ -109,6 +109,10 @@ constexpr TileConfig kTileConfigs[kNumTileConfigs] = {
     // per CU level with configuration 17, which keeps those shapes
     {256, 256, 2, 2, 2, 1.19f, 1, 1.08f, 1, 0, 16, 64},  // 26: 4 waves of 128x128
     {256, 160, 2, 2, 2, 1.04f, 1, 1.05f, 1, 0, 16, 64},  // 27: 4 waves of 128x80
+    // 28: 256 x 224 (a 7168-wide output splits into 32 columns of tiles, 1024
+    // tiles fill four rounds of all 256 compute units where 256 x 256 tiles
+    // leave 32 of them idle)
+    {256, 224, 2, 2, 2, 1.15f, 1, 1.07f, 1, 0, 16, 64},  // 28: 4 waves of 128x112
 };
 constexpr int kStreamConfig = 14;      // the planner's stream configuration up to 32 rows,
 constexpr int kStreamConfig64 = 15;    // from 33 to 64 rows,

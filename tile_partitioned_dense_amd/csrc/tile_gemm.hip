@@ -92,10 +92,11 @@ hipError_t dispatch_tile(int cfg, const tg::TileArgs& a, int64_t grid, const tg:
     case 25: return tg::launch_tile<25>(a, grid, v, st);
     case 26: return tg::launch_tile<26>(a, grid, v, st);
     case 27: return tg::launch_tile<27>(a, grid, v, st);
+    case 28: return tg::launch_tile<28>(a, grid, v, st);
   }
   return hipErrorInvalidValue;
 }
-static_assert(tg::kNumTileConfigs == 28, "dispatch_tile covers every tile configuration");
+static_assert(tg::kNumTileConfigs == 29, "dispatch_tile covers every tile configuration");
 
 hipError_t dispatch_skinny(int cfg, const tg::SkinnyArgs& a, int64_t grid, const tg::Variant& v,
                            hipStream_t st) {
