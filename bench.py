@@ -357,7 +357,7 @@ def time_mx_workload(b, w, steps, warmup):
     est = w0.elapsed_time(w1) * 1e-3 / max(warmup, 1)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
-    plan = b.tg.tile_gemm_plan_mx(w.M, w.N, w.K, CU_COUNT)
+    plan = b.tg.tile_gemm_plan_mx(w.M, w.N, w.K, fmt, CU_COUNT)
     with b.clock(0.7 * est * steps, plan.grid):
         t0 = time.perf_counter()
         for i in range(steps):

@@ -323,9 +323,11 @@ typedef struct {
 tile_gemm_status_t tile_gemm_plan(int64_t M, int64_t N, int64_t K, int b_col_major,
                                   int cu_count, tile_gemm_plan_t* out);
 
-/* The plan of tile_gemm_run_mx for a shape (variant TILE_GEMM_VARIANT_MX). */
-tile_gemm_status_t tile_gemm_plan_mx(int64_t M, int64_t N, int64_t K, int cu_count,
-                                     tile_gemm_plan_t* out);
+/* The plan of tile_gemm_run_mx for a shape and element format (variant
+ * TILE_GEMM_VARIANT_MX; the configurations rank differently for E4M3 and
+ * E2M1). An unknown fmt is TILE_GEMM_ERR_DTYPE. */
+tile_gemm_status_t tile_gemm_plan_mx(int64_t M, int64_t N, int64_t K, tile_gemm_mx_format_t fmt,
+                                     int cu_count, tile_gemm_plan_t* out);
 
 /*
  * Tile number `wg` (0 <= wg < plan->tiles) under `plan`: rows [m0, m0 + rows)

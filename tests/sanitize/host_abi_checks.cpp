@@ -78,11 +78,13 @@ void plans() {
             require(known(s), "plan: unknown status", M, N, K);
             if (s == TILE_GEMM_OK && M > 0 && N > 0 && M <= 65536 && N <= 65536) check_map(p, M, N);
           }
-          tile_gemm_plan_t p;
-          const tile_gemm_status_t s = tile_gemm_plan_mx(M, N, K, cu, &p);
-          ++g_calls;
-          require(known(s), "plan_mx: unknown status", M, N, K);
-          if (s == TILE_GEMM_OK && M > 0 && N > 0 && M <= 65536 && N <= 65536) check_map(p, M, N);
+          for (int fmt = -1; fmt < 3; ++fmt) {
+            tile_gemm_plan_t p;
+            const tile_gemm_status_t s = tile_gemm_plan_mx(M, N, K, (tile_gemm_mx_format_t)fmt, cu, &p);
+            ++g_calls;
+            require(known(s), "plan_mx: unknown status", M, N, K);
+            if (s == TILE_GEMM_OK && M > 0 && N > 0 && M <= 65536 && N <= 65536) check_map(p, M, N);
+          }
         }
       }
   require(tile_gemm_plan(16, 16, 16, 0, 256, nullptr) == TILE_GEMM_ERR_NULL_ARG, "plan: NULL out");

@@ -56,6 +56,13 @@ def mx_stream_configs():
             if len(r) > 6 and int(r[6]) > 0]
 
 
+def mx_k_unit(cfg, fmt):
+    """K values per slab of a configuration: 128 for E2M1 and for the
+    16x16x128 configurations (their K steps), else 64."""
+    r = _mx_config_rows()[cfg]
+    return 128 if fmt == "e2m1" or (len(r) > 9 and int(r[9]) == 16) else 64
+
+
 FMTS = {"e4m3": tg.MX_E4M3, "e2m1": tg.MX_E2M1}
 
 
@@ -126,7 +133,7 @@ def test_mx_configs(g, fmt, cfg, slabs):
     the LDS scale windows."""
     bm, bn = mx_config_table()[cfg]
     M, N = 2 * bm + 37, 2 * bn + 19
-    K = slabs * (128 if fmt == "e2m1" else 64)
+    K = slabs * mx_k_unit(cfg, fmt)
     print(f"[mx {fmt} cfg {cfg} {M}x{N}x{K}]", flush=True)
     _run_and_check(g, MxCase(M, N, K, seed=cfg * 10 + slabs, fmt=fmt), tg.DEBUG_FORCE_TILE(cfg),
                    label=f"{fmt} cfg {cfg}")
@@ -152,7 +159,7 @@ def test_mx_configs_scaled_integer_exact(g, fmt, cfg):
     and columns plus ragged edges."""
     bm, bn = mx_config_table()[cfg]
     M, N = 2 * bm + 37, 2 * bn + 19
-    K = 19 * (128 if fmt == "e2m1" else 64)
+    K = 19 * mx_k_unit(cfg, fmt)
     print(f"[mx scaled int {fmt} cfg {cfg} {M}x{N}x{K}]", flush=True)
     case = MxCase(M, N, K, dist="int3", seed=80 + cfg, fmt=fmt, varied_scales=True)
     _run_and_check(g, case, tg.DEBUG_FORCE_TILE(cfg), integer=True,
@@ -288,3 +295,17 @@ def test_mx_workload_sampled(g, name):
         rep = oracle.mx.check_mx(out[ii, jj], c, t, out_bf16=dt == torch.bfloat16)
         assert rep.ok, f"{name} {dt}: {rep}"
         del C
+
+
+def test_mx_16x16_configuration_rejects_k_not_a_multiple_of_128(g):
+    """The 16x16x128 configurations take K in steps of 128; forced onto an
+    E4M3 product whose K is only a multiple of 64 they refuse it (the
+    planner never picks them for such a K)."""
+    cfg = next(i for i, r in enumerate(_mx_config_rows()) if len(r) > 9 and int(r[9]) == 16)
+    case = MxCase(300, 260, 192, seed=7)
+    _, out = case.out(torch.float32)
+    with pytest.raises(tg.TileGemmError) as e:
+        g.mx(case.A_dev, case.Bt_dev, out, case.sA_dev, case.sB_dev, flags=tg.DEBUG_FORCE_TILE(cfg))
+    assert "multiple of 128" in str(e.value)
+    p = tg.tile_gemm_plan_mx(300, 7168, 192, tg.MX_E4M3)
+    assert p.config != cfg

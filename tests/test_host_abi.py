@@ -218,11 +218,20 @@ def test_check_mx(kw, want):
 
 
 def test_mx_plan():
-    """The MX MLP shard: 256 x 256 tiles of the 128-byte-row kernel
-    (configuration 6, two slabs of 64 bytes per stage row)."""
-    p = tg.tile_gemm_plan_mx(8192, 7168, 8192)
-    assert p.variant == tg.VARIANT_MX and p.config == 6 and p.bm == 256 and p.bn == 256 and p.bk == 128
+    """The MX MLP shard. E4M3: 256 x 224 tiles on 16x16x128 blocks
+    (configuration 7), 1024 tiles in four rounds of all 256 compute units.
+    E2M1: 256 x 256 tiles of the 128-byte-row 32x32x64 kernel (configuration
+    6), where the 16x16 form measured slower. An unknown format is refused."""
+    p = tg.tile_gemm_plan_mx(8192, 7168, 8192, tg.MX_E4M3)
+    assert p.variant == tg.VARIANT_MX and p.config == 7 and (p.bm, p.bn, p.bk) == (256, 224, 128)
+    assert p.tiles == 32 * 32 and p.grid == 256
+    p = tg.tile_gemm_plan_mx(8192, 7168, 8192, tg.MX_E2M1)
+    assert p.variant == tg.VARIANT_MX and p.config == 6 and (p.bm, p.bn, p.bk) == (256, 256, 128)
     assert p.tiles == 32 * 28 and p.grid == 224
+    # a K that is not a multiple of 128 keeps E4M3 off the 16x16x128 blocks
+    assert tg.tile_gemm_plan_mx(8192, 7168, 8192 + 64, tg.MX_E4M3).config == 6
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan_mx(8192, 7168, 8192, 7)
 
 
 def test_mx_plan_few_rows_take_the_stream_kernel():

@@ -1,6 +1,6 @@
 """Hazard check of the built kernels whose MFMAs are written out with tied
 accumulators (the one-wave-per-SIMD tile kernels, mma16<true>, and the
-128-byte-row MX kernel, mma_mx_tied).
+128-byte-row MX kernels, mma_mx_tied and mma16_mx_tied).
 
 The compiler inserts the wait states an MFMA needs only around MFMAs it
 generated itself; around a written-out one the kernel keeps them: a vector
@@ -24,7 +24,7 @@ import pytest
 from tile_partitioned_dense_amd import binding
 
 LLVM = "/opt/rocm/llvm/bin"
-TIED_KERNEL = re.compile(r"^_ZN2tg(?:1[68]tile(16|64)|17mx128)_gemm_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E")
+TIED_KERNEL = re.compile(r"^_ZN2tg(?:1[68]tile(16|64)|17mx128|16mx16)_gemm_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E")
 REG = re.compile(r"\b([va])(?:\[(\d+):(\d+)\]|(\d+)(?!\d))")
 VALU_WRITE_BEFORE_MFMA = 2
 MFMA_RESULT_LATENCY = {"16x16": 19, "32x32": 24}
@@ -206,7 +206,7 @@ def test_tied_kernels_are_present(tied_functions):
     # the one-wave-per-SIMD configurations of both tile kernels and the
     # 128-byte-row MX kernel, every variant
     bits = {n.split("kernel")[0] for n in tied_functions}
-    assert all(any(k in b for b in bits) for k in ("tile16", "tile64", "mx128")), sorted(tied_functions)
+    assert all(any(k in b for b in bits) for k in ("tile16", "tile64", "mx128", "mx16_")), sorted(tied_functions)
 
 
 def test_tied_kernels_keep_mfma_hazards(tied_functions):

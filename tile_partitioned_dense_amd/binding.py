@@ -67,7 +67,7 @@ def DEBUG_GROUP_M(g: int) -> int:
 
 
 N_TILE_CONFIGS = 29
-N_MX_CONFIGS = 7
+N_MX_CONFIGS = 8
 MX_E4M3 = 0
 MX_E2M1 = 1
 N_SKINNY_CONFIGS = 6
@@ -140,7 +140,7 @@ def load_library():
     lib.tile_gemm_check_args.restype = i32
     lib.tile_gemm_plan.argtypes = [i64, i64, i64, i32, i32, P(Plan)]
     lib.tile_gemm_plan.restype = i32
-    lib.tile_gemm_plan_mx.argtypes = [i64, i64, i64, i32, P(Plan)]
+    lib.tile_gemm_plan_mx.argtypes = [i64, i64, i64, i32, i32, P(Plan)]
     lib.tile_gemm_plan_mx.restype = i32
     lib.tile_gemm_run_mx.argtypes = [vp, vp, vp, vp, i64, i64, i64, P(Strides), vp, vp, i64, i32,
                                      i32, vp, i32, vp]
@@ -392,9 +392,10 @@ def tile_gemm_check_mx(A, B, C, M, N, K, strides, a_scale, b_scale, scale_stride
                                                     int(dtype), bias, int(act)))
 
 
-def tile_gemm_plan_mx(M, N, K, cu_count=256) -> Plan:
+def tile_gemm_plan_mx(M, N, K, fmt=0, cu_count=256) -> Plan:
     p = Plan()
-    _raise_if(load_library().tile_gemm_plan_mx(int(M), int(N), int(K), int(cu_count), ctypes.byref(p)))
+    _raise_if(load_library().tile_gemm_plan_mx(int(M), int(N), int(K), int(fmt), int(cu_count),
+                                               ctypes.byref(p)))
     return p
 
 

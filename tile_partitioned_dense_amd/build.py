@@ -28,7 +28,7 @@ ARCH = "gfx950"
 
 N_TILE_CONFIGS = 29
 N_SKINNY_CONFIGS = 6
-N_MX_CONFIGS = 7
+N_MX_CONFIGS = 8
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -328,14 +328,16 @@ tile_gemm_status_t tile_gemm_check_mx(const void* A, const void* B, const void* 
                   bias, (int)act);
 }
 
-tile_gemm_status_t tile_gemm_plan_mx(int64_t M, int64_t N, int64_t K, int cu_count,
-                                     tile_gemm_plan_t* out) {
+tile_gemm_status_t tile_gemm_plan_mx(int64_t M, int64_t N, int64_t K, tile_gemm_mx_format_t fmt,
+                                     int cu_count, tile_gemm_plan_t* out) {
   g_detail[0] = '\0';
   if (!out) return fail(TILE_GEMM_ERR_NULL_ARG, "out: NULL");
   if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
     return fail(TILE_GEMM_ERR_BAD_SHAPE, "shape out of range");
+  if (fmt != TILE_GEMM_MX_E4M3 && fmt != TILE_GEMM_MX_E2M1)
+    return fail(TILE_GEMM_ERR_DTYPE, "fmt: unknown MX format %d", (int)fmt);
   if (cu_count <= 0) return fail(TILE_GEMM_ERR_DEVICE, "cu_count: %d", cu_count);
-  fill_plan(tg::make_plan_mx(M, N, K, cu_count), out);
+  fill_plan(tg::make_plan_mx(M, N, K, fmt == TILE_GEMM_MX_E2M1, cu_count), out);
   return TILE_GEMM_OK;
 }
 

@@ -14,6 +14,8 @@ const void* mx_fn() {
   constexpr MxConfig c = kMxConfigs[CFG];
   if constexpr (c.sb > 0)
     return reinterpret_cast<const void*>(&mx_stream_kernel<c.bm, c.bn, c.sb, c.stages, c.ks, FMT, OB, DB>);
+  else if constexpr (c.mi == 16)
+    return reinterpret_cast<const void*>(&mx16_gemm_kernel<c.bm, c.bn, c.wm, c.wn, FMT, OB, DB>);
   else if constexpr (c.rb == 128)
     return reinterpret_cast<const void*>(&mx128_gemm_kernel<c.bm, c.bn, c.wm, c.wn, FMT, OB, DB>);
   else

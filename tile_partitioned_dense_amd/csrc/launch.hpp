@@ -7,6 +7,7 @@
 
 #include "ksplit_kernel.hpp"
 #include "mx128_kernel.hpp"
+#include "mx16_kernel.hpp"
 #include "mx_kernel.hpp"
 #include "mx_stream_kernel.hpp"
 #include "skinny_kernel.hpp"

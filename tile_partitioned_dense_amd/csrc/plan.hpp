@@ -139,8 +139,11 @@ struct MxConfig {
   int sb = 0;  // stream kernel: bytes of K per row and stage; 0: tile kernel
   int ks = 1;  // stream kernel: waves per 32-column block (each a share of every stage's K)
   int rb = 64;  // tile kernel: bytes per row and stage (128: two slabs, mx128_kernel.hpp)
+  int mi = 32;  // tile kernel: MFMA block, 32 (32x32x64) or 16 (16x16x128, mx16_kernel.hpp;
+                // K a multiple of 128)
+  float eff4 = 0.0f;  // tile kernel: rate with E2M1 elements (0: eff)
 };
-constexpr int kNumMxConfigs = 7;
+constexpr int kNumMxConfigs = 8;
 constexpr MxConfig kMxConfigs[kNumMxConfigs] = {
     {256, 256, 2, 2, 4, 1.00f},  // 0: 4 waves of 128x128
     {128, 128, 2, 2, 4, 0.70f},  // 1: 4 waves of 64x64
@@ -155,7 +158,13 @@ constexpr MxConfig kMxConfigs[kNumMxConfigs] = {
     // 6: 4 waves of 128x128, 128-byte rows (two slabs per stage, two stages;
     // 1.09 times configuration 0 on the MXFP8 MLP shard, 1.06 on MXFP4,
     // interleaved in one process)
-    {256, 256, 2, 2, 2, 1.09f, 0, 1, 128},
+    {256, 256, 2, 2, 2, 1.09f, 0, 1, 128, 32, 1.06f},
+    // 7: 4 waves of 128x112 on 16x16x128 blocks, 128-byte rows (one E4M3 or
+    // two E2M1 K steps per stage, two stages): 256 x 224 tiles fill all
+    // compute units on a 7168-wide output. Per compute unit 0.92 times
+    // configuration 6 with E4M3 (the MLP shard's launch 3-6% shorter) and 0.83
+    // times with E2M1 (6% longer), interleaved in one process.
+    {256, 224, 2, 2, 2, 1.00f, 0, 1, 128, 16, 0.88f},
 };
 constexpr int kMxBK = 64;          // bytes of K per row in one slab of the MX tile kernel
 constexpr int kMxStreamMaxM = 64;  // M at or below this takes the stream kernel
@@ -306,9 +315,8 @@ inline Plan plan_for_mx(int config, int64_t M, int64_t N, int cu_count) {
 // MX plan: outputs of at most kMxStreamMaxM rows stream B through the
 // stream kernel (one tile row of 32 or 64 rows); otherwise the tile-kernel configuration
 // minimising (tiles on the busiest CU) x (tile area) / rate, as for the bf16
-// tile kernel.
-inline Plan make_plan_mx(int64_t M, int64_t N, int64_t K, int cu_count) {
-  (void)K;
+// tile kernel, with the rate of the element format (fp4: E2M1).
+inline Plan make_plan_mx(int64_t M, int64_t N, int64_t K, bool fp4, int cu_count) {
   if (M <= 0 || N <= 0) return plan_for(0, 0, M, N, cu_count);
   if (M <= kMxStreamMaxM) {
     // up to 32 rows: 128-column tiles, or 64-column ones when those would
@@ -320,9 +328,10 @@ inline Plan make_plan_mx(int64_t M, int64_t N, int64_t K, int cu_count) {
   double best_cost = 0.0;
   for (int i = 0; i < kNumMxConfigs; ++i) {
     const MxConfig& c = kMxConfigs[i];
-    if (c.sb) continue;
+    if (c.sb || (c.mi == 16 && K % 128 != 0)) continue;
     const int64_t per_cu = ceil_div(ceil_div(M, c.bm) * ceil_div(N, c.bn), cu_count);
-    const double cost = (double)per_cu * c.bm * c.bn / c.eff;
+    const float eff = (fp4 && c.eff4 > 0.0f) ? c.eff4 : c.eff;
+    const double cost = (double)per_cu * c.bm * c.bn / eff;
     if (i == 0 || cost < best_cost * 0.999) {
       best = i;
       best_cost = cost;

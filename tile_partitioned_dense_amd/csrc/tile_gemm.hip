@@ -122,10 +122,11 @@ hipError_t dispatch_mx(int cfg, const tg::MxArgs& a, int fmt, int64_t grid, cons
     case 4: return tg::launch_mx<4>(a, fmt, grid, v, st);
     case 5: return tg::launch_mx<5>(a, fmt, grid, v, st);
     case 6: return tg::launch_mx<6>(a, fmt, grid, v, st);
+    case 7: return tg::launch_mx<7>(a, fmt, grid, v, st);
   }
   return hipErrorInvalidValue;
 }
-static_assert(tg::kNumMxConfigs == 7, "dispatch_mx covers every MX configuration");
+static_assert(tg::kNumMxConfigs == 8, "dispatch_mx covers every MX configuration");
 
 tile_gemm_status_t run_mx_impl(tile_gemm_t h, const void* A, const void* B, void* C, int64_t M,
                                int64_t N, int64_t K, const tile_gemm_strides_t* s, const void* sa,
@@ -143,11 +144,14 @@ tile_gemm_status_t run_mx_impl(tile_gemm_t h, const void* A, const void* B, void
                 h->device);
   if ((flags & TILE_GEMM_DEBUG_COUNT_WRITES) && !counts)
     return fail(TILE_GEMM_ERR_NULL_ARG, "counts: NULL with TILE_GEMM_DEBUG_COUNT_WRITES");
-  tg::Plan p = tg::make_plan_mx(M, N, K, h->cu_count);
+  tg::Plan p = tg::make_plan_mx(M, N, K, fmt == TILE_GEMM_MX_E2M1, h->cu_count);
   const int force = (flags >> 8) & 0xff;
   if (force) {
     if (force > tg::kNumMxConfigs)
       return fail(TILE_GEMM_ERR_BAD_SHAPE, "debug: no MX configuration %d", force - 1);
+    if (tg::kMxConfigs[force - 1].mi == 16 && K % 128 != 0)
+      return fail(TILE_GEMM_ERR_BAD_SHAPE, "debug: MX configuration %d needs K a multiple of 128",
+                  force - 1);
     p = tg::plan_for_mx(force - 1, M, N, h->cu_count);
   }
   const int force_grid = (flags >> 24) & 0x7f;
