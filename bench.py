@@ -451,9 +451,11 @@ def run_probes(torch, clock):
     mfma = []
     for shape, sname in ((0, "v_mfma_f32_32x32x16_bf16"), (1, "v_mfma_f32_16x16x32_bf16"),
                          (2, "v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3)"),
-                         (3, "v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3)")):
+                         (3, "v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3)"),
+                         (4, "v_mfma_scale_f32_32x32x64_f8f6f4 (E2M1)"),
+                         (5, "v_mfma_scale_f32_16x16x128_f8f6f4 (E2M1)")):
         f8 = shape >= 2
-        peak = PEAK_FP8_TFLOPS if f8 else PEAK_BF16_TFLOPS
+        peak = PEAK_FP4_TFLOPS if shape >= 4 else PEAK_FP8_TFLOPS if f8 else PEAK_BF16_TFLOPS
         for wps in (1, 2):
             for data, src in (("random N(0,1)", rnd), ("constant 1.0", const)):
                 iters = (1200 if f8 else 2400) // wps

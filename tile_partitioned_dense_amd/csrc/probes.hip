@@ -76,12 +76,13 @@ __global__ __launch_bounds__(512) void mfma_probe(const u32x4* __restrict__ src,
   out[blockIdx.x * blockDim.x + threadIdx.x] = total;
 }
 
-// As mfma_probe for the block-scaled E4M3 forms (SHAPE 0: 32x32x64, 1:
-// 16x16x128): 32-byte fragments (kF8Ops per side, so that fragments and
-// accumulators fit the registers of two waves per SIMD without spilling),
-// every scale byte 127 (a factor of 1).
+// As mfma_probe for the block-scaled forms (SHAPE 0: 32x32x64, 1:
+// 16x16x128) with E4M3 (FMT 0) or E2M1 (FMT 4: the first 16 bytes of each
+// fragment) elements: 32-byte fragments (kF8Ops per side, so that fragments
+// and accumulators fit the registers of two waves per SIMD without
+// spilling), every scale byte 127 (a factor of 1).
 constexpr int kF8Ops = 4;
-template <int SHAPE>
+template <int SHAPE, int FMT>
 __global__ __launch_bounds__(512) void mfma_probe_f8(const u32x4* __restrict__ src, float* __restrict__ out,
                                                     int iters) {
   const int lane = threadIdx.x & 63;
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(512) void mfma_probe_f8(const u32x4* __restrict__ s
 #pragma unroll
         for (int i = 0; i < kOps; ++i)
           acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[(i + j) % kF8Ops], b[(3 * i + j) % kF8Ops],
-                                                                   acc[i], 0, 0, 0, kScale, 0, kScale);
+                                                                   acc[i], FMT, FMT, 0, kScale, 0, kScale);
     }
 #pragma unroll
     for (int i = 0; i < kOps; ++i)
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(512) void mfma_probe_f8(const u32x4* __restrict__ s
 #pragma unroll
         for (int i = 0; i < 2 * kOps; ++i)
           acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[(i + j) % kF8Ops], b[(3 * i + j) % kF8Ops],
-                                                                    acc[i], 0, 0, 0, kScale, 0, kScale);
+                                                                    acc[i], FMT, FMT, 0, kScale, 0, kScale);
     }
 #pragma unroll
     for (int i = 0; i < 2 * kOps; ++i)
@@ -205,15 +206,16 @@ int tg_probe_clock(unsigned long long* out, long long ticks, void* stream) {
 
 // Launch the MFMA probe: `grid` workgroups of 4 * waves_per_simd waves (one
 // workgroup per compute unit when grid = CU count), shape 0 = 32x32x16 bf16,
-// 1 = 16x16x32 bf16, 2 = 32x32x64 scaled E4M3, 3 = 16x16x128 scaled E4M3.
+// 1 = 16x16x32 bf16, 2 = 32x32x64 scaled E4M3, 3 = 16x16x128 scaled E4M3,
+// 4 = 32x32x64 scaled E2M1, 5 = 16x16x128 scaled E2M1.
 // `src` holds at least grid * 4 * waves_per_simd * 16 KiB of operand bytes,
 // `out` grid * 256 * waves_per_simd floats.
 // Returns a hipError_t. FLOP per launch: waves * iters * 64 * 32768 for the
-// bf16 shapes, four times that for the E4M3 ones (the 16x16 forms issue twice
-// the instructions of half the size).
+// bf16 shapes, four times that for the scaled ones (the 16x16 forms issue
+// twice the instructions of half the size).
 int tg_probe_mfma(const void* src, float* out, int grid, int waves_per_simd, int shape, int iters,
                   void* stream) {
-  if (grid <= 0 || (waves_per_simd != 1 && waves_per_simd != 2) || shape < 0 || shape > 3 ||
+  if (grid <= 0 || (waves_per_simd != 1 && waves_per_simd != 2) || shape < 0 || shape > 5 ||
       iters <= 0)
     return (int)hipErrorInvalidValue;
   const dim3 block(256 * waves_per_simd);
@@ -225,11 +227,17 @@ int tg_probe_mfma(const void* src, float* out, int grid, int waves_per_simd, int
     hipLaunchKernelGGL(mfma_probe<1>, dim3(grid), block, 0, st, static_cast<const u32x4*>(src), out,
                        iters);
   else if (shape == 2)
-    hipLaunchKernelGGL(mfma_probe_f8<0>, dim3(grid), block, 0, st, static_cast<const u32x4*>(src), out,
-                       iters);
+    hipLaunchKernelGGL((mfma_probe_f8<0, 0>), dim3(grid), block, 0, st, static_cast<const u32x4*>(src),
+                       out, iters);
+  else if (shape == 3)
+    hipLaunchKernelGGL((mfma_probe_f8<1, 0>), dim3(grid), block, 0, st, static_cast<const u32x4*>(src),
+                       out, iters);
+  else if (shape == 4)
+    hipLaunchKernelGGL((mfma_probe_f8<0, 4>), dim3(grid), block, 0, st, static_cast<const u32x4*>(src),
+                       out, iters);
   else
-    hipLaunchKernelGGL(mfma_probe_f8<1>, dim3(grid), block, 0, st, static_cast<const u32x4*>(src), out,
-                       iters);
+    hipLaunchKernelGGL((mfma_probe_f8<1, 4>), dim3(grid), block, 0, st, static_cast<const u32x4*>(src),
+                       out, iters);
   return (int)hipGetLastError();
 }
 
