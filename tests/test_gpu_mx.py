@@ -242,6 +242,29 @@ def test_mx_fused_epilogue(g, M):
             assert rep.ok, f"{act.name} {dt}: {rep}"
 
 
+@pytest.mark.parametrize("fmt", sorted(FMTS))
+@pytest.mark.parametrize("cfg", [i for i, r in enumerate(_mx_config_rows()) if not (len(r) > 6 and int(r[6]) > 0)])
+def test_mx_fused_epilogue_every_tile_config(g, fmt, cfg):
+    """bias + activation in the store of every MX tile configuration (forced),
+    ragged in both dimensions, against the oracle's epilogue."""
+    bm, bn = mx_config_table()[cfg]
+    case = MxCase(bm + 37, bn + 19, 4 * mx_k_unit(cfg, fmt), seed=70 + cfg, fmt=fmt,
+                  b_scale=512 ** -0.5)
+    print(f"[mx epilogue {fmt} cfg {cfg} {case.M}x{case.N}x{case.K}]", flush=True)
+    C, D = case.ref()
+    b = synth.draw_bias(case.N, 901)
+    bd = torch.from_numpy(b).cuda()
+    for act in (tg.Act.RELU, tg.Act.SILU):
+        for dt in (torch.float32, torch.bfloat16):
+            _, out = case.out(dt)
+            g.mx(case.A_dev, case.Bt_dev, out, case.sA_dev, case.sB_dev, bias=bd, act=act,
+                 flags=tg.DEBUG_FORCE_TILE(cfg), fmt=FMTS[fmt])
+            torch.cuda.synchronize()
+            rep = oracle.check_epilogue(host_out(out), C, D, b, act.name.lower(),
+                                        out_bf16=dt == torch.bfloat16, tau=case.bound())
+            assert rep.ok, f"cfg {cfg} {fmt} {act.name} {dt}: {rep}"
+
+
 def test_mx_deterministic_and_bf16_is_rne_of_fp32(g):
     case = MxCase(1024, 1024, 2048, seed=63)
     outs = []
