@@ -218,16 +218,16 @@ def test_check_mx(kw, want):
 
 
 def test_mx_plan():
-    """The MX MLP shard. E4M3: 256 x 224 tiles on 16x16x128 blocks
+    """The MX MLP shard, both formats: 256 x 224 tiles on 16x16x128 blocks
     (configuration 7), 1024 tiles in four rounds of all 256 compute units.
-    E2M1: 256 x 256 tiles of the 128-byte-row 32x32x64 kernel (configuration
-    6), where the 16x16 form measured slower. An unknown format is refused."""
-    p = tg.tile_gemm_plan_mx(8192, 7168, 8192, tg.MX_E4M3)
-    assert p.variant == tg.VARIANT_MX and p.config == 7 and (p.bm, p.bn, p.bk) == (256, 224, 128)
-    assert p.tiles == 32 * 32 and p.grid == 256
-    p = tg.tile_gemm_plan_mx(8192, 7168, 8192, tg.MX_E2M1)
-    assert p.variant == tg.VARIANT_MX and p.config == 6 and (p.bm, p.bn, p.bk) == (256, 256, 128)
-    assert p.tiles == 32 * 28 and p.grid == 224
+    At 4096^3 the 256 x 256 tiles of the 128-byte-row 32x32x64 kernel
+    (configuration 6) fill one round. An unknown format is refused."""
+    for fmt in (tg.MX_E4M3, tg.MX_E2M1):
+        p = tg.tile_gemm_plan_mx(8192, 7168, 8192, fmt)
+        assert p.variant == tg.VARIANT_MX and p.config == 7 and (p.bm, p.bn, p.bk) == (256, 224, 128)
+        assert p.tiles == 32 * 32 and p.grid == 256
+        p = tg.tile_gemm_plan_mx(4096, 4096, 4096, fmt)
+        assert p.config == 6 and (p.bm, p.bn, p.tiles) == (256, 256, 256)
     # a K that is not a multiple of 128 keeps E4M3 off the 16x16x128 blocks
     assert tg.tile_gemm_plan_mx(8192, 7168, 8192 + 64, tg.MX_E4M3).config == 6
     with pytest.raises(tg.TileGemmError):

@@ -46,16 +46,20 @@ namespace tg {
 
 // One scaled 16 x 16 x 128 step of a C block held transposed (lane l: row
 // l % 16, columns 4 (l / 16) .. + 3), the accumulator tied in place as in
-// mma_mx_tied, with the two wait states a vector write of an operand needs
-// before it. E4M3 operands are 8 registers, E2M1 operands 4.
+// mma_mx_tied. E4M3 operands are 8 registers, E2M1 operands 4. Unlike
+// mma_mx_tied it issues no wait states of its own (two per instruction cost
+// the 16-cycle E2M1 form 5% of its shard): the vector writes its operands
+// can follow are the scale shifts, which take_scales() ends with a wait, and
+// the accumulators' zeroing, which settle_tied(acc) ends; the hazard check
+// of the built code covers the rest.
 __device__ __forceinline__ void mma16_mx_tied(floatx4& acc, const i32x8& a_frag, const i32x8& b_frag,
                                               int a_scale, int b_scale) {
-  asm volatile("s_nop 1\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+  asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
                : "+a"(acc) : "v"(b_frag), "v"(a_frag), "v"(b_scale), "v"(a_scale));
 }
 __device__ __forceinline__ void mma16_mx_tied(floatx4& acc, const i32x4& a_half, const i32x4& b_half,
                                               int a_scale, int b_scale) {
-  asm volatile("s_nop 1\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+  asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
                : "+a"(acc) : "v"(b_half), "v"(a_half), "v"(b_scale), "v"(a_scale));
 }
 
@@ -191,6 +195,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx16_gemm_kernel(MxArgs p) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{};
+    settle_tied(acc);  // (the zeroing is a vector write of every MFMA's accumulator)
 
     // scale dwords of a stage's K steps (raw, then shifted to this lane's byte)
     uint32_t rsa[KH][FM], rsb[KH][FN];
@@ -218,6 +223,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void mx16_gemm_kernel(MxArgs p) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) scb[h][j] = (int)(rsb[h][j] >> sh);
       }
+      // every shift before one wait of two states, every MFMA after it
+#pragma unroll
+      for (int h = 0; h < KH; ++h) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(sca[h][i]));
+#pragma unroll
+        for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(scb[h][j]));
+      }
+      asm volatile("s_nop 1");
     };
     auto frag = [&](uint32_t row_base, int st, int blk) -> i32x8 {
       const uint32_t b = row_base + (uint32_t)(st * STAGE + blk * 16 * RB);
