@@ -111,6 +111,39 @@ def test_workgroups_owning_several_tiles(g, cfg, grid):
         assert rep.ok, rep
 
 
+@pytest.mark.parametrize("cfg", [26, 27, 28])
+@pytest.mark.parametrize("K", [512, 500])
+@pytest.mark.parametrize("bcol", [True, False])
+def test_one_wave_per_simd_tiles_several_per_workgroup(g, cfg, K, bcol):
+    """The one-wave-per-SIMD 64-deep configurations with several tiles per
+    workgroup (eight slabs, the last one through the register path when
+    K = 500): every element written once, exactly the one-tile-per-workgroup
+    result and the oracle's, for the plain store and for a fused bias + SiLU
+    (the steady loop, the slab-at-a-time tail and the store all run again for
+    each of a workgroup's tiles)."""
+    case = Case(700, 900, K, bcol, seed=60 + cfg, pad=8)
+    print(f"[several tiles one wave per SIMD cfg {cfg} K {K} bcol {bcol}]", flush=True)
+    Cr, Dr = case.ref()
+    for dt in (torch.float32, torch.bfloat16):
+        store, C, counts = _counts_run(g, case, dt, tg.DEBUG_COUNT_WRITES | tg.DEBUG_FORCE_TILE(cfg)
+                                       | tg.DEBUG_FORCE_GRID(3))
+        assert int(counts.min()) == 1 and int(counts.max()) == 1
+        assert torch.isnan(store[:, case.N:].float()).all()
+        _, C1, _ = _counts_run(g, case, dt, tg.DEBUG_FORCE_TILE(cfg) | tg.DEBUG_ONE_TILE_PER_WG)
+        assert torch.equal(_as_int(C), _as_int(C1))
+        rep = check(host_out(C), Cr, Dr, dt == torch.bfloat16, False)
+        assert rep.ok, rep
+        bias = torch.linspace(-1.0, 1.0, case.N, dtype=torch.float32, device="cuda")
+        outs = []
+        for fl in (tg.DEBUG_FORCE_GRID(3), tg.DEBUG_ONE_TILE_PER_WG):
+            _, Ce = case.out(dt)
+            g.run_debug(case.A_dev, case.B_dev, Ce, flags=tg.DEBUG_FORCE_TILE(cfg) | fl, bias=bias,
+                        act=tg.Act.SILU)
+            torch.cuda.synchronize()
+            outs.append(Ce)
+        assert torch.equal(_as_int(outs[0]), _as_int(outs[1]))
+
+
 def test_forced_grid_rejected_for_the_skinny_kernel(g):
     case = Case(16, 512, 64, False, seed=3)
     store, C = case.out(torch.float32)
