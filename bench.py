@@ -414,13 +414,15 @@ def measured_traffic(workload):
 
 
 def run_probes(torch, clock):
-    """The MFMA-rate and HBM streaming-read probes (csrc/probes.hip): the
-    ceilings the GEMM kernels meet on this machine, beside the published peaks."""
+    """The MFMA-rate, LDS-read and HBM streaming-read probes
+    (csrc/probes.hip): the ceilings the GEMM kernels meet on this machine, beside
+    the published peaks."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "tile_partitioned_dense_amd", "libtile_probes.so"))
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     lib.tg_probe_mfma.argtypes = [vp, vp, i32, i32, i32, i32, vp]
     lib.tg_probe_read.argtypes = [vp, vp, i64, i32, i32, vp]
+    lib.tg_probe_lds.argtypes = [vp, i32, i32, i32, vp]
     stream = torch.cuda.current_stream().cuda_stream
     grid = 256
     out = torch.empty(grid * 512, dtype=torch.float32, device="cuda")
@@ -488,7 +490,20 @@ def run_probes(torch, clock):
         log(f"[probe] read {read[-1]['pattern']} x{g}: {gbs:.0f} GB/s")
     del buf
     torch.cuda.empty_cache()
-    return {"mfma": mfma, "hbm_read": read}
+    lout = torch.empty(grid * 1024, dtype=torch.int32, device="cuda")
+    lds = []
+    for iters in (4096, 16384):
+        fn = lambda: lib.tg_probe_lds(lout.data_ptr(), grid, iters, 1024, stream)
+        t, clk = timed(fn, n=10)
+        nbytes = grid * 16 * iters * 8 * 1024
+        mhz = clk["shader_clock_mhz"]
+        per_cu_clk = nbytes / grid / (t * mhz * 1e6) if mhz else None
+        lds.append({"reads_per_wave": iters * 8, "bytes": nbytes, "launch_ms": round(t * 1e3, 3),
+                    "gbs": round(nbytes / t / 1e9, 1), "shader_clock_mhz": mhz,
+                    "bytes_per_cu_per_clock": round(per_cu_clk, 1) if per_cu_clk else None})
+        log(f"[probe] lds read x{iters * 8}/wave: {nbytes / t / 1e9:.0f} GB/s, "
+            f"{per_cu_clk if per_cu_clk else float('nan'):.1f} B per CU per clock at {mhz:.0f} MHz")
+    return {"mfma": mfma, "hbm_read": read, "lds_read": lds}
 
 
 def roofline(res, hbm_bound):

@@ -8,6 +8,7 @@
 //    and one or two waves per SIMD, for the 32x32x16 and 16x16x32 shapes,
 //    and of the block-scaled FP8 (E4M3) forms 32x32x64 and 16x16x128;
 //  * the rate at which HBM delivers a plain streaming read;
+//  * the rate at which a compute unit's LDS serves 16-byte reads;
 //  * the average shader clock over a window (a one-wave kernel beside the
 //    measured work).
 // Under sustained MFMA load the clock settles below the 2.4 GHz that the
@@ -192,6 +193,30 @@ __global__ __launch_bounds__(64) void clock_probe(unsigned long long* __restrict
 
 }  // namespace
 
+// LDS read rate: every wave of a 16-wave workgroup (one per compute unit)
+// reads 16-byte chunks of a 64 KiB LDS buffer, eight reads in flight at a
+// time, 64 consecutive chunks per wave-read (no bank conflicts); an empty asm
+// statement takes the values, so no read is dropped or narrowed and no vector
+// ALU work competes with the reads. `step` (in chunks, a kernel argument so
+// the addresses stay in the loop) spaces a wave's eight reads.
+__global__ __launch_bounds__(1024) void lds_probe(uint32_t* __restrict__ out, int iters, int step) {
+  __shared__ u32x4 buf[4096];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 4096; i += blockDim.x)
+    buf[i] = u32x4{(uint32_t)i, (uint32_t)(3 * i), (uint32_t)(5 * i), (uint32_t)(7 * i)};
+  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6;
+  int base = wave * 64 + lane;
+  for (int it = 0; it < iters; ++it) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = buf[(base + u * step) & 4095];
+    asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
+    base += 8 * step;
+  }
+  out[blockIdx.x * blockDim.x + tid] = (uint32_t)base;
+}
+
 extern "C" {
 
 // Launch the clock probe for `ticks` real-time ticks (at most 10^9; the
@@ -238,6 +263,15 @@ int tg_probe_mfma(const void* src, float* out, int grid, int waves_per_simd, int
   else
     hipLaunchKernelGGL((mfma_probe_f8<1, 4>), dim3(grid), block, 0, st, static_cast<const u32x4*>(src),
                        out, iters);
+  return (int)hipGetLastError();
+}
+
+// Launch the LDS probe: `grid` workgroups of 16 waves, each wave 8 * iters
+// reads of 1 KiB; `out` holds grid * 1024 uint32. Returns a hipError_t.
+int tg_probe_lds(uint32_t* out, int grid, int iters, int step, void* stream) {
+  if (grid <= 0 || iters <= 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(lds_probe, dim3(grid), dim3(1024), 0, static_cast<hipStream_t>(stream), out, iters,
+                     step);
   return (int)hipGetLastError();
 }
 
